@@ -1,0 +1,13 @@
+"""CPU oracle for the 1.58-bit linear layer (test infrastructure only).
+
+Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The GPU library never does.
+"""
+from .oracle import (  # noqa: F401
+    build,
+    library_path,
+    oracle_gemm,
+    oracle_pack,
+    oracle_quantize,
+    oracle_unpack,
+)

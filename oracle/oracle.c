@@ -1,0 +1,233 @@
+/*
+ * CPU oracle for the 1.58-bit linear layer: test infrastructure only.
+ *
+ * This file is the plain, slow reference that the GPU library is checked
+ * against.  Only the test suite, the smoke check and the CPU-baseline leg of
+ * the benchmark load it; the GPU library never does, and the two share no
+ * code, header, table or helper.  Everything here is scalar C with double
+ * accumulation, no SIMD intrinsics, no BLAS and no fast-math.
+ *
+ * What it computes, and where the definition comes from:
+ *
+ *  - Ternary weights in {-1, 0, +1}, BitNet-b1.58 style ("1.58-bit FLUX",
+ *    abstract and section 1 Introduction; section 2 Related Work names
+ *    BitNet b1.58).  The pages give no formula; the reading used is the
+ *    per-output-channel absmean rule s_n = mean_k |w_nk|,
+ *    T = clip(round(w / s_n), -1, 1) with round-half-to-even.
+ *  - Storage as 2-bit signed integers, four per byte ("1.58-bit FLUX",
+ *    section 1 Introduction, the storage paragraph).
+ *  - The layer output Y = (X . T^T) (.) s for unquantized bf16 activations
+ *    ("1.58-bit FLUX", section 4, limitation on speed: activations are not
+ *    quantized).
+ *
+ * Readings where the pages are silent (all listed in the design notes):
+ *  - the mean is taken in 64-bit fixed point relative to the row's largest
+ *    binade, so that its value does not depend on summation order
+ *    (oracle_quantize, steps 3-5);
+ *  - the half-way case |w|/s = 1/2 rounds to 0 (ties to even), decided by the
+ *    exact test 2|w| > s instead of a division;
+ *  - a row of zeros gets s = 0 and T = 0 (no epsilon);
+ *  - 2-bit codes are two's complement (+1 = 01, 0 = 00, -1 = 11), packed
+ *    along K, least significant bits first; code 10 decodes to -2.
+ *
+ * Parity pins for every function live in tests/test_oracle_pins.py.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_OK 0
+#define ORACLE_BAD_ARG 1
+
+/* bf16 -> fp32: a bf16 value is the upper half of an fp32 bit pattern. */
+static float bf16_bits_to_float(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return f;
+}
+
+static float load_weight(const void* w, int w_is_bf16, int64_t idx) {
+  if (w_is_bf16) return bf16_bits_to_float(((const uint16_t*)w)[idx]);
+  return ((const float*)w)[idx];
+}
+
+/*
+ * Absmean ternarization of one row (per output channel).
+ *
+ * Steps, for row n with K entries:
+ *  1. a_k = |w_k| in fp32 (bf16 input widened exactly first).
+ *  2. A = max_k a_k.  If A == 0 the row is all zeros: s = 0, T = 0.
+ *  3. E = floor(log2 A), exactly, from frexp: A = f * 2^e with f in [1/2, 1).
+ *  4. q_k = floor(a_k * 2^(48 - E)) as an unsigned 64-bit integer.  The
+ *     scaling by a power of two is exact in double and floor is the only
+ *     rounding; q_k < 2^49, so the sum below cannot overflow for K <= 32768.
+ *  5. s = (float)( (double)Q * 2^(E - 48) / (double)K ), Q = sum_k q_k.
+ *  6. T_k = +1 or -1 (sign of w_k) when 2 * a_k > s, else 0.  This is
+ *     clip(round(w/s), -1, 1) with ties to even: |w|/s > 1/2 gives +-1, and
+ *     |w|/s == 1/2 rounds to 0.
+ */
+static void quantize_row(const void* w, int w_is_bf16, int64_t row_off, int64_t k,
+                         int8_t* t_row, float* s_out) {
+  float amax = 0.0f;
+  for (int64_t i = 0; i < k; ++i) {
+    float a = fabsf(load_weight(w, w_is_bf16, row_off + i));
+    if (a > amax) amax = a;
+  }
+  if (amax == 0.0f) {
+    *s_out = 0.0f;
+    for (int64_t i = 0; i < k; ++i) t_row[i] = 0;
+    return;
+  }
+  int e;
+  (void)frexp((double)amax, &e);
+  int E = e - 1;
+
+  uint64_t Q = 0;
+  for (int64_t i = 0; i < k; ++i) {
+    double a = (double)fabsf(load_weight(w, w_is_bf16, row_off + i));
+    Q += (uint64_t)floor(ldexp(a, 48 - E));
+  }
+  double mean = ldexp((double)Q, E - 48) / (double)k;
+  float s = (float)mean;
+  *s_out = s;
+
+  for (int64_t i = 0; i < k; ++i) {
+    float wv = load_weight(w, w_is_bf16, row_off + i);
+    float a = fabsf(wv);
+    if (2.0f * a > s)
+      t_row[i] = (wv < 0.0f) ? (int8_t)-1 : (int8_t)1;
+    else
+      t_row[i] = 0;
+  }
+}
+
+/* w_dtype: 0 = fp32, 1 = bf16 (raw 16-bit patterns). */
+int oracle_quantize(const void* w, int w_dtype, int64_t n, int64_t k, int64_t ldw,
+                    int8_t* t, int64_t ldt, float* s) {
+  if (n < 0 || k < 1 || k > 32768 || ldw < k || ldt < k) return ORACLE_BAD_ARG;
+  if (w_dtype != 0 && w_dtype != 1) return ORACLE_BAD_ARG;
+  for (int64_t r = 0; r < n; ++r)
+    quantize_row(w, w_dtype == 1, r * ldw, k, t + r * ldt, s + r);
+  return ORACLE_OK;
+}
+
+/*
+ * 2-bit packing, four weights per byte along K, least significant first:
+ * weight k sits in bits 2*(k%4) .. 2*(k%4)+1 of byte k/4 of its row, as the
+ * low two bits of its two's-complement value (+1 -> 01, 0 -> 00, -1 -> 11).
+ * Positions past the end of a row (K % 4 != 0) hold code 00.
+ */
+int oracle_pack(const int8_t* t, int64_t n, int64_t k, int64_t ldt, uint8_t* p, int64_t ldp) {
+  int64_t nbytes = (k + 3) / 4;
+  if (n < 0 || k < 0 || ldt < k || ldp < nbytes) return ORACLE_BAD_ARG;
+  for (int64_t r = 0; r < n; ++r) {
+    for (int64_t j = 0; j < nbytes; ++j) {
+      unsigned byte = 0;
+      for (int i = 0; i < 4; ++i) {
+        int64_t kk = 4 * j + i;
+        unsigned code = 0;
+        if (kk < k) code = (unsigned)(uint8_t)t[r * ldt + kk] & 3u;
+        byte |= code << (2 * i);
+      }
+      p[r * ldp + j] = (uint8_t)byte;
+    }
+  }
+  return ORACLE_OK;
+}
+
+/* Sign-extend a 2-bit field: 00 -> 0, 01 -> +1, 10 -> -2, 11 -> -1. */
+static int decode_code(unsigned code) {
+  return (code & 2u) ? (int)code - 4 : (int)code;
+}
+
+int oracle_unpack(const uint8_t* p, int64_t n, int64_t k, int64_t ldp, int8_t* t, int64_t ldt) {
+  if (n < 0 || k < 0 || ldp < (k + 3) / 4 || ldt < k) return ORACLE_BAD_ARG;
+  for (int64_t r = 0; r < n; ++r)
+    for (int64_t kk = 0; kk < k; ++kk) {
+      unsigned code = (p[r * ldp + kk / 4] >> (2 * (kk % 4))) & 3u;
+      t[r * ldt + kk] = (int8_t)decode_code(code);
+    }
+  return ORACLE_OK;
+}
+
+/*
+ * Layer output, unrounded: y[m][n] = s_n * sum_k x[m][k] * T[n][k], with x the
+ * bf16 activations widened exactly, T decoded from the packed bytes, the sum
+ * taken in double in ascending k, and one double multiply by s_n.  The result
+ * is left in double: the GPU's bf16 output is compared against it with a
+ * tolerance, never against a rounded copy.
+ *
+ * Work is split over output columns n across threads; each thread decodes one
+ * weight row at a time and runs it against every activation row.
+ */
+typedef struct {
+  const double* xd;  /* m x k, widened activations */
+  int64_t m, k;
+  const uint8_t* p;
+  int64_t ldp;
+  const float* s;
+  double* y;
+  int64_t ldy;
+  int64_t n_begin, n_end;
+} gemm_job;
+
+static void* gemm_worker(void* arg) {
+  gemm_job* j = (gemm_job*)arg;
+  int8_t* trow = (int8_t*)malloc((size_t)(j->k > 0 ? j->k : 1));
+  if (!trow) return (void*)1;
+  for (int64_t n = j->n_begin; n < j->n_end; ++n) {
+    for (int64_t kk = 0; kk < j->k; ++kk) {
+      unsigned code = (j->p[n * j->ldp + kk / 4] >> (2 * (kk % 4))) & 3u;
+      trow[kk] = (int8_t)decode_code(code);
+    }
+    double sn = (double)j->s[n];
+    for (int64_t mm = 0; mm < j->m; ++mm) {
+      const double* xr = j->xd + mm * j->k;
+      double acc = 0.0;
+      for (int64_t kk = 0; kk < j->k; ++kk) acc += xr[kk] * (double)trow[kk];
+      j->y[mm * j->ldy + n] = sn * acc;
+    }
+  }
+  free(trow);
+  return NULL;
+}
+
+int oracle_gemm(const uint16_t* x_bf16, int64_t m, int64_t k, int64_t ldx, const uint8_t* p,
+                int64_t n, int64_t ldp, const float* s, double* y, int64_t ldy, int nthreads) {
+  if (m < 0 || n < 0 || k < 0 || ldx < k || ldp < (k + 3) / 4 || ldy < n) return ORACLE_BAD_ARG;
+  if (m == 0 || n == 0) return ORACLE_OK;
+  double* xd = (double*)malloc((size_t)(m * (k > 0 ? k : 1)) * sizeof(double));
+  if (!xd) return ORACLE_BAD_ARG;
+  for (int64_t mm = 0; mm < m; ++mm)
+    for (int64_t kk = 0; kk < k; ++kk)
+      xd[mm * k + kk] = (double)bf16_bits_to_float(x_bf16[mm * ldx + kk]);
+
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > n) nthreads = (int)n;
+  pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nthreads);
+  gemm_job* jobs = (gemm_job*)malloc(sizeof(gemm_job) * (size_t)nthreads);
+  int rc = ORACLE_OK;
+  if (!th || !jobs) rc = ORACLE_BAD_ARG;
+  int started = 0;
+  for (int i = 0; rc == ORACLE_OK && i < nthreads; ++i) {
+    gemm_job jb = {xd, m, k, p, ldp, s, y, ldy, n * i / nthreads, n * (i + 1) / nthreads};
+    jobs[i] = jb;
+    if (pthread_create(&th[i], NULL, gemm_worker, &jobs[i]) != 0) {
+      rc = ORACLE_BAD_ARG;
+      break;
+    }
+    ++started;
+  }
+  for (int i = 0; i < started; ++i) {
+    void* ret = NULL;
+    pthread_join(th[i], &ret);
+    if (ret != NULL) rc = ORACLE_BAD_ARG;
+  }
+  free(jobs);
+  free(th);
+  free(xd);
+  return rc;
+}

@@ -1,0 +1,133 @@
+"""ctypes front end of the C oracle in ``oracle.c`` (test infrastructure only).
+
+The C source is compiled with gcc at -O2, without fast-math, into
+``liboracle.so`` next to it, on first use or whenever the source is newer than
+the library.  Arguments are numpy arrays in host memory; the wrappers only
+check shapes and pass pointers.  What each function computes, and the reading
+of the pages behind it, is documented in ``oracle.c``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import tempfile
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB
+
+
+def build(force: bool = False, src: str = _SRC, out: str = _LIB) -> str:
+    """Compile the oracle with gcc (plain -O2, no fast-math) and return its path."""
+    if not force and os.path.exists(out) and os.path.getmtime(out) >= os.path.getmtime(src):
+        return out
+    fd, tmp = tempfile.mkstemp(suffix=".so", dir=os.path.dirname(out))
+    os.close(fd)
+    cmd = ["gcc", "-O2", "-std=c99", "-D_POSIX_C_SOURCE=200809L", "-fPIC", "-shared",
+           "-fno-fast-math", "-ffp-contract=off", "-pthread", "-o", tmp, src, "-lm"]
+    try:
+        subprocess.run(cmd, check=True, capture_output=True, text=True)
+        os.replace(tmp, out)
+    except subprocess.CalledProcessError as e:
+        os.unlink(tmp)
+        raise RuntimeError(f"oracle build failed:\n{e.stderr}") from e
+    return out
+
+
+def load(path: str | None = None):
+    """Load (building first if needed) and type the oracle's entry points."""
+    global _lib
+    if path is None and _lib is not None:
+        return _lib
+    lib = ctypes.CDLL(path or build())
+    i64, vp = ctypes.c_int64, ctypes.c_void_p
+    lib.oracle_quantize.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, i64, vp]
+    lib.oracle_pack.argtypes = [vp, i64, i64, i64, vp, i64]
+    lib.oracle_unpack.argtypes = [vp, i64, i64, i64, vp, i64]
+    lib.oracle_gemm.argtypes = [vp, i64, i64, i64, vp, i64, i64, vp, vp, i64, ctypes.c_int]
+    for f in (lib.oracle_quantize, lib.oracle_pack, lib.oracle_unpack, lib.oracle_gemm):
+        f.restype = ctypes.c_int
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def _check(rc: int, name: str) -> None:
+    if rc != 0:
+        raise ValueError(f"{name}: bad arguments (oracle returned {rc})")
+
+
+def oracle_quantize(w: np.ndarray, lib=None):
+    """Absmean-ternarize each row of ``w`` (float32, or bf16 given as uint16 bits).
+
+    Returns ``(t, s)``: int8 ``[N, K]`` in {-1, 0, 1} and float32 ``[N]``.
+    """
+    lib = lib or load()
+    w = np.ascontiguousarray(w)
+    if w.dtype == np.float32:
+        dt = 0
+    elif w.dtype == np.uint16:
+        dt = 1
+    else:
+        raise TypeError("w must be float32 or bf16 bits as uint16")
+    n, k = w.shape
+    t = np.empty((n, k), np.int8)
+    s = np.empty((n,), np.float32)
+    _check(lib.oracle_quantize(_ptr(w), dt, n, k, k, _ptr(t), k, _ptr(s)), "oracle_quantize")
+    return t, s
+
+
+def oracle_pack(t: np.ndarray, lib=None) -> np.ndarray:
+    """Pack int8 ``[N, K]`` into uint8 ``[N, ceil(K/4)]`` (2-bit codes, LSB first)."""
+    lib = lib or load()
+    t = np.ascontiguousarray(t, dtype=np.int8)
+    n, k = t.shape
+    nb = (k + 3) // 4
+    p = np.empty((n, nb), np.uint8)
+    _check(lib.oracle_pack(_ptr(t), n, k, k, _ptr(p), nb), "oracle_pack")
+    return p
+
+
+def oracle_unpack(p: np.ndarray, k: int, lib=None) -> np.ndarray:
+    """Unpack uint8 ``[N, >=ceil(K/4)]`` into int8 ``[N, K]`` (sign-extended 2-bit codes)."""
+    lib = lib or load()
+    p = np.ascontiguousarray(p, dtype=np.uint8)
+    n, ldp = p.shape
+    t = np.empty((n, k), np.int8)
+    _check(lib.oracle_unpack(_ptr(p), n, k, ldp, _ptr(t), k), "oracle_unpack")
+    return t
+
+
+def oracle_gemm(x_bf16_bits: np.ndarray, p: np.ndarray, s: np.ndarray, k: int | None = None,
+                nthreads: int | None = None, lib=None) -> np.ndarray:
+    """Unrounded layer output ``y = s_n * sum_k x[m,k] * T[n,k]`` in float64 ``[M, N]``.
+
+    ``x_bf16_bits`` holds the bf16 activations as uint16 bit patterns ``[M, K]``.
+    """
+    lib = lib or load()
+    x = np.ascontiguousarray(x_bf16_bits, dtype=np.uint16)
+    p = np.ascontiguousarray(p, dtype=np.uint8)
+    s = np.ascontiguousarray(s, dtype=np.float32)
+    m, kx = x.shape
+    k = kx if k is None else k
+    n, ldp = p.shape
+    if s.shape != (n,):
+        raise ValueError("s must have one entry per weight row")
+    y = np.empty((m, n), np.float64)
+    if nthreads is None:
+        nthreads = len(os.sched_getaffinity(0))
+    _check(lib.oracle_gemm(_ptr(x), m, k, kx, _ptr(p), n, ldp, _ptr(s), _ptr(y), n, nthreads),
+           "oracle_gemm")
+    return y

@@ -1,0 +1,379 @@
+"""Pins of the CPU oracle against facts fixed by the pages and by mathematics.
+
+None of these tests retypes the oracle's own formula: each compares it with a
+printed figure, a hand-worked example, a closed form, exact rational
+arithmetic, brute force over every case, or a library routine.  The mutation
+test at the end plants plausible mistakes in a copy of the oracle's C source
+and checks that these pins catch every one.
+"""
+from __future__ import annotations
+
+import math
+import os
+import shutil
+import tempfile
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import oracle as oracle_mod
+import tern_inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# --------------------------------------------------------------------------
+# fixtures read from tests/golden
+# --------------------------------------------------------------------------
+
+def _read_lines(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return [ln.strip() for ln in f if ln.strip() and not ln.startswith("#")]
+
+
+def _pages_storage():
+    return {k: float(v) for k, v in (ln.split() for ln in _read_lines("pages_storage.txt"))}
+
+
+def _pack_examples():
+    out = []
+    for ln in _read_lines("pack_examples.txt"):
+        parts = ln.split()
+        out.append(([int(v) for v in parts[:4]], int(parts[4], 16)))
+    return out
+
+
+def _quantize_examples():
+    out = []
+    for ln in _read_lines("quantize_examples.txt"):
+        w, s, t = (part.split() for part in ln.split(";"))
+        out.append((np.array([float(v) for v in w], np.float32), float(s[0]),
+                    np.array([int(v) for v in t], np.int8)))
+    return out
+
+
+# --------------------------------------------------------------------------
+# exact helpers (independent of the oracle)
+# --------------------------------------------------------------------------
+
+def _rn32(fr: Fraction) -> np.float32:
+    """Round a non-negative rational to the nearest fp32 (ties to even), exactly."""
+    if fr == 0:
+        return np.float32(0.0)
+    lo = np.float32(float(fr))  # candidate; adjust by exact comparison
+    cands = sorted({lo, np.nextafter(lo, np.float32(0)), np.nextafter(lo, np.float32(np.inf))},
+                   key=lambda c: (abs(Fraction(float(c)) - fr),
+                                  int(np.array(c, np.float32).view(np.uint32)) & 1))
+    return np.float32(cands[0])
+
+
+def _fp32_midpoint_distance(fr: Fraction) -> Fraction:
+    """Relative distance from fr to the nearest point half-way between fp32 neighbours."""
+    c = _rn32(fr)
+    up = np.nextafter(c, np.float32(np.inf))
+    dn = np.nextafter(c, np.float32(0))
+    mids = [(Fraction(float(c)) + Fraction(float(up))) / 2,
+            (Fraction(float(c)) + Fraction(float(dn))) / 2]
+    return min(abs(fr - m) for m in mids) / fr
+
+
+def _bf16_values(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+# --------------------------------------------------------------------------
+# storage format
+# --------------------------------------------------------------------------
+
+def test_pack_worked_examples():
+    for t, byte in _pack_examples():
+        p = oracle.oracle_pack(np.array([t], np.int8))
+        assert p.shape == (1, 1) and int(p[0, 0]) == byte, (t, hex(byte), hex(int(p[0, 0])))
+        back = oracle.oracle_unpack(p, 4)
+        assert back.tolist() == [t]
+
+
+def test_pack_exhaustive_valid_quads_round_trip():
+    quads = np.array([[a, b, c, d] for a in (-1, 0, 1) for b in (-1, 0, 1)
+                      for c in (-1, 0, 1) for d in (-1, 0, 1)], np.int8)
+    assert quads.shape == (81, 4)
+    p = oracle.oracle_pack(quads)
+    assert len(set(p[:, 0].tolist())) == 81           # injective
+    assert np.array_equal(oracle.oracle_unpack(p, 4), quads)
+    # no valid ternary value ever produces the unused code 10
+    for byte in p[:, 0].tolist():
+        for i in range(4):
+            assert (byte >> (2 * i)) & 3 != 2
+
+
+def test_pack_unpack_all_bytes_and_all_codes():
+    allbytes = np.arange(256, dtype=np.uint8).reshape(256, 1)
+    t = oracle.oracle_unpack(allbytes, 4)
+    assert t.min() == -2 and t.max() == 1                # code 10 decodes to -2
+    assert np.array_equal(oracle.oracle_pack(t), allbytes)
+    quads = np.array([[a, b, c, d] for a in range(-2, 2) for b in range(-2, 2)
+                      for c in range(-2, 2) for d in range(-2, 2)], np.int8)
+    assert np.array_equal(oracle.oracle_unpack(oracle.oracle_pack(quads), 4), quads)
+
+
+def test_pack_ragged_tail_and_layout_along_k():
+    rng = np.random.default_rng(7)
+    for k in (1, 2, 3, 5, 7, 13, 64, 255):
+        t = rng.integers(-1, 2, size=(3, k)).astype(np.int8)
+        p = oracle.oracle_pack(t)
+        assert p.shape == (3, (k + 3) // 4)
+        assert np.array_equal(oracle.oracle_unpack(p, k), t)
+        # brute force: weight kk lives in byte kk//4 at bits 2*(kk%4)
+        for r in range(3):
+            for kk in range(k):
+                code = (int(p[r, kk // 4]) >> (2 * (kk % 4))) & 3
+                assert code == (int(t[r, kk]) & 3)
+        # positions past the end of the row hold code 00
+        if k % 4:
+            last = int(p[0, -1])
+            assert last >> (2 * (k % 4)) == 0
+
+
+def test_storage_ratio_matches_pages():
+    pages = _pages_storage()
+    n, k = 64, 3072
+    t = tern_inputs.random_ternary(n, k, seed=5).numpy()
+    p = oracle.oracle_pack(t)
+    bits_per_weight = 8.0 * p.nbytes / (n * k)
+    assert bits_per_weight == pages["quantized_bits_stored"] == 2.0
+    # per layer against 16-bit weights: exactly 8x, and 8K/(K+16) with fp32 scales
+    assert (pages["source_bits"] * n * k / 8) / p.nbytes == 8.0
+    with_scales = (2 * n * k) / (p.nbytes + 4 * n)
+    assert with_scales == pytest.approx(8 * k / (k + 16))
+    # whole model: 99.5 % of parameters at 2 bits, the rest at 16 bits
+    f = pages["quantized_parameter_fraction"]
+    model = pages["source_bits"] / (f * bits_per_weight + (1 - f) * pages["source_bits"])
+    assert round(model, 1) == pages["model_storage_reduction"]
+
+
+# --------------------------------------------------------------------------
+# quantizer
+# --------------------------------------------------------------------------
+
+def test_quantize_worked_examples():
+    for w, s_ref, t_ref in _quantize_examples():
+        t, s = oracle.oracle_quantize(w.reshape(1, -1))
+        assert float(s[0]) == s_ref, (w, s, s_ref)
+        assert np.array_equal(t[0], t_ref), (w, t, t_ref)
+
+
+def test_quantize_value_set_and_packed_codes():
+    x, w = tern_inputs.draw(4, 1024, 300, seed=11)
+    t, s = oracle.oracle_quantize(w.numpy())
+    assert set(np.unique(t).tolist()) <= {-1, 0, 1}
+    p = oracle.oracle_pack(t)
+    codes = np.stack([(p >> (2 * i)) & 3 for i in range(4)])
+    assert not np.any(codes == 2)
+    assert np.all(s > 0)
+
+
+def test_quantize_fixed_point_of_scaled_ternary():
+    rng = np.random.default_rng(3)
+    for k in (1, 7, 64, 3072, 32768):
+        t0 = rng.integers(-1, 2, size=(4, k)).astype(np.int8)
+        t0[:, 0] = 1  # at least one non-zero per row
+        for c in (2.0 ** -20, 0.015625, 0.02, 1.0, 3.0e5):
+            w = (np.float32(c) * t0.astype(np.float32))
+            t, s = oracle.oracle_quantize(w)
+            assert np.array_equal(t, t0)
+            nnz = np.count_nonzero(t0, axis=1)
+            exact = [Fraction(float(np.float32(c))) * int(z) / k for z in nnz]
+            for si, ei in zip(s, exact):
+                assert abs(Fraction(float(si)) - ei) <= ei * Fraction(1, 2 ** 23)
+            # dequantize then quantize returns the same codes
+            t2, _ = oracle.oracle_quantize((t.astype(np.float32) * s[:, None]).astype(np.float32))
+            assert np.array_equal(t2, t0)
+
+
+def test_quantize_mean_is_correctly_rounded_exact_mean():
+    _, w = tern_inputs.draw(1, 3072, 64, seed=21)
+    w = w.numpy()
+    _, s = oracle.oracle_quantize(w)
+    checked = 0
+    for r in range(w.shape[0]):
+        exact = sum(Fraction(float(abs(v))) for v in w[r]) / w.shape[1]
+        if _fp32_midpoint_distance(exact) > Fraction(1, 2 ** 31):
+            assert s[r] == _rn32(exact), r
+            checked += 1
+    assert checked >= 60
+    # a row spanning many binades, where truncation to 2^-48 of the top binade matters least
+    row = np.array([1.0, 2.0 ** -30, 2.0 ** -60, 3.0, 2.0 ** -100], np.float32)
+    _, s1 = oracle.oracle_quantize(row.reshape(1, -1))
+    exact = sum(Fraction(float(v)) for v in row) / len(row)
+    assert abs(Fraction(float(s1[0])) - exact) <= exact * Fraction(1, 2 ** 23)
+
+
+def test_quantize_matches_division_formula_away_from_ties():
+    _, w = tern_inputs.draw(1, 3072, 512, seed=31)
+    w = w.numpy()
+    t, s = oracle.oracle_quantize(w)
+    ratio = w.astype(np.float64) / s.astype(np.float64)[:, None]
+    literal = np.clip(np.round(ratio), -1, 1).astype(np.int8)   # numpy rounds half to even
+    bad = np.argwhere(literal != t)
+    for r, c in bad:  # any disagreement must sit on the 1/2 tie, decided exactly
+        exact = Fraction(float(abs(w[r, c]))) / Fraction(float(s[r]))
+        assert abs(exact - Fraction(1, 2)) < Fraction(1, 2 ** 45)
+    assert len(bad) <= 2
+
+
+def test_quantize_gaussian_statistics():
+    # T = 0 iff |w| <= s/2 with s ~ E|w| = sigma*sqrt(2/pi): P = erf(1/(2*sqrt(pi)))
+    _, w = tern_inputs.draw(1, 3072, 512, seed=41)
+    t, s = oracle.oracle_quantize(w.numpy())
+    zero_frac = float(np.mean(t == 0))
+    assert abs(zero_frac - math.erf(1.0 / (2.0 * math.sqrt(math.pi)))) < 3e-3
+    assert math.erf(1.0 / (2.0 * math.sqrt(math.pi))) == pytest.approx(0.3101, abs=1e-4)
+    mean_s = float(np.mean(s.astype(np.float64)))
+    expect = tern_inputs.W_STD * math.sqrt(2.0 / math.pi)
+    sd_row = tern_inputs.W_STD * math.sqrt(1.0 - 2.0 / math.pi) / math.sqrt(3072)
+    assert abs(mean_s - expect) < 5.0 * sd_row / math.sqrt(512)
+    assert abs(float(np.std(s)) - sd_row) < 0.25 * sd_row
+    # signs are balanced
+    assert abs(float(np.mean(t == 1)) - float(np.mean(t == -1))) < 5e-3
+
+
+def test_quantize_bf16_input_equals_widened_fp32():
+    _, w = tern_inputs.draw(1, 512, 40, seed=51)
+    wb = w.to(torch.bfloat16)
+    t1, s1 = oracle.oracle_quantize(tern_inputs.bf16_bits(wb))
+    t2, s2 = oracle.oracle_quantize(wb.to(torch.float32).numpy())
+    assert np.array_equal(t1, t2) and np.array_equal(s1, s2)
+
+
+def test_quantize_rejects_out_of_range_k():
+    with pytest.raises(ValueError):
+        oracle.oracle_quantize(np.zeros((1, 32769), np.float32))
+    with pytest.raises(ValueError):
+        oracle.oracle_quantize(np.zeros((1, 0), np.float32))
+
+
+# --------------------------------------------------------------------------
+# layer output
+# --------------------------------------------------------------------------
+
+def _single_layer():
+    x, w = tern_inputs.draw_layer(tern_inputs.WORKLOADS["single"][0])
+    t, s = oracle.oracle_quantize(w.numpy())
+    return x, t, s, oracle.oracle_pack(t)
+
+
+def test_gemm_sign_sum_identity_exact():
+    x, t, s, p = _single_layer()
+    xb = tern_inputs.bf16_bits(x)
+    y = oracle.oracle_gemm(xb, p, s)
+    xv = _bf16_values(xb)
+    assert y.shape == (16, 512)
+    for m in range(16):
+        xf = [Fraction(float(v)) for v in xv[m]]
+        for n in range(0, 512, 7):
+            plus = sum((xf[k] for k in range(256) if t[n, k] == 1), Fraction(0))
+            minus = sum((xf[k] for k in range(256) if t[n, k] == -1), Fraction(0))
+            assert y[m, n] == float(Fraction(float(s[n])) * (plus - minus)), (m, n)
+
+
+def test_gemm_equals_float64_matmul_on_exact_inputs():
+    rng = np.random.default_rng(61)
+    m, k, n = 5, 36, 9
+    xi = rng.integers(-64, 65, size=(m, k)).astype(np.float32)
+    x = torch.from_numpy(xi).to(torch.bfloat16)          # small integers are exact in bf16
+    t = rng.integers(-1, 2, size=(n, k)).astype(np.int8)
+    ones = np.ones(n, np.float32)
+    y = oracle.oracle_gemm(tern_inputs.bf16_bits(x), oracle.oracle_pack(t), ones, k=k)
+    ref = torch.matmul(torch.from_numpy(xi).double(), torch.from_numpy(t).double().T).numpy()
+    assert np.array_equal(y, ref)
+    # a scale per output column multiplies column n
+    sc = (2.0 ** rng.integers(-3, 4, size=n)).astype(np.float32)
+    y2 = oracle.oracle_gemm(tern_inputs.bf16_bits(x), oracle.oracle_pack(t), sc, k=k)
+    assert np.array_equal(y2, ref * sc.astype(np.float64)[None, :])
+
+
+def test_gemm_against_numpy_on_random_data():
+    x, w = tern_inputs.draw(7, 384, 33, seed=71, x_dist="student_t3")
+    t, s = oracle.oracle_quantize(w.numpy())
+    y = oracle.oracle_gemm(tern_inputs.bf16_bits(x), oracle.oracle_pack(t), s, nthreads=3)
+    ref = (x.double().numpy() @ t.astype(np.float64).T) * s.astype(np.float64)[None, :]
+    assert np.allclose(y, ref, rtol=1e-13, atol=1e-13 * np.abs(ref).max())
+
+
+def test_gemm_zero_row_and_zero_sizes():
+    x, w = tern_inputs.draw(3, 64, 4, seed=81)
+    w[2] = 0.0
+    t, s = oracle.oracle_quantize(w.numpy())
+    y = oracle.oracle_gemm(tern_inputs.bf16_bits(x), oracle.oracle_pack(t), s)
+    assert s[2] == 0 and np.all(y[:, 2] == 0)
+    y0 = oracle.oracle_gemm(np.zeros((0, 64), np.uint16), oracle.oracle_pack(t), s)
+    assert y0.shape == (0, 4)
+
+
+def test_gemm_thread_count_does_not_change_result():
+    x, w = tern_inputs.draw(9, 256, 37, seed=91)
+    t, s = oracle.oracle_quantize(w.numpy())
+    p = oracle.oracle_pack(t)
+    xb = tern_inputs.bf16_bits(x)
+    assert np.array_equal(oracle.oracle_gemm(xb, p, s, nthreads=1),
+                          oracle.oracle_gemm(xb, p, s, nthreads=5))
+
+
+# --------------------------------------------------------------------------
+# mutation check: the pins above must catch plausible mistakes in the oracle
+# --------------------------------------------------------------------------
+
+MUTANTS = {
+    "tie_rounds_away": ("if (2.0f * a > s)", "if (2.0f * a >= s)"),
+    "sign_flipped": ("(wv < 0.0f) ? (int8_t)-1 : (int8_t)1", "(wv < 0.0f) ? (int8_t)1 : (int8_t)-1"),
+    "mean_over_k_minus_1": ("/ (double)k;", "/ (double)(k > 1 ? k - 1 : 1);"),
+    "mean_rescaled_wrong": ("ldexp((double)Q, E - 48)", "ldexp((double)Q, E - 47)"),
+    "fixed_point_too_narrow": ("ldexp(a, 48 - E)", "ldexp(a, 12 - E)"),
+    "pack_msb_first": ("byte |= code << (2 * i);", "byte |= code << (6 - 2 * i);"),
+    "unpack_no_sign_extension": ("return (code & 2u) ? (int)code - 4 : (int)code;",
+                                 "return (int)code;"),
+    "gemm_drops_last_k": ("for (int64_t kk = 0; kk < j->k; ++kk) acc +=",
+                          "for (int64_t kk = 0; kk + 1 < j->k; ++kk) acc +="),
+    "gemm_no_scale": ("j->y[mm * j->ldy + n] = sn * acc;", "j->y[mm * j->ldy + n] = acc;"),
+    "gemm_wrong_weight_row": ("unsigned code = (j->p[n * j->ldp + kk / 4]",
+                              "unsigned code = (j->p[(n ^ 1) % (j->n_end > 0 ? j->n_end : 1) * j->ldp + kk / 4]"),
+    "gemm_x_transposed_index": ("const double* xr = j->xd + mm * j->k;",
+                                "const double* xr = j->xd + (mm % 2) * j->k;"),
+}
+
+PIN_TESTS = [
+    test_pack_worked_examples, test_pack_exhaustive_valid_quads_round_trip,
+    test_pack_unpack_all_bytes_and_all_codes, test_pack_ragged_tail_and_layout_along_k,
+    test_storage_ratio_matches_pages, test_quantize_worked_examples,
+    test_quantize_fixed_point_of_scaled_ternary, test_quantize_mean_is_correctly_rounded_exact_mean,
+    test_quantize_gaussian_statistics, test_gemm_sign_sum_identity_exact,
+    test_gemm_equals_float64_matmul_on_exact_inputs, test_gemm_against_numpy_on_random_data,
+]
+
+
+def test_pins_catch_planted_mistakes(monkeypatch):
+    with open(oracle_mod._SRC) as f:
+        src = f.read()
+    tmpdir = tempfile.mkdtemp(prefix="oracle_mutants_")
+    try:
+        for name, (old, new) in MUTANTS.items():
+            assert src.count(old) == 1, f"mutation site for {name} not unique in oracle.c"
+            path = os.path.join(tmpdir, f"{name}.c")
+            with open(path, "w") as f:
+                f.write(src.replace(old, new))
+            lib = oracle_mod.load(oracle_mod.build(force=True, src=path,
+                                                   out=os.path.join(tmpdir, f"{name}.so")))
+            caught = []
+            with monkeypatch.context() as mp:
+                mp.setattr(oracle_mod, "_lib", lib)
+                for pin in PIN_TESTS:
+                    try:
+                        pin()
+                    except (AssertionError, ValueError):
+                        caught.append(pin.__name__)
+            assert caught, f"no pin catches the planted mistake {name!r}"
+    finally:
+        shutil.rmtree(tmpdir, ignore_errors=True)
