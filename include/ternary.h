@@ -1,0 +1,147 @@
+/*
+ * libternary: the 1.58-bit (ternary-weight) linear layer on AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The operation is the one "1.58-bit FLUX" (arXiv 2412.18653) builds its
+ * custom kernel around: every weight of a linear layer is restricted to
+ * {-1, 0, +1} in the manner of BitNet b1.58 (abstract; section 1
+ * Introduction; section 2 Related Work), the ternary weights are stored as
+ * 2-bit signed integers instead of 16-bit values (section 1, storage
+ * paragraph), and the activations stay unquantized (section 4, limitation on
+ * speed).  The library turns full-precision weights into ternary codes and a
+ * per-output-channel scale, packs them four to a byte, and computes
+ * Y = (X . T^T) (.) s with bf16 X and Y.
+ *
+ * Conventions shared by every call:
+ *  - All data pointers are DEVICE pointers owned by the caller.  The library
+ *    allocates, frees and keeps no device memory and holds no global state.
+ *  - Matrices are row-major.  Leading dimensions (ld*) count elements, except
+ *    ldp, which counts bytes.
+ *  - Every call is asynchronous on `stream` (a hipStream_t passed as void*;
+ *    NULL is the default stream) and returns after enqueueing.  Faults inside
+ *    a kernel surface at the caller's next synchronisation with that stream.
+ *  - Arguments are validated on the host, before anything is enqueued, in
+ *    this order: dtype, sizes, (no-op check), null pointers, leading
+ *    dimensions, alignment.  A call whose output is empty (a zero size) is a
+ *    no-op that returns TERN_OK without touching any pointer.
+ *  - A kernel launch that the HIP runtime rejects returns TERN_ERR_HIP.
+ *  - Outputs must not overlap inputs.  Calls are re-entrant and thread-safe.
+ *  - Inputs are assumed finite; results for NaN or infinite inputs are
+ *    unspecified.
+ */
+#ifndef TERNARY_H_
+#define TERNARY_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TERN_OK = 0,
+  TERN_ERR_NULL = 1,   /* a required pointer is NULL */
+  TERN_ERR_SHAPE = 2,  /* a size is negative or outside the supported range */
+  TERN_ERR_ALIGN = 3,  /* a pointer or leading dimension breaks an alignment rule */
+  TERN_ERR_STRIDE = 4, /* a leading dimension is too short for its row, or too long */
+  TERN_ERR_DTYPE = 5,  /* unknown element type */
+  TERN_ERR_HIP = 6     /* the HIP runtime rejected a launch */
+} tern_status;
+
+typedef enum { TERN_F32 = 0, TERN_BF16 = 1 } tern_dtype;
+
+/* Largest row length tern_quantize accepts (see the scale definition below). */
+#define TERN_QUANTIZE_MAX_K 32768
+
+/*
+ * tern_quantize: absmean ternarization, one scale per output channel.
+ *
+ * Definition ("1.58-bit FLUX", section 1: weights restricted to {+1, 0, -1}
+ * as in BitNet b1.58; the pages give no formula, and the per-output-channel
+ * absmean rule below is the reading used):
+ *   s_n  = mean_k |w[n][k]|
+ *   T_nk = clip(round(w[n][k] / s_n), -1, 1), ties to even, so |w|/s_n = 1/2
+ *          gives 0; decided by the exact test 2|w| > s_n (no division).
+ *   A row of zeros gives s_n = 0 and T = 0.
+ * To make s_n independent of summation order (bit-identical on any device),
+ * the mean is taken in 64-bit fixed point: with E = floor(log2(max_k |w|)),
+ *   s_n = fp32( fp64(sum_k floor(|w| * 2^(48-E))) * 2^(E-48) / K ),
+ * every rounding being IEEE round-to-nearest-even.  This equals the correctly
+ * rounded mean except when the exact mean lies within 2^-33 (relative) of a
+ * point half-way between two fp32 values.
+ *
+ *   w      [n, ldw] fp32 (w_dtype = TERN_F32) or bf16 (TERN_BF16), read only
+ *   t      [n, ldt] int8 output, values in {-1, 0, +1}; columns >= k untouched
+ *   s      [n] fp32 output
+ * Sizes: 0 <= n <= 2^31 - 1, 1 <= k <= TERN_QUANTIZE_MAX_K (else
+ * TERN_ERR_SHAPE); n == 0 is a no-op.  ldw >= k and ldt >= k (else
+ * TERN_ERR_STRIDE).  w aligned to its element size and s to 4 bytes (else
+ * TERN_ERR_ALIGN).
+ */
+tern_status tern_quantize(const void* w, tern_dtype w_dtype, int64_t n, int64_t k, int64_t ldw,
+                          int8_t* t, int64_t ldt, float* s, void* stream);
+
+/*
+ * tern_pack: 2-bit storage of ternary weights, four per byte
+ * ("1.58-bit FLUX", section 1: the 1.58-bit weights are stored as 2-bit
+ * signed integers).  Reading of the layout: weight k of a row sits in bits
+ * 2*(k%4) and 2*(k%4)+1 of byte k/4 of that row, as the low two bits of its
+ * two's-complement value (+1 -> 01, 0 -> 00, -1 -> 11).
+ *
+ *   t  [n, ldt] int8 input; only the low two bits of each value are used
+ *      (values outside {-1, 0, +1} are not rejected)
+ *   p  [n, ldp] uint8 output; bytes 0 .. ceil(k/4)-1 of each row are written,
+ *      fields past column k-1 in the last byte are 00, and bytes from
+ *      ceil(k/4) to ldp-1 are left untouched
+ * Sizes: n, k >= 0; a zero size is a no-op.  ldt >= k, ldp >= ceil(k/4).
+ */
+tern_status tern_pack(const int8_t* t, int64_t n, int64_t k, int64_t ldt, uint8_t* p, int64_t ldp,
+                      void* stream);
+
+/*
+ * tern_unpack: the inverse of tern_pack.  Each 2-bit field is sign-extended:
+ * 00 -> 0, 01 -> +1, 11 -> -1, and the unused code 10 -> -2 (so that a
+ * corrupted code stays visible).
+ *
+ *   p  [n, ldp] uint8 input; t [n, ldt] int8 output, columns >= k untouched
+ * Sizes: n, k >= 0; a zero size is a no-op.  ldp >= ceil(k/4), ldt >= k.
+ */
+tern_status tern_unpack(const uint8_t* p, int64_t n, int64_t k, int64_t ldp, int8_t* t,
+                        int64_t ldt, void* stream);
+
+/*
+ * tern_gemm: the ternary linear layer with a fused scale epilogue
+ * ("1.58-bit FLUX", section 1 contributions and section 3.2 Results: the
+ * efficient linear kernel for 1.58-bit weights; section 4: activations are
+ * not quantized).
+ *
+ *   Y[m][n] = bf16( fp32(acc[m][n]) * s[n] ),  acc[m][n] = sum_k X[m][k] * T[n][k]
+ *
+ * with T decoded from p as tern_unpack does, the products exact, acc an fp32
+ * sum in an unspecified order, and one round-to-nearest-even conversion to
+ * bf16.  Codes 10 give an unspecified result.  No bias is added.
+ *
+ *   x  [m, ldx] bf16 activations
+ *   p  [n, ldp] packed weights, as written by tern_pack for a row length k
+ *   s  [n] fp32 per-output-channel scales
+ *   y  [m, ldy] bf16 output; columns >= n untouched
+ * Sizes: m, n, k >= 0 and k % 64 == 0 (else TERN_ERR_SHAPE); m == 0 or
+ * n == 0 is a no-op; k == 0 writes zeros.  m, n <= 2^31 - 1,
+ * k <= 2^31 - 64 and ceil(m/256) * ceil(n/256) <= 2^31 - 1.
+ * ldx >= k, ldp >= k/4, ldy >= n, and ldx < 2^23, ldp < 2^24, ldy < 2^31
+ * (else TERN_ERR_STRIDE).
+ * Alignment (else TERN_ERR_ALIGN): x and p 16-byte aligned, ldx % 8 == 0,
+ * ldp % 16 == 0; y 2-byte aligned; s 4-byte aligned.
+ */
+tern_status tern_gemm(const void* x_bf16, int64_t m, int64_t k, int64_t ldx, const uint8_t* p,
+                      int64_t n, int64_t ldp, const float* s, void* y_bf16, int64_t ldy,
+                      void* stream);
+
+/* Static, never-NULL description of a status code. */
+const char* tern_status_string(tern_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TERNARY_H_ */

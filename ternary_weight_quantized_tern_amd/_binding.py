@@ -1,0 +1,200 @@
+"""ctypes binding of libternary: argument marshalling only.
+
+Each ``tern_*`` function here has the name of the C entry point declared in
+``include/ternary.h`` and takes its tensors in the same order.  It checks that the torch
+tensors it is given are on the GPU with the documented dtypes and unit column
+stride, reads their device pointers, leading dimensions and the current HIP
+stream, and calls the library.  All arithmetic runs in the library's kernels;
+nothing here computes any part of the layer, and there is no fallback: if
+``libternary.so`` is missing or cannot be loaded, importing this module fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("TERN_LIB", os.path.join(_PKG_DIR, "libternary.so"))
+
+TERN_OK = 0
+TERN_ERR_NULL = 1
+TERN_ERR_SHAPE = 2
+TERN_ERR_ALIGN = 3
+TERN_ERR_STRIDE = 4
+TERN_ERR_DTYPE = 5
+TERN_ERR_HIP = 6
+TERN_F32 = 0
+TERN_BF16 = 1
+TERN_QUANTIZE_MAX_K = 32768
+
+EXPORTED = ("tern_quantize", "tern_pack", "tern_unpack", "tern_gemm", "tern_status_string")
+
+
+class TernError(RuntimeError):
+    """A libternary call returned a status other than TERN_OK."""
+
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {tern_status_string(status)}")
+
+
+def _load(path: str):
+    if not os.path.exists(path):
+        raise ImportError(
+            f"libternary.so not found at {path}; build it with "
+            "`python -m ternary_weight_quantized_tern_amd.build` (no CPU fallback exists)")
+    lib = ctypes.CDLL(path)
+    i64, vp = ctypes.c_int64, ctypes.c_void_p
+    lib.tern_quantize.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, i64, vp, vp]
+    lib.tern_pack.argtypes = [vp, i64, i64, i64, vp, i64, vp]
+    lib.tern_unpack.argtypes = [vp, i64, i64, i64, vp, i64, vp]
+    lib.tern_gemm.argtypes = [vp, i64, i64, i64, vp, i64, i64, vp, vp, i64, vp]
+    for name in ("tern_quantize", "tern_pack", "tern_unpack", "tern_gemm"):
+        getattr(lib, name).restype = ctypes.c_int
+    lib.tern_status_string.argtypes = [ctypes.c_int]
+    lib.tern_status_string.restype = ctypes.c_char_p
+    return lib
+
+
+_lib = _load(LIB_PATH)
+
+
+def library():
+    """The loaded ``ctypes.CDLL`` (for ABI tests)."""
+    return _lib
+
+
+def tern_status_string(status: int) -> str:
+    return _lib.tern_status_string(int(status)).decode()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _mat(a: torch.Tensor, name: str, dtypes) -> int:
+    if not isinstance(a, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if a.device.type != "cuda":
+        raise TypeError(f"{name} must be a GPU tensor, got {a.device}")
+    if a.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {a.dtype}, expected one of {dtypes}")
+    if a.dim() != 2 or (a.shape[1] > 1 and a.stride(1) != 1):
+        raise ValueError(f"{name} must be a 2-D row-major view (unit column stride)")
+    if a.shape[0] > 1:
+        return a.stride(0)
+    # With a single row the leading dimension is never used to step between
+    # rows; report the row length rounded up to 16 elements.
+    return (a.shape[1] + 15) // 16 * 16
+
+
+def _vec(a: torch.Tensor, name: str, dtype) -> None:
+    if not isinstance(a, torch.Tensor) or a.device.type != "cuda" or a.dtype != dtype:
+        raise TypeError(f"{name} must be a GPU tensor of dtype {dtype}")
+    if a.dim() != 1 or (a.numel() > 1 and a.stride(0) != 1):
+        raise ValueError(f"{name} must be a contiguous 1-D tensor")
+
+
+def _check(fn: str, status: int) -> None:
+    if status != TERN_OK:
+        raise TernError(fn, status)
+
+
+def tern_quantize(w: torch.Tensor, t: torch.Tensor, s: torch.Tensor, stream=None) -> None:
+    """Absmean-ternarize ``w`` [n, k] (fp32 or bf16) into ``t`` int8 [n, >=k] and ``s`` fp32 [n]."""
+    ldw = _mat(w, "w", (torch.float32, torch.bfloat16))
+    ldt = _mat(t, "t", (torch.int8,))
+    _vec(s, "s", torch.float32)
+    n, k = w.shape
+    if t.shape[0] != n or t.shape[1] < k or s.shape[0] != n:
+        raise ValueError("t must be [n, >=k] and s [n]")
+    dt = TERN_F32 if w.dtype == torch.float32 else TERN_BF16
+    _check("tern_quantize", _lib.tern_quantize(w.data_ptr(), dt, n, k, ldw, t.data_ptr(), ldt,
+                                               s.data_ptr(), _stream(stream)))
+
+
+def tern_pack(t: torch.Tensor, p: torch.Tensor, k: int | None = None, stream=None) -> None:
+    """Pack int8 ``t`` [n, k] into ``p`` uint8 [n, >=ceil(k/4)]."""
+    ldt = _mat(t, "t", (torch.int8,))
+    ldp = _mat(p, "p", (torch.uint8,))
+    n = t.shape[0]
+    k = t.shape[1] if k is None else int(k)
+    if p.shape[0] != n or k > t.shape[1] or p.shape[1] < (k + 3) // 4:
+        raise ValueError("p must be [n, >=ceil(k/4)] for t [n, k]")
+    _check("tern_pack", _lib.tern_pack(t.data_ptr(), n, k, ldt, p.data_ptr(), ldp, _stream(stream)))
+
+
+def tern_unpack(p: torch.Tensor, t: torch.Tensor, k: int | None = None, stream=None) -> None:
+    """Unpack ``p`` uint8 [n, >=ceil(k/4)] into int8 ``t`` [n, >=k] (k defaults to t's width)."""
+    ldp = _mat(p, "p", (torch.uint8,))
+    ldt = _mat(t, "t", (torch.int8,))
+    n = p.shape[0]
+    k = t.shape[1] if k is None else int(k)
+    if t.shape[0] != n or t.shape[1] < k or p.shape[1] < (k + 3) // 4:
+        raise ValueError("t must be [n, >=k] and p [n, >=ceil(k/4)]")
+    _check("tern_unpack", _lib.tern_unpack(p.data_ptr(), n, int(k), ldp, t.data_ptr(), ldt,
+                                           _stream(stream)))
+
+
+def tern_gemm(x: torch.Tensor, p: torch.Tensor, s: torch.Tensor, y: torch.Tensor,
+              k: int | None = None, stream=None) -> None:
+    """``y`` [m, n] bf16 = bf16((x [m, k] . T^T) * s), T decoded from ``p`` [n, >=k/4].
+
+    k defaults to x's width.
+    """
+    ldx = _mat(x, "x", (torch.bfloat16,))
+    ldp = _mat(p, "p", (torch.uint8,))
+    ldy = _mat(y, "y", (torch.bfloat16,))
+    _vec(s, "s", torch.float32)
+    m = x.shape[0]
+    k = x.shape[1] if k is None else int(k)
+    n = p.shape[0]
+    if k > x.shape[1] or p.shape[1] < k // 4 or s.shape[0] != n or tuple(y.shape[:1]) != (m,) \
+            or y.shape[1] < n:
+        raise ValueError("shapes must be x [m, k], p [n, >=k/4], s [n], y [m, >=n]")
+    _check("tern_gemm", _lib.tern_gemm(x.data_ptr(), m, k, ldx, p.data_ptr(), n, ldp,
+                                       s.data_ptr(), y.data_ptr(), ldy, _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# allocating conveniences (torch allocates the outputs; the library computes)
+# ---------------------------------------------------------------------------
+
+def quantize(w: torch.Tensor, stream=None):
+    """Return ``(t, s)`` for full-precision weights ``w`` [n, k]."""
+    n, k = w.shape
+    t = torch.empty((n, k), dtype=torch.int8, device=w.device)
+    s = torch.empty((n,), dtype=torch.float32, device=w.device)
+    tern_quantize(w, t, s, stream)
+    return t, s
+
+
+def packed_row_bytes(k: int) -> int:
+    """Row pitch used for packed weights: ceil(k/4) rounded up to 16 bytes."""
+    return ((k + 3) // 4 + 15) // 16 * 16
+
+
+def pack(t: torch.Tensor, stream=None) -> torch.Tensor:
+    n, k = t.shape
+    p = torch.zeros((n, packed_row_bytes(k)), dtype=torch.uint8, device=t.device)
+    tern_pack(t, p, k, stream)
+    return p
+
+
+def unpack(p: torch.Tensor, k: int, stream=None) -> torch.Tensor:
+    t = torch.empty((p.shape[0], k), dtype=torch.int8, device=p.device)
+    tern_unpack(p, t, k, stream)
+    return t
+
+
+def linear(x: torch.Tensor, p: torch.Tensor, s: torch.Tensor, stream=None) -> torch.Tensor:
+    """Ternary linear layer: bf16 ``x`` [m, k] -> bf16 [m, n]."""
+    y = torch.empty((x.shape[0], p.shape[0]), dtype=torch.bfloat16, device=x.device)
+    tern_gemm(x, p, s, y, None, stream)
+    return y

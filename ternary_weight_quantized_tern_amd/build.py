@@ -1,0 +1,61 @@
+"""Build libternary.so in-tree with hipcc for gfx950.
+
+``python -m ternary_weight_quantized_tern_amd.build`` (or ``build_library()``)
+compiles every ``csrc/*.hip`` into one shared library next to this file.
+"""
+from __future__ import annotations
+
+import glob
+import os
+import subprocess
+import sys
+import tempfile
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG_DIR)
+CSRC = os.path.join(PKG_DIR, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB_NAME = "libternary.so"
+LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
+ARCH = os.environ.get("TERN_ARCH", "gfx950")
+
+
+def hipcc() -> str:
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    return os.path.join(rocm, "bin", "hipcc")
+
+
+def compile_flags(arch: str = ARCH) -> list:
+    return [
+        f"--offload-arch={arch}", "-O3", "-std=c++17", "-fPIC",
+        # Packed fp32 VALU instructions are kept out of every kernel.
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-Wall", "-Wno-unused-function",
+        f"-I{INCLUDE}", f"-I{CSRC}",
+    ]
+
+
+def sources() -> list:
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+
+
+def build_library(out: str = LIB_PATH, extra: list | None = None, verbose: bool = False) -> str:
+    """Compile all HIP sources into ``out`` (atomically replaced)."""
+    fd, tmp = tempfile.mkstemp(suffix=".so.tmp", dir=os.path.dirname(out))
+    os.close(fd)
+    cmd = [hipcc()] + compile_flags() + (extra or []) + ["-shared", "-o", tmp] + sources()
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    try:
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed ({r.returncode}):\n{r.stderr}")
+        os.replace(tmp, out)
+    finally:
+        if os.path.exists(tmp):
+            os.unlink(tmp)
+    return out
+
+
+if __name__ == "__main__":
+    print(build_library(verbose="-v" in sys.argv))

@@ -1,0 +1,88 @@
+// C-ABI of libternary (declared in include/ternary.h): host-side argument
+// validation, then one asynchronous launch on the caller's stream.  No HIP
+// call is made before every argument has been checked, and the library keeps
+// no state between calls.
+#include "ternary.h"
+
+#include "internal.h"
+
+namespace {
+
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+inline tern_status from_hip(hipError_t e) { return e == hipSuccess ? TERN_OK : TERN_ERR_HIP; }
+
+constexpr int64_t kMaxInt = 2147483647;  // 2^31 - 1
+// The GEMM addresses one 256-row block of X (or of the packed weights) with
+// 32-bit byte offsets.
+constexpr int64_t kGemmMaxLdx = (int64_t(1) << 23) - 1;
+constexpr int64_t kGemmMaxLdp = (int64_t(1) << 24) - 1;
+
+}  // namespace
+
+extern "C" {
+
+tern_status tern_quantize(const void* w, tern_dtype w_dtype, int64_t n, int64_t k, int64_t ldw,
+                          int8_t* t, int64_t ldt, float* s, void* stream) {
+  if (w_dtype != TERN_F32 && w_dtype != TERN_BF16) return TERN_ERR_DTYPE;
+  if (n < 0 || n > kMaxInt || k < 0 || k > TERN_QUANTIZE_MAX_K) return TERN_ERR_SHAPE;
+  if (n == 0) return TERN_OK;
+  if (k == 0) return TERN_ERR_SHAPE;
+  if (w == nullptr || t == nullptr || s == nullptr) return TERN_ERR_NULL;
+  if (ldw < k || ldt < k) return TERN_ERR_STRIDE;
+  const uintptr_t esz = (w_dtype == TERN_F32) ? 4 : 2;
+  if (!aligned(w, esz) || !aligned(s, 4)) return TERN_ERR_ALIGN;
+  return from_hip(tern::launch_quantize(w, w_dtype == TERN_BF16, n, k, ldw, t, ldt, s,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+tern_status tern_pack(const int8_t* t, int64_t n, int64_t k, int64_t ldt, uint8_t* p, int64_t ldp,
+                      void* stream) {
+  if (n < 0 || k < 0) return TERN_ERR_SHAPE;
+  if (n == 0 || k == 0) return TERN_OK;
+  if (t == nullptr || p == nullptr) return TERN_ERR_NULL;
+  if (ldt < k || ldp < (k + 3) / 4) return TERN_ERR_STRIDE;
+  return from_hip(tern::launch_pack(t, n, k, ldt, p, ldp, static_cast<hipStream_t>(stream)));
+}
+
+tern_status tern_unpack(const uint8_t* p, int64_t n, int64_t k, int64_t ldp, int8_t* t,
+                        int64_t ldt, void* stream) {
+  if (n < 0 || k < 0) return TERN_ERR_SHAPE;
+  if (n == 0 || k == 0) return TERN_OK;
+  if (p == nullptr || t == nullptr) return TERN_ERR_NULL;
+  if (ldp < (k + 3) / 4 || ldt < k) return TERN_ERR_STRIDE;
+  return from_hip(tern::launch_unpack(p, n, k, ldp, t, ldt, static_cast<hipStream_t>(stream)));
+}
+
+tern_status tern_gemm(const void* x_bf16, int64_t m, int64_t k, int64_t ldx, const uint8_t* p,
+                      int64_t n, int64_t ldp, const float* s, void* y_bf16, int64_t ldy,
+                      void* stream) {
+  if (m < 0 || n < 0 || k < 0 || m > kMaxInt || n > kMaxInt || k > kMaxInt - 63 || k % 64 != 0)
+    return TERN_ERR_SHAPE;
+  if (((m + 255) / 256) * ((n + 255) / 256) > kMaxInt) return TERN_ERR_SHAPE;
+  if (m == 0 || n == 0) return TERN_OK;
+  if (x_bf16 == nullptr || p == nullptr || s == nullptr || y_bf16 == nullptr) return TERN_ERR_NULL;
+  if (ldx < k || ldp < k / 4 || ldy < n) return TERN_ERR_STRIDE;
+  if (ldx > kGemmMaxLdx || ldp > kGemmMaxLdp || ldy > kMaxInt) return TERN_ERR_STRIDE;
+  if (!aligned(x_bf16, 16) || ldx % 8 != 0 || !aligned(p, 16) || ldp % 16 != 0 ||
+      !aligned(y_bf16, 2) || !aligned(s, 4))
+    return TERN_ERR_ALIGN;
+  return from_hip(tern::launch_gemm(static_cast<const uint16_t*>(x_bf16), m, k, ldx, p, n, ldp, s,
+                                    static_cast<uint16_t*>(y_bf16), ldy,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+const char* tern_status_string(tern_status status) {
+  switch (status) {
+    case TERN_OK: return "TERN_OK: success";
+    case TERN_ERR_NULL: return "TERN_ERR_NULL: a required pointer is NULL";
+    case TERN_ERR_SHAPE: return "TERN_ERR_SHAPE: a size is negative or outside the supported range";
+    case TERN_ERR_ALIGN: return "TERN_ERR_ALIGN: a pointer or leading dimension breaks an alignment rule";
+    case TERN_ERR_STRIDE: return "TERN_ERR_STRIDE: a leading dimension is too short or too long";
+    case TERN_ERR_DTYPE: return "TERN_ERR_DTYPE: unknown element type";
+    case TERN_ERR_HIP: return "TERN_ERR_HIP: the HIP runtime rejected a launch";
+  }
+  return "unknown tern_status";
+}
+
+}  // extern "C"

@@ -1,0 +1,27 @@
+// Internal declarations of libternary: kernel launchers called by the C-ABI
+// layer (api.hip) after it has validated every argument.  Not installed and
+// not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tern {
+
+// Launch geometry and the ld / alignment facts the launchers rely on are
+// established by the caller (api.hip); each launcher returns the HIP status of
+// its launch.
+hipError_t launch_quantize(const void* w, bool w_is_bf16, int64_t n, int64_t k, int64_t ldw,
+                           int8_t* t, int64_t ldt, float* s, hipStream_t stream);
+
+hipError_t launch_pack(const int8_t* t, int64_t n, int64_t k, int64_t ldt, uint8_t* p,
+                       int64_t ldp, hipStream_t stream);
+
+hipError_t launch_unpack(const uint8_t* p, int64_t n, int64_t k, int64_t ldp, int8_t* t,
+                         int64_t ldt, hipStream_t stream);
+
+hipError_t launch_gemm(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const uint8_t* p,
+                       int64_t n, int64_t ldp, const float* s, uint16_t* y, int64_t ldy,
+                       hipStream_t stream);
+
+}  // namespace tern

@@ -1,0 +1,140 @@
+// 2-bit storage of ternary weights and its inverse.
+//
+// "1.58-bit FLUX" (arXiv 2412.18653), section 1: the 1.58-bit weights are
+// stored as 2-bit signed integers, compressing them from 16 bits.  Layout
+// (the reading used; the pages do not fix it): weight k of a row is the low
+// two bits of its two's-complement value, in bits 2*(k%4) .. 2*(k%4)+1 of byte
+// k/4 of the row.
+//
+// Both kernels are HBM-bound streams.  One thread handles one 16-weight group
+// (16 int8 <-> one 32-bit word of codes) with 16-byte int8 accesses when the
+// row pointer allows it; a grid-stride loop covers any n x k.
+#include "internal.h"
+
+namespace tern {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ inline bool aligned_dev(const void* p, uintptr_t a) {
+  return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
+}
+
+// Four int8 values (one per byte of v) -> one byte of 2-bit codes.
+__device__ inline uint32_t pack4(uint32_t v) {
+  const uint32_t x = v & 0x03030303u;
+  return (x | (x >> 6) | (x >> 12) | (x >> 18)) & 0xFFu;
+}
+
+// One byte of 2-bit codes -> four sign-extended int8 values (one per byte).
+// The 2-bit fields are spread to the low bits of each byte, then a byte
+// permute looks each one up in {00 -> 0, 01 -> 1, 10 -> -2, 11 -> -1}.
+__device__ inline uint32_t unpack4(uint32_t b) {
+  const uint32_t sel = (b | (b << 6) | (b << 12) | (b << 18)) & 0x03030303u;
+  return __builtin_amdgcn_perm(0u, 0xFFFE0100u, sel);
+}
+
+__global__ __launch_bounds__(kThreads) void pack_kernel(const int8_t* __restrict__ t, int64_t n,
+                                                        int64_t k, int64_t ldt,
+                                                        uint8_t* __restrict__ p, int64_t ldp) {
+  const int64_t nbytes = (k + 3) / 4;
+  const int64_t groups = (nbytes + 3) / 4;  // 16 weights per group
+  const int64_t total = n * groups;
+  for (int64_t idx = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; idx < total;
+       idx += static_cast<int64_t>(gridDim.x) * kThreads) {
+    const int64_t row = idx / groups;
+    const int64_t g = idx - row * groups;
+    const int64_t k0 = g * 16;
+    const int8_t* src = t + row * ldt + k0;
+    uint32_t d[4];
+    if (k0 + 16 <= k && aligned_dev(src, 16)) {
+      const uint4 v = *reinterpret_cast<const uint4*>(src);
+      d[0] = v.x;
+      d[1] = v.y;
+      d[2] = v.z;
+      d[3] = v.w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t kk = k0 + 4 * j + i;
+          if (kk < k) w |= static_cast<uint32_t>(static_cast<uint8_t>(src[4 * j + i])) << (8 * i);
+        }
+        d[j] = w;
+      }
+    }
+    const uint32_t word = pack4(d[0]) | (pack4(d[1]) << 8) | (pack4(d[2]) << 16) | (pack4(d[3]) << 24);
+    uint8_t* dst = p + row * ldp + 4 * g;
+    if (4 * g + 4 <= nbytes && aligned_dev(dst, 4)) {
+      *reinterpret_cast<uint32_t*>(dst) = word;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (4 * g + j < nbytes) dst[j] = static_cast<uint8_t>(word >> (8 * j));
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void unpack_kernel(const uint8_t* __restrict__ p, int64_t n,
+                                                          int64_t k, int64_t ldp,
+                                                          int8_t* __restrict__ t, int64_t ldt) {
+  const int64_t nbytes = (k + 3) / 4;
+  const int64_t groups = (nbytes + 3) / 4;
+  const int64_t total = n * groups;
+  for (int64_t idx = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; idx < total;
+       idx += static_cast<int64_t>(gridDim.x) * kThreads) {
+    const int64_t row = idx / groups;
+    const int64_t g = idx - row * groups;
+    const uint8_t* src = p + row * ldp + 4 * g;
+    uint32_t word = 0;
+    if (4 * g + 4 <= nbytes && aligned_dev(src, 4)) {
+      word = *reinterpret_cast<const uint32_t*>(src);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (4 * g + j < nbytes) word |= static_cast<uint32_t>(src[j]) << (8 * j);
+    }
+    uint32_t d[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) d[j] = unpack4((word >> (8 * j)) & 0xFFu);
+    const int64_t k0 = g * 16;
+    int8_t* dst = t + row * ldt + k0;
+    if (k0 + 16 <= k && aligned_dev(dst, 16)) {
+      *reinterpret_cast<uint4*>(dst) = make_uint4(d[0], d[1], d[2], d[3]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (k0 + j < k) dst[j] = static_cast<int8_t>(d[j / 4] >> (8 * (j % 4)));
+    }
+  }
+}
+
+inline unsigned grid_for(int64_t work_items) {
+  int64_t blocks = (work_items + kThreads - 1) / kThreads;
+  const int64_t cap = 256 * 64;  // enough workgroups to fill 256 CUs many times over
+  if (blocks > cap) blocks = cap;
+  if (blocks < 1) blocks = 1;
+  return static_cast<unsigned>(blocks);
+}
+
+}  // namespace
+
+hipError_t launch_pack(const int8_t* t, int64_t n, int64_t k, int64_t ldt, uint8_t* p,
+                       int64_t ldp, hipStream_t stream) {
+  const int64_t groups = ((k + 3) / 4 + 3) / 4;
+  hipLaunchKernelGGL(pack_kernel, dim3(grid_for(n * groups)), dim3(kThreads), 0, stream, t, n, k,
+                     ldt, p, ldp);
+  return hipGetLastError();
+}
+
+hipError_t launch_unpack(const uint8_t* p, int64_t n, int64_t k, int64_t ldp, int8_t* t,
+                         int64_t ldt, hipStream_t stream) {
+  const int64_t groups = ((k + 3) / 4 + 3) / 4;
+  hipLaunchKernelGGL(unpack_kernel, dim3(grid_for(n * groups)), dim3(kThreads), 0, stream, p, n,
+                     k, ldp, t, ldt);
+  return hipGetLastError();
+}
+
+}  // namespace tern

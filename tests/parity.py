@@ -1,0 +1,139 @@
+"""Shared helpers of the GPU parity tests: run a case through the C-ABI on the
+GPU and through the CPU oracle on the same seeded inputs, then compare.
+
+Bars (the readings behind them are documented in the design notes):
+  * ternary codes, scales and packed bytes: bit-exact;
+  * layer output: |y - y_ref| <= 8e-3 |y_ref| + 1e-3 s_n ||x_m||_2 for every
+    compared element, y_ref being the oracle's unrounded double result.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+import tern_inputs
+import ternary_weight_quantized_tern_amd as tern
+
+REL_TOL = 8e-3
+NORM_TOL = 1e-3
+DEV = "cuda:0"
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+
+
+def gpu_quantize_pack(w_cpu: torch.Tensor):
+    """GPU path: W -> (T, s) -> P, returned on the host."""
+    w = w_cpu.to(DEV)
+    t, s = tern.quantize(w)
+    p = tern.pack(t)
+    torch.cuda.synchronize()
+    return t, s, p
+
+
+def oracle_weights(w_cpu: torch.Tensor):
+    if w_cpu.dtype == torch.bfloat16:
+        t, s = oracle.oracle_quantize(tern_inputs.bf16_bits(w_cpu))
+    else:
+        t, s = oracle.oracle_quantize(w_cpu.numpy())
+    return t, s, oracle.oracle_pack(t)
+
+
+def assert_bitexact_weights(t_gpu, s_gpu, p_gpu, t_ref, s_ref, p_ref, what=""):
+    k = t_ref.shape[1]
+    tg = t_gpu.cpu().numpy()
+    sg = s_gpu.cpu().numpy()
+    pg = p_gpu.cpu().numpy()[:, : p_ref.shape[1]]
+    bad_t = int(np.count_nonzero(tg[:, :k] != t_ref))
+    bad_s = int(np.count_nonzero(sg.view(np.uint32) != s_ref.view(np.uint32)))
+    bad_p = int(np.count_nonzero(pg != p_ref))
+    assert bad_t == 0 and bad_s == 0 and bad_p == 0, \
+        f"{what}: {bad_t} codes, {bad_s} scales, {bad_p} packed bytes differ"
+
+
+def row_norms(x_bits: np.ndarray) -> np.ndarray:
+    xv = (x_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return np.sqrt(np.sum(xv * xv, axis=1))
+
+
+def bf16_to_f64(y: torch.Tensor) -> np.ndarray:
+    return y.cpu().float().numpy().astype(np.float64)
+
+
+def assert_within_tolerance(y_gpu: np.ndarray, y_ref: np.ndarray, s: np.ndarray,
+                            xnorm: np.ndarray, what=""):
+    bound = REL_TOL * np.abs(y_ref) + NORM_TOL * s.astype(np.float64)[None, :] * xnorm[:, None]
+    err = np.abs(y_gpu - y_ref)
+    bad = err > bound
+    if np.any(bad) or not np.all(np.isfinite(y_gpu)):
+        idx = np.argwhere(bad | ~np.isfinite(y_gpu))
+        r, c = idx[0]
+        raise AssertionError(
+            f"{what}: {len(idx)} of {y_ref.size} outputs outside tolerance; first at (m={r}, n={c}):"
+            f" gpu={y_gpu[r, c]!r} ref={y_ref[r, c]!r} bound={bound[r, c]!r}")
+    return float(np.max(err / np.maximum(bound, 1e-300)))
+
+
+def edge_indices(size: int, tile: int = 256, extra: int = 0, seed: int = 0) -> np.ndarray:
+    """Rows/columns at every tile and MFMA-subtile edge, plus a seeded random sample."""
+    idx = set()
+    for base in range(0, size, tile):
+        for off in (0, 1, 31, 32, 63, 64, 127, 128, 129, 191, 255):
+            if base + off < size:
+                idx.add(base + off)
+        if len(idx) > 4096:
+            break
+    for v in (size - 1, size - 2, size - 31, size - 32, size - 33):
+        if 0 <= v < size:
+            idx.add(v)
+    if extra:
+        rng = np.random.default_rng(seed)
+        idx.update(rng.integers(0, size, size=extra).tolist())
+    return np.array(sorted(idx), dtype=np.int64)
+
+
+def gemm_gpu(x_cpu: torch.Tensor, p_gpu: torch.Tensor, s_gpu: torch.Tensor, k: int):
+    x = x_cpu.to(DEV)
+    y = torch.empty((x.shape[0], p_gpu.shape[0]), dtype=torch.bfloat16, device=DEV)
+    tern.tern_gemm(x, p_gpu, s_gpu, y, k)
+    torch.cuda.synchronize()
+    return y
+
+
+def check_layer(x_cpu: torch.Tensor, w_cpu: torch.Tensor, what: str, rows=None, cols=None,
+                full: bool = False, repeat_check: bool = False):
+    """Quantize+pack bit-exact on every weight; layer output on every element
+    (``full``) or on the given rows x all columns plus all rows x given columns."""
+    m, k = x_cpu.shape
+    t_ref, s_ref, p_ref = oracle_weights(w_cpu)
+    t_g, s_g, p_g = gpu_quantize_pack(w_cpu)
+    assert_bitexact_weights(t_g, s_g, p_g, t_ref, s_ref, p_ref, what)
+    # the packed codes round-trip on the GPU
+    back = tern.unpack(p_g, k)
+    torch.cuda.synchronize()
+    assert torch.equal(back.cpu(), torch.from_numpy(t_ref)), f"{what}: unpack(pack(T)) != T"
+    del back, t_g
+
+    y = gemm_gpu(x_cpu, p_g, s_g, k)
+    if repeat_check:
+        y2 = gemm_gpu(x_cpu, p_g, s_g, k)
+        assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), f"{what}: not deterministic"
+    yh = bf16_to_f64(y)
+    xb = tern_inputs.bf16_bits(x_cpu)
+    xnorm = row_norms(xb)
+    worst = 0.0
+    if full:
+        y_ref = oracle.oracle_gemm(xb, p_ref, s_ref, k=k)
+        worst = assert_within_tolerance(yh, y_ref, s_ref, xnorm, what)
+    else:
+        if rows is not None:
+            y_ref = oracle.oracle_gemm(xb[rows], p_ref, s_ref, k=k)
+            worst = max(worst, assert_within_tolerance(yh[rows], y_ref, s_ref, xnorm[rows],
+                                                       what + " (rows)"))
+        if cols is not None:
+            y_ref = oracle.oracle_gemm(xb, p_ref[cols], s_ref[cols], k=k)
+            worst = max(worst, assert_within_tolerance(yh[:, cols], y_ref, s_ref[cols], xnorm,
+                                                       what + " (cols)"))
+    return worst

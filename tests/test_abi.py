@@ -1,0 +1,149 @@
+"""Host-side checks of the C-ABI library (no GPU needed, no kernel launched).
+
+The library must load, export every function ``include/ternary.h`` declares,
+and reject bad arguments with the documented status before touching the GPU.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ternary.h")
+
+tern = pytest.importorskip("ternary_weight_quantized_tern_amd",
+                           reason="libternary.so not built")
+lib = tern.library()
+
+
+def declared_functions():
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tern_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted(tern.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", tern.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (tern_[a-z_]+)\b", out))
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_header_compiles_as_c_and_matches_enum_values(tmp_path):
+    src = tmp_path / "probe.c"
+    src.write_text(
+        '#include "ternary.h"\n#include <stdio.h>\n'
+        "int main(void){printf(\"%d %d %d %d %d %d %d %d %d %d\\n\", TERN_OK, TERN_ERR_NULL,"
+        " TERN_ERR_SHAPE, TERN_ERR_ALIGN, TERN_ERR_STRIDE, TERN_ERR_DTYPE, TERN_ERR_HIP,"
+        " TERN_F32, TERN_BF16, TERN_QUANTIZE_MAX_K); return 0;}\n")
+    exe = tmp_path / "probe"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", f"-I{os.path.dirname(HEADER)}",
+                    str(src), "-o", str(exe)], check=True)
+    vals = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True,
+                                           check=True).stdout.split()]
+    assert vals == [tern.TERN_OK, tern.TERN_ERR_NULL, tern.TERN_ERR_SHAPE, tern.TERN_ERR_ALIGN,
+                    tern.TERN_ERR_STRIDE, tern.TERN_ERR_DTYPE, tern.TERN_ERR_HIP, tern.TERN_F32,
+                    tern.TERN_BF16, tern.TERN_QUANTIZE_MAX_K]
+
+
+def test_status_strings():
+    seen = set()
+    for code in range(7):
+        sstr = tern.tern_status_string(code)
+        assert sstr and sstr not in seen
+        seen.add(sstr)
+    assert "unknown" in tern.tern_status_string(99)
+
+
+# Fake but well-aligned, non-null device addresses: every call below is
+# rejected (or is a no-op) during host validation, so nothing is dereferenced
+# and no HIP call is made.
+A = 1 << 20
+NULL = None
+
+
+def test_quantize_validation():
+    q = lib.tern_quantize
+    assert q(A, 7, 4, 64, 64, A, 64, A, NULL) == tern.TERN_ERR_DTYPE
+    assert q(A, 0, -1, 64, 64, A, 64, A, NULL) == tern.TERN_ERR_SHAPE
+    assert q(A, 0, 4, 32769, 32769, A, 32769, A, NULL) == tern.TERN_ERR_SHAPE
+    assert q(A, 0, 4, 0, 64, A, 64, A, NULL) == tern.TERN_ERR_SHAPE
+    assert q(NULL, 0, 0, 64, 64, NULL, 64, NULL, NULL) == tern.TERN_OK   # n == 0: no-op
+    assert q(NULL, 0, 4, 64, 64, A, 64, A, NULL) == tern.TERN_ERR_NULL
+    assert q(A, 0, 4, 64, 64, NULL, 64, A, NULL) == tern.TERN_ERR_NULL
+    assert q(A, 0, 4, 64, 64, A, 64, NULL, NULL) == tern.TERN_ERR_NULL
+    assert q(A, 0, 4, 64, 63, A, 64, A, NULL) == tern.TERN_ERR_STRIDE
+    assert q(A, 0, 4, 64, 64, A, 63, A, NULL) == tern.TERN_ERR_STRIDE
+    assert q(A + 2, 0, 4, 64, 64, A, 64, A, NULL) == tern.TERN_ERR_ALIGN  # fp32 needs 4 bytes
+    assert q(A, 0, 4, 64, 64, A, 64, A + 1, NULL) == tern.TERN_ERR_ALIGN
+
+
+def test_pack_unpack_validation():
+    for fn in (lib.tern_pack, lib.tern_unpack):
+        assert fn(A, -1, 8, 8, A, 2, NULL) == tern.TERN_ERR_SHAPE
+        assert fn(A, 3, -8, 8, A, 2, NULL) == tern.TERN_ERR_SHAPE
+        assert fn(NULL, 0, 8, 8, NULL, 2, NULL) == tern.TERN_OK
+        assert fn(NULL, 3, 0, 8, NULL, 2, NULL) == tern.TERN_OK
+        assert fn(NULL, 3, 8, 8, A, 8, NULL) == tern.TERN_ERR_NULL
+        assert fn(A, 3, 8, 8, NULL, 8, NULL) == tern.TERN_ERR_NULL
+    assert lib.tern_pack(A, 3, 9, 8, A, 3, NULL) == tern.TERN_ERR_STRIDE     # ldt < k
+    assert lib.tern_pack(A, 3, 9, 9, A, 2, NULL) == tern.TERN_ERR_STRIDE     # ldp < ceil(k/4)
+    assert lib.tern_unpack(A, 3, 9, 2, A, 9, NULL) == tern.TERN_ERR_STRIDE
+    assert lib.tern_unpack(A, 3, 9, 3, A, 8, NULL) == tern.TERN_ERR_STRIDE
+
+
+def test_gemm_validation():
+    g = lib.tern_gemm
+    ok = dict(x=A, m=8, k=128, ldx=128, p=A, n=16, ldp=32, s=A, y=A, ldy=16)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return g(a["x"], a["m"], a["k"], a["ldx"], a["p"], a["n"], a["ldp"], a["s"], a["y"],
+                 a["ldy"], NULL)
+
+    assert call(m=-1) == tern.TERN_ERR_SHAPE
+    assert call(k=100, ldx=128) == tern.TERN_ERR_SHAPE        # k % 64 != 0
+    assert call(n=2 ** 31) == tern.TERN_ERR_SHAPE
+    assert call(m=0, x=NULL, p=NULL, s=NULL, y=NULL) == tern.TERN_OK
+    assert call(n=0, x=NULL, p=NULL, s=NULL, y=NULL) == tern.TERN_OK
+    for name in ("x", "p", "s", "y"):
+        assert call(**{name: NULL}) == tern.TERN_ERR_NULL
+    assert call(ldx=120) == tern.TERN_ERR_STRIDE
+    assert call(ldp=16) == tern.TERN_ERR_STRIDE                # < k/4
+    assert call(ldy=15) == tern.TERN_ERR_STRIDE
+    assert call(ldx=1 << 23) == tern.TERN_ERR_STRIDE           # beyond 32-bit block offsets
+    assert call(ldp=1 << 24) == tern.TERN_ERR_STRIDE
+    assert call(x=A + 8) == tern.TERN_ERR_ALIGN
+    assert call(p=A + 4) == tern.TERN_ERR_ALIGN
+    assert call(ldx=132) == tern.TERN_ERR_ALIGN
+    assert call(ldp=40) == tern.TERN_ERR_ALIGN
+    assert call(y=A + 1) == tern.TERN_ERR_ALIGN
+    assert call(s=A + 2) == tern.TERN_ERR_ALIGN
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(4, 64, dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        tern.tern_gemm(x, torch.zeros(4, 16, dtype=torch.uint8), torch.zeros(4),
+                       torch.zeros(4, 4, dtype=torch.bfloat16))
+    with pytest.raises(TypeError):
+        tern.quantize(torch.zeros(4, 64))
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    env = dict(os.environ, TERN_LIB=str(tmp_path / "nope.so"))
+    r = subprocess.run(["python", "-c", "import ternary_weight_quantized_tern_amd"], cwd=ROOT,
+                       env=env, capture_output=True, text=True)
+    assert r.returncode != 0 and "no CPU fallback" in r.stderr

@@ -1,0 +1,208 @@
+"""GPU parity: every library entry point against the CPU oracle, through the
+C-ABI, on seeded inputs.  Small cases span several 256-wide tiles and ragged
+edges and are compared on every element; the five workloads run at their
+full sizes with every weight compared bit-exactly and the layer output
+compared on tile-edge and sampled rows and columns.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tern_inputs
+from parity import (DEV, assert_bitexact_weights, assert_within_tolerance, bf16_to_f64,
+                    check_layer, edge_indices, gemm_gpu, gpu_quantize_pack, log,
+                    oracle_weights, row_norms)
+
+pytestmark = pytest.mark.gpu
+tern = pytest.importorskip("ternary_weight_quantized_tern_amd")
+
+
+# ---------------------------------------------------------------------------
+# quantize / pack / unpack on small and edge-case inputs
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,k", [(1, 1), (3, 5), (7, 64), (33, 257), (64, 3072), (5, 32768),
+                                 (300, 1000), (2, 12289)])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_quantize_pack_random(n, k, dtype):
+    log(f"quantize n={n} k={k} {dtype}")
+    _, w = tern_inputs.draw(1, k, n, seed=1000 * n + k)
+    w = w.to(dtype)
+    t_ref, s_ref, p_ref = oracle_weights(w)
+    t, s, p = gpu_quantize_pack(w)
+    assert_bitexact_weights(t, s, p, t_ref, s_ref, p_ref, f"n={n} k={k}")
+
+
+def test_quantize_special_rows():
+    rows = [
+        [3.0, 2.0, 1.0, 0.0], [-3.0, -2.0, -1.0, -0.0], [0.0, 0.0, 0.0, 0.0],
+        [-0.0, 0.0, -0.0, 0.0], [0.0, 0.0, 0.0, 8.0], [0.5, -0.5, 0.5, -0.5],
+        [1.0, 1.0, 1.0, -5.0], [0.75, -1.0, -4.25, 0.0],
+        [1e-45, 0.0, 0.0, 0.0],                      # subnormal maximum
+        [1e-40, -3e-41, 7e-42, 0.0],                 # all subnormal
+        [3e38, -3e38, 1.0, 0.0],                     # near the top of fp32
+        [1.0, 2.0 ** -30, 2.0 ** -60, 2.0 ** -100],  # many binades
+    ]
+    w = torch.tensor(rows, dtype=torch.float32)
+    t_ref, s_ref, p_ref = oracle_weights(w)
+    t, s, p = gpu_quantize_pack(w)
+    assert_bitexact_weights(t, s, p, t_ref, s_ref, p_ref, "special rows")
+
+
+def test_quantize_strided_views_and_bf16_special():
+    _, w = tern_inputs.draw(1, 200, 40, seed=7)
+    big = torch.zeros(40, 264)
+    big[:, :200] = w
+    big[:, 200:] = 99.0                     # must be ignored
+    view = big[:, :200]
+    t_ref, s_ref, _ = oracle_weights(w)
+    wg = big.to(DEV)[:, :200]
+    t = torch.full((40, 208), 7, dtype=torch.int8, device=DEV)[:, :200]
+    s = torch.empty(40, device=DEV)
+    tern.tern_quantize(wg, t, s)
+    torch.cuda.synchronize()
+    assert view.stride(0) == 264
+    assert np.array_equal(t.cpu().numpy(), t_ref)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5, 15, 16, 17, 63, 64, 65, 255, 1153])
+def test_pack_unpack_ragged(k):
+    n = 37
+    t = tern_inputs.random_ternary(n, k, seed=k).numpy()
+    p_ref = oracle.oracle_pack(t)
+    nb = (k + 3) // 4
+    ldp = nb + 13
+    tg = torch.from_numpy(t).to(DEV)
+    p = torch.full((n, ldp), 0xA5, dtype=torch.uint8, device=DEV)
+    tern.tern_pack(tg, p, k)
+    tout = torch.full((n, k + 3), 77, dtype=torch.int8, device=DEV)
+    tern.tern_unpack(p, tout, k)
+    torch.cuda.synchronize()
+    ph = p.cpu().numpy()
+    assert np.array_equal(ph[:, :nb], p_ref)
+    assert np.all(ph[:, nb:] == 0xA5)               # bytes past ceil(k/4) untouched
+    th = tout.cpu().numpy()
+    assert np.array_equal(th[:, :k], t)
+    assert np.all(th[:, k:] == 77)
+
+
+def test_unpack_all_byte_values():
+    allb = np.tile(np.arange(256, dtype=np.uint8), (3, 1))      # [3, 256] -> k = 1024
+    t_ref = oracle.oracle_unpack(allb, 1024)
+    t = tern.unpack(torch.from_numpy(allb).to(DEV), 1024)
+    torch.cuda.synchronize()
+    assert np.array_equal(t.cpu().numpy(), t_ref)
+    assert t_ref.min() == -2
+
+
+# ---------------------------------------------------------------------------
+# layer output on small shapes (every element)
+# ---------------------------------------------------------------------------
+
+GEMM_SHAPES = [
+    (1, 64, 1), (16, 256, 512), (8, 1152, 300), (300, 320, 520), (257, 128, 255),
+    (513, 192, 700), (256, 64, 256), (255, 512, 257), (64, 4096, 96), (1000, 64, 33),
+]
+
+
+@pytest.mark.parametrize("m,k,n", GEMM_SHAPES)
+def test_gemm_small_all_elements(m, k, n):
+    log(f"gemm m={m} k={k} n={n}")
+    x, w = tern_inputs.draw(m, k, n, seed=m * 7919 + k * 31 + n,
+                            x_dist="student_t3" if m % 2 else "normal")
+    check_layer(x, w, f"gemm {m}x{k}x{n}", full=True, repeat_check=True)
+
+
+def test_gemm_strided_operands():
+    m, k, n = 130, 192, 140
+    x, w = tern_inputs.draw(m, k, n, seed=99)
+    t_ref, s_ref, p_ref = oracle_weights(w)
+    xg = torch.zeros((m, k + 72), dtype=torch.bfloat16, device=DEV)
+    xg[:, :k] = x.to(DEV)
+    xg[:, k:] = float("nan")                          # must never be read
+    pg = torch.zeros((n, 80), dtype=torch.uint8, device=DEV)
+    pg[:, : k // 4] = torch.from_numpy(p_ref).to(DEV)
+    pg[:, k // 4:] = 0xAA                              # would decode as -2s
+    sg = torch.from_numpy(s_ref).to(DEV)
+    y = torch.full((m, n + 6), 1.0, dtype=torch.bfloat16, device=DEV)
+    tern.tern_gemm(xg[:, :k], pg, sg, y[:, :n], k)
+    torch.cuda.synchronize()
+    yh = bf16_to_f64(y)
+    assert np.all(yh[:, n:] == 1.0)                   # columns past n untouched
+    xb = tern_inputs.bf16_bits(x)
+    y_ref = oracle.oracle_gemm(xb, p_ref, s_ref, k=k)
+    assert_within_tolerance(yh[:, :n], y_ref, s_ref, row_norms(xb), "strided")
+
+
+def test_gemm_k_zero_writes_zeros():
+    m, n = 5, 7
+    y = torch.full((m, n), 3.0, dtype=torch.bfloat16, device=DEV)
+    x = torch.zeros((m, 64), dtype=torch.bfloat16, device=DEV)
+    p = torch.zeros((n, 16), dtype=torch.uint8, device=DEV)
+    s = torch.ones(n, device=DEV)
+    tern.tern_gemm(x, p, s, y, 0)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(y.float()).item() == 0
+
+
+def test_gemm_zero_scale_row_gives_zero_column():
+    m, k, n = 40, 128, 50
+    x, w = tern_inputs.draw(m, k, n, seed=5)
+    w[3] = 0.0
+    t, s, p = gpu_quantize_pack(w)
+    y = gemm_gpu(x, p, s, k)
+    assert torch.count_nonzero(y[:, 3].float()).item() == 0
+
+
+def test_gemm_error_status_through_binding():
+    x = torch.zeros((4, 100), dtype=torch.bfloat16, device=DEV)
+    p = torch.zeros((4, 32), dtype=torch.uint8, device=DEV)
+    s = torch.ones(4, device=DEV)
+    y = torch.empty((4, 4), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(tern.TernError) as e:
+        tern.tern_gemm(x, p, s, y, 100)
+    assert e.value.status == tern.TERN_ERR_SHAPE
+
+
+# ---------------------------------------------------------------------------
+# the five workloads at full size
+# ---------------------------------------------------------------------------
+
+def _run_workload_layer(layer, n_extra=192):
+    log(f"workload layer {layer.name} m={layer.m} k={layer.k} n={layer.n} seed={layer.seed}")
+    x, w = tern_inputs.draw_layer(layer)
+    rows = edge_indices(layer.m, extra=n_extra, seed=layer.seed)
+    cols = edge_indices(layer.n, extra=n_extra, seed=layer.seed + 1)
+    full = layer.m * layer.n * layer.k <= 2 ** 26
+    worst = check_layer(x, w, layer.name, rows=rows, cols=cols, full=full,
+                        repeat_check=(layer.seed % 7 == 0))
+    log(f"  ok, worst error / bound = {worst:.3f}")
+
+
+def test_workload_single():
+    _run_workload_layer(tern_inputs.WORKLOADS["single"][0])
+
+
+def test_workload_flux_qkv():
+    _run_workload_layer(tern_inputs.WORKLOADS["flux_qkv"][0])
+
+
+@pytest.mark.parametrize("i", [0, 1])
+def test_workload_flux_mlp(i):
+    _run_workload_layer(tern_inputs.WORKLOADS["flux_mlp"][i])
+
+
+@pytest.mark.parametrize("i", [0, 1, 2, 3])
+def test_workload_dit(i):
+    _run_workload_layer(tern_inputs.WORKLOADS["dit"][i])
+
+
+@pytest.mark.parametrize("block", range(38))
+def test_workload_flux_single_stream(block):
+    layers = tern_inputs.WORKLOADS["flux_single_stream"]
+    for layer in layers[2 * block: 2 * block + 2]:
+        _run_workload_layer(layer, n_extra=64)
