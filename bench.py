@@ -1,0 +1,290 @@
+#!/usr/bin/env python3
+"""Throughput of the 1.58-bit linear layer on one MI355X.
+
+One step is one pass of the whole path over one layer's synthetic inputs,
+already resident in HBM: tern_quantize (fp32 weights -> codes + scales),
+tern_pack, tern_unpack, and tern_gemm (bf16 X times the packed ternary
+weights, fused scale epilogue).  The reported value is whole-step throughput
+in effective TFLOP/s, 2*M*N*K per step; the roofline object describes the
+dominant kernel (tern_gemm) measured with HIP events on the stream it is
+launched on; the CPU baseline is the oracle timed on this host on a bounded
+sample of the same step.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload flux_qkv]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "tern_gemm effective TFLOP/s + % of MFMA/HBM roofline, FLUX linears M=4608"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak
+RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+GEMM_SRC = os.path.join(ROOT, "ternary_weight_quantized_tern_amd", "csrc", "gemm.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="flux_qkv")
+    ap.add_argument("--layers", type=int, default=0,
+                    help="use only the first L layers of a multi-layer workload (0 = all)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle's layer-output sample")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run a device copy of this size (for counter calibration)")
+    ap.add_argument("--gemm-only-reps", type=int, default=0,
+                    help="after the steps, launch tern_gemm alone this many times (profiling)")
+    return ap.parse_args()
+
+
+def gemm_alg_bytes(m, k, n):
+    return 2 * m * k + n * k // 4 + 4 * n + 2 * m * n
+
+
+def source_digest(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def load_traffic(workload):
+    """HBM bytes per tern_gemm launch from committed counter summaries, if
+    they were taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"tern_gemm_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("gemm_source_sha256") != source_digest(GEMM_SRC):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(layers, inputs, target_s):
+    """The oracle, as it stands, on this host: all weights of every layer go
+    through quantize, pack and unpack; the layer output is computed for a
+    leading sample of X rows and scaled to all M rows."""
+    import oracle
+    import tern_inputs
+    cores = min(len(os.sched_getaffinity(0)), 16)
+    t_weights = 0.0
+    t_gemm = 0.0
+    rows_used = []
+    flops = 0
+    for layer, (x, w) in zip(layers, inputs):
+        t0 = time.perf_counter()
+        t_ref, s_ref = oracle.oracle_quantize(w.numpy())
+        p_ref = oracle.oracle_pack(t_ref)
+        oracle.oracle_unpack(p_ref, layer.k)
+        t_weights += time.perf_counter() - t0
+        xb = tern_inputs.bf16_bits(x)
+        pilot = min(8, layer.m)
+        t0 = time.perf_counter()
+        oracle.oracle_gemm(xb[:pilot], p_ref, s_ref, nthreads=cores)
+        dt = time.perf_counter() - t0
+        per_row = dt / pilot
+        rows = int(max(pilot, min(layer.m, (target_s / len(layers)) / max(per_row, 1e-9))))
+        if rows > pilot:
+            t0 = time.perf_counter()
+            oracle.oracle_gemm(xb[:rows], p_ref, s_ref, nthreads=cores)
+            dt = time.perf_counter() - t0
+        t_gemm += dt * layer.m / rows
+        rows_used.append(rows)
+        flops += 2 * layer.m * layer.n * layer.k
+    t_step = t_weights + t_gemm
+    return {
+        "value": flops / t_step / 1e12,
+        "unit": "TFLOP/s",
+        "cores": cores,
+        "kind": "oracle",
+        "seconds_per_step_extrapolated": t_step,
+        "sample": (f"oracle quantize+pack+unpack on all weights ({t_weights:.2f} s), oracle layer "
+                   f"output on the first {rows_used} X rows of M={[l.m for l in layers]} "
+                   f"scaled to all rows; {cores} threads"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(the ternary linear layer is measured on one MI355X).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import tern_inputs
+    import ternary_weight_quantized_tern_amd as tern
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    layers = list(tern_inputs.iter_layers(args.workload))
+    if args.layers:
+        layers = layers[: args.layers]
+    print(f"# workload {args.workload}: {len(layers)} layer(s), drawing inputs", file=sys.stderr,
+          flush=True)
+    host_inputs = [tern_inputs.draw_layer(layer) for layer in layers]
+
+    bufs = []
+    for layer, (x, w) in zip(layers, host_inputs):
+        ldp = tern.packed_row_bytes(layer.k)
+        bufs.append(dict(
+            x=x.to(dev), w=w.to(dev),
+            t=torch.empty((layer.n, layer.k), dtype=torch.int8, device=dev),
+            s=torch.empty((layer.n,), dtype=torch.float32, device=dev),
+            p=torch.zeros((layer.n, ldp), dtype=torch.uint8, device=dev),
+            tu=torch.empty((layer.n, layer.k), dtype=torch.int8, device=dev),
+            y=torch.empty((layer.m, layer.n), dtype=torch.bfloat16, device=dev),
+        ))
+    torch.cuda.synchronize()
+
+    names = ("tern_quantize", "tern_pack", "tern_unpack", "tern_gemm")
+
+    def step(events=None):
+        for li, (layer, b) in enumerate(zip(layers, bufs)):
+            ev = events[li] if events is not None else None
+            if ev:
+                ev[0].record()
+            tern.tern_quantize(b["w"], b["t"], b["s"])
+            if ev:
+                ev[1].record()
+            tern.tern_pack(b["t"], b["p"], layer.k)
+            if ev:
+                ev[2].record()
+            tern.tern_unpack(b["p"], b["tu"], layer.k)
+            if ev:
+                ev[3].record()
+            tern.tern_gemm(b["x"], b["p"], b["s"], b["y"], layer.k)
+            if ev:
+                ev[4].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    per_step_events = [[[torch.cuda.Event(enable_timing=True) for _ in range(5)]
+                        for _ in layers] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(per_step_events[i])
+    end.record()
+    torch.cuda.synchronize()
+    ms_total = start.elapsed_time(end)
+    ms_per_step = ms_total / args.steps
+
+    kern_ms = {nm: 0.0 for nm in names}
+    gemm_launch_ms = []
+    for i in range(args.steps):
+        for li in range(len(layers)):
+            ev = per_step_events[i][li]
+            for j, nm in enumerate(names):
+                d = ev[j].elapsed_time(ev[j + 1])
+                kern_ms[nm] += d
+                if nm == "tern_gemm":
+                    gemm_launch_ms.append(d)
+    launches = args.steps * len(layers)
+    for nm in names:
+        kern_ms[nm] /= launches
+
+    flops_step = sum(2 * l.m * l.n * l.k for l in layers)
+    value = flops_step / (ms_per_step * 1e-3) / 1e12
+
+    # Dominant kernel: tern_gemm.  Algorithmic work per launch, averaged over layers.
+    gemm_flops = flops_step / len(layers)
+    gemm_bytes = sum(gemm_alg_bytes(l.m, l.k, l.n) for l in layers) / len(layers)
+    gemm_ms = kern_ms["tern_gemm"]
+    ai = gemm_flops / gemm_bytes
+    if ai >= RIDGE:
+        achieved = gemm_flops / (gemm_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS}
+    else:
+        achieved = gemm_bytes / (gemm_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS}
+    roof["traffic"] = load_traffic(args.workload)
+    roof["kernel"] = "tern_gemm"
+    roof["avg_launch_ms"] = gemm_ms
+    roof["alg_flops_per_launch"] = gemm_flops
+    roof["alg_bytes_per_launch"] = gemm_bytes
+    roof["gbs"] = gemm_bytes / (gemm_ms * 1e-3) / 1e9
+
+    kernels = {}
+    for nm in names:
+        d = {"avg_ms": kern_ms[nm]}
+        if nm == "tern_quantize":
+            byts = sum(l.n * l.k * 4 + l.n * l.k + 4 * l.n for l in layers) / len(layers)
+        elif nm == "tern_pack":
+            byts = sum(l.n * l.k + l.n * ((l.k + 3) // 4) for l in layers) / len(layers)
+        elif nm == "tern_unpack":
+            byts = sum(l.n * ((l.k + 3) // 4) + l.n * l.k for l in layers) / len(layers)
+        else:
+            byts = gemm_bytes
+            d["tflops"] = gemm_flops / (kern_ms[nm] * 1e-3) / 1e12
+        d["alg_bytes"] = byts
+        d["gbs"] = byts / (kern_ms[nm] * 1e-3) / 1e9
+        kernels[nm] = d
+
+    if args.gemm_only_reps:
+        b, layer = bufs[0], layers[0]
+        for _ in range(args.gemm_only_reps):
+            tern.tern_gemm(b["x"], b["p"], b["s"], b["y"], layer.k)
+        torch.cuda.synchronize()
+    if args.copy_calibration_mib:
+        nbytes = args.copy_calibration_mib << 20
+        src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"# copy calibration: {nbytes} bytes read and written", file=sys.stderr)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("# timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(layers, host_inputs, args.cpu_seconds)
+
+    shape = layers[0]
+    config = {"workload": args.workload, "layers": len(layers), "m": shape.m, "k": shape.k,
+              "n": shape.n, "step": "tern_quantize+tern_pack+tern_unpack+tern_gemm",
+              "x": f"bf16 {shape.x_dist}", "w": "fp32 N(0, 0.02^2)", "seed": shape.seed}
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": config,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

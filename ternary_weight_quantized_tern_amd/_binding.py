@@ -44,7 +44,7 @@ def _load(path: str):
     if not os.path.exists(path):
         raise ImportError(
             f"libternary.so not found at {path}; build it with "
-            "`python -m ternary_weight_quantized_tern_amd.build` (no CPU fallback exists)")
+            "`python ternary_weight_quantized_tern_amd/build.py` (no CPU fallback exists)")
     lib = ctypes.CDLL(path)
     i64, vp = ctypes.c_int64, ctypes.c_void_p
     lib.tern_quantize.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, i64, vp, vp]

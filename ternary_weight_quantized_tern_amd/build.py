@@ -1,7 +1,8 @@
 """Build libternary.so in-tree with hipcc for gfx950.
 
-``python -m ternary_weight_quantized_tern_amd.build`` (or ``build_library()``)
-compiles every ``csrc/*.hip`` into one shared library next to this file.
+``python ternary_weight_quantized_tern_amd/build.py`` (or ``build_library()``)
+compiles every ``csrc/*.hip`` into one shared library next to this file.  Run
+it by path: importing the package would first try to load the library.
 """
 from __future__ import annotations
 
@@ -50,6 +51,12 @@ def build_library(out: str = LIB_PATH, extra: list | None = None, verbose: bool 
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed ({r.returncode}):\n{r.stderr}")
+        # A kernel whose host stub was not emitted shows up as an undefined
+        # symbol only when the library is loaded: load it in a child process.
+        chk = subprocess.run([sys.executable, "-c", f"import ctypes; ctypes.CDLL({tmp!r})"],
+                             capture_output=True, text=True)
+        if chk.returncode != 0:
+            raise RuntimeError(f"built library does not load:\n{chk.stderr}")
         os.replace(tmp, out)
     finally:
         if os.path.exists(tmp):
