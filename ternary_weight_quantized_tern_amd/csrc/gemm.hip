@@ -7,23 +7,25 @@
 // the bf16 matrix cores of gfx950 with fp32 accumulation.
 //
 // Design:
-//  * Block tile BM (X rows, "M") x BN (weight rows = output channels, "N"),
-//    K step 64, 256 threads = 4 waves as 2 x 2.  Each wave owns
-//    (BM/2) x (BN/2) outputs as 16 x 16 tiles of v_mfma_f32_16x16x32_bf16.
-//    288 x 192 divides M = 4608 and every FLUX width N into a multiple of
-//    256 blocks, so all 256 CUs stay busy to the last block.
+//  * Block tile 144 (X rows, "M") x 384 (weight rows = output channels, "N"),
+//    K step 64, 256 threads = 4 waves side by side along N.  Each wave owns
+//    144 x 96 outputs as 9 x 6 tiles of v_mfma_f32_16x16x32_bf16 (216
+//    accumulator registers).  144 x 384 cuts M = 4608 and every FLUX width N
+//    (3072, 9216, 12288, 15360, 21504) into an exact multiple of 256 tiles.
 //  * The weight tile is the MFMA's A operand and X the B operand, so every
 //    lane ends up with four consecutive output channels of one token and the
 //    epilogue writes 8-byte runs of Y.
-//  * Operands reach LDS without passing through registers: buffer loads with
-//    the LDS-DMA form (16 bytes per lane) fill a 3-stage ring, so the loads
-//    of step s+2 are in flight while step s computes.  Loads past the last
-//    valid row of X or of the weights return zeros (buffer range checking).
+//  * Operands reach LDS without passing through registers: buffer loads in
+//    the LDS-DMA form (16 bytes per lane) fill a 6-stage ring, four stages in
+//    flight while one is computed and the next one's operands are read.  Loads
+//    past the last valid row of X or of the weights return zeros (buffer
+//    range checking).  One barrier per K step, in its middle: the second half
+//    of the MFMAs covers the LDS reads of the next step and the DMA requests.
 //  * X rows are 128 bytes per stage, stored as 16-byte chunks XOR-swizzled
-//    by (row & 7); the swizzle is applied on the global side (each lane
+//    by ((row >> 1) & 7); the swizzle is applied on the global side (each lane
 //    fetches the chunk that belongs in its LDS slot), so the MFMA operand
-//    reads (one 16-byte chunk per lane, 16 rows at a time) hit 8 distinct
-//    bank groups.
+//    reads (one 16-byte chunk per lane, 16 rows at a time) are free of bank
+//    conflicts.
 //  * The packed weights stay packed in LDS (16 bytes = 64 codes per row per
 //    step).  Each lane reads one 32-bit word (16 codes) per 16-row tile and
 //    decodes it in registers: with codes 00 / 01 / 11 the bf16 value
@@ -33,7 +35,12 @@
 //  * Epilogue: fp32 accumulator times the fp32 channel scale, one
 //    round-to-nearest-even conversion to bf16.
 //  * Workgroups are renumbered so that each XCD (which owns its own L2)
-//    walks a contiguous, grouped range of tiles.
+//    walks a contiguous, grouped range of tiles.  When there are more tiles
+//    than CUs and K / 64 is a multiple of 6, 256 persistent workgroups walk
+//    the tiles with one unbroken DMA stream, hiding each tile's start-up
+//    latency behind the previous tile's last steps.
+#include <type_traits>
+
 #include "internal.h"
 
 namespace tern {
@@ -127,12 +134,12 @@ __device__ inline void tile_of(int bid, int grid, int tiles_m, int tiles_n, int&
   tn = r / gsm;
 }
 
-// X chunk swizzle of LDS row r: the 16-byte chunk c of a row is stored in
-// slot c ^ xswz(r).
-template <int SWZ>
-__device__ inline uint32_t xswz(uint32_t r) {
-  return SWZ == 0 ? (r & 7u) : ((r >> 1) & 7u);
-}
+// X chunk swizzle of LDS row r: the 16-byte chunk c of a 128-byte row is
+// stored in slot c ^ xswz(r).  Two rows share one 256-byte line of the 64
+// LDS banks; with ((r >> 1) & 7) the 16 rows that one 16-lane group of an
+// operand read touches (same logical chunk) land in 16 distinct 16-byte bank
+// groups, so a ds_read_b128 of 64 lanes takes the minimum four passes.
+__device__ inline uint32_t xswz(uint32_t r) { return (r >> 1) & 7u; }
 
 template <int BM, int BN, int WAVES_M>
 struct TileCfg {
@@ -155,12 +162,21 @@ struct TileCfg {
   static_assert((kWM * 128) % 1024 == 0 || kWavesM == 1, "row swizzle period");
 };
 
-template <int BM, int BN, int WAVES_M, int GM, int SWZ>
+// Y tile kernel.  With PERSIST, workgroup b computes tiles b, b + G, b + 2G,
+// ... of the XCD-aware order (G = gridDim.x, a multiple of 8, so that all of
+// a workgroup's tiles stay on its XCD), and the K steps of consecutive tiles
+// form one stream through the LDS ring: the requests run kRing-1 steps ahead
+// of the MFMAs and cross into the next tile, so a tile's first stages are in
+// LDS by the time the previous tile's epilogue ends.  Tile boundaries must
+// fall between iterations of the kRing-step unrolled loop: PERSIST requires
+// (k / 64) % kRing == 0.  Without PERSIST each workgroup computes tile b
+// only, for any k that is a multiple of 64.
+template <int BM, int BN, int WAVES_M, int GM, bool PERSIST>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
                        const uint8_t* __restrict__ p, int n, int ldp,
                        const float* __restrict__ s, uint16_t* __restrict__ y, int ldy,
-                       int tiles_m, int tiles_n, int y_vec_ok) {
+                       int tiles_m, int tiles_n, int y_flags) {
 #if defined(__HIP_DEVICE_COMPILE__)
   // (The body uses LDS address-space casts that only the device pass accepts.)
   using C = TileCfg<BM, BN, WAVES_M>;
@@ -168,8 +184,7 @@ void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
   constexpr int kTN = C::kTN;
   // One LDS object per ring stage, so that the compiler tracks each stage's
   // DMA writes separately.  kRing = 6 stages: one being read, one being read
-  // next, four in flight (the DMA stream is latency-bound, so the bytes in
-  // flight set its rate).
+  // next, four in flight.
   constexpr int kRing = 6;
   __shared__ __attribute__((aligned(1024))) uint8_t lds0[C::kStage];
   __shared__ __attribute__((aligned(1024))) uint8_t lds1[C::kStage];
@@ -178,12 +193,11 @@ void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
   __shared__ __attribute__((aligned(1024))) uint8_t lds4[C::kStage];
   __shared__ __attribute__((aligned(1024))) uint8_t lds5[C::kStage];
 
-  int tile_m, tile_n;
-  tile_of<GM>(blockIdx.x, gridDim.x, tiles_m, tiles_n, tile_m, tile_n);
-  const int m0 = tile_m * BM;
-  const int n0 = tile_n * BN;
-  const int rows_m = (m - m0) < BM ? (m - m0) : BM;
-  const int rows_n = (n - n0) < BN ? (n - n0) : BN;
+  const int num_tiles = tiles_m * tiles_n;
+  const int grid = gridDim.x;
+  const int bid = blockIdx.x;
+  const int my_tiles = PERSIST ? (num_tiles - bid + grid - 1) / grid : 1;
+  const int stages = k / kBK;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -193,12 +207,25 @@ void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
   const int l16 = lane & 15;
   const int g = lane >> 4;  // k-group of the MFMA operands
 
-  const __amdgpu_buffer_rsrc_t x_rsrc =
-      make_rsrc(x + static_cast<int64_t>(m0) * ldx,
-                static_cast<uint32_t>((static_cast<int64_t>(rows_m - 1) * ldx + k) * 2));
-  const __amdgpu_buffer_rsrc_t p_rsrc =
-      make_rsrc(p + static_cast<int64_t>(n0) * ldp,
-                static_cast<uint32_t>(static_cast<int64_t>(rows_n - 1) * ldp + k / 4));
+  // Tile coordinates and buffer resources of this workgroup's t-th tile.
+  // The resources are rebased at the tile's first row: reads past its last
+  // valid row fall outside num_records and return zeros.
+  auto tile_coords = [&](int t, int& m0, int& n0) {
+    int tm, tn;
+    tile_of<GM>(bid + t * grid, num_tiles, tiles_m, tiles_n, tm, tn);
+    m0 = tm * BM;
+    n0 = tn * BN;
+  };
+  auto tile_rsrc = [&](int t, __amdgpu_buffer_rsrc_t& xr, __amdgpu_buffer_rsrc_t& pr) {
+    int m0, n0;
+    tile_coords(t, m0, n0);
+    const int rows_m = (m - m0) < BM ? (m - m0) : BM;
+    const int rows_n = (n - n0) < BN ? (n - n0) : BN;
+    xr = make_rsrc(x + static_cast<int64_t>(m0) * ldx,
+                   static_cast<uint32_t>((static_cast<int64_t>(rows_m - 1) * ldx + k) * 2));
+    pr = make_rsrc(p + static_cast<int64_t>(n0) * ldp,
+                   static_cast<uint32_t>(static_cast<int64_t>(rows_n - 1) * ldp + k / 4));
+  };
 
   // DMA plan.  A stage is kXInstr + kPInstr loads of 1 KiB (16 bytes per
   // lane); wave w issues loads w, w+4, w+8, ... in that list.  X load q fills
@@ -214,7 +241,7 @@ void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
     dma_is_x[q] = gi < C::kXInstr;
     if (dma_is_x[q]) {
       const uint32_t r = 8u * gi + (lane >> 3);
-      const uint32_t c = (lane & 7) ^ xswz<SWZ>(r);
+      const uint32_t c = (lane & 7) ^ xswz(r);
       dma_voff[q] = (r * static_cast<uint32_t>(ldx) + 8u * c) * 2u;
       dma_lds[q] = 1024u * gi;
     } else {
@@ -224,34 +251,32 @@ void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
     }
   }
 
-  // Requests step `stage` into ring stage BUF (one of the lds* arrays, named
-  // directly so that the compiler can tell the stages apart).
-#define TERN_GEMM_DMA(BUF, STAGE, Q)                                                   \
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(dma_is_x[Q] ? x_rsrc : p_rsrc,               \
+  // Requests one step (stage STAGE of the tile whose resources are XR, PR)
+  // into ring stage BUF, one of the lds* arrays, named directly so that the
+  // compiler can tell the ring stages apart.
+#define TERN_GEMM_DMA(BUF, XR, PR, STAGE, Q)                                            \
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(dma_is_x[Q] ? (XR) : (PR),                   \
                                            (lds_void_t*)(&BUF[dma_lds[Q]]), 16,        \
                                            dma_voff[Q],                                \
                                            (STAGE) * (dma_is_x[Q] ? kBK * 2 : kBK / 4), 0, 0);
-#define TERN_GEMM_ISSUE(BUF, STAGE) \
-  _Pragma("unroll") for (int q = 0; q < C::kLoads; ++q) TERN_GEMM_DMA(BUF, STAGE, q)
+#define TERN_GEMM_ISSUE(BUF, XR, PR, STAGE) \
+  _Pragma("unroll") for (int q = 0; q < C::kLoads; ++q) TERN_GEMM_DMA(BUF, XR, PR, STAGE, q)
 
   // MFMA operand reads.  Block b of a step covers, for the lanes of k-group
   // g, k = 16 g + 8 b .. 16 g + 8 b + 7 of the step: X chunk 2 g + b of row
   // (wm*kWM + 16 i + l16), and codes 8 b .. 8 b + 7 of 32-bit word g of
   // weight row (wn*kWN + 16 j + l16).
   const uint32_t x_row0 = static_cast<uint32_t>(wm * C::kWM + l16);
-  const uint32_t xo0 = x_row0 * 128u + ((static_cast<uint32_t>(2 * g + 0) ^ xswz<SWZ>(x_row0)) << 4);
-  const uint32_t xo1 = x_row0 * 128u + ((static_cast<uint32_t>(2 * g + 1) ^ xswz<SWZ>(x_row0)) << 4);
+  const uint32_t xo0 = x_row0 * 128u + ((static_cast<uint32_t>(2 * g + 0) ^ xswz(x_row0)) << 4);
+  const uint32_t xo1 = x_row0 * 128u + ((static_cast<uint32_t>(2 * g + 1) ^ xswz(x_row0)) << 4);
   const uint32_t po = C::kXBytes + static_cast<uint32_t>(wn * C::kWN + l16) * 16u + 4u * g;
+  static_assert(C::kWM % 16 == 0, "xswz(row + 16 i) == xswz(row)");
 
   f32x4_t acc[kTN][kTM];
-#pragma unroll
-  for (int j = 0; j < kTN; ++j)
-#pragma unroll
-    for (int i = 0; i < kTM; ++i) acc[j][i] = f32x4_t{};
 
-  // Operand reads out of ring stage BUF (named directly, see above): the
-  // 32-bit code words of every weight tile and the X chunks of k-block 0
-  // (READ_A), or the X chunks of k-block 1 (READ_B).
+  // Operand reads out of ring stage BUF: the 32-bit code words of every
+  // weight tile and the X chunks of k-block 0 (READ_A), or the X chunks of
+  // k-block 1 (READ_B).
 #define TERN_GEMM_READ_A(BUF)                                                               \
   _Pragma("unroll") for (int j = 0; j < kTN; ++j)                                           \
       pw[j] = *reinterpret_cast<const uint32_t*>(&BUF[po + j * 256]);                       \
@@ -263,13 +288,18 @@ void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
       xb[i] = __builtin_bit_cast(bf16x8_t,                                                  \
                                  *reinterpret_cast<const u32x4_t*>(&BUF[xo1 + i * 2048]));
 
-  auto mfma_block = [&](const bf16x8_t (&w)[kTN], const bf16x8_t (&xv)[kTM]) {
+  // ZERO starts a new sum (the MFMA's C operand is the constant 0), so the
+  // accumulators of consecutive tiles never meet in one register value.
+  auto mfma_block = [&](const bf16x8_t (&w)[kTN], const bf16x8_t (&xv)[kTM], auto zero) {
 #pragma unroll
     for (int j = 0; j < kTN; ++j)
 #pragma unroll
       for (int i = 0; i < kTM; ++i)
-        acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w[j], xv[i], acc[j][i], 0, 0, 0);
+        acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            w[j], xv[i], decltype(zero)::value ? f32x4_t{} : acc[j][i], 0, 0, 0);
   };
+  using kAcc = std::false_type;
+  using kZero = std::true_type;
 
   // Scheduling hint for the phase after the barrier: spread the DMA requests
   // and the operand reads of the next stage between the MFMAs instead of
@@ -281,130 +311,235 @@ void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
     constexpr int kMfma = kTN * kTM;
 #pragma unroll
     for (int i = 0; i < kGroups; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x0010, 1, 0);                       // DMA
+      __builtin_amdgcn_sched_group_barrier(0x0010, 1, 0);                                 // DMA
       __builtin_amdgcn_sched_group_barrier(0x0100, (kReads + kGroups - 1) / kGroups, 0);  // LDS reads
-      __builtin_amdgcn_sched_group_barrier(0x0008, kMfma / kGroups, 0);         // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x0008, kMfma / kGroups, 0);                   // MFMA
     }
   };
 
-  // Step ST computes out of ring stage CUR.  Its k-block 0 operands were read
-  // during the previous step.  It reads k-block 1 and runs k-block 0; then,
-  // once every wave is past the barrier (so stage ST+1 has landed everywhere
-  // and stage ST-1 is no longer read by anyone), it requests stage
-  // ST+kRing-1 into ST-1's buffer DMA, reads stage ST+1's k-block 0 out of NXT, and runs
-  // k-block 1.  LDS serves each batch of reads while the other k-block's
-  // MFMAs run, and at most one batch is outstanding at any time.
-  //
-  // The main loop keeps exactly kRing-2 stages in flight at every barrier: a
-  // request past the last stage re-loads the last stage into the dead buffer
-  // (in range, never read), so that every step issues the same instructions
-  // and the compiler's wait counts stay exact.  The last one to four steps
-  // run in a tail with the waits shortened accordingly.
-  const int stages = k / kBK;
-#define TERN_GEMM_STAGE(S) ((S) < stages ? (S) : stages - 1)
-#define TERN_GEMM_HALF_A(CUR)                                      \
+  // One step out of ring stage CUR (k-block 0 operands already read): read
+  // k-block 1 and run k-block 0; then, once every wave is past the barrier
+  // (the next step's stage has landed everywhere and the previous step's stage
+  // is no longer read by anyone), request the step under the issue cursor
+  // into the previous step's buffer DMA, read the next step's k-block 0 out
+  // of NXT, and run k-block 1.  At every barrier of the unrolled loop exactly
+  // kRing-2 steps are in flight.
+#define TERN_GEMM_HALF_A(CUR, ZERO)                                    \
   phase_fence();                                                   \
   wait_lgkm0();                                                    \
   TERN_GEMM_READ_B(CUR)                                            \
   phase_fence();                                                   \
   bf16x8_t wa[kTN], wb[kTN];                                       \
   _Pragma("unroll") for (int j = 0; j < kTN; ++j) decode16(pw[j], wa[j], wb[j]); \
-  mfma_block(wa, xa);                                              \
+  mfma_block(wa, xa, ZERO{});                                      \
   phase_fence();                                                   \
   wait_lgkm0();
-#define TERN_GEMM_STEP(ST, CUR, NXT, DMA)                          \
+#define TERN_GEMM_STEP(CUR, NXT, DMA, XR, PR, STAGE, ZERO)         \
   {                                                                \
-    TERN_GEMM_HALF_A(CUR)                                          \
+    TERN_GEMM_HALF_A(CUR, ZERO)                                          \
     wait_vmcnt<(kRing - 3) * C::kLoads, true>();                   \
     lds_barrier();                                                 \
-    TERN_GEMM_ISSUE(DMA, TERN_GEMM_STAGE((ST) + kRing - 1))        \
+    TERN_GEMM_ISSUE(DMA, XR, PR, STAGE)                            \
     TERN_GEMM_READ_A(NXT)                                          \
-    mfma_block(wb, xb);                                            \
+    mfma_block(wb, xb, kAcc{});                                    \
     interleave_loads_with_mfma();                                  \
   }
-  // Tail step: requests stage ST+kRing-1 if it exists (only the first tail step
-  // can have one), waits for everything in flight, and reads the next stage
-  // if there is one.
-#define TERN_GEMM_TAIL(ST, CUR, NXT, DMA)                          \
+  // Last steps of the last tile: the next stage is waited for in full, and a
+  // request is due only while one is left.
+#define TERN_GEMM_TAIL(ST, CUR, NXT, DMA, ZERO)                    \
   {                                                                \
-    TERN_GEMM_HALF_A(CUR)                                          \
+    TERN_GEMM_HALF_A(CUR, ZERO)                                        \
     if ((ST) + 1 < stages) {                                       \
       wait_vmcnt<0, true>();                                       \
       lds_barrier();                                               \
-      if ((ST) + kRing - 1 < stages) TERN_GEMM_ISSUE(DMA, (ST) + kRing - 1) \
+      if ((ST) + kRing - 1 < stages) TERN_GEMM_ISSUE(DMA, cur_xr, cur_pr, (ST) + kRing - 1) \
       TERN_GEMM_READ_A(NXT)                                        \
       phase_fence();                                               \
     }                                                              \
-    mfma_block(wb, xb);                                            \
+    mfma_block(wb, xb, kAcc{});                                    \
   }
+
+  // Epilogue of tile t.  For MFMA tile (j, i) the lane holds output channels
+  // n = wn*kWN + 16 j + 4 g + e (e = 0..3) of token m = wm*kWM + 16 i + l16.
+  // The decode produced 2 T, so y = bf16(fp32(acc * s) * 0.5), which equals
+  // bf16(fp32(acc / 2 * s)) exactly.
+  //
+  // Whole tiles with a 16-byte aligned Y and scale vector go through LDS:
+  // each wave writes 16 of its rows at a time into its own part of ring
+  // stage lds5 (pitch kEpiPitch bytes, conflict-free for the 8-byte writes)
+  // and stores them back as 16-byte pieces of whole row segments, so every
+  // store instruction writes 5 1/3 contiguous 192-byte runs instead of 16
+  // scattered 32-byte ones.  lds5 holds no live stage here: it held the
+  // tile's last stage (all reads of it end at the barrier below) and the
+  // next request into it follows the next step's barrier.  Other tiles take
+  // the direct path, with 8-byte stores where Y allows them.
+  constexpr int kEpiPitch = 2 * C::kWN + 16;
+  static_assert(kThreads / 64 * 16 * kEpiPitch <= C::kStage, "epilogue staging fits a stage");
+  static_assert((16 * 2 * C::kWN / 16) % 64 == 0, "whole store instructions");
+  auto epilogue = [&](int t) {
+    int m0, n0;
+    tile_coords(t, m0, n0);
+    if ((y_flags & 2) && m0 + BM <= m && n0 + BN <= n) {
+      constexpr int kChunksPerRow = 2 * C::kWN / 16;              // 16-byte pieces of a row
+      constexpr int kStores = 16 * kChunksPerRow / 64;            // per lane per 16 rows
+      const uint32_t area = static_cast<uint32_t>(wave) * (16 * kEpiPitch);
+      const int col0 = n0 + wn * C::kWN;
+      f32x4_t sc[kTN];
+#pragma unroll
+      for (int j = 0; j < kTN; ++j) sc[j] = *reinterpret_cast<const f32x4_t*>(s + col0 + 16 * j + 4 * g);
+      uint32_t rd_off[kStores];
+      int64_t st_off[kStores];
+#pragma unroll
+      for (int q = 0; q < kStores; ++q) {
+        const int c = lane + 64 * q;
+        const int row = c / kChunksPerRow;
+        const int cc = c - row * kChunksPerRow;
+        rd_off[q] = area + static_cast<uint32_t>(row * kEpiPitch + cc * 16);
+        st_off[q] = static_cast<int64_t>(m0 + wm * C::kWM + row) * ldy + col0 + cc * 8;
+      }
+      const uint32_t wr_off = area + static_cast<uint32_t>(l16 * kEpiPitch + 8 * g);
+      lds_barrier();
+#pragma unroll
+      for (int i = 0; i < kTM; ++i) {
+#pragma unroll
+        for (int j = 0; j < kTN; ++j) {
+          __bf16 b[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) b[e] = static_cast<__bf16>((acc[j][i][e] * sc[j][e]) * 0.5f);
+          u32x2_t o;
+          o[0] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b[0])) |
+                 (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b[1])) << 16);
+          o[1] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b[2])) |
+                 (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b[3])) << 16);
+          *reinterpret_cast<u32x2_t*>(&lds5[wr_off + 32 * j]) = o;
+        }
+#pragma unroll
+        for (int q = 0; q < kStores; ++q) {
+          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&lds5[rd_off[q]]);
+          *reinterpret_cast<u32x4_t*>(y + st_off[q] + static_cast<int64_t>(16 * i) * ldy) = v;
+        }
+      }
+      return;
+    }
+#pragma unroll
+    for (int j = 0; j < kTN; ++j) {
+      const int ng = n0 + wn * C::kWN + 16 * j + 4 * g;
+      float sc[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sc[e] = (ng + e < n) ? s[ng + e] : 0.0f;
+#pragma unroll
+      for (int i = 0; i < kTM; ++i) {
+        const int mg = m0 + wm * C::kWM + 16 * i + l16;
+        __bf16 b[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) b[e] = static_cast<__bf16>((acc[j][i][e] * sc[e]) * 0.5f);
+        if (mg >= m) continue;
+        uint16_t* yr = y + static_cast<int64_t>(mg) * ldy + ng;
+        if ((y_flags & 1) && ng + 4 <= n) {
+          u32x2_t o;
+          o[0] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b[0])) |
+                 (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b[1])) << 16);
+          o[1] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b[2])) |
+                 (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b[3])) << 16);
+          *reinterpret_cast<u32x2_t*>(yr) = o;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (ng + e < n) yr[e] = __builtin_bit_cast(uint16_t, b[e]);
+        }
+      }
+    }
+  };
+
+  // Stage S of the current tile, clamped to its last stage: requests past
+  // the end re-load that stage into the dead buffer (in range, never read),
+  // so every step of the unrolled loop issues the same instructions and the
+  // wait counts stay exact.
+#define TERN_GEMM_CLAMP(S) ((S) < stages ? (S) : stages - 1)
+  // One unrolled iteration: steps st .. st + kRing - 1 out of ring stages 0 ..
+  // kRing - 1.  The first request is stage st + kRing - 1 of this tile, the
+  // others stages B0 .. B0 + kRing - 2 of the tile with resources BX, BP.
+#define TERN_GEMM_ITER(BX, BP, B0, ZERO)                                                 \
+  TERN_GEMM_STEP(lds0, lds1, lds5, cur_xr, cur_pr, TERN_GEMM_CLAMP(st + kRing - 1), ZERO) \
+  TERN_GEMM_STEP(lds1, lds2, lds0, BX, BP, TERN_GEMM_CLAMP(B0), kAcc)                     \
+  TERN_GEMM_STEP(lds2, lds3, lds1, BX, BP, TERN_GEMM_CLAMP((B0) + 1), kAcc)               \
+  TERN_GEMM_STEP(lds3, lds4, lds2, BX, BP, TERN_GEMM_CLAMP((B0) + 2), kAcc)               \
+  TERN_GEMM_STEP(lds4, lds5, lds3, BX, BP, TERN_GEMM_CLAMP((B0) + 3), kAcc)               \
+  TERN_GEMM_STEP(lds5, lds0, lds4, BX, BP, TERN_GEMM_CLAMP((B0) + 4), kAcc)
+
+  __amdgpu_buffer_rsrc_t cur_xr, cur_pr;
+  tile_rsrc(0, cur_xr, cur_pr);
   uint32_t pw[kTN];
   bf16x8_t xa[kTM], xb[kTM];
-  TERN_GEMM_ISSUE(lds0, 0)
-  TERN_GEMM_ISSUE(lds1, TERN_GEMM_STAGE(1))
-  TERN_GEMM_ISSUE(lds2, TERN_GEMM_STAGE(2))
-  TERN_GEMM_ISSUE(lds3, TERN_GEMM_STAGE(3))
-  TERN_GEMM_ISSUE(lds4, TERN_GEMM_STAGE(4))
+  TERN_GEMM_ISSUE(lds0, cur_xr, cur_pr, 0)
+  TERN_GEMM_ISSUE(lds1, cur_xr, cur_pr, TERN_GEMM_CLAMP(1))
+  TERN_GEMM_ISSUE(lds2, cur_xr, cur_pr, TERN_GEMM_CLAMP(2))
+  TERN_GEMM_ISSUE(lds3, cur_xr, cur_pr, TERN_GEMM_CLAMP(3))
+  TERN_GEMM_ISSUE(lds4, cur_xr, cur_pr, TERN_GEMM_CLAMP(4))
   wait_vmcnt<(kRing - 2) * C::kLoads, true>();
   lds_barrier();
   TERN_GEMM_READ_A(lds0)
-  int st = 0;
-  for (; st + kRing < stages; st += kRing) {
-    TERN_GEMM_STEP(st, lds0, lds1, lds5)
-    TERN_GEMM_STEP(st + 1, lds1, lds2, lds0)
-    TERN_GEMM_STEP(st + 2, lds2, lds3, lds1)
-    TERN_GEMM_STEP(st + 3, lds3, lds4, lds2)
-    TERN_GEMM_STEP(st + 4, lds4, lds5, lds3)
-    TERN_GEMM_STEP(st + 5, lds5, lds0, lds4)
+
+  if constexpr (PERSIST) {
+    for (int t = 0; t < my_tiles; ++t) {
+      // Where the requests of the tile's last iteration continue: stages
+      // 0 .. kRing - 2 of the next tile, or, after the last tile, dummy
+      // re-loads of this tile's last stage.
+      const bool last = t + 1 == my_tiles;
+      __amdgpu_buffer_rsrc_t nxt_xr = cur_xr, nxt_pr = cur_pr;
+      if (!last) tile_rsrc(t + 1, nxt_xr, nxt_pr);
+      const int nb0 = last ? stages : 0;
+      int st = 0;
+      {
+        const bool wrap = st + kRing == stages;
+        const __amdgpu_buffer_rsrc_t bx = wrap ? nxt_xr : cur_xr;
+        const __amdgpu_buffer_rsrc_t bp = wrap ? nxt_pr : cur_pr;
+        const int b0 = wrap ? nb0 : st + kRing;
+        TERN_GEMM_ITER(bx, bp, b0, kZero)
+      }
+      for (st = kRing; st < stages; st += kRing) {
+        const bool wrap = st + kRing == stages;
+        const __amdgpu_buffer_rsrc_t bx = wrap ? nxt_xr : cur_xr;
+        const __amdgpu_buffer_rsrc_t bp = wrap ? nxt_pr : cur_pr;
+        const int b0 = wrap ? nb0 : st + kRing;
+        TERN_GEMM_ITER(bx, bp, b0, kAcc)
+      }
+      phase_fence();
+      epilogue(t);
+      phase_fence();
+      cur_xr = nxt_xr;
+      cur_pr = nxt_pr;
+    }
+    wait_vmcnt<0>();  // no DMA may outlive the workgroup's LDS
+  } else {
+    int st = 0;
+    if (st + kRing < stages) {
+      TERN_GEMM_ITER(cur_xr, cur_pr, st + kRing, kZero)
+      for (st = kRing; st + kRing < stages; st += kRing) {
+        TERN_GEMM_ITER(cur_xr, cur_pr, st + kRing, kAcc)
+      }
+      // 1 to kRing steps remain, starting at ring stage 0.
+      TERN_GEMM_TAIL(st, lds0, lds1, lds5, kAcc)
+    } else {
+      TERN_GEMM_TAIL(st, lds0, lds1, lds5, kZero)
+    }
+    if (st + 1 < stages) TERN_GEMM_TAIL(st + 1, lds1, lds2, lds0, kAcc)
+    if (st + 2 < stages) TERN_GEMM_TAIL(st + 2, lds2, lds3, lds1, kAcc)
+    if (st + 3 < stages) TERN_GEMM_TAIL(st + 3, lds3, lds4, lds2, kAcc)
+    if (st + 4 < stages) TERN_GEMM_TAIL(st + 4, lds4, lds5, lds3, kAcc)
+    if (st + 5 < stages) TERN_GEMM_TAIL(st + 5, lds5, lds0, lds4, kAcc)
+    wait_vmcnt<0>();  // no DMA may outlive the workgroup's LDS
+    epilogue(0);
   }
-  // 1 to kRing steps remain, starting at ring stage 0.
-  TERN_GEMM_TAIL(st, lds0, lds1, lds5)
-  if (st + 1 < stages) TERN_GEMM_TAIL(st + 1, lds1, lds2, lds0)
-  if (st + 2 < stages) TERN_GEMM_TAIL(st + 2, lds2, lds3, lds1)
-  if (st + 3 < stages) TERN_GEMM_TAIL(st + 3, lds3, lds4, lds2)
-  if (st + 4 < stages) TERN_GEMM_TAIL(st + 4, lds4, lds5, lds3)
-  if (st + 5 < stages) TERN_GEMM_TAIL(st + 5, lds5, lds0, lds4)
-  wait_vmcnt<0>();  // no DMA may outlive the workgroup's LDS
-#undef TERN_GEMM_STEP
+#undef TERN_GEMM_ITER
+#undef TERN_GEMM_CLAMP
 #undef TERN_GEMM_TAIL
+#undef TERN_GEMM_STEP
 #undef TERN_GEMM_HALF_A
-#undef TERN_GEMM_STAGE
 #undef TERN_GEMM_ISSUE
 #undef TERN_GEMM_DMA
 #undef TERN_GEMM_READ_A
 #undef TERN_GEMM_READ_B
-
-  // Epilogue.  For tile (j, i) the lane holds output channels
-  // n = wn*kWN + 16 j + 4 g + e (e = 0..3) of token m = wm*kWM + 16 i + l16.
-  // The decode produced 2 T, so y = bf16(fp32(acc * s) * 0.5), which equals
-  // bf16(fp32(acc / 2 * s)) exactly.
-#pragma unroll
-  for (int j = 0; j < kTN; ++j) {
-    const int ng = n0 + wn * C::kWN + 16 * j + 4 * g;
-    float sc[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) sc[e] = (ng + e < n) ? s[ng + e] : 0.0f;
-#pragma unroll
-    for (int i = 0; i < kTM; ++i) {
-      const int mg = m0 + wm * C::kWM + 16 * i + l16;
-      if (mg >= m) continue;
-      __bf16 b[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) b[e] = static_cast<__bf16>((acc[j][i][e] * sc[e]) * 0.5f);
-      uint16_t* yr = y + static_cast<int64_t>(mg) * ldy + ng;
-      if (y_vec_ok && ng + 4 <= n) {
-        u32x2_t o;
-        o[0] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b[0])) |
-               (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b[1])) << 16);
-        o[1] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b[2])) |
-               (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b[3])) << 16);
-        *reinterpret_cast<u32x2_t*>(yr) = o;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (ng + e < n) yr[e] = __builtin_bit_cast(uint16_t, b[e]);
-      }
-    }
-  }
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
@@ -418,18 +553,37 @@ __global__ void fill_zero_bf16(uint16_t* y, int m, int n, int ldy) {
   }
 }
 
-template <int BM, int BN, int WAVES_M, int GM, int SWZ>
+// Workgroups per launch: persistent (a multiple of 8, at most one per CU)
+// when the K steps can run as one ring stream across tiles, else one per
+// tile.
+constexpr int kPersistentGrid = 256;
+
+template <int BM, int BN, int WAVES_M, int GM>
 hipError_t launch_tiles(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const uint8_t* p,
                         int64_t n, int64_t ldp, const float* s, uint16_t* y, int64_t ldy,
                         hipStream_t stream) {
   const int tiles_m = static_cast<int>((m + BM - 1) / BM);
   const int tiles_n = static_cast<int>((n + BN - 1) / BN);
-  const int y_vec_ok = ((reinterpret_cast<uintptr_t>(y) & 7) == 0) && (ldy % 4 == 0);
-  hipLaunchKernelGGL((gemm_ternary_mfma<BM, BN, WAVES_M, GM, SWZ>),
-                     dim3(static_cast<unsigned>(tiles_m) * static_cast<unsigned>(tiles_n)),
-                     dim3(kThreads), 0, stream, x, static_cast<int>(m), static_cast<int>(k),
-                     static_cast<int>(ldx), p, static_cast<int>(n), static_cast<int>(ldp), s, y,
-                     static_cast<int>(ldy), tiles_m, tiles_n, y_vec_ok);
+  const int64_t tiles = static_cast<int64_t>(tiles_m) * tiles_n;
+  const int stages = static_cast<int>(k / kBK);
+  // Bit 0: 8-byte stores of Y; bit 1: 16-byte stores of Y and 16-byte loads
+  // of the scales.
+  const int y_flags =
+      (((reinterpret_cast<uintptr_t>(y) & 7) == 0 && ldy % 4 == 0) ? 1 : 0) |
+      (((reinterpret_cast<uintptr_t>(y) & 15) == 0 && ldy % 8 == 0 &&
+        (reinterpret_cast<uintptr_t>(s) & 15) == 0) ? 2 : 0);
+  if (stages % 6 == 0 && tiles > kPersistentGrid) {
+    hipLaunchKernelGGL((gemm_ternary_mfma<BM, BN, WAVES_M, GM, true>), dim3(kPersistentGrid),
+                       dim3(kThreads), 0, stream, x, static_cast<int>(m), static_cast<int>(k),
+                       static_cast<int>(ldx), p, static_cast<int>(n), static_cast<int>(ldp), s, y,
+                       static_cast<int>(ldy), tiles_m, tiles_n, y_flags);
+  } else {
+    hipLaunchKernelGGL((gemm_ternary_mfma<BM, BN, WAVES_M, GM, false>),
+                       dim3(static_cast<unsigned>(tiles)), dim3(kThreads), 0, stream, x,
+                       static_cast<int>(m), static_cast<int>(k), static_cast<int>(ldx), p,
+                       static_cast<int>(n), static_cast<int>(ldp), s, y, static_cast<int>(ldy),
+                       tiles_m, tiles_n, y_flags);
+  }
   return hipGetLastError();
 }
 
@@ -445,10 +599,7 @@ hipError_t launch_gemm(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, con
                        y, static_cast<int>(m), static_cast<int>(n), static_cast<int>(ldy));
     return hipGetLastError();
   }
-#ifndef TERN_GEMM_SWZ
-#define TERN_GEMM_SWZ 0
-#endif
-  return launch_tiles<144, 384, 1, 4, TERN_GEMM_SWZ>(x, m, k, ldx, p, n, ldp, s, y, ldy, stream);
+  return launch_tiles<144, 384, 1, 4>(x, m, k, ldx, p, n, ldp, s, y, ldy, stream);
 }
 
 }  // namespace tern
