@@ -113,6 +113,23 @@ __device__ inline void decode16(uint32_t w, bf16x8_t& lo, bf16x8_t& hi) {
   hi = __builtin_bit_cast(bf16x8_t, b);
 }
 
+// One v_mfma_f32_16x16x32_bf16 with the accumulator tied to the same
+// AGPRs on input and output (ZERO: C is the constant 0).  Written as inline
+// asm because the compiler's own form of this loop copies accumulators
+// between AGPRs with v_accvgpr_mov, which costs about a quarter of the
+// matrix-core throughput.  The compiler does not see the MFMA inside, so the
+// asm keeps its hazards itself: the leading s_nop 1 gives the two wait states
+// that a VALU write of an A or B operand needs before an MFMA reads it (the
+// decoded weights are VALU results).
+template <bool ZERO>
+__device__ inline void mfma16(f32x4_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
+  if constexpr (ZERO) {
+    asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=a"(acc) : "v"(a), "v"(b));
+  } else {
+    asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  }
+}
+
 // Maps the hardware workgroup id to a (tile_m, tile_n) pair.  Workgroups are
 // dealt to the 8 XCDs round-robin; renumbering gives each XCD a contiguous
 // block of the logical order, and the logical order visits tiles in groups
@@ -202,6 +219,7 @@ void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  __builtin_assume(wave >= 0 && wave < kThreads / 64);  // lets DMA slots 0-3 and 5 fold
   const int wm = wave % C::kWavesM;
   const int wn = wave / C::kWavesM;
   const int l16 = lane & 15;
@@ -290,31 +308,23 @@ void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
 
   // ZERO starts a new sum (the MFMA's C operand is the constant 0), so the
   // accumulators of consecutive tiles never meet in one register value.
+  using kAcc = std::false_type;
+  using kZero = std::true_type;
   auto mfma_block = [&](const bf16x8_t (&w)[kTN], const bf16x8_t (&xv)[kTM], auto zero) {
 #pragma unroll
     for (int j = 0; j < kTN; ++j)
 #pragma unroll
-      for (int i = 0; i < kTM; ++i)
-        acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            w[j], xv[i], decltype(zero)::value ? f32x4_t{} : acc[j][i], 0, 0, 0);
+      for (int i = 0; i < kTM; ++i) mfma16<decltype(zero)::value>(acc[j][i], w[j], xv[i]);
   };
-  using kAcc = std::false_type;
-  using kZero = std::true_type;
-
-  // Scheduling hint for the phase after the barrier: spread the DMA requests
-  // and the operand reads of the next stage between the MFMAs instead of
-  // issuing them back to back (a stalled memory instruction would hold up the
-  // MFMAs behind it).
-  auto interleave_loads_with_mfma = [&]() {
-    constexpr int kReads = kTM + (kTN + 1) / 2;   // ds_read instructions of READ_A
-    constexpr int kGroups = C::kLoads;
-    constexpr int kMfma = kTN * kTM;
+  // Before the accumulators are read: an MFMA result may be read by other
+  // instructions only after up to 19 wait states.  The empty asm statements
+  // order every read of acc after the s_nop block.
+  auto acc_ready = [&]() {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 #pragma unroll
-    for (int i = 0; i < kGroups; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x0010, 1, 0);                                 // DMA
-      __builtin_amdgcn_sched_group_barrier(0x0100, (kReads + kGroups - 1) / kGroups, 0);  // LDS reads
-      __builtin_amdgcn_sched_group_barrier(0x0008, kMfma / kGroups, 0);                   // MFMA
-    }
+    for (int j = 0; j < kTN; ++j)
+#pragma unroll
+      for (int i = 0; i < kTM; ++i) asm volatile("" : "+a"(acc[j][i]));
   };
 
   // One step out of ring stage CUR (k-block 0 operands already read): read
@@ -324,25 +334,43 @@ void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
   // into the previous step's buffer DMA, read the next step's k-block 0 out
   // of NXT, and run k-block 1.  At every barrier of the unrolled loop exactly
   // kRing-2 steps are in flight.
-#define TERN_GEMM_HALF_A(CUR, ZERO)                                    \
-  phase_fence();                                                   \
-  wait_lgkm0();                                                    \
-  TERN_GEMM_READ_B(CUR)                                            \
-  phase_fence();                                                   \
-  bf16x8_t wa[kTN], wb[kTN];                                       \
-  _Pragma("unroll") for (int j = 0; j < kTN; ++j) decode16(pw[j], wa[j], wb[j]); \
-  mfma_block(wa, xa, ZERO{});                                      \
-  phase_fence();                                                   \
-  wait_lgkm0();
-#define TERN_GEMM_STEP(CUR, NXT, DMA, XR, PR, STAGE, ZERO)         \
-  {                                                                \
-    TERN_GEMM_HALF_A(CUR, ZERO)                                          \
-    wait_vmcnt<(kRing - 3) * C::kLoads, true>();                   \
-    lds_barrier();                                                 \
-    TERN_GEMM_ISSUE(DMA, XR, PR, STAGE)                            \
-    TERN_GEMM_READ_A(NXT)                                          \
-    mfma_block(wb, xb, kAcc{});                                    \
-    interleave_loads_with_mfma();                                  \
+#define TERN_GEMM_HALF_A(CUR, ZERO)                                                     \
+  bf16x8_t wa[kTN], wb[kTN];                                                            \
+  _Pragma("unroll") for (int j = 0; j < kTN; ++j) decode16(pw[j], wa[j], wb[j]);        \
+  _Pragma("unroll") for (int j = 0; j < kTN; ++j)                                       \
+  _Pragma("unroll") for (int i = 0; i < kTM; ++i) {                                     \
+    mfma16<ZERO::value>(acc[j][i], wa[j], xa[i]);                                       \
+    if (j == 0)                                                                         \
+      xb[i] = __builtin_bit_cast(bf16x8_t,                                              \
+                                 *reinterpret_cast<const u32x4_t*>(&CUR[xo1 + i * 2048])); \
+  }
+  // The second half interleaves, one after every second MFMA, the DMA
+  // requests of step s + kRing - 1 and the reads of the next step's first
+  // k-block (weight words, then X chunks).  The MFMAs are volatile asm, so
+  // the memory instructions stay where they are written.
+#define TERN_GEMM_STEP(CUR, NXT, DMA, XR, PR, STAGE, ZERO)                                \
+  {                                                                                      \
+    TERN_GEMM_HALF_A(CUR, ZERO)                                                          \
+    wait_vmcnt<(kRing - 3) * C::kLoads, true>();                                         \
+    lds_barrier();                                                                       \
+    _Pragma("unroll") for (int t = 0; t < kTN * kTM; ++t) {                              \
+      mfma16<false>(acc[t / kTM][t % kTM], wb[t / kTM], xb[t % kTM]);                    \
+      constexpr int kOps = C::kLoads + kTN + kTM;                                        \
+      static_assert(2 * kOps <= kTN * kTM, "every operation gets a slot");              \
+      const int op = t / 2;                                                              \
+      if (t % 2 == 1 && op < kOps) {                                                     \
+        if (op < C::kLoads) {                                                            \
+          TERN_GEMM_DMA(DMA, XR, PR, STAGE, op)                                          \
+        } else if (op < C::kLoads + kTN) {                                               \
+          const int j = op - C::kLoads;                                                  \
+          pw[j] = *reinterpret_cast<const uint32_t*>(&NXT[po + j * 256]);                \
+        } else {                                                                         \
+          const int i = op - C::kLoads - kTN;                                            \
+          xa[i] = __builtin_bit_cast(bf16x8_t,                                           \
+                                     *reinterpret_cast<const u32x4_t*>(&NXT[xo0 + i * 2048])); \
+        }                                                                                \
+      }                                                                                  \
+    }                                                                                    \
   }
   // Last steps of the last tile: the next stage is waited for in full, and a
   // request is due only while one is left.
@@ -377,35 +405,42 @@ void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
   static_assert(kThreads / 64 * 16 * kEpiPitch <= C::kStage, "epilogue staging fits a stage");
   static_assert((16 * 2 * C::kWN / 16) % 64 == 0, "whole store instructions");
   auto epilogue = [&](int t) {
+    acc_ready();
     int m0, n0;
     tile_coords(t, m0, n0);
-    if ((y_flags & 2) && m0 + BM <= m && n0 + BN <= n) {
+    if (PERSIST || ((y_flags & 2) && m0 + BM <= m && n0 + BN <= n)) {
       constexpr int kChunksPerRow = 2 * C::kWN / 16;              // 16-byte pieces of a row
       constexpr int kStores = 16 * kChunksPerRow / 64;            // per lane per 16 rows
       const uint32_t area = static_cast<uint32_t>(wave) * (16 * kEpiPitch);
       const int col0 = n0 + wn * C::kWN;
+      // The factor 1/2 of the decode goes into the scale: (acc * (s / 2))
+      // rounds like (acc * s) / 2 except where a result is subnormal.
       f32x4_t sc[kTN];
 #pragma unroll
-      for (int j = 0; j < kTN; ++j) sc[j] = *reinterpret_cast<const f32x4_t*>(s + col0 + 16 * j + 4 * g);
-      uint32_t rd_off[kStores];
-      int64_t st_off[kStores];
+      for (int j = 0; j < kTN; ++j)
+        sc[j] = *reinterpret_cast<const f32x4_t*>(s + col0 + 16 * j + 4 * g) * 0.5f;
+      uint32_t rd_off[kStores], st_off[kStores];
 #pragma unroll
       for (int q = 0; q < kStores; ++q) {
         const int c = lane + 64 * q;
         const int row = c / kChunksPerRow;
         const int cc = c - row * kChunksPerRow;
         rd_off[q] = area + static_cast<uint32_t>(row * kEpiPitch + cc * 16);
-        st_off[q] = static_cast<int64_t>(m0 + wm * C::kWM + row) * ldy + col0 + cc * 8;
+        st_off[q] = static_cast<uint32_t>(row * ldy + cc * 8);   // 16 * ldy < 2^31 (host)
       }
       const uint32_t wr_off = area + static_cast<uint32_t>(l16 * kEpiPitch + 8 * g);
+      uint16_t* const yt = y + static_cast<int64_t>(m0 + wm * C::kWM) * ldy + col0;
       lds_barrier();
 #pragma unroll
       for (int i = 0; i < kTM; ++i) {
 #pragma unroll
         for (int j = 0; j < kTN; ++j) {
+          // Keeps this read of the accumulators here, next to its use,
+          // instead of hoisted into one burst that needs 216 VGPRs.
+          asm volatile("" : "+a"(acc[j][i]));
           __bf16 b[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) b[e] = static_cast<__bf16>((acc[j][i][e] * sc[j][e]) * 0.5f);
+          for (int e = 0; e < 4; ++e) b[e] = static_cast<__bf16>(acc[j][i][e] * sc[j][e]);
           u32x2_t o;
           o[0] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b[0])) |
                  (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b[1])) << 16);
@@ -413,39 +448,42 @@ void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
                  (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b[3])) << 16);
           *reinterpret_cast<u32x2_t*>(&lds5[wr_off + 32 * j]) = o;
         }
+        uint16_t* const yi = yt + static_cast<int64_t>(16 * i) * ldy;
 #pragma unroll
         for (int q = 0; q < kStores; ++q) {
           const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&lds5[rd_off[q]]);
-          *reinterpret_cast<u32x4_t*>(y + st_off[q] + static_cast<int64_t>(16 * i) * ldy) = v;
+          *reinterpret_cast<u32x4_t*>(yi + st_off[q]) = v;
         }
       }
       return;
     }
+    if constexpr (!PERSIST) {
 #pragma unroll
-    for (int j = 0; j < kTN; ++j) {
-      const int ng = n0 + wn * C::kWN + 16 * j + 4 * g;
-      float sc[4];
+      for (int j = 0; j < kTN; ++j) {
+        const int ng = n0 + wn * C::kWN + 16 * j + 4 * g;
+        float sc[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sc[e] = (ng + e < n) ? s[ng + e] : 0.0f;
+        for (int e = 0; e < 4; ++e) sc[e] = (ng + e < n) ? s[ng + e] : 0.0f;
 #pragma unroll
-      for (int i = 0; i < kTM; ++i) {
-        const int mg = m0 + wm * C::kWM + 16 * i + l16;
-        __bf16 b[4];
+        for (int i = 0; i < kTM; ++i) {
+          const int mg = m0 + wm * C::kWM + 16 * i + l16;
+          __bf16 b[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) b[e] = static_cast<__bf16>((acc[j][i][e] * sc[e]) * 0.5f);
-        if (mg >= m) continue;
-        uint16_t* yr = y + static_cast<int64_t>(mg) * ldy + ng;
-        if ((y_flags & 1) && ng + 4 <= n) {
-          u32x2_t o;
-          o[0] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b[0])) |
-                 (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b[1])) << 16);
-          o[1] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b[2])) |
-                 (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b[3])) << 16);
-          *reinterpret_cast<u32x2_t*>(yr) = o;
-        } else {
+          for (int e = 0; e < 4; ++e) b[e] = static_cast<__bf16>((acc[j][i][e] * sc[e]) * 0.5f);
+          if (mg >= m) continue;
+          uint16_t* yr = y + static_cast<int64_t>(mg) * ldy + ng;
+          if ((y_flags & 1) && ng + 4 <= n) {
+            u32x2_t o;
+            o[0] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b[0])) |
+                   (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b[1])) << 16);
+            o[1] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b[2])) |
+                   (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b[3])) << 16);
+            *reinterpret_cast<u32x2_t*>(yr) = o;
+          } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (ng + e < n) yr[e] = __builtin_bit_cast(uint16_t, b[e]);
+            for (int e = 0; e < 4; ++e)
+              if (ng + e < n) yr[e] = __builtin_bit_cast(uint16_t, b[e]);
+          }
         }
       }
     }
@@ -482,33 +520,29 @@ void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
 
   if constexpr (PERSIST) {
     for (int t = 0; t < my_tiles; ++t) {
-      // Where the requests of the tile's last iteration continue: stages
-      // 0 .. kRing - 2 of the next tile, or, after the last tile, dummy
-      // re-loads of this tile's last stage.
-      const bool last = t + 1 == my_tiles;
-      __amdgpu_buffer_rsrc_t nxt_xr = cur_xr, nxt_pr = cur_pr;
-      if (!last) tile_rsrc(t + 1, nxt_xr, nxt_pr);
-      const int nb0 = last ? stages : 0;
+      // In the tile's last iteration the requests after the first continue
+      // with stages 0 .. kRing - 2 of the next tile, or, after the last tile,
+      // with dummy re-loads of this tile's last stage.
+#define TERN_GEMM_PITER(ZERO)                               \
+      {                                                     \
+        __amdgpu_buffer_rsrc_t bx = cur_xr, bp = cur_pr;    \
+        int b0 = st + kRing;                                \
+        if (st + kRing == stages) {                         \
+          if (t + 1 < my_tiles) {                           \
+            tile_rsrc(t + 1, bx, bp);                       \
+            b0 = 0;                                         \
+          } else {                                          \
+            b0 = stages;                                    \
+          }                                                 \
+        }                                                   \
+        TERN_GEMM_ITER(bx, bp, b0, ZERO)                    \
+      }
       int st = 0;
-      {
-        const bool wrap = st + kRing == stages;
-        const __amdgpu_buffer_rsrc_t bx = wrap ? nxt_xr : cur_xr;
-        const __amdgpu_buffer_rsrc_t bp = wrap ? nxt_pr : cur_pr;
-        const int b0 = wrap ? nb0 : st + kRing;
-        TERN_GEMM_ITER(bx, bp, b0, kZero)
-      }
-      for (st = kRing; st < stages; st += kRing) {
-        const bool wrap = st + kRing == stages;
-        const __amdgpu_buffer_rsrc_t bx = wrap ? nxt_xr : cur_xr;
-        const __amdgpu_buffer_rsrc_t bp = wrap ? nxt_pr : cur_pr;
-        const int b0 = wrap ? nb0 : st + kRing;
-        TERN_GEMM_ITER(bx, bp, b0, kAcc)
-      }
-      phase_fence();
+      TERN_GEMM_PITER(kZero)
+      for (st = kRing; st < stages; st += kRing) TERN_GEMM_PITER(kAcc)
+#undef TERN_GEMM_PITER
       epilogue(t);
-      phase_fence();
-      cur_xr = nxt_xr;
-      cur_pr = nxt_pr;
+      if (t + 1 < my_tiles) tile_rsrc(t + 1, cur_xr, cur_pr);
     }
     wait_vmcnt<0>();  // no DMA may outlive the workgroup's LDS
   } else {
@@ -566,13 +600,15 @@ hipError_t launch_tiles(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, co
   const int tiles_n = static_cast<int>((n + BN - 1) / BN);
   const int64_t tiles = static_cast<int64_t>(tiles_m) * tiles_n;
   const int stages = static_cast<int>(k / kBK);
-  // Bit 0: 8-byte stores of Y; bit 1: 16-byte stores of Y and 16-byte loads
-  // of the scales.
+  // Bit 0: 8-byte stores of Y; bit 1: 16-byte stores of Y, 16-byte loads of
+  // the scales and 32-bit offsets within 16 rows of Y.
   const int y_flags =
       (((reinterpret_cast<uintptr_t>(y) & 7) == 0 && ldy % 4 == 0) ? 1 : 0) |
-      (((reinterpret_cast<uintptr_t>(y) & 15) == 0 && ldy % 8 == 0 &&
+      (((reinterpret_cast<uintptr_t>(y) & 15) == 0 && ldy % 8 == 0 && ldy < (int64_t{1} << 27) &&
         (reinterpret_cast<uintptr_t>(s) & 15) == 0) ? 2 : 0);
-  if (stages % 6 == 0 && tiles > kPersistentGrid) {
+  // The persistent kernel takes whole tiles only (its epilogue has no edge
+  // handling) and needs the ring stream to restart at a tile boundary.
+  if (stages % 6 == 0 && tiles > kPersistentGrid && m % BM == 0 && n % BN == 0 && (y_flags & 2)) {
     hipLaunchKernelGGL((gemm_ternary_mfma<BM, BN, WAVES_M, GM, true>), dim3(kPersistentGrid),
                        dim3(kThreads), 0, stream, x, static_cast<int>(m), static_cast<int>(k),
                        static_cast<int>(ldx), p, static_cast<int>(n), static_cast<int>(ldp), s, y,
