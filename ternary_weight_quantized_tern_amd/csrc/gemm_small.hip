@@ -1,0 +1,193 @@
+// Ternary linear layer for a handful of tokens (m <= 32):
+// Y = bf16((X . T^T) (.) s), bf16 X, 2-bit packed T.
+//
+// "1.58-bit FLUX" (arXiv 2412.18653) stores the transformer's linear weights
+// as 2-bit signed integers and keeps activations in 16 bits (section 1
+// contributions, section 3.2, section 4 limitations).  With one or a few
+// tokens per call the layer reads every packed weight once and does little
+// arithmetic per byte, so this path is built around the weight stream: every
+// weight byte is fetched exactly once, straight into registers, with as many
+// fetches in flight per wave as its registers allow.
+//
+// Design:
+//  * A workgroup owns 16 output channels (one MFMA A operand) and its four
+//    waves split K: wave w takes the 256-wide K chunks w, w + 4, w + 8, ...
+//    This gives N / 16 workgroups (288 for a 4608-wide layer), enough to keep
+//    every CU fetching even for small layers.
+//  * Lane (r, g) of a wave (r = lane % 16, g = lane / 16) fetches 16 bytes of
+//    weight row r per chunk: codes 64 g .. 64 g + 63 of the chunk.  MFMA j of
+//    the chunk (j = 0..7) uses codes 8 j .. 8 j + 7 of them, decoded in
+//    registers to bf16 0 / +2 / -2 (the factor 2 is removed in the epilogue),
+//    and the B operand is the matching 16-byte piece of X for token r (plus
+//    16 per extra MFMA row block).  X is small and stays in L2.
+//  * Loads use buffer resources: rows past n and tokens past m read as zero;
+//    the part of a last chunk past k is read at an out-of-range offset, so it
+//    is zero as well.
+//  * The four per-wave partial sums are added through LDS; wave 0 applies the
+//    fp32 channel scale and rounds once to bf16.
+#include <type_traits>
+
+#include "gemm_common.h"
+#include "internal.h"
+
+namespace tern {
+namespace {
+
+constexpr int kSmallThreads = 256;
+constexpr int kChunk = 256;           // K per chunk and wave
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+// R MFMA row blocks (m <= 16 R), DEPTH chunks in flight per wave.
+template <int R, int DEPTH>
+__global__ __launch_bounds__(kSmallThreads) void gemm_ternary_small(
+    const uint16_t* __restrict__ x, int m, int k, int ldx, const uint8_t* __restrict__ p, int n,
+    int ldp, const float* __restrict__ s, uint16_t* __restrict__ y, int ldy, int y_vec_ok) {
+  __shared__ f32x4_t red[kSmallThreads / 64 - 1][R][64];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r16 = lane & 15;
+  const int g = lane >> 4;
+  const int n0 = blockIdx.x * 16;
+  const int rows = (n - n0) < 16 ? (n - n0) : 16;
+
+  const __amdgpu_buffer_rsrc_t prs = make_rsrc(
+      p + static_cast<int64_t>(n0) * ldp, static_cast<uint32_t>((rows - 1) * ldp + k / 4));
+  const __amdgpu_buffer_rsrc_t xrs =
+      make_rsrc(x, static_cast<uint32_t>((static_cast<int64_t>(m) - 1) * ldx * 2 + k * 2));
+
+  const int chunks = (k + kChunk - 1) / kChunk;
+  const int mine = (chunks - wave + 3) / 4;  // chunks wave, wave + 4, ...
+
+  // Per-lane byte offsets of chunk 0; chunk c adds c * kChunk codes.
+  const uint32_t p_off = static_cast<uint32_t>(r16 * ldp + 16 * g);
+  uint32_t x_off[R];
+#pragma unroll
+  for (int b = 0; b < R; ++b) x_off[b] = static_cast<uint32_t>(((16 * b + r16) * ldx + 64 * g) * 2);
+
+  u32x4_t wq[DEPTH];
+  u32x4_t xq[DEPTH][R][8];
+  // Each chunk's loads are issued as one group, in chunk order (the fences
+  // keep the scheduler from interleaving groups), so that waiting for the
+  // oldest chunk never waits for a younger one.
+  auto fence = []() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto fetch = [&](int slot, int c) {
+    fence();
+    // Codes kc .. kc + 63 of this lane lie past k exactly when kc >= k; then
+    // the offsets get the out-of-range bit (arithmetic, so that the compiler
+    // keeps one unconditional load per operand).
+    const int kc = c * kChunk + 64 * g;
+    const uint32_t oob = static_cast<uint32_t>(k - 1 - kc) & kOutOfRange;
+    const uint32_t po = (p_off + static_cast<uint32_t>(c * (kChunk / 4))) | oob;
+    wq[slot] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(prs, po, 0, 0));
+#pragma unroll
+    for (int b = 0; b < R; ++b)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t xo = (x_off[b] + static_cast<uint32_t>((c * kChunk + 8 * j) * 2)) | oob;
+        xq[slot][b][j] =
+            __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(xrs, xo, 0, 0));
+      }
+    fence();
+  };
+
+  f32x4_t acc[R];
+#pragma unroll
+  for (int b = 0; b < R; ++b) acc[b] = f32x4_t{};
+  auto compute = [&](int slot) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      bf16x8_t lo, hi;
+      decode16(wq[slot][d], lo, hi);
+#pragma unroll
+      for (int b = 0; b < R; ++b) {
+        mfma16<false>(acc[b], lo, __builtin_bit_cast(bf16x8_t, xq[slot][b][2 * d]));
+        mfma16<false>(acc[b], hi, __builtin_bit_cast(bf16x8_t, xq[slot][b][2 * d + 1]));
+      }
+    }
+  };
+
+  // The wave's i-th chunk is global chunk wave + 4 i, fetched DEPTH chunks
+  // ahead of its use into register slot i % DEPTH.  Fetches and MFMAs run
+  // unconditionally in whole rounds of DEPTH chunks (chunks past the end read
+  // as zero), so that the compiler's wait counts stay exact.
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) fetch(d, wave + 4 * d);
+  for (int i0 = 0; i0 < mine; i0 += DEPTH) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      compute(d);
+      fetch(d, wave + 4 * (i0 + d + DEPTH));
+    }
+  }
+
+  // MFMA results may be read by other instructions only after up to 19 wait
+  // states; the empty asm statements keep every read of acc after them.
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+  for (int b = 0; b < R; ++b) asm volatile("" : "+v"(acc[b]));
+
+  if (wave > 0) {
+#pragma unroll
+    for (int b = 0; b < R; ++b) red[wave - 1][b][lane] = acc[b];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+
+  const int nb = n0 + 4 * g;  // output channels nb .. nb + 3 of this lane
+  float sc[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) sc[e] = (nb + e < n) ? s[nb + e] * 0.5f : 0.0f;
+#pragma unroll
+  for (int b = 0; b < R; ++b) {
+    f32x4_t v = acc[b];
+#pragma unroll
+    for (int w = 0; w < kSmallThreads / 64 - 1; ++w) v += red[w][b][lane];
+    const int token = 16 * b + r16;
+    if (token >= m) continue;
+    __bf16 o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = static_cast<__bf16>(v[e] * sc[e]);
+    uint16_t* yr = y + static_cast<int64_t>(token) * ldy + nb;
+    if (y_vec_ok && nb + 4 <= n) {
+      u32x2_t q;
+      q[0] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, o[0])) |
+             (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, o[1])) << 16);
+      q[1] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, o[2])) |
+             (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, o[3])) << 16);
+      *reinterpret_cast<u32x2_t*>(yr) = q;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (nb + e < n) yr[e] = __builtin_bit_cast(uint16_t, o[e]);
+    }
+  }
+}
+
+template <int R, int DEPTH>
+hipError_t launch_small(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const uint8_t* p,
+                        int64_t n, int64_t ldp, const float* s, uint16_t* y, int64_t ldy,
+                        hipStream_t stream) {
+  const int64_t blocks = (n + 15) / 16;
+  const int y_vec_ok = ((reinterpret_cast<uintptr_t>(y) & 7) == 0) && (ldy % 4 == 0);
+  hipLaunchKernelGGL((gemm_ternary_small<R, DEPTH>), dim3(static_cast<unsigned>(blocks)),
+                     dim3(kSmallThreads), 0, stream, x, static_cast<int>(m), static_cast<int>(k),
+                     static_cast<int>(ldx), p, static_cast<int>(n), static_cast<int>(ldp), s, y,
+                     static_cast<int>(ldy), y_vec_ok);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_small(const uint16_t* x, int64_t m, int64_t k, int64_t ldx,
+                             const uint8_t* p, int64_t n, int64_t ldp, const float* s,
+                             uint16_t* y, int64_t ldy, hipStream_t stream) {
+  if (m <= 16) return launch_small<1, 4>(x, m, k, ldx, p, n, ldp, s, y, ldy, stream);
+  return launch_small<2, 2>(x, m, k, ldx, p, n, ldp, s, y, ldy, stream);
+}
+
+}  // namespace tern

@@ -24,4 +24,9 @@ hipError_t launch_gemm(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, con
                        int64_t n, int64_t ldp, const float* s, uint16_t* y, int64_t ldy,
                        hipStream_t stream);
 
+// m <= 32 (called by launch_gemm).
+hipError_t launch_gemm_small(const uint16_t* x, int64_t m, int64_t k, int64_t ldx,
+                             const uint8_t* p, int64_t n, int64_t ldp, const float* s,
+                             uint16_t* y, int64_t ldy, hipStream_t stream);
+
 }  // namespace tern

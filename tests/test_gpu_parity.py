@@ -106,6 +106,10 @@ def test_unpack_all_byte_values():
 GEMM_SHAPES = [
     (1, 64, 1), (16, 256, 512), (8, 1152, 300), (300, 320, 520), (257, 128, 255),
     (513, 192, 700), (256, 64, 256), (255, 512, 257), (64, 4096, 96), (1000, 64, 33),
+    # few-token path (m <= 32): ragged n, k not a multiple of the 256-wide chunk,
+    # one or two MFMA row blocks, and the first size past it
+    (2, 320, 50), (5, 448, 33), (16, 4608, 1152), (17, 832, 100), (31, 1088, 47),
+    (32, 256, 16), (33, 576, 40), (8, 64, 4608),
 ]
 
 
@@ -117,9 +121,11 @@ def test_gemm_small_all_elements(m, k, n):
     check_layer(x, w, f"gemm {m}x{k}x{n}", full=True, repeat_check=True)
 
 
-def test_gemm_strided_operands():
-    m, k, n = 130, 192, 140
-    x, w = tern_inputs.draw(m, k, n, seed=99)
+@pytest.mark.parametrize("m", [130, 7, 20])
+def test_gemm_strided_operands(m):
+    k, n = 192, 140
+    log(f"gemm strided m={m} k={k} n={n}")
+    x, w = tern_inputs.draw(m, k, n, seed=99 + m)
     t_ref, s_ref, p_ref = oracle_weights(w)
     xg = torch.zeros((m, k + 72), dtype=torch.bfloat16, device=DEV)
     xg[:, :k] = x.to(DEV)
