@@ -10,6 +10,12 @@ dominant kernel (tern_gemm) measured with HIP events on the stream it is
 launched on; the CPU baseline is the oracle timed on this host on a bounded
 sample of the same step.
 
+After the timed steps, every layer shape of the five workloads is timed on its
+own ("rows"): tern_gemm per launch, as effective TFLOP/s, GB/s and the
+fraction of the bound that applies (MFMA or HBM).  The two few-token layers
+cycle through a pool of distinct packed weights larger than every cache, so
+that each launch streams its weights from HBM.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload flux_qkv]
 """
 from __future__ import annotations
@@ -28,7 +34,8 @@ METRIC = "tern_gemm effective TFLOP/s + % of MFMA/HBM roofline, FLUX linears M=4
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak
 RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
-GEMM_SRC = os.path.join(ROOT, "ternary_weight_quantized_tern_amd", "csrc", "gemm.hip")
+CSRC = os.path.join(ROOT, "ternary_weight_quantized_tern_amd", "csrc")
+GEMM_SRCS = [os.path.join(CSRC, f) for f in ("gemm.hip", "gemm_small.hip", "gemm_common.h")]
 
 
 def parse():
@@ -46,6 +53,10 @@ def parse():
                     help="also run a device copy of this size (for counter calibration)")
     ap.add_argument("--gemm-only-reps", type=int, default=0,
                     help="after the steps, launch tern_gemm alone this many times (profiling)")
+    ap.add_argument("--no-rows", action="store_true", help="skip the per-layer-shape table")
+    ap.add_argument("--row-reps", type=int, default=30, help="timed launches per row")
+    ap.add_argument("--pool-mib", type=int, default=1024,
+                    help="packed-weight pool cycled by the few-token rows")
     return ap.parse_args()
 
 
@@ -53,9 +64,13 @@ def gemm_alg_bytes(m, k, n):
     return 2 * m * k + n * k // 4 + 4 * n + 2 * m * n
 
 
-def source_digest(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def source_digest(paths=GEMM_SRCS):
+    """sha256 over the GEMM kernel sources, in a fixed order."""
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def load_traffic(workload):
@@ -66,7 +81,7 @@ def load_traffic(workload):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("gemm_source_sha256") != source_digest(GEMM_SRC):
+    if rec.get("gemm_source_sha256") != source_digest():
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -113,6 +128,111 @@ def cpu_baseline(layers, inputs, target_s):
                    f"output on the first {rows_used} X rows of M={[l.m for l in layers]} "
                    f"scaled to all rows; {cores} threads"),
     }
+
+
+def roofline_of(flops, byts, seconds):
+    """Effective rates and the fraction of the bound that applies."""
+    tf = flops / seconds / 1e12
+    gbs = byts / seconds / 1e9
+    bound = "mfma" if flops / byts >= RIDGE else "hbm"
+    t_ideal = max(flops / (PEAK_BF16_TFLOPS * 1e12), byts / (PEAK_HBM_GBS * 1e9))
+    return {"tflops": tf, "gbs": gbs, "pct_mfma": 100 * tf / PEAK_BF16_TFLOPS,
+            "pct_hbm": 100 * gbs / PEAK_HBM_GBS, "bound": bound,
+            "pct_roofline": 100 * t_ideal / seconds}
+
+
+def time_rows(tern, tern_inputs, torch, dev, reps, pool_mib):
+    """tern_gemm alone on every layer shape of the workloads (layer 0 inputs of
+    each shape).  Few-token shapes cycle through a pool of distinct packed
+    weights of at least pool_mib MiB (seeded normal weights quantized on the
+    GPU), one launch per pool entry."""
+    import statistics
+    shapes = [("single", tern_inputs.WORKLOADS["single"][0]),
+              ("flux_qkv", tern_inputs.WORKLOADS["flux_qkv"][0]),
+              ("flux_mlp.up", tern_inputs.WORKLOADS["flux_mlp"][0]),
+              ("flux_mlp.down", tern_inputs.WORKLOADS["flux_mlp"][1]),
+              ("flux_single_stream.in_proj", tern_inputs.WORKLOADS["flux_single_stream"][0]),
+              ("flux_single_stream.out_proj", tern_inputs.WORKLOADS["flux_single_stream"][1])]
+    shapes += [(l.name, l) for l in tern_inputs.WORKLOADS["dit"]]
+    rows = []
+    for name, layer in shapes:
+        x, w = tern_inputs.draw_layer(layer)
+        xd = x.to(dev)
+        ldp = tern.packed_row_bytes(layer.k)
+        y = torch.empty((layer.m, layer.n), dtype=torch.bfloat16, device=dev)
+        pool = layer.m <= 64 and layer.n * layer.k >= (1 << 20)
+        if pool:
+            per = layer.n * ldp + 4 * layer.n
+            count = max(1, -(-(pool_mib << 20) // per))
+            gen = torch.Generator(device=dev).manual_seed(layer.seed)
+            ps = torch.empty((count, layer.n, ldp), dtype=torch.uint8, device=dev)
+            ss = torch.empty((count, layer.n), dtype=torch.float32, device=dev)
+            t = torch.empty((layer.n, layer.k), dtype=torch.int8, device=dev)
+            for i in range(count):
+                wi = torch.randn((layer.n, layer.k), generator=gen, device=dev) * tern_inputs.W_STD
+                tern.tern_quantize(wi, t, ss[i])
+                tern.tern_pack(t, ps[i], layer.k)
+            operands = [(ps[i], ss[i]) for i in range(count)]
+            launches = count
+        else:
+            t, s = tern.quantize(w.to(dev))
+            operands = [(tern.pack(t), s)]
+            launches = reps
+        for i in range(min(5, launches)):
+            p_i, s_i = operands[i % len(operands)]
+            tern.tern_gemm(xd, p_i, s_i, y, layer.k)
+        torch.cuda.synchronize()
+        # Per-launch durations with events around each launch (they include
+        # the host's submission gaps), and the same launches captured in a
+        # HIP graph and replayed back to back (no host in the loop).
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(launches)]
+        for i in range(launches):
+            p_i, s_i = operands[i % len(operands)]
+            ev[i][0].record()
+            tern.tern_gemm(xd, p_i, s_i, y, layer.k)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        d = [a.elapsed_time(b) * 1e-3 for a, b in ev]
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            tern.tern_gemm(xd, operands[0][0], operands[0][1], y, layer.k)
+        torch.cuda.current_stream().wait_stream(side)
+        with torch.cuda.graph(graph):
+            for i in range(launches):
+                p_i, s_i = operands[i % len(operands)]
+                tern.tern_gemm(xd, p_i, s_i, y, layer.k)
+        graph.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        graph.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        per_launch = g0.elapsed_time(g1) * 1e-3 / launches
+        del graph
+        med = statistics.median(d)
+        flops = 2 * layer.m * layer.n * layer.k
+        byts = gemm_alg_bytes(layer.m, layer.k, layer.n)
+        # The table's rate is the back-to-back (graph) time per launch unless
+        # the event-bracketed median is lower.
+        t = min(per_launch, med)
+        row = {"layer": name, "m": layer.m, "k": layer.k, "n": layer.n,
+               "launches": launches, "us_per_launch": t * 1e6,
+               "graph_us_per_launch": per_launch * 1e6, "event_median_us": med * 1e6,
+               "event_min_us": min(d) * 1e6, "alg_flops": flops, "alg_bytes": byts}
+        row.update(roofline_of(flops, byts, t))
+        if pool:
+            row["weight_pool_mib"] = round(launches * per / 2**20, 1)
+        rows.append(row)
+        print(f"# row {name}: {t * 1e6:.1f} us per launch, {row['tflops']:.0f} TFLOP/s, "
+              f"{row['gbs']:.0f} GB/s, {row['pct_roofline']:.1f}% of roofline",
+              file=sys.stderr, flush=True)
+        del operands
+        torch.cuda.empty_cache()
+    return rows
 
 
 def main():
@@ -256,6 +376,11 @@ def main():
         torch.cuda.synchronize()
         print(f"# copy calibration: {nbytes} bytes read and written", file=sys.stderr)
 
+    rows = None
+    if not args.no_rows:
+        print("# timing tern_gemm on every layer shape", file=sys.stderr, flush=True)
+        rows = time_rows(tern, tern_inputs, torch, dev, args.row_reps, args.pool_mib)
+
     cpu = None
     if not args.no_cpu_baseline:
         print("# timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
@@ -282,6 +407,8 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels": kernels,
+        "rows": rows,
+        "peaks": {"bf16_mfma_tflops": PEAK_BF16_TFLOPS, "hbm_gbs": PEAK_HBM_GBS},
     }
     print(json.dumps(out), flush=True)
 
