@@ -220,12 +220,16 @@ void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
 
   // Requests one step (stage STAGE of the tile whose resources are XR, PR)
   // into ring stage BUF, one of the lds* arrays, named directly so that the
-  // compiler can tell the ring stages apart.
-#define TERN_GEMM_DMA(BUF, XR, PR, STAGE, Q)                                            \
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(dma_is_x[Q] ? (XR) : (PR),                   \
-                                           (lds_void_t*)(&BUF[dma_lds[Q]]), 16,        \
-                                           dma_voff[Q],                                \
-                                           (STAGE) * (dma_is_x[Q] ? kBK * 2 : kBK / 4), 0, 0);
+  // compiler can tell the ring stages apart.  A stage past the end of K is
+  // requested through an empty buffer resource and arrives as zeros, so every
+  // iteration of the unrolled loop issues the same instructions (the wait
+  // counts stay exact) and steps past the end add nothing.
+  const __amdgpu_buffer_rsrc_t null_rsrc = make_rsrc(x, 0);
+#define TERN_GEMM_DMA(BUF, XR, PR, STAGE, Q)                                                \
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                 \
+      (STAGE) < stages ? (dma_is_x[Q] ? (XR) : (PR)) : null_rsrc,                          \
+      (lds_void_t*)(&BUF[dma_lds[Q]]), 16, dma_voff[Q],                                    \
+      ((STAGE) < stages ? (STAGE) : 0) * (dma_is_x[Q] ? kBK * 2 : kBK / 4), 0, 0);
 #define TERN_GEMM_ISSUE(BUF, XR, PR, STAGE) \
   _Pragma("unroll") for (int q = 0; q < C::kLoads; ++q) TERN_GEMM_DMA(BUF, XR, PR, STAGE, q)
 
@@ -240,30 +244,34 @@ void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
   static_assert(C::kWM % 16 == 0, "xswz(row + 16 i) == xswz(row)");
 
   f32x4_t acc[kTN][kTM];
+  uint32_t pw[kTN], w2[kTN], h0[kTN], h1[kTN];
+  u32x4_t wa[kTN], wb[kTN];
+  bf16x8_t xa[kTM], xb[kTM];
 
   // Operand reads out of ring stage BUF: the 32-bit code words of every
   // weight tile and the X chunks of k-block 0 (READ_A), or the X chunks of
   // k-block 1 (READ_B).
-#define TERN_GEMM_READ_A(BUF)                                                               \
-  _Pragma("unroll") for (int j = 0; j < kTN; ++j)                                           \
-      pw[j] = *reinterpret_cast<const uint32_t*>(&BUF[po + j * 256]);                       \
-  _Pragma("unroll") for (int i = 0; i < kTM; ++i)                                           \
-      xa[i] = __builtin_bit_cast(bf16x8_t,                                                  \
-                                 *reinterpret_cast<const u32x4_t*>(&BUF[xo0 + i * 2048]));
-#define TERN_GEMM_READ_B(BUF)                                                               \
-  _Pragma("unroll") for (int i = 0; i < kTM; ++i)                                           \
-      xb[i] = __builtin_bit_cast(bf16x8_t,                                                  \
-                                 *reinterpret_cast<const u32x4_t*>(&BUF[xo1 + i * 2048]));
+#define TERN_GEMM_READ_PW(BUF, J) pw[J] = *reinterpret_cast<const uint32_t*>(&BUF[po + (J) * 256]);
+#define TERN_GEMM_READ_XA(BUF, I) \
+  xa[I] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(&BUF[xo0 + (I) * 2048]));
+#define TERN_GEMM_READ_XB(BUF, I) \
+  xb[I] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(&BUF[xo1 + (I) * 2048]));
+#define TERN_GEMM_READ_A(BUF)                                         \
+  _Pragma("unroll") for (int j = 0; j < kTN; ++j) TERN_GEMM_READ_PW(BUF, j) \
+  _Pragma("unroll") for (int i = 0; i < kTM; ++i) TERN_GEMM_READ_XA(BUF, i)
+#define TERN_GEMM_READ_B(BUF) \
+  _Pragma("unroll") for (int i = 0; i < kTM; ++i) TERN_GEMM_READ_XB(BUF, i)
 
   // ZERO starts a new sum (the MFMA's C operand is the constant 0), so the
   // accumulators of consecutive tiles never meet in one register value.
   using kAcc = std::false_type;
   using kZero = std::true_type;
-  auto mfma_block = [&](const bf16x8_t (&w)[kTN], const bf16x8_t (&xv)[kTM], auto zero) {
+  auto mfma_block = [&](const u32x4_t (&w)[kTN], const bf16x8_t (&xv)[kTM], auto zero) {
 #pragma unroll
     for (int j = 0; j < kTN; ++j)
 #pragma unroll
-      for (int i = 0; i < kTM; ++i) mfma16<decltype(zero)::value>(acc[j][i], w[j], xv[i]);
+      for (int i = 0; i < kTM; ++i)
+        mfma16<decltype(zero)::value>(acc[j][i], __builtin_bit_cast(bf16x8_t, w[j]), xv[i]);
   };
   // Before the accumulators are read: an MFMA result may be read by other
   // instructions only after up to 19 wait states.  The empty asm statements
@@ -276,66 +284,80 @@ void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
       for (int i = 0; i < kTM; ++i) asm volatile("" : "+a"(acc[j][i]));
   };
 
-  // One step out of ring stage CUR (k-block 0 operands already read): read
-  // k-block 1 and run k-block 0; then, once every wave is past the barrier
-  // (the next step's stage has landed everywhere and the previous step's stage
-  // is no longer read by anyone), request the step under the issue cursor
-  // into the previous step's buffer DMA, read the next step's k-block 0 out
-  // of NXT, and run k-block 1.  At every barrier of the unrolled loop exactly
-  // kRing-2 steps are in flight.
+  // Decode of weight word j in units of at most two VALU instructions, so
+  // that it can be spread between MFMAs.  After the byte permute, half-word 0
+  // of h holds the codes in place and half-word 1 the same codes moved down
+  // one field; a left shift by 14 - 4q and a mask leave code 2q in bits 14..15
+  // and code 2q+1 in bits 30..31, i.e. bf16 0 / +2 / -2.  The lo units (0..4)
+  // produce the k-block 0 operand wa[j] (codes 0..7) and keep pw >> 2 in w2;
+  // the hi units produce wb[j] (codes 8..15).
+  auto lo_unit = [&](int j, int u) {
+    if (u == 0) {
+      w2[j] = pw[j] >> 2;
+      h0[j] = __builtin_amdgcn_perm(w2[j], pw[j], 0x05040100u);
+    } else {
+      wa[j][u - 1] = (h0[j] << (18 - 4 * u)) & 0xC000C000u;
+    }
+  };
+  auto hi_unit = [&](int j, int u) {
+    if (u == 0) {
+      h1[j] = __builtin_amdgcn_perm(w2[j], pw[j], 0x07060302u);
+    } else {
+      wb[j][u - 1] = (h1[j] << (18 - 4 * u)) & 0xC000C000u;
+    }
+  };
+  auto decode_lo_all = [&]() {  // the first step's wa
+#pragma unroll
+    for (int j = 0; j < kTN; ++j)
+#pragma unroll
+      for (int u = 0; u < 5; ++u) lo_unit(j, u);
+  };
+  constexpr int kSlots = kTN * kTM;       // MFMAs per half step
+  constexpr int kUnits = 5 * kTN;         // decode units per half step
+  static_assert(kUnits <= kSlots, "one decode unit per MFMA slot");
+
+  // One step out of ring stage CUR.  On entry the weight words pw, their
+  // k-block 0 operands wa (and w2) and the X chunks xa of this step are in
+  // registers.  Half A runs k-block 0; between its MFMAs it reads the X
+  // chunks xb of k-block 1 and decodes the k-block 1 operands wb.  Then, once
+  // every wave is past the barrier (the next step's stage has landed
+  // everywhere and the previous step's stage is no longer read by anyone),
+  // half B runs k-block 1; between its MFMAs it reads the next step's weight
+  // words out of NXT, requests the step under the issue cursor into the
+  // previous step's buffer DMA, reads the next step's xa, and decodes the
+  // next step's wa.  The MFMAs are volatile asm and every slot ends in a
+  // scheduling barrier, so this interleave is the issue order.  At every
+  // barrier of the unrolled loop exactly kRing-2 steps are in flight.
 #define TERN_GEMM_HALF_A(CUR, ZERO)                                                     \
-  bf16x8_t wa[kTN], wb[kTN];                                                            \
-  _Pragma("unroll") for (int j = 0; j < kTN; ++j) decode16(pw[j], wa[j], wb[j]);        \
-  _Pragma("unroll") for (int j = 0; j < kTN; ++j)                                       \
-  _Pragma("unroll") for (int i = 0; i < kTM; ++i) {                                     \
-    mfma16<ZERO::value>(acc[j][i], wa[j], xa[i]);                                       \
-    if (j == 0)                                                                         \
-      xb[i] = __builtin_bit_cast(bf16x8_t,                                              \
-                                 *reinterpret_cast<const u32x4_t*>(&CUR[xo1 + i * 2048])); \
+  _Pragma("unroll") for (int t = 0; t < kSlots; ++t) {                                  \
+    mfma16<ZERO::value>(acc[t / kTM][t % kTM], __builtin_bit_cast(bf16x8_t, wa[t / kTM]), \
+                        xa[t % kTM]);                                                   \
+    if (t < kTM) TERN_GEMM_READ_XB(CUR, t)                                              \
+    if (t < kUnits) hi_unit(t / 5, t % 5);                                              \
+    __builtin_amdgcn_sched_barrier(0);                                                  \
   }
-  // The second half interleaves, one after every second MFMA, the DMA
-  // requests of step s + kRing - 1 and the reads of the next step's first
-  // k-block (weight words, then X chunks).  The MFMAs are volatile asm, so
-  // the memory instructions stay where they are written.
 #define TERN_GEMM_STEP(CUR, NXT, DMA, XR, PR, STAGE, ZERO)                                \
   {                                                                                      \
     TERN_GEMM_HALF_A(CUR, ZERO)                                                          \
     wait_vmcnt<(kRing - 3) * C::kLoads, true>();                                         \
     lds_barrier();                                                                       \
-    _Pragma("unroll") for (int t = 0; t < kTN * kTM; ++t) {                              \
-      mfma16<false>(acc[t / kTM][t % kTM], wb[t / kTM], xb[t % kTM]);                    \
-      constexpr int kOps = C::kLoads + kTN + kTM;                                        \
-      static_assert(2 * kOps <= kTN * kTM, "every operation gets a slot");              \
-      const int op = t / 2;                                                              \
-      if (t % 2 == 1 && op < kOps) {                                                     \
-        if (op < C::kLoads) {                                                            \
-          TERN_GEMM_DMA(DMA, XR, PR, STAGE, op)                                          \
-        } else if (op < C::kLoads + kTN) {                                               \
-          const int j = op - C::kLoads;                                                  \
-          pw[j] = *reinterpret_cast<const uint32_t*>(&NXT[po + j * 256]);                \
-        } else {                                                                         \
-          const int i = op - C::kLoads - kTN;                                            \
-          xa[i] = __builtin_bit_cast(bf16x8_t,                                           \
-                                     *reinterpret_cast<const u32x4_t*>(&NXT[xo0 + i * 2048])); \
-        }                                                                                \
+    _Pragma("unroll") for (int t = 0; t < kSlots; ++t) {                                 \
+      mfma16<false>(acc[t / kTM][t % kTM], __builtin_bit_cast(bf16x8_t, wb[t / kTM]),    \
+                    xb[t % kTM]);                                                        \
+      constexpr int kOps = kTN + C::kLoads + kTM;                                        \
+      constexpr int kDecodeFrom = kSlots - kUnits;                                       \
+      static_assert(kOps <= kDecodeFrom, "memory operations before the decode");        \
+      if (t < kTN) {                                                                     \
+        TERN_GEMM_READ_PW(NXT, t)                                                        \
+      } else if (t < kTN + C::kLoads) {                                                  \
+        TERN_GEMM_DMA(DMA, XR, PR, STAGE, t - kTN)                                       \
+      } else if (t < kOps) {                                                             \
+        TERN_GEMM_READ_XA(NXT, t - kTN - C::kLoads)                                      \
       }                                                                                  \
+      if (t >= kDecodeFrom) lo_unit((t - kDecodeFrom) / 5, (t - kDecodeFrom) % 5);       \
+      __builtin_amdgcn_sched_barrier(0);                                                 \
     }                                                                                    \
   }
-  // Last steps of the last tile: the next stage is waited for in full, and a
-  // request is due only while one is left.
-#define TERN_GEMM_TAIL(ST, CUR, NXT, DMA, ZERO)                    \
-  {                                                                \
-    TERN_GEMM_HALF_A(CUR, ZERO)                                        \
-    if ((ST) + 1 < stages) {                                       \
-      wait_vmcnt<0, true>();                                       \
-      lds_barrier();                                               \
-      if ((ST) + kRing - 1 < stages) TERN_GEMM_ISSUE(DMA, cur_xr, cur_pr, (ST) + kRing - 1) \
-      TERN_GEMM_READ_A(NXT)                                        \
-      phase_fence();                                               \
-    }                                                              \
-    mfma_block(wb, xb, kAcc{});                                    \
-  }
-
   // Epilogue of tile t.  For MFMA tile (j, i) the lane holds output channels
   // n = wn*kWN + 16 j + 4 g + e (e = 0..3) of token m = wm*kWM + 16 i + l16.
   // The decode produced 2 T, so y = bf16(fp32(acc * s) * 0.5), which equals
@@ -438,34 +460,29 @@ void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
     }
   };
 
-  // Stage S of the current tile, clamped to its last stage: requests past
-  // the end re-load that stage into the dead buffer (in range, never read),
-  // so every step of the unrolled loop issues the same instructions and the
-  // wait counts stay exact.
-#define TERN_GEMM_CLAMP(S) ((S) < stages ? (S) : stages - 1)
   // One unrolled iteration: steps st .. st + kRing - 1 out of ring stages 0 ..
   // kRing - 1.  The first request is stage st + kRing - 1 of this tile, the
   // others stages B0 .. B0 + kRing - 2 of the tile with resources BX, BP.
-#define TERN_GEMM_ITER(BX, BP, B0, ZERO)                                                 \
-  TERN_GEMM_STEP(lds0, lds1, lds5, cur_xr, cur_pr, TERN_GEMM_CLAMP(st + kRing - 1), ZERO) \
-  TERN_GEMM_STEP(lds1, lds2, lds0, BX, BP, TERN_GEMM_CLAMP(B0), kAcc)                     \
-  TERN_GEMM_STEP(lds2, lds3, lds1, BX, BP, TERN_GEMM_CLAMP((B0) + 1), kAcc)               \
-  TERN_GEMM_STEP(lds3, lds4, lds2, BX, BP, TERN_GEMM_CLAMP((B0) + 2), kAcc)               \
-  TERN_GEMM_STEP(lds4, lds5, lds3, BX, BP, TERN_GEMM_CLAMP((B0) + 3), kAcc)               \
-  TERN_GEMM_STEP(lds5, lds0, lds4, BX, BP, TERN_GEMM_CLAMP((B0) + 4), kAcc)
+#define TERN_GEMM_ITER(BX, BP, B0, ZERO)                                          \
+  /* several statements: use inside braces */                                     \
+  TERN_GEMM_STEP(lds0, lds1, lds5, cur_xr, cur_pr, st + kRing - 1, ZERO)          \
+  TERN_GEMM_STEP(lds1, lds2, lds0, BX, BP, (B0), kAcc)                            \
+  TERN_GEMM_STEP(lds2, lds3, lds1, BX, BP, (B0) + 1, kAcc)                        \
+  TERN_GEMM_STEP(lds3, lds4, lds2, BX, BP, (B0) + 2, kAcc)                        \
+  TERN_GEMM_STEP(lds4, lds5, lds3, BX, BP, (B0) + 3, kAcc)                        \
+  TERN_GEMM_STEP(lds5, lds0, lds4, BX, BP, (B0) + 4, kAcc)
 
   __amdgpu_buffer_rsrc_t cur_xr, cur_pr;
   tile_rsrc(0, cur_xr, cur_pr);
-  uint32_t pw[kTN];
-  bf16x8_t xa[kTM], xb[kTM];
   TERN_GEMM_ISSUE(lds0, cur_xr, cur_pr, 0)
-  TERN_GEMM_ISSUE(lds1, cur_xr, cur_pr, TERN_GEMM_CLAMP(1))
-  TERN_GEMM_ISSUE(lds2, cur_xr, cur_pr, TERN_GEMM_CLAMP(2))
-  TERN_GEMM_ISSUE(lds3, cur_xr, cur_pr, TERN_GEMM_CLAMP(3))
-  TERN_GEMM_ISSUE(lds4, cur_xr, cur_pr, TERN_GEMM_CLAMP(4))
+  TERN_GEMM_ISSUE(lds1, cur_xr, cur_pr, 1)
+  TERN_GEMM_ISSUE(lds2, cur_xr, cur_pr, 2)
+  TERN_GEMM_ISSUE(lds3, cur_xr, cur_pr, 3)
+  TERN_GEMM_ISSUE(lds4, cur_xr, cur_pr, 4)
   wait_vmcnt<(kRing - 2) * C::kLoads, true>();
   lds_barrier();
   TERN_GEMM_READ_A(lds0)
+  decode_lo_all();
 
   if constexpr (PERSIST) {
     for (int t = 0; t < my_tiles; ++t) {
@@ -495,34 +512,25 @@ void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
     }
     wait_vmcnt<0>();  // no DMA may outlive the workgroup's LDS
   } else {
+    // One tile; the last iteration may run past the end of K on zeros.
     int st = 0;
-    if (st + kRing < stages) {
-      TERN_GEMM_ITER(cur_xr, cur_pr, st + kRing, kZero)
-      for (st = kRing; st + kRing < stages; st += kRing) {
-        TERN_GEMM_ITER(cur_xr, cur_pr, st + kRing, kAcc)
-      }
-      // 1 to kRing steps remain, starting at ring stage 0.
-      TERN_GEMM_TAIL(st, lds0, lds1, lds5, kAcc)
-    } else {
-      TERN_GEMM_TAIL(st, lds0, lds1, lds5, kZero)
+    TERN_GEMM_ITER(cur_xr, cur_pr, st + kRing, kZero)
+    for (st = kRing; st < stages; st += kRing) {
+      TERN_GEMM_ITER(cur_xr, cur_pr, st + kRing, kAcc)
     }
-    if (st + 1 < stages) TERN_GEMM_TAIL(st + 1, lds1, lds2, lds0, kAcc)
-    if (st + 2 < stages) TERN_GEMM_TAIL(st + 2, lds2, lds3, lds1, kAcc)
-    if (st + 3 < stages) TERN_GEMM_TAIL(st + 3, lds3, lds4, lds2, kAcc)
-    if (st + 4 < stages) TERN_GEMM_TAIL(st + 4, lds4, lds5, lds3, kAcc)
-    if (st + 5 < stages) TERN_GEMM_TAIL(st + 5, lds5, lds0, lds4, kAcc)
     wait_vmcnt<0>();  // no DMA may outlive the workgroup's LDS
     epilogue(0);
   }
 #undef TERN_GEMM_ITER
-#undef TERN_GEMM_CLAMP
-#undef TERN_GEMM_TAIL
 #undef TERN_GEMM_STEP
 #undef TERN_GEMM_HALF_A
 #undef TERN_GEMM_ISSUE
 #undef TERN_GEMM_DMA
 #undef TERN_GEMM_READ_A
 #undef TERN_GEMM_READ_B
+#undef TERN_GEMM_READ_PW
+#undef TERN_GEMM_READ_XA
+#undef TERN_GEMM_READ_XB
 #endif  // __HIP_DEVICE_COMPILE__
 }
 

@@ -11,8 +11,9 @@
 // and kept in registers (up to 128 elements per thread, K <= 32768); the two
 // reductions (max of |w|, then the integer sum) are wave-level butterflies
 // followed by a 4-entry LDS combine; then each thread writes its ternary
-// codes.  The work is HBM-bound: 4 (or 2) bytes read and 1 byte written per
-// weight.
+// codes.  Per weight: 4 (or 2) bytes read, 1 byte written, and about fifteen
+// VALU instructions (the fixed-point term is formed with exact fp32 scaling
+// and floors rather than 64-bit integer shifts).
 #include "internal.h"
 
 namespace tern {
@@ -48,20 +49,36 @@ __device__ inline uint32_t bits_of<uint16_t>(uint16_t v) {
   return static_cast<uint32_t>(v) << 16;
 }
 
-// floor(|a| * 2^(48 - E)) for the fp32 magnitude with bit pattern `abits`,
-// computed on the integer significand: |a| = m * 2^(ef - 150), ef >= 1.
-__device__ inline unsigned long long fixed_point_term(uint32_t abits, int E) {
-  uint32_t ef = abits >> 23;
-  uint32_t m = abits & 0x7FFFFFu;
-  if (ef != 0) {
-    m |= 0x800000u;
-  } else {
-    ef = 1;
-  }
-  int sh = static_cast<int>(ef) - 102 - E;  // <= 25 because |a| <= 2^(E+1)
-  if (sh >= 0) return static_cast<unsigned long long>(m) << sh;
-  if (sh > -32) return static_cast<unsigned long long>(m >> (-sh));
-  return 0ull;
+// Adds q = floor(|a| * 2^(48 - E)) for the fp32 magnitude with bit pattern
+// `abits` (|a| <= 2^(E+1), so q < 2^49) to a split accumulator: q = h * 2^32 +
+// l with h < 2^17 and l < 2^32.  Every step is exact in fp32: the scaling by a
+// power of two (a result below 1 may lose bits but floors to 0 either way),
+// the floors of values below 2^49, and l = x - h * 2^32, a multiple of
+// ulp(x) below 2^32.
+__device__ inline void fixed_point_add(uint32_t abits, int E, uint32_t& acc_hi,
+                                       unsigned long long& acc_lo) {
+  const float x = __builtin_floorf(__builtin_ldexpf(__uint_as_float(abits), 48 - E));
+  const float h = __builtin_floorf(x * 0x1p-32f);
+  const float l = __builtin_fmaf(h, -0x1p32f, x);
+  acc_hi += static_cast<uint32_t>(h);
+  acc_lo += static_cast<uint32_t>(l);
+}
+
+// Code of one weight (fp32 bit pattern b) against the row scale s.
+__device__ inline int8_t ternary_code(uint32_t b, float s) {
+  const float mag = __uint_as_float(b & 0x7FFFFFFFu);
+  return (2.0f * mag > s) ? ((b >> 31) ? int8_t(-1) : int8_t(1)) : int8_t(0);
+}
+
+// E = floor(log2(m)) for the fp32 magnitude bits m != 0 (normal or subnormal).
+__device__ inline int floor_log2_bits(uint32_t m) {
+  const uint32_t ef = m >> 23;
+  return ef != 0 ? static_cast<int>(ef) - 127 : (31 - __clz(static_cast<int>(m))) - 149;
+}
+
+// s = fp32(Q * 2^(E - 48) / k), each step rounded to nearest.
+__device__ inline float scale_of(unsigned long long q, int E, int64_t k) {
+  return static_cast<float>(ldexp(static_cast<double>(q), E - 48) / static_cast<double>(k));
 }
 
 template <typename TIn, int VEC, int CAP>
@@ -123,36 +140,31 @@ __global__ __launch_bounds__(kThreads) void quantize_rows(const TIn* __restrict_
   float scale = 0.0f;
   if (amax != 0u) {
     // E = floor(log2(max |w|)), exact for normal and subnormal maxima.
-    const uint32_t ef = amax >> 23;
-    const int E = ef != 0 ? static_cast<int>(ef) - 127 : (31 - __clz(static_cast<int>(amax))) - 149;
-    unsigned long long q = 0;
+    const int E = floor_log2_bits(amax);
+    uint32_t q_hi = 0;           // < 2^17 * CAP
+    unsigned long long q_lo = 0;  // < 2^32 * CAP
 #pragma unroll
-    for (int i = 0; i < CAP; ++i) q += fixed_point_term(a[i] & 0x7FFFFFFFu, E);
-    q = wave_sum_u64(q);
+    for (int i = 0; i < CAP; ++i) fixed_point_add(a[i] & 0x7FFFFFFFu, E, q_hi, q_lo);
+    const unsigned long long q = wave_sum_u64((static_cast<unsigned long long>(q_hi) << 32) + q_lo);
     if (lane == 0) red_sum[wave] = q;
     __syncthreads();
     unsigned long long total = 0;
 #pragma unroll
     for (int i = 0; i < kWaves; ++i) total += red_sum[i];
-    const double mean = ldexp(static_cast<double>(total), E - 48) / static_cast<double>(k);
-    scale = static_cast<float>(mean);
+    scale = scale_of(total, E, k);
   }
   if (tid == 0) s[row] = scale;
 
-  // T = sign(w) where 2|w| > s (exact in double), else 0.  An all-zero row has
-  // s = 0 and every |w| = 0, so it also yields T = 0.
-  const double sd = static_cast<double>(scale);
+  // T = sign(w) where 2|w| > s, else 0.  The comparison is exact in fp32:
+  // doubling is exact (a magnitude of 2^127 or more doubles to +inf, which
+  // exceeds every finite s, as 2|w| does).  An all-zero row has s = 0 and
+  // every |w| = 0, so it also yields T = 0.
 #pragma unroll
   for (int c = 0; c < kChunks; ++c) {
     const int64_t e0 = (static_cast<int64_t>(c) * kThreads + tid) * VEC;
     int8_t code[VEC];
 #pragma unroll
-    for (int v = 0; v < VEC; ++v) {
-      const uint32_t b = a[c * VEC + v];
-      const double mag = static_cast<double>(__uint_as_float(b & 0x7FFFFFFFu));
-      const bool nz = 2.0 * mag > sd && amax != 0u;
-      code[v] = nz ? ((b >> 31) ? int8_t(-1) : int8_t(1)) : int8_t(0);
-    }
+    for (int v = 0; v < VEC; ++v) code[v] = ternary_code(a[c * VEC + v], scale);
     if constexpr (VEC == 4) {
       if (e0 + 4 <= k) {
         uint32_t packed = (uint32_t(uint8_t(code[0]))) | (uint32_t(uint8_t(code[1])) << 8) |
@@ -176,6 +188,7 @@ __global__ __launch_bounds__(kThreads) void quantize_rows(const TIn* __restrict_
       if (e0 + v < k) tr[e0 + v] = code[v];
   }
 }
+
 
 template <typename TIn, int VEC>
 hipError_t launch_cap(const TIn* w, int64_t n, int64_t k, int64_t ldw, int8_t* t, int64_t ldt,
