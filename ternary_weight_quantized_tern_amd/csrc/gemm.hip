@@ -120,11 +120,12 @@ struct TileCfg {
   static constexpr int kStage = kXBytes + kPBytes;
   static constexpr int kXInstr = kXBytes / 1024;   // 1 KiB DMA instructions per stage: X
   static constexpr int kPInstr = kPBytes / 1024;   // ... packed weights
-  static constexpr int kLoads = (kXInstr + kPInstr) / 4;  // per wave per stage
+  static constexpr int kInstr = kXInstr + kPInstr;
+  static constexpr int kLoads = (kInstr + 3) / 4;  // per wave per stage (the last ones may
+                                                   // repeat load 0 to even the count)
   static_assert(WAVES_M == 1 || WAVES_M == 2 || WAVES_M == 4, "4 waves");
   static_assert(kWM % 16 == 0 && kWN % 16 == 0, "whole MFMA tiles");
   static_assert(BM % 8 == 0 && BN % 64 == 0, "whole DMA instructions");
-  static_assert((kXInstr + kPInstr) % 4 == 0, "same DMA count on every wave");
   static_assert((kWM * 128) % 1024 == 0 || kWavesM == 1, "row swizzle period");
 };
 
@@ -137,8 +138,8 @@ struct TileCfg {
 // fall between iterations of the kRing-step unrolled loop: PERSIST requires
 // (k / 64) % kRing == 0.  Without PERSIST each workgroup computes tile b
 // only, for any k that is a multiple of 64.
-template <int BM, int BN, int WAVES_M, int GM, bool PERSIST>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int BM, int BN, int WAVES_M, int GM, bool PERSIST, int WPE>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
                        const uint8_t* __restrict__ p, int n, int ldp,
                        const float* __restrict__ s, uint16_t* __restrict__ y, int ldy,
@@ -195,7 +196,8 @@ void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
   };
 
   // DMA plan.  A stage is kXInstr + kPInstr loads of 1 KiB (16 bytes per
-  // lane); wave w issues loads w, w+4, w+8, ... in that list.  X load q fills
+  // lane); wave w issues loads w, w+4, w+8, ... in that list, every wave the
+  // same number of them.  X load q fills
   // LDS bytes [1024 q, +1024): rows 8 q + lane/8, slot lane%8, which holds
   // logical chunk (lane%8) ^ xswz(row).  Weight load p fills [kXBytes +
   // 1024 p, +1024): rows 64 p + lane, 16 bytes each.
@@ -204,7 +206,8 @@ void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
   bool dma_is_x[C::kLoads];
 #pragma unroll
   for (int q = 0; q < C::kLoads; ++q) {
-    const int gi = wave + 4 * q;
+    // A slot past the last load repeats load 0 (same bytes to the same place).
+    const int gi = (wave + 4 * q) < C::kInstr ? wave + 4 * q : 0;
     dma_is_x[q] = gi < C::kXInstr;
     if (dma_is_x[q]) {
       const uint32_t r = 8u * gi + (lane >> 3);
@@ -314,7 +317,14 @@ void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
   };
   constexpr int kSlots = kTN * kTM;       // MFMAs per half step
   constexpr int kUnits = 5 * kTN;         // decode units per half step
-  static_assert(kUnits <= kSlots, "one decode unit per MFMA slot");
+  // Half A: one X read (kTM) and one decode unit per slot.  Half B: the
+  // memory operations first, the decode of the next wa as late as possible but
+  // after them.  Small wave tiles have fewer MFMA slots than operations; the
+  // slots past kSlots carry no MFMA.
+  constexpr int kSlotsA = kSlots > kUnits ? kSlots : kUnits;
+  constexpr int kOpsB = kTN + C::kLoads + kTM;
+  constexpr int kDecodeFrom = (kSlots - kUnits) > kOpsB ? kSlots - kUnits : kOpsB;
+  constexpr int kSlotsB = kSlots > kDecodeFrom + kUnits ? kSlots : kDecodeFrom + kUnits;
 
   // One step out of ring stage CUR.  On entry the weight words pw, their
   // k-block 0 operands wa (and w2) and the X chunks xa of this step are in
@@ -329,9 +339,10 @@ void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
   // scheduling barrier, so this interleave is the issue order.  At every
   // barrier of the unrolled loop exactly kRing-2 steps are in flight.
 #define TERN_GEMM_HALF_A(CUR, ZERO)                                                     \
-  _Pragma("unroll") for (int t = 0; t < kSlots; ++t) {                                  \
-    mfma16<ZERO::value>(acc[t / kTM][t % kTM], __builtin_bit_cast(bf16x8_t, wa[t / kTM]), \
-                        xa[t % kTM]);                                                   \
+  _Pragma("unroll") for (int t = 0; t < kSlotsA; ++t) {                                 \
+    if (t < kSlots)                                                                     \
+      mfma16<ZERO::value>(acc[t / kTM][t % kTM],                                        \
+                          __builtin_bit_cast(bf16x8_t, wa[t / kTM]), xa[t % kTM]);      \
     if (t < kTM) TERN_GEMM_READ_XB(CUR, t)                                              \
     if (t < kUnits) hi_unit(t / 5, t % 5);                                              \
     __builtin_amdgcn_sched_barrier(0);                                                  \
@@ -341,20 +352,19 @@ void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
     TERN_GEMM_HALF_A(CUR, ZERO)                                                          \
     wait_vmcnt<(kRing - 3) * C::kLoads, true>();                                         \
     lds_barrier();                                                                       \
-    _Pragma("unroll") for (int t = 0; t < kSlots; ++t) {                                 \
-      mfma16<false>(acc[t / kTM][t % kTM], __builtin_bit_cast(bf16x8_t, wb[t / kTM]),    \
-                    xb[t % kTM]);                                                        \
-      constexpr int kOps = kTN + C::kLoads + kTM;                                        \
-      constexpr int kDecodeFrom = kSlots - kUnits;                                       \
-      static_assert(kOps <= kDecodeFrom, "memory operations before the decode");        \
+    _Pragma("unroll") for (int t = 0; t < kSlotsB; ++t) {                                \
+      if (t < kSlots)                                                                    \
+        mfma16<false>(acc[t / kTM][t % kTM], __builtin_bit_cast(bf16x8_t, wb[t / kTM]),  \
+                      xb[t % kTM]);                                                      \
       if (t < kTN) {                                                                     \
         TERN_GEMM_READ_PW(NXT, t)                                                        \
       } else if (t < kTN + C::kLoads) {                                                  \
         TERN_GEMM_DMA(DMA, XR, PR, STAGE, t - kTN)                                       \
-      } else if (t < kOps) {                                                             \
+      } else if (t < kOpsB) {                                                            \
         TERN_GEMM_READ_XA(NXT, t - kTN - C::kLoads)                                      \
       }                                                                                  \
-      if (t >= kDecodeFrom) lo_unit((t - kDecodeFrom) / 5, (t - kDecodeFrom) % 5);       \
+      if (t >= kDecodeFrom && t < kDecodeFrom + kUnits)                                  \
+        lo_unit((t - kDecodeFrom) / 5, (t - kDecodeFrom) % 5);                           \
       __builtin_amdgcn_sched_barrier(0);                                                 \
     }                                                                                    \
   }
@@ -373,13 +383,14 @@ void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
   // next request into it follows the next step's barrier.  Other tiles take
   // the direct path, with 8-byte stores where Y allows them.
   constexpr int kEpiPitch = 2 * C::kWN + 16;
-  static_assert(kThreads / 64 * 16 * kEpiPitch <= C::kStage, "epilogue staging fits a stage");
-  static_assert((16 * 2 * C::kWN / 16) % 64 == 0, "whole store instructions");
+  constexpr bool kEpiLds = kThreads / 64 * 16 * kEpiPitch <= C::kStage &&  // fits a stage
+                           (16 * 2 * C::kWN / 16) % 64 == 0;               // whole stores
+  static_assert(kEpiLds || !PERSIST, "the persistent kernel stores through LDS");
   auto epilogue = [&](int t) {
     acc_ready();
     int m0, n0;
     tile_coords(t, m0, n0);
-    if (PERSIST || ((y_flags & 2) && m0 + BM <= m && n0 + BN <= n)) {
+    if (kEpiLds && (PERSIST || ((y_flags & 2) && m0 + BM <= m && n0 + BN <= n))) {
       constexpr int kChunksPerRow = 2 * C::kWN / 16;              // 16-byte pieces of a row
       constexpr int kStores = 16 * kChunksPerRow / 64;            // per lane per 16 rows
       const uint32_t area = static_cast<uint32_t>(wave) * (16 * kEpiPitch);
@@ -550,7 +561,7 @@ __global__ void fill_zero_bf16(uint16_t* y, int m, int n, int ldy) {
 constexpr int kPersistentGrid = 256;
 constexpr int64_t kSmallMaxM = 32;
 
-template <int BM, int BN, int WAVES_M, int GM>
+template <int BM, int BN, int WAVES_M, int GM, int WPE>
 hipError_t launch_tiles(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const uint8_t* p,
                         int64_t n, int64_t ldp, const float* s, uint16_t* y, int64_t ldy,
                         hipStream_t stream) {
@@ -566,18 +577,22 @@ hipError_t launch_tiles(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, co
         (reinterpret_cast<uintptr_t>(s) & 15) == 0) ? 2 : 0);
   // The persistent kernel takes whole tiles only (its epilogue has no edge
   // handling) and needs the ring stream to restart at a tile boundary.
-  if (stages % 6 == 0 && tiles > kPersistentGrid && m % BM == 0 && n % BN == 0 && (y_flags & 2)) {
-    hipLaunchKernelGGL((gemm_ternary_mfma<BM, BN, WAVES_M, GM, true>), dim3(kPersistentGrid),
-                       dim3(kThreads), 0, stream, x, static_cast<int>(m), static_cast<int>(k),
-                       static_cast<int>(ldx), p, static_cast<int>(n), static_cast<int>(ldp), s, y,
-                       static_cast<int>(ldy), tiles_m, tiles_n, y_flags);
-  } else {
-    hipLaunchKernelGGL((gemm_ternary_mfma<BM, BN, WAVES_M, GM, false>),
-                       dim3(static_cast<unsigned>(tiles)), dim3(kThreads), 0, stream, x,
-                       static_cast<int>(m), static_cast<int>(k), static_cast<int>(ldx), p,
-                       static_cast<int>(n), static_cast<int>(ldp), s, y, static_cast<int>(ldy),
-                       tiles_m, tiles_n, y_flags);
+  if constexpr (WPE == 1) {
+    if (stages % 6 == 0 && tiles > kPersistentGrid && m % BM == 0 && n % BN == 0 &&
+        (y_flags & 2)) {
+      hipLaunchKernelGGL((gemm_ternary_mfma<BM, BN, WAVES_M, GM, true, WPE>),
+                         dim3(kPersistentGrid), dim3(kThreads), 0, stream, x,
+                         static_cast<int>(m), static_cast<int>(k), static_cast<int>(ldx), p,
+                         static_cast<int>(n), static_cast<int>(ldp), s, y, static_cast<int>(ldy),
+                         tiles_m, tiles_n, y_flags);
+      return hipGetLastError();
+    }
   }
+  hipLaunchKernelGGL((gemm_ternary_mfma<BM, BN, WAVES_M, GM, false, WPE>),
+                     dim3(static_cast<unsigned>(tiles)), dim3(kThreads), 0, stream, x,
+                     static_cast<int>(m), static_cast<int>(k), static_cast<int>(ldx), p,
+                     static_cast<int>(n), static_cast<int>(ldp), s, y, static_cast<int>(ldy),
+                     tiles_m, tiles_n, y_flags);
   return hipGetLastError();
 }
 
@@ -595,7 +610,16 @@ hipError_t launch_gemm(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, con
   }
   // A few tokens: the weight stream dominates; see gemm_small.hip.
   if (m <= kSmallMaxM) return launch_gemm_small(x, m, k, ldx, p, n, ldp, s, y, ldy, stream);
-  return launch_tiles<144, 384, 1, 4>(x, m, k, ldx, p, n, ldp, s, y, ldy, stream);
+  // Layers with at least one 144 x 384 tile per CU use the big tile (one
+  // workgroup per CU, 147 KiB of LDS).  Smaller layers use 64-row tiles, two
+  // workgroups per CU, with 256 or 128 output channels per tile, whichever
+  // still gives two tiles per CU, so that every CU has work.
+  const auto tiles = [&](int64_t bm, int64_t bn) { return ((m + bm - 1) / bm) * ((n + bn - 1) / bn); };
+  if (tiles(144, 384) >= kPersistentGrid)
+    return launch_tiles<144, 384, 1, 4, 1>(x, m, k, ldx, p, n, ldp, s, y, ldy, stream);
+  if (tiles(64, 256) >= 2 * kPersistentGrid)
+    return launch_tiles<64, 256, 1, 4, 2>(x, m, k, ldx, p, n, ldp, s, y, ldy, stream);
+  return launch_tiles<64, 128, 1, 4, 2>(x, m, k, ldx, p, n, ldp, s, y, ldy, stream);
 }
 
 }  // namespace tern

@@ -110,6 +110,8 @@ GEMM_SHAPES = [
     # one or two MFMA row blocks, and the first size past it
     (2, 320, 50), (5, 448, 33), (16, 4608, 1152), (17, 832, 100), (31, 1088, 47),
     (32, 256, 16), (33, 576, 40), (8, 64, 4608),
+    # 64 x 256 tiles (fewer than 256 big tiles, at least 512 of these): ragged m and n
+    (1100, 128, 7500),
 ]
 
 
