@@ -37,20 +37,22 @@ constexpr int kSmallThreads = 256;
 constexpr int kChunk = 256;           // K per chunk and wave
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
-// R MFMA row blocks (m <= 16 R), DEPTH chunks in flight per wave.
-template <int R, int DEPTH>
+// R MFMA row blocks (m <= 16 R), B blocks of 16 output channels per
+// workgroup (every wave covers all of them for its K chunks, so one X operand
+// serves B MFMAs), DEPTH chunks in flight per wave.
+template <int R, int B, int DEPTH>
 __global__ __launch_bounds__(kSmallThreads) void gemm_ternary_small(
     const uint16_t* __restrict__ x, int m, int k, int ldx, const uint8_t* __restrict__ p, int n,
     int ldp, const float* __restrict__ s, uint16_t* __restrict__ y, int ldy, int y_vec_ok) {
-  __shared__ f32x4_t red[kSmallThreads / 64 - 1][R][64];
+  __shared__ f32x4_t red[kSmallThreads / 64 - 1][B][R][64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15;
   const int g = lane >> 4;
-  const int n0 = blockIdx.x * 16;
-  const int rows = (n - n0) < 16 ? (n - n0) : 16;
+  const int n0 = blockIdx.x * (16 * B);
+  const int rows = (n - n0) < 16 * B ? (n - n0) : 16 * B;
 
   const __amdgpu_buffer_rsrc_t prs = make_rsrc(
       p + static_cast<int64_t>(n0) * ldp, static_cast<uint32_t>((rows - 1) * ldp + k / 4));
@@ -66,7 +68,7 @@ __global__ __launch_bounds__(kSmallThreads) void gemm_ternary_small(
 #pragma unroll
   for (int b = 0; b < R; ++b) x_off[b] = static_cast<uint32_t>(((16 * b + r16) * ldx + 64 * g) * 2);
 
-  u32x4_t wq[DEPTH];
+  u32x4_t wq[DEPTH][B];
   u32x4_t xq[DEPTH][R][8];
   // Each chunk's loads are issued as one group, in chunk order (the fences
   // keep the scheduler from interleaving groups), so that waiting for the
@@ -82,8 +84,13 @@ __global__ __launch_bounds__(kSmallThreads) void gemm_ternary_small(
     // keeps one unconditional load per operand).
     const int kc = c * kChunk + 64 * g;
     const uint32_t oob = static_cast<uint32_t>(k - 1 - kc) & kOutOfRange;
-    const uint32_t po = (p_off + static_cast<uint32_t>(c * (kChunk / 4))) | oob;
-    wq[slot] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(prs, po, 0, 0));
+#pragma unroll
+    for (int bl = 0; bl < B; ++bl) {
+      const uint32_t po =
+          (p_off + static_cast<uint32_t>(bl * 16 * ldp + c * (kChunk / 4))) | oob;
+      wq[slot][bl] =
+          __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(prs, po, 0, 0));
+    }
 #pragma unroll
     for (int b = 0; b < R; ++b)
 #pragma unroll
@@ -95,20 +102,24 @@ __global__ __launch_bounds__(kSmallThreads) void gemm_ternary_small(
     fence();
   };
 
-  f32x4_t acc[R];
+  f32x4_t acc[B][R];
 #pragma unroll
-  for (int b = 0; b < R; ++b) acc[b] = f32x4_t{};
+  for (int bl = 0; bl < B; ++bl)
+#pragma unroll
+    for (int b = 0; b < R; ++b) acc[bl][b] = f32x4_t{};
   auto compute = [&](int slot) {
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      bf16x8_t lo, hi;
-      decode16(wq[slot][d], lo, hi);
+    for (int bl = 0; bl < B; ++bl)
 #pragma unroll
-      for (int b = 0; b < R; ++b) {
-        mfma16<false>(acc[b], lo, __builtin_bit_cast(bf16x8_t, xq[slot][b][2 * d]));
-        mfma16<false>(acc[b], hi, __builtin_bit_cast(bf16x8_t, xq[slot][b][2 * d + 1]));
+      for (int d = 0; d < 4; ++d) {
+        bf16x8_t lo, hi;
+        decode16(wq[slot][bl][d], lo, hi);
+#pragma unroll
+        for (int b = 0; b < R; ++b) {
+          mfma16<false>(acc[bl][b], lo, __builtin_bit_cast(bf16x8_t, xq[slot][b][2 * d]));
+          mfma16<false>(acc[bl][b], hi, __builtin_bit_cast(bf16x8_t, xq[slot][b][2 * d + 1]));
+        }
       }
-    }
   };
 
   // The wave's i-th chunk is global chunk wave + 4 i, fetched DEPTH chunks
@@ -129,24 +140,30 @@ __global__ __launch_bounds__(kSmallThreads) void gemm_ternary_small(
   // states; the empty asm statements keep every read of acc after them.
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 #pragma unroll
-  for (int b = 0; b < R; ++b) asm volatile("" : "+v"(acc[b]));
+  for (int bl = 0; bl < B; ++bl)
+#pragma unroll
+    for (int b = 0; b < R; ++b) asm volatile("" : "+v"(acc[bl][b]));
 
   if (wave > 0) {
 #pragma unroll
-    for (int b = 0; b < R; ++b) red[wave - 1][b][lane] = acc[b];
+    for (int bl = 0; bl < B; ++bl)
+#pragma unroll
+      for (int b = 0; b < R; ++b) red[wave - 1][bl][b][lane] = acc[bl][b];
   }
   __syncthreads();
   if (wave != 0) return;
 
-  const int nb = n0 + 4 * g;  // output channels nb .. nb + 3 of this lane
+#pragma unroll
+  for (int bl = 0; bl < B; ++bl) {
+  const int nb = n0 + 16 * bl + 4 * g;  // output channels nb .. nb + 3 of this lane
   float sc[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) sc[e] = (nb + e < n) ? s[nb + e] * 0.5f : 0.0f;
 #pragma unroll
   for (int b = 0; b < R; ++b) {
-    f32x4_t v = acc[b];
+    f32x4_t v = acc[bl][b];
 #pragma unroll
-    for (int w = 0; w < kSmallThreads / 64 - 1; ++w) v += red[w][b][lane];
+    for (int w = 0; w < kSmallThreads / 64 - 1; ++w) v += red[w][bl][b][lane];
     const int token = 16 * b + r16;
     if (token >= m) continue;
     __bf16 o[4];
@@ -166,15 +183,16 @@ __global__ __launch_bounds__(kSmallThreads) void gemm_ternary_small(
         if (nb + e < n) yr[e] = __builtin_bit_cast(uint16_t, o[e]);
     }
   }
+  }
 }
 
-template <int R, int DEPTH>
+template <int R, int B, int DEPTH>
 hipError_t launch_small(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const uint8_t* p,
                         int64_t n, int64_t ldp, const float* s, uint16_t* y, int64_t ldy,
                         hipStream_t stream) {
-  const int64_t blocks = (n + 15) / 16;
+  const int64_t blocks = (n + 16 * B - 1) / (16 * B);
   const int y_vec_ok = ((reinterpret_cast<uintptr_t>(y) & 7) == 0) && (ldy % 4 == 0);
-  hipLaunchKernelGGL((gemm_ternary_small<R, DEPTH>), dim3(static_cast<unsigned>(blocks)),
+  hipLaunchKernelGGL((gemm_ternary_small<R, B, DEPTH>), dim3(static_cast<unsigned>(blocks)),
                      dim3(kSmallThreads), 0, stream, x, static_cast<int>(m), static_cast<int>(k),
                      static_cast<int>(ldx), p, static_cast<int>(n), static_cast<int>(ldp), s, y,
                      static_cast<int>(ldy), y_vec_ok);
@@ -186,8 +204,15 @@ hipError_t launch_small(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, co
 hipError_t launch_gemm_small(const uint16_t* x, int64_t m, int64_t k, int64_t ldx,
                              const uint8_t* p, int64_t n, int64_t ldp, const float* s,
                              uint16_t* y, int64_t ldy, hipStream_t stream) {
-  if (m <= 16) return launch_small<1, 4>(x, m, k, ldx, p, n, ldp, s, y, ldy, stream);
-  return launch_small<2, 2>(x, m, k, ldx, p, n, ldp, s, y, ldy, stream);
+  // Four channel blocks per workgroup when that still leaves a workgroup
+  // per CU: each X operand then feeds four MFMAs instead of one.
+  const bool wide = (n + 63) / 64 >= 256;
+  if (m <= 16) {
+    if (wide) return launch_small<1, 4, 3>(x, m, k, ldx, p, n, ldp, s, y, ldy, stream);
+    return launch_small<1, 1, 4>(x, m, k, ldx, p, n, ldp, s, y, ldy, stream);
+  }
+  if (wide) return launch_small<2, 4, 2>(x, m, k, ldx, p, n, ldp, s, y, ldy, stream);
+  return launch_small<2, 1, 2>(x, m, k, ldx, p, n, ldp, s, y, ldy, stream);
 }
 
 }  // namespace tern

@@ -112,6 +112,8 @@ GEMM_SHAPES = [
     (32, 256, 16), (33, 576, 40), (8, 64, 4608),
     # 64 x 256 tiles (fewer than 256 big tiles, at least 512 of these): ragged m and n
     (1100, 128, 7500),
+    # few-token path with four 16-channel blocks per workgroup (n >= 256 * 64)
+    (5, 320, 16400), (20, 256, 16448),
 ]
 
 
