@@ -29,9 +29,10 @@
 //  * The packed weights stay packed in LDS (16 bytes = 64 codes per row per
 //    step).  Each lane reads one 32-bit word (16 codes) per 16-row tile and
 //    decodes it in registers: with codes 00 / 01 / 11 the bf16 value
-//    code << 14 is exactly 0 / +2.0 / -2.0, so two weights cost a shift and
-//    a mask after one byte permute.  The factor 2 is removed exactly in the
-//    epilogue.
+//    code << 14 is exactly 0 / +2.0 / -2.0.  Four shift-and-mask vectors
+//    put every code in the top bits of a byte, and one byte permute per
+//    operand register places two of them: 15 VALU instructions per 16
+//    weights.  The factor 2 is removed exactly in the epilogue.
 //  * Epilogue: fp32 accumulator times the fp32 channel scale, one
 //    round-to-nearest-even conversion to bf16.
 //  * Workgroups are renumbered so that each XCD (which owns its own L2)
@@ -247,13 +248,13 @@ void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
   static_assert(C::kWM % 16 == 0, "xswz(row + 16 i) == xswz(row)");
 
   f32x4_t acc[kTN][kTM];
-  uint32_t pw[kTN], w2[kTN], h0[kTN], h1[kTN];
+  uint32_t pw[kTN], tq[kTN][4];
   u32x4_t wa[kTN], wb[kTN];
   bf16x8_t xa[kTM], xb[kTM];
 
   // Operand reads out of ring stage BUF: the 32-bit code words of every
-  // weight tile and the X chunks of k-block 0 (READ_A), or the X chunks of
-  // k-block 1 (READ_B).
+  // weight tile (READ_PW), the X chunks of k-block 0 (READ_XA) and of k-block
+  // 1 (READ_XB); READ_A is all of a step's words and k-block 0 chunks.
 #define TERN_GEMM_READ_PW(BUF, J) pw[J] = *reinterpret_cast<const uint32_t*>(&BUF[po + (J) * 256]);
 #define TERN_GEMM_READ_XA(BUF, I) \
   xa[I] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(&BUF[xo0 + (I) * 2048]));
@@ -262,20 +263,11 @@ void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
 #define TERN_GEMM_READ_A(BUF)                                         \
   _Pragma("unroll") for (int j = 0; j < kTN; ++j) TERN_GEMM_READ_PW(BUF, j) \
   _Pragma("unroll") for (int i = 0; i < kTM; ++i) TERN_GEMM_READ_XA(BUF, i)
-#define TERN_GEMM_READ_B(BUF) \
-  _Pragma("unroll") for (int i = 0; i < kTM; ++i) TERN_GEMM_READ_XB(BUF, i)
 
   // ZERO starts a new sum (the MFMA's C operand is the constant 0), so the
   // accumulators of consecutive tiles never meet in one register value.
   using kAcc = std::false_type;
   using kZero = std::true_type;
-  auto mfma_block = [&](const u32x4_t (&w)[kTN], const bf16x8_t (&xv)[kTM], auto zero) {
-#pragma unroll
-    for (int j = 0; j < kTN; ++j)
-#pragma unroll
-      for (int i = 0; i < kTM; ++i)
-        mfma16<decltype(zero)::value>(acc[j][i], __builtin_bit_cast(bf16x8_t, w[j]), xv[i]);
-  };
   // Before the accumulators are read: an MFMA result may be read by other
   // instructions only after up to 19 wait states.  The empty asm statements
   // order every read of acc after the s_nop block.
@@ -287,44 +279,69 @@ void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
       for (int i = 0; i < kTM; ++i) asm volatile("" : "+a"(acc[j][i]));
   };
 
-  // Decode of weight word j in units of at most two VALU instructions, so
-  // that it can be spread between MFMAs.  After the byte permute, half-word 0
-  // of h holds the codes in place and half-word 1 the same codes moved down
-  // one field; a left shift by 14 - 4q and a mask leave code 2q in bits 14..15
-  // and code 2q+1 in bits 30..31, i.e. bf16 0 / +2 / -2.  The lo units (0..4)
-  // produce the k-block 0 operand wa[j] (codes 0..7) and keep pw >> 2 in w2;
-  // the hi units produce wb[j] (codes 8..15).
+  // Decode of weight word j (16 codes, code c in bits 2c..2c+1) in units of
+  // at most two VALU instructions, so that it can be spread between MFMAs.
+  // The lo units build four byte-lane vectors, tq[j][r] = (pw << (6 - 2r)) &
+  // 0xC0C0C0C0: byte b of tq[j][r] holds code 4b + r in bits 6..7 and zeros
+  // below, which is the high byte of the bf16 value 0 / +2 / -2 of that code.
+  // A byte permute then places two such bytes over zero low bytes, giving the
+  // two bf16 values of one operand register: register q of k-block h takes
+  // codes 8h + 2q and 8h + 2q + 1.  Lo units 0..3 build tq[j], 4..5 the
+  // k-block 0 operand wa[j] (codes 0..7); the hi units build wb[j] (codes
+  // 8..15) out of the same tq[j] in the next half step.
+  constexpr int kLoUnits = 6;
+  constexpr int kHiUnits = 2;
   auto lo_unit = [&](int j, int u) {
-    if (u == 0) {
-      w2[j] = pw[j] >> 2;
-      h0[j] = __builtin_amdgcn_perm(w2[j], pw[j], 0x05040100u);
+    constexpr uint32_t kTop2 = 0xC0C0C0C0u;
+    if (u < 4) {
+      tq[j][u] = (pw[j] << (6 - 2 * u)) & kTop2;
     } else {
-      wa[j][u - 1] = (h0[j] << (18 - 4 * u)) & 0xC000C000u;
+      const uint32_t sel = u == 4 ? 0x040C000Cu : 0x050C010Cu;
+      wa[j][2 * (u - 4)] = __builtin_amdgcn_perm(tq[j][1], tq[j][0], sel);
+      wa[j][2 * (u - 4) + 1] = __builtin_amdgcn_perm(tq[j][3], tq[j][2], sel);
     }
   };
   auto hi_unit = [&](int j, int u) {
-    if (u == 0) {
-      h1[j] = __builtin_amdgcn_perm(w2[j], pw[j], 0x07060302u);
-    } else {
-      wb[j][u - 1] = (h1[j] << (18 - 4 * u)) & 0xC000C000u;
-    }
+    const uint32_t sel = u == 0 ? 0x060C020Cu : 0x070C030Cu;
+    wb[j][2 * u] = __builtin_amdgcn_perm(tq[j][1], tq[j][0], sel);
+    wb[j][2 * u + 1] = __builtin_amdgcn_perm(tq[j][3], tq[j][2], sel);
   };
   auto decode_lo_all = [&]() {  // the first step's wa
 #pragma unroll
     for (int j = 0; j < kTN; ++j)
 #pragma unroll
-      for (int u = 0; u < 5; ++u) lo_unit(j, u);
+      for (int u = 0; u < kLoUnits; ++u) lo_unit(j, u);
   };
-  constexpr int kSlots = kTN * kTM;       // MFMAs per half step
-  constexpr int kUnits = 5 * kTN;         // decode units per half step
-  // Half A: one X read (kTM) and one decode unit per slot.  Half B: the
-  // memory operations first, the decode of the next wa as late as possible but
-  // after them.  Small wave tiles have fewer MFMA slots than operations; the
-  // slots past kSlots carry no MFMA.
-  constexpr int kSlotsA = kSlots > kUnits ? kSlots : kUnits;
+  constexpr int kSlots = kTN * kTM;         // MFMAs per half step
+  constexpr int kUnitsA = kHiUnits * kTN;   // decode units of half A
+  constexpr int kUnitsB = kLoUnits * kTN;   // ... of half B
+  // Half A: one X read (kTM) and kUpsA decode units per slot.  Half B: the
+  // memory operations, and the decode of the next wa as late as possible.
+  // Wave tiles with at least 32 MFMAs per half step start that decode once
+  // the first weight words have had a few MFMAs to arrive and fit every unit
+  // into the MFMA slots (several per slot when there are more units than
+  // slots); smaller ones decode after all of half B's memory operations, one
+  // unit per slot, and the slots past kSlots carry no MFMA.
+  constexpr bool kWide = kSlots >= 32;
+  constexpr int kUpsA = (kWide && kUnitsA > kSlots) ? (kUnitsA + kSlots - 1) / kSlots : 1;
+  constexpr int kUpsB = (kWide && kUnitsB > kSlots) ? (kUnitsB + kSlots - 1) / kSlots : 1;
+  constexpr int kUnitSlotsA = (kUnitsA + kUpsA - 1) / kUpsA;
+  constexpr int kUnitSlotsB = (kUnitsB + kUpsB - 1) / kUpsB;
+  constexpr int kSlotsA = kSlots > kUnitSlotsA ? kSlots : kUnitSlotsA;
   constexpr int kOpsB = kTN + C::kLoads + kTM;
-  constexpr int kDecodeFrom = (kSlots - kUnits) > kOpsB ? kSlots - kUnits : kOpsB;
-  constexpr int kSlotsB = kSlots > kDecodeFrom + kUnits ? kSlots : kDecodeFrom + kUnits;
+  constexpr int kDecodeEarliest = kWide ? (kTN < 6 ? kTN : 6) : kOpsB;
+  constexpr int kDecodeFrom =
+      (kSlots - kUnitSlotsB) > kDecodeEarliest ? kSlots - kUnitSlotsB : kDecodeEarliest;
+  constexpr int kSlotsB =
+      kSlots > kDecodeFrom + kUnitSlotsB ? kSlots : kDecodeFrom + kUnitSlotsB;
+  // An MFMA may read a VGPR only two wait states after a VALU instruction
+  // wrote it.  In the wide schedules every operand is produced at least a
+  // dozen slots before its MFMA (wa in the previous half B, wb in half A,
+  // X chunks by LDS reads), so their MFMAs carry no padding; the small
+  // schedules can put a decode unit right before the MFMA that reads its
+  // result, and pad every MFMA with s_nop 1.  A CPU test checks the compiled
+  // kernels for this hazard.
+  constexpr bool kPad = !kWide;
 
   // One step out of ring stage CUR.  On entry the weight words pw, their
   // k-block 0 operands wa (and w2) and the X chunks xa of this step are in
@@ -341,10 +358,11 @@ void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
 #define TERN_GEMM_HALF_A(CUR, ZERO)                                                     \
   _Pragma("unroll") for (int t = 0; t < kSlotsA; ++t) {                                 \
     if (t < kSlots)                                                                     \
-      mfma16<ZERO::value>(acc[t / kTM][t % kTM],                                        \
-                          __builtin_bit_cast(bf16x8_t, wa[t / kTM]), xa[t % kTM]);      \
+      mfma16<ZERO::value, kPad>(acc[t / kTM][t % kTM],                                  \
+                                __builtin_bit_cast(bf16x8_t, wa[t / kTM]), xa[t % kTM]);  \
     if (t < kTM) TERN_GEMM_READ_XB(CUR, t)                                              \
-    if (t < kUnits) hi_unit(t / 5, t % 5);                                              \
+    _Pragma("unroll") for (int u = t * kUpsA; u < (t + 1) * kUpsA && u < kUnitsA; ++u)  \
+      hi_unit(u / kHiUnits, u % kHiUnits);                                              \
     __builtin_amdgcn_sched_barrier(0);                                                  \
   }
 #define TERN_GEMM_STEP(CUR, NXT, DMA, XR, PR, STAGE, ZERO)                                \
@@ -354,8 +372,8 @@ void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
     lds_barrier();                                                                       \
     _Pragma("unroll") for (int t = 0; t < kSlotsB; ++t) {                                \
       if (t < kSlots)                                                                    \
-        mfma16<false>(acc[t / kTM][t % kTM], __builtin_bit_cast(bf16x8_t, wb[t / kTM]),  \
-                      xb[t % kTM]);                                                      \
+        mfma16<false, kPad>(acc[t / kTM][t % kTM],                                       \
+                            __builtin_bit_cast(bf16x8_t, wb[t / kTM]), xb[t % kTM]);     \
       if (t < kTN) {                                                                     \
         TERN_GEMM_READ_PW(NXT, t)                                                        \
       } else if (t < kTN + C::kLoads) {                                                  \
@@ -363,8 +381,11 @@ void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
       } else if (t < kOpsB) {                                                            \
         TERN_GEMM_READ_XA(NXT, t - kTN - C::kLoads)                                      \
       }                                                                                  \
-      if (t >= kDecodeFrom && t < kDecodeFrom + kUnits)                                  \
-        lo_unit((t - kDecodeFrom) / 5, (t - kDecodeFrom) % 5);                           \
+      if (t >= kDecodeFrom) {                                                            \
+        _Pragma("unroll") for (int u = (t - kDecodeFrom) * kUpsB;                        \
+                               u < (t - kDecodeFrom + 1) * kUpsB && u < kUnitsB; ++u)    \
+          lo_unit(u / kLoUnits, u % kLoUnits);                                           \
+      }                                                                                  \
       __builtin_amdgcn_sched_barrier(0);                                                 \
     }                                                                                    \
   }
@@ -374,25 +395,33 @@ void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
   // bf16(fp32(acc / 2 * s)) exactly.
   //
   // Whole tiles with a 16-byte aligned Y and scale vector go through LDS:
-  // each wave writes 16 of its rows at a time into its own part of ring
-  // stage lds5 (pitch kEpiPitch bytes, conflict-free for the 8-byte writes)
-  // and stores them back as 16-byte pieces of whole row segments, so every
-  // store instruction writes 5 1/3 contiguous 192-byte runs instead of 16
-  // scattered 32-byte ones.  lds5 holds no live stage here: it held the
-  // tile's last stage (all reads of it end at the barrier below) and the
+  // each wave writes 16 of its rows at a time, kEpiJ MFMA tiles (16 kEpiJ
+  // columns) per pass, into its own part of ring stage lds5 (pitch kEpiPitch
+  // bytes, conflict-free for the 8-byte writes) and stores them back as
+  // 16-byte pieces of whole row segments (32 kEpiJ bytes per row), so that a
+  // store instruction writes a few long contiguous runs instead of 16
+  // scattered 32-byte ones.  kEpiJ is the largest divisor of kTN whose four
+  // staging areas fit one ring stage.  lds5 holds no live stage here: it held
+  // the tile's last stage (all reads of it end at the barrier below) and the
   // next request into it follows the next step's barrier.  Other tiles take
   // the direct path, with 8-byte stores where Y allows them.
-  constexpr int kEpiPitch = 2 * C::kWN + 16;
-  constexpr bool kEpiLds = kThreads / 64 * 16 * kEpiPitch <= C::kStage &&  // fits a stage
-                           (16 * 2 * C::kWN / 16) % 64 == 0;               // whole stores
+  constexpr int kEpiJ = [] {
+    int best = 0;
+    for (int d = 1; d <= kTN; ++d)
+      if (kTN % d == 0 && kThreads / 64 * 16 * (32 * d + 16) <= C::kStage) best = d;
+    return best;
+  }();
+  constexpr bool kEpiLds = kEpiJ > 0;
   static_assert(kEpiLds || !PERSIST, "the persistent kernel stores through LDS");
   auto epilogue = [&](int t) {
     acc_ready();
     int m0, n0;
     tile_coords(t, m0, n0);
     if (kEpiLds && (PERSIST || ((y_flags & 2) && m0 + BM <= m && n0 + BN <= n))) {
-      constexpr int kChunksPerRow = 2 * C::kWN / 16;              // 16-byte pieces of a row
-      constexpr int kStores = 16 * kChunksPerRow / 64;            // per lane per 16 rows
+      constexpr int kEpiPitch = 32 * kEpiJ + 16;
+      constexpr int kChunksPerRow = 2 * kEpiJ;                    // 16-byte pieces of a row
+      constexpr int kChunks = 16 * kChunksPerRow;                 // per pass
+      constexpr int kStores = (kChunks + 63) / 64;                // per lane per pass
       const uint32_t area = static_cast<uint32_t>(wave) * (16 * kEpiPitch);
       const int col0 = n0 + wn * C::kWN;
       // The factor 1/2 of the decode goes into the scale: (acc * (s / 2))
@@ -416,25 +445,32 @@ void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
 #pragma unroll
       for (int i = 0; i < kTM; ++i) {
 #pragma unroll
-        for (int j = 0; j < kTN; ++j) {
-          // Keeps this read of the accumulators here, next to its use,
-          // instead of hoisted into one burst that needs 216 VGPRs.
-          asm volatile("" : "+a"(acc[j][i]));
-          __bf16 b[4];
+        for (int jp = 0; jp < kTN; jp += kEpiJ) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) b[e] = static_cast<__bf16>(acc[j][i][e] * sc[j][e]);
-          u32x2_t o;
-          o[0] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b[0])) |
-                 (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b[1])) << 16);
-          o[1] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b[2])) |
-                 (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b[3])) << 16);
-          *reinterpret_cast<u32x2_t*>(&lds5[wr_off + 32 * j]) = o;
-        }
-        uint16_t* const yi = yt + static_cast<int64_t>(16 * i) * ldy;
+          for (int j = jp; j < jp + kEpiJ; ++j) {
+            // Keeps this read of the accumulators here, next to its use,
+            // instead of hoisted into one burst that needs 216 VGPRs.
+            asm volatile("" : "+a"(acc[j][i]));
+            __bf16 b[4];
 #pragma unroll
-        for (int q = 0; q < kStores; ++q) {
-          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&lds5[rd_off[q]]);
-          *reinterpret_cast<u32x4_t*>(yi + st_off[q]) = v;
+            for (int e = 0; e < 4; ++e) b[e] = static_cast<__bf16>(acc[j][i][e] * sc[j][e]);
+            u32x2_t o;
+            o[0] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b[0])) |
+                   (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b[1])) << 16);
+            o[1] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b[2])) |
+                   (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b[3])) << 16);
+            *reinterpret_cast<u32x2_t*>(&lds5[wr_off + 32 * (j - jp)]) = o;
+          }
+          // (LDS accesses of one wave complete in order: the reads below see
+          // the writes above, and the next pass's writes follow these reads.)
+          uint16_t* const yi = yt + static_cast<int64_t>(16 * i) * ldy + 16 * jp;
+#pragma unroll
+          for (int q = 0; q < kStores; ++q) {
+            if (kChunks % 64 == 0 || lane + 64 * q < kChunks) {
+              const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&lds5[rd_off[q]]);
+              *reinterpret_cast<u32x4_t*>(yi + st_off[q]) = v;
+            }
+          }
         }
       }
       return;
@@ -538,7 +574,6 @@ void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
 #undef TERN_GEMM_ISSUE
 #undef TERN_GEMM_DMA
 #undef TERN_GEMM_READ_A
-#undef TERN_GEMM_READ_B
 #undef TERN_GEMM_READ_PW
 #undef TERN_GEMM_READ_XA
 #undef TERN_GEMM_READ_XB

@@ -21,24 +21,26 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t by
                                            static_cast<int>(bytes), static_cast<int>(kRsrcWord3));
 }
 
-// Sixteen 2-bit codes -> two MFMA operands of eight bf16 values (0 / +2 / -2)
-// in ascending k: `lo` gets codes 0..7, `hi` codes 8..15.  After the byte
-// permute, half-word 0 holds the selected codes in place and half-word 1 the
-// same codes moved down one field, so a left shift by 14 - 4q and a mask
-// leave code 2q in bits 14..15 and code 2q+1 in bits 30..31.
+// Sixteen 2-bit codes (code c in bits 2c..2c+1 of w) -> two MFMA operands
+// of eight bf16 values 0 / +2 / -2 in ascending k: `lo` gets codes 0..7, `hi`
+// codes 8..15.  t[r] = (w << (6 - 2r)) & 0xC0C0C0C0 holds code 4b + r in bits
+// 6..7 of byte b with zeros below: the high byte of that code's bf16 value
+// (00 -> 0x00, 01 -> 0x40 = +2, 11 -> 0xC0 = -2).  A byte permute puts two
+// such bytes over zero low bytes: operand register q of block h holds codes
+// 8h + 2q and 8h + 2q + 1.  15 VALU instructions for 16 codes.
 __device__ inline void decode16(uint32_t w, bf16x8_t& lo, bf16x8_t& hi) {
-  const uint32_t w2 = w >> 2;
-  const uint32_t h0 = __builtin_amdgcn_perm(w2, w, 0x05040100u);
-  const uint32_t h1 = __builtin_amdgcn_perm(w2, w, 0x07060302u);
+  uint32_t t[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) t[r] = (w << (6 - 2 * r)) & 0xC0C0C0C0u;
   u32x4_t a, b;
-  a[0] = (h0 << 14) & 0xC000C000u;
-  a[1] = (h0 << 10) & 0xC000C000u;
-  a[2] = (h0 << 6) & 0xC000C000u;
-  a[3] = (h0 << 2) & 0xC000C000u;
-  b[0] = (h1 << 14) & 0xC000C000u;
-  b[1] = (h1 << 10) & 0xC000C000u;
-  b[2] = (h1 << 6) & 0xC000C000u;
-  b[3] = (h1 << 2) & 0xC000C000u;
+  a[0] = __builtin_amdgcn_perm(t[1], t[0], 0x040C000Cu);
+  a[1] = __builtin_amdgcn_perm(t[3], t[2], 0x040C000Cu);
+  a[2] = __builtin_amdgcn_perm(t[1], t[0], 0x050C010Cu);
+  a[3] = __builtin_amdgcn_perm(t[3], t[2], 0x050C010Cu);
+  b[0] = __builtin_amdgcn_perm(t[1], t[0], 0x060C020Cu);
+  b[1] = __builtin_amdgcn_perm(t[3], t[2], 0x060C020Cu);
+  b[2] = __builtin_amdgcn_perm(t[1], t[0], 0x070C030Cu);
+  b[3] = __builtin_amdgcn_perm(t[3], t[2], 0x070C030Cu);
   lo = __builtin_bit_cast(bf16x8_t, a);
   hi = __builtin_bit_cast(bf16x8_t, b);
 }
@@ -48,15 +50,21 @@ __device__ inline void decode16(uint32_t w, bf16x8_t& lo, bf16x8_t& hi) {
 // asm because the compiler's own form of this loop copies accumulators
 // between AGPRs with v_accvgpr_mov, which costs about a quarter of the
 // matrix-core throughput.  The compiler does not see the MFMA inside, so the
-// asm keeps its hazards itself: the leading s_nop 1 gives the two wait states
-// that a VALU write of an A or B operand needs before an MFMA reads it (the
-// decoded weights are VALU results).
-template <bool ZERO>
+// caller keeps its hazards: an MFMA may read a VGPR only two wait states
+// after a VALU instruction wrote it.  PAD puts an s_nop 1 in front of the
+// MFMA for that; a caller whose schedule keeps every VALU-written operand
+// further away passes PAD = false (each s_nop 1 costs issue cycles that the
+// MFMA stream does not hide).
+template <bool ZERO, bool PAD = true>
 __device__ inline void mfma16(f32x4_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
-  if constexpr (ZERO) {
+  if constexpr (ZERO && PAD) {
     asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=a"(acc) : "v"(a), "v"(b));
-  } else {
+  } else if constexpr (ZERO) {
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=a"(acc) : "v"(a), "v"(b));
+  } else if constexpr (PAD) {
     asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  } else {
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
   }
 }
 
