@@ -101,6 +101,14 @@ __device__ inline void tile_of(int bid, int grid, int tiles_m, int tiles_n, int&
   tn = r / gsm;
 }
 
+// Two fp32 values rounded to bf16 (nearest even) in one 32-bit word, the
+// first in the low half (one v_cvt_pk_bf16_f32).
+__device__ inline uint32_t pack_bf16x2(float a, float b) {
+  typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+
 // X chunk swizzle of LDS row r: the 16-byte chunk c of a 128-byte row is
 // stored in slot c ^ xswz(r).  Two rows share one 256-byte line of the 64
 // LDS banks; with ((r >> 1) & 7) the 16 rows that one 16-lane group of an
@@ -441,37 +449,56 @@ void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
       }
       const uint32_t wr_off = area + static_cast<uint32_t>(l16 * kEpiPitch + 8 * g);
       uint16_t* const yt = y + static_cast<int64_t>(m0 + wm * C::kWM) * ldy + col0;
+      // Pass p covers MFMA row block i = p / kJPasses and tiles jp .. jp +
+      // kEpiJ - 1 (jp = kEpiJ (p % kJPasses)).  The passes are software
+      // pipelined: pass p's staging writes and read-backs are issued, then
+      // pass p + 1's accumulators are scaled and converted while those LDS
+      // accesses complete, then pass p's rows are stored.  (LDS accesses of
+      // one wave complete in order: the read-backs see the writes before
+      // them, and the next pass's writes follow them.)
+      constexpr int kJPasses = kTN / kEpiJ;
+      constexpr int kPasses = kTM * kJPasses;
+      u32x2_t o[2][kEpiJ];
+      auto convert = [&](int p, u32x2_t (&out)[kEpiJ]) {
+        const int i = p / kJPasses;
+        const int jp = (p % kJPasses) * kEpiJ;
+        // All of the pass's accumulator reads first, then the products, then
+        // the conversions: independent instructions back to back instead of
+        // dependent chains.  (The empty asm statements keep the reads here
+        // instead of hoisted into one burst that needs 216 VGPRs.)
+        f32x4_t v[kEpiJ];
+#pragma unroll
+        for (int jj = 0; jj < kEpiJ; ++jj) {
+          asm volatile("" : "+a"(acc[jp + jj][i]));
+          v[jj] = acc[jp + jj][i];
+        }
+#pragma unroll
+        for (int jj = 0; jj < kEpiJ; ++jj) v[jj] *= sc[jp + jj];
+#pragma unroll
+        for (int jj = 0; jj < kEpiJ; ++jj) {
+          out[jj][0] = pack_bf16x2(v[jj][0], v[jj][1]);
+          out[jj][1] = pack_bf16x2(v[jj][2], v[jj][3]);
+        }
+      };
+      convert(0, o[0]);
       lds_barrier();
 #pragma unroll
-      for (int i = 0; i < kTM; ++i) {
+      for (int p = 0; p < kPasses; ++p) {
 #pragma unroll
-        for (int jp = 0; jp < kTN; jp += kEpiJ) {
+        for (int jj = 0; jj < kEpiJ; ++jj)
+          *reinterpret_cast<u32x2_t*>(&lds5[wr_off + 32 * jj]) = o[p % 2][jj];
+        u32x4_t v[kStores];
 #pragma unroll
-          for (int j = jp; j < jp + kEpiJ; ++j) {
-            // Keeps this read of the accumulators here, next to its use,
-            // instead of hoisted into one burst that needs 216 VGPRs.
-            asm volatile("" : "+a"(acc[j][i]));
-            __bf16 b[4];
+        for (int q = 0; q < kStores; ++q)
+          if (kChunks % 64 == 0 || lane + 64 * q < kChunks)
+            v[q] = *reinterpret_cast<const u32x4_t*>(&lds5[rd_off[q]]);
+        if (p + 1 < kPasses) convert(p + 1, o[(p + 1) % 2]);
+        uint16_t* const yi =
+            yt + static_cast<int64_t>(16 * (p / kJPasses)) * ldy + 16 * kEpiJ * (p % kJPasses);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) b[e] = static_cast<__bf16>(acc[j][i][e] * sc[j][e]);
-            u32x2_t o;
-            o[0] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b[0])) |
-                   (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b[1])) << 16);
-            o[1] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b[2])) |
-                   (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b[3])) << 16);
-            *reinterpret_cast<u32x2_t*>(&lds5[wr_off + 32 * (j - jp)]) = o;
-          }
-          // (LDS accesses of one wave complete in order: the reads below see
-          // the writes above, and the next pass's writes follow these reads.)
-          uint16_t* const yi = yt + static_cast<int64_t>(16 * i) * ldy + 16 * jp;
-#pragma unroll
-          for (int q = 0; q < kStores; ++q) {
-            if (kChunks % 64 == 0 || lane + 64 * q < kChunks) {
-              const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&lds5[rd_off[q]]);
-              *reinterpret_cast<u32x4_t*>(yi + st_off[q]) = v;
-            }
-          }
-        }
+        for (int q = 0; q < kStores; ++q)
+          if (kChunks % 64 == 0 || lane + 64 * q < kChunks)
+            *reinterpret_cast<u32x4_t*>(yi + st_off[q]) = v[q];
       }
       return;
     }
