@@ -673,12 +673,16 @@ hipError_t launch_gemm(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, con
   // A few tokens: the weight stream dominates; see gemm_small.hip.
   if (m <= kSmallMaxM) return launch_gemm_small(x, m, k, ldx, p, n, ldp, s, y, ldy, stream);
   // Layers with at least one 144 x 384 tile per CU use the big tile (one
-  // workgroup per CU, 147 KiB of LDS).  Smaller layers use 64-row tiles, two
-  // workgroups per CU, with 256 or 128 output channels per tile, whichever
-  // still gives two tiles per CU, so that every CU has work.
+  // workgroup per CU, 147 KiB of LDS).  Smaller layers that 64 x 576 tiles
+  // cut into exactly one tile per CU use those (wave tile 64 x 144, still on
+  // the wide schedule; e.g. M = 2048, N = 4608).  Others use 64-row tiles,
+  // two workgroups per CU, with 256 or 128 output channels per tile,
+  // whichever still gives two tiles per CU, so that every CU has work.
   const auto tiles = [&](int64_t bm, int64_t bn) { return ((m + bm - 1) / bm) * ((n + bn - 1) / bn); };
   if (tiles(144, 384) >= kPersistentGrid)
     return launch_tiles<144, 384, 1, 4, 1>(x, m, k, ldx, p, n, ldp, s, y, ldy, stream);
+  if (m % 64 == 0 && n % 576 == 0 && tiles(64, 576) == kPersistentGrid)
+    return launch_tiles<64, 576, 1, 4, 1>(x, m, k, ldx, p, n, ldp, s, y, ldy, stream);
   if (tiles(64, 256) >= 2 * kPersistentGrid)
     return launch_tiles<64, 256, 1, 4, 2>(x, m, k, ldx, p, n, ldp, s, y, ldy, stream);
   return launch_tiles<64, 128, 1, 4, 2>(x, m, k, ldx, p, n, ldp, s, y, ldy, stream);

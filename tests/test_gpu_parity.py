@@ -114,6 +114,8 @@ GEMM_SHAPES = [
     (1100, 128, 7500),
     # few-token path with four 16-channel blocks per workgroup (n >= 256 * 64)
     (5, 320, 16400), (20, 256, 16448),
+    # 64 x 576 tiles, one per CU; k of 3 pipeline stages (fewer than the ring)
+    (1024, 192, 9216),
 ]
 
 
