@@ -102,6 +102,18 @@ __global__ __launch_bounds__(kSmallThreads) void gemm_ternary_small(
     fence();
   };
 
+  // The channel scales of this lane's outputs, requested before the weight
+  // stream so that they have arrived by the epilogue (a late request would
+  // put a whole memory latency after the last MFMA).
+  float sc[B][4];
+#pragma unroll
+  for (int bl = 0; bl < B; ++bl)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int nc = n0 + 16 * bl + 4 * g + e;
+      sc[bl][e] = nc < n ? s[nc] * 0.5f : 0.0f;
+    }
+
   f32x4_t acc[B][R];
 #pragma unroll
   for (int bl = 0; bl < B; ++bl)
@@ -156,9 +168,6 @@ __global__ __launch_bounds__(kSmallThreads) void gemm_ternary_small(
 #pragma unroll
   for (int bl = 0; bl < B; ++bl) {
   const int nb = n0 + 16 * bl + 4 * g;  // output channels nb .. nb + 3 of this lane
-  float sc[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) sc[e] = (nb + e < n) ? s[nb + e] * 0.5f : 0.0f;
 #pragma unroll
   for (int b = 0; b < R; ++b) {
     f32x4_t v = acc[bl][b];
@@ -168,7 +177,7 @@ __global__ __launch_bounds__(kSmallThreads) void gemm_ternary_small(
     if (token >= m) continue;
     __bf16 o[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) o[e] = static_cast<__bf16>(v[e] * sc[e]);
+    for (int e = 0; e < 4; ++e) o[e] = static_cast<__bf16>(v[e] * sc[bl][e]);
     uint16_t* yr = y + static_cast<int64_t>(token) * ldy + nb;
     if (y_vec_ok && nb + 4 <= n) {
       u32x2_t q;
@@ -204,15 +213,34 @@ hipError_t launch_small(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, co
 hipError_t launch_gemm_small(const uint16_t* x, int64_t m, int64_t k, int64_t ldx,
                              const uint8_t* p, int64_t n, int64_t ldp, const float* s,
                              uint16_t* y, int64_t ldy, hipStream_t stream) {
-  // Four channel blocks per workgroup when that still leaves a workgroup
-  // per CU: each X operand then feeds four MFMAs instead of one.
-  const bool wide = (n + 63) / 64 >= 256;
-  if (m <= 16) {
-    if (wide) return launch_small<1, 4, 3>(x, m, k, ldx, p, n, ldp, s, y, ldy, stream);
-    return launch_small<1, 1, 4>(x, m, k, ldx, p, n, ldp, s, y, ldy, stream);
+  // Channel blocks per workgroup.  The weight stream is latency-bound: every
+  // CU keeps a fixed number of bytes in flight per workgroup, and a CU that
+  // holds two workgroups finishes them well after the CUs that hold one.  So
+  // B is chosen to minimize the blocks of the busiest CU, B * ceil(ceil(nb /
+  // B) / 256) for nb blocks of 16 channels, the larger B on ties (each X
+  // operand then feeds B MFMAs).  E.g. N = 21504: B = 6, 224 workgroups,
+  // instead of 336 with B = 4.
+  const int64_t nb = (n + 15) / 16;
+  int best = 1;
+  int64_t best_cost = -1;
+  for (int b : {6, 3, 2, 1}) {
+    const int64_t wgs = (nb + b - 1) / b;
+    const int64_t cost = b * ((wgs + 255) / 256);
+    if (best_cost < 0 || cost < best_cost) {
+      best = b;
+      best_cost = cost;
+    }
   }
-  if (wide) return launch_small<2, 4, 2>(x, m, k, ldx, p, n, ldp, s, y, ldy, stream);
-  return launch_small<2, 1, 2>(x, m, k, ldx, p, n, ldp, s, y, ldy, stream);
+#define TERN_SMALL(R, DEPTH6, DEPTH3, DEPTH2, DEPTH1)                                            \
+  switch (best) {                                                                                \
+    case 6: return launch_small<R, 6, DEPTH6>(x, m, k, ldx, p, n, ldp, s, y, ldy, stream);       \
+    case 3: return launch_small<R, 3, DEPTH3>(x, m, k, ldx, p, n, ldp, s, y, ldy, stream);       \
+    case 2: return launch_small<R, 2, DEPTH2>(x, m, k, ldx, p, n, ldp, s, y, ldy, stream);       \
+    default: return launch_small<R, 1, DEPTH1>(x, m, k, ldx, p, n, ldp, s, y, ldy, stream);      \
+  }
+  if (m <= 16) TERN_SMALL(1, 3, 3, 4, 4)
+  TERN_SMALL(2, 2, 2, 2, 2)
+#undef TERN_SMALL
 }
 
 }  // namespace tern

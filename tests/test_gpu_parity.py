@@ -112,7 +112,9 @@ GEMM_SHAPES = [
     (32, 256, 16), (33, 576, 40), (8, 64, 4608),
     # 64 x 256 tiles (fewer than 256 big tiles, at least 512 of these): ragged m and n
     (1100, 128, 7500),
-    # few-token path with four 16-channel blocks per workgroup (n >= 256 * 64)
+    # few-token path, every channel-block count per workgroup (6, 3, 2) with
+    # one and two MFMA row blocks, each with a ragged last block
+    (3, 1088, 24536), (24, 320, 21496), (4, 704, 12280), (20, 576, 9208), (30, 448, 4600),
     (5, 320, 16400), (20, 256, 16448),
     # 64 x 576 tiles, one per CU; k of 3 pipeline stages (fewer than the ring)
     (1024, 192, 9216),
