@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--gemm-only-reps", type=int, default=0,
                     help="after the steps, launch tern_gemm alone this many times (profiling)")
     ap.add_argument("--no-rows", action="store_true", help="skip the per-layer-shape table")
+    ap.add_argument("--separate-quantize", action="store_true",
+                    help="run quantize and pack as two calls in the step instead of the fused pass")
     ap.add_argument("--row-reps", type=int, default=30, help="timed launches per row")
     ap.add_argument("--pool-mib", type=int, default=1024,
                     help="packed-weight pool cycled by the few-token rows")
@@ -272,31 +274,45 @@ def main():
         ))
     torch.cuda.synchronize()
 
-    names = ("tern_quantize", "tern_pack", "tern_unpack", "tern_gemm")
+    # A step runs every row of the path on every layer: quantize and pack
+    # (one fused pass, writing the codes, the scales and the packed bytes),
+    # unpack, and the layer.  --separate-quantize runs quantize and pack as two
+    # calls instead.
+    if args.separate_quantize:
+        names = ("tern_quantize", "tern_pack", "tern_unpack", "tern_gemm")
+    else:
+        names = ("tern_quantize_pack", "tern_unpack", "tern_gemm")
 
     def step(events=None):
         for li, (layer, b) in enumerate(zip(layers, bufs)):
             ev = events[li] if events is not None else None
             if ev:
                 ev[0].record()
-            tern.tern_quantize(b["w"], b["t"], b["s"])
+            j = 1
+            if args.separate_quantize:
+                tern.tern_quantize(b["w"], b["t"], b["s"])
+                if ev:
+                    ev[j].record()
+                j += 1
+                tern.tern_pack(b["t"], b["p"], layer.k)
+            else:
+                tern.tern_quantize_pack(b["w"], b["t"], b["p"], b["s"])
             if ev:
-                ev[1].record()
-            tern.tern_pack(b["t"], b["p"], layer.k)
-            if ev:
-                ev[2].record()
+                ev[j].record()
+            j += 1
             tern.tern_unpack(b["p"], b["tu"], layer.k)
             if ev:
-                ev[3].record()
+                ev[j].record()
+            j += 1
             tern.tern_gemm(b["x"], b["p"], b["s"], b["y"], layer.k)
             if ev:
-                ev[4].record()
+                ev[j].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    per_step_events = [[[torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    per_step_events = [[[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
                         for _ in layers] for _ in range(args.steps)]
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
@@ -346,13 +362,40 @@ def main():
     roof["alg_bytes_per_launch"] = gemm_bytes
     roof["gbs"] = gemm_bytes / (gemm_ms * 1e-3) / 1e9
 
+    # The separate quantize and pack entry points, timed after the step loop
+    # on the same buffers (not part of the step when the fused pass is used):
+    # ten back-to-back launches of each between two events, queued behind one
+    # layer so that the host's launch latency stays off the GPU's clock.
+    if not args.separate_quantize:
+        reps = 10
+        b0, l0 = bufs[0], layers[0]
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        tern.tern_gemm(b0["x"], b0["p"], b0["s"], b0["y"], l0.k)
+        e[0].record()
+        for _ in range(reps):
+            tern.tern_quantize(b0["w"], b0["t"], b0["s"])
+        e[1].record()
+        for _ in range(reps):
+            tern.tern_pack(b0["t"], b0["p"], l0.k)
+        e[2].record()
+        torch.cuda.synchronize()
+        kern_ms["tern_quantize"] = e[0].elapsed_time(e[1]) / reps
+        kern_ms["tern_pack"] = e[1].elapsed_time(e[2]) / reps
+
     kernels = {}
-    for nm in names:
+    for nm in kern_ms:
         d = {"avg_ms": kern_ms[nm]}
-        if nm == "tern_quantize":
-            byts = sum(l.n * l.k * 4 + l.n * l.k + 4 * l.n for l in layers) / len(layers)
+        if nm in ("tern_quantize", "tern_pack"):
+            d["in_step"] = bool(args.separate_quantize)
+        if nm == "tern_quantize_pack":
+            byts = sum(l.n * l.k * 4 + l.n * l.k + l.n * ((l.k + 3) // 4) + 4 * l.n
+                       for l in layers) / len(layers)
+        elif nm == "tern_quantize":
+            ls = layers if args.separate_quantize else layers[:1]
+            byts = sum(l.n * l.k * 4 + l.n * l.k + 4 * l.n for l in ls) / len(ls)
         elif nm == "tern_pack":
-            byts = sum(l.n * l.k + l.n * ((l.k + 3) // 4) for l in layers) / len(layers)
+            ls = layers if args.separate_quantize else layers[:1]
+            byts = sum(l.n * l.k + l.n * ((l.k + 3) // 4) for l in ls) / len(ls)
         elif nm == "tern_unpack":
             byts = sum(l.n * ((l.k + 3) // 4) + l.n * l.k for l in layers) / len(layers)
         else:
@@ -388,7 +431,7 @@ def main():
 
     shape = layers[0]
     config = {"workload": args.workload, "layers": len(layers), "m": shape.m, "k": shape.k,
-              "n": shape.n, "step": "tern_quantize+tern_pack+tern_unpack+tern_gemm",
+              "n": shape.n, "step": "+".join(names),
               "x": f"bf16 {shape.x_dist}", "w": "fp32 N(0, 0.02^2)", "seed": shape.seed}
     out = {
         "metric": METRIC,

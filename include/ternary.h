@@ -99,6 +99,27 @@ tern_status tern_pack(const int8_t* t, int64_t n, int64_t k, int64_t ldt, uint8_
                       void* stream);
 
 /*
+ * tern_quantize_pack: tern_quantize and tern_pack of its result in one pass
+ * over the weights, for the conversion of a full-precision layer into the
+ * stored 2-bit form ("1.58-bit FLUX", section 1: ternary weights as in
+ * BitNet b1.58, stored as 2-bit signed integers).  The outputs are
+ * bit-identical to tern_quantize followed by tern_pack; the codes are not
+ * read back from memory, so the int8 matrix may be skipped.
+ *
+ *   w, w_dtype, n, k, ldw, s: as tern_quantize
+ *   t  [n, ldt] int8 output as tern_quantize, or NULL to skip it (ldt is then
+ *      ignored)
+ *   p  [n, ldp] uint8 output as tern_pack: bytes 0 .. ceil(k/4)-1 of each row
+ *      written, fields past column k-1 zero, bytes from ceil(k/4) on untouched
+ * Sizes as tern_quantize (TERN_ERR_SHAPE).  ldw >= k, ldt >= k when t is not
+ * NULL, ldp >= ceil(k/4) (else TERN_ERR_STRIDE).  w, p and s must not be NULL
+ * (TERN_ERR_NULL).  Alignment as tern_quantize (TERN_ERR_ALIGN).
+ */
+tern_status tern_quantize_pack(const void* w, tern_dtype w_dtype, int64_t n, int64_t k,
+                               int64_t ldw, int8_t* t, int64_t ldt, uint8_t* p, int64_t ldp,
+                               float* s, void* stream);
+
+/*
  * tern_unpack: the inverse of tern_pack.  Each 2-bit field is sign-extended:
  * 00 -> 0, 01 -> +1, 11 -> -1, and the unused code 10 -> -2 (so that a
  * corrupted code stays visible).

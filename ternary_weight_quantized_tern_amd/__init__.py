@@ -26,6 +26,7 @@ from ._binding import (  # noqa: F401
     tern_gemm,
     tern_pack,
     tern_quantize,
+    tern_quantize_pack,
     tern_status_string,
     tern_unpack,
     unpack,

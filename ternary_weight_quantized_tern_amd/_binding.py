@@ -29,7 +29,8 @@ TERN_F32 = 0
 TERN_BF16 = 1
 TERN_QUANTIZE_MAX_K = 32768
 
-EXPORTED = ("tern_quantize", "tern_pack", "tern_unpack", "tern_gemm", "tern_status_string")
+EXPORTED = ("tern_quantize", "tern_quantize_pack", "tern_pack", "tern_unpack", "tern_gemm",
+            "tern_status_string")
 
 
 class TernError(RuntimeError):
@@ -48,10 +49,11 @@ def _load(path: str):
     lib = ctypes.CDLL(path)
     i64, vp = ctypes.c_int64, ctypes.c_void_p
     lib.tern_quantize.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, i64, vp, vp]
+    lib.tern_quantize_pack.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, i64, vp, i64, vp, vp]
     lib.tern_pack.argtypes = [vp, i64, i64, i64, vp, i64, vp]
     lib.tern_unpack.argtypes = [vp, i64, i64, i64, vp, i64, vp]
     lib.tern_gemm.argtypes = [vp, i64, i64, i64, vp, i64, i64, vp, vp, i64, vp]
-    for name in ("tern_quantize", "tern_pack", "tern_unpack", "tern_gemm"):
+    for name in ("tern_quantize", "tern_quantize_pack", "tern_pack", "tern_unpack", "tern_gemm"):
         getattr(lib, name).restype = ctypes.c_int
     lib.tern_status_string.argtypes = [ctypes.c_int]
     lib.tern_status_string.restype = ctypes.c_char_p
@@ -117,6 +119,28 @@ def tern_quantize(w: torch.Tensor, t: torch.Tensor, s: torch.Tensor, stream=None
     dt = TERN_F32 if w.dtype == torch.float32 else TERN_BF16
     _check("tern_quantize", _lib.tern_quantize(w.data_ptr(), dt, n, k, ldw, t.data_ptr(), ldt,
                                                s.data_ptr(), _stream(stream)))
+
+
+def tern_quantize_pack(w: torch.Tensor, t, p: torch.Tensor, s: torch.Tensor, stream=None) -> None:
+    """``tern_quantize`` and ``tern_pack`` of its result in one pass: ``w`` [n, k]
+    (fp32 or bf16) -> ``p`` uint8 [n, >=ceil(k/4)], ``s`` fp32 [n], and ``t`` int8
+    [n, >=k] unless ``t`` is None."""
+    ldw = _mat(w, "w", (torch.float32, torch.bfloat16))
+    ldp = _mat(p, "p", (torch.uint8,))
+    _vec(s, "s", torch.float32)
+    n, k = w.shape
+    if p.shape[0] != n or p.shape[1] < (k + 3) // 4 or s.shape[0] != n:
+        raise ValueError("p must be [n, >=ceil(k/4)] and s [n] for w [n, k]")
+    t_ptr, ldt = None, 0
+    if t is not None:
+        ldt = _mat(t, "t", (torch.int8,))
+        if t.shape[0] != n or t.shape[1] < k:
+            raise ValueError("t must be [n, >=k]")
+        t_ptr = t.data_ptr()
+    dt = TERN_F32 if w.dtype == torch.float32 else TERN_BF16
+    _check("tern_quantize_pack", _lib.tern_quantize_pack(w.data_ptr(), dt, n, k, ldw, t_ptr, ldt,
+                                                         p.data_ptr(), ldp, s.data_ptr(),
+                                                         _stream(stream)))
 
 
 def tern_pack(t: torch.Tensor, p: torch.Tensor, k: int | None = None, stream=None) -> None:

@@ -32,7 +32,22 @@ tern_status tern_quantize(const void* w, tern_dtype w_dtype, int64_t n, int64_t 
   if (ldw < k || ldt < k) return TERN_ERR_STRIDE;
   const uintptr_t esz = (w_dtype == TERN_F32) ? 4 : 2;
   if (!aligned(w, esz) || !aligned(s, 4)) return TERN_ERR_ALIGN;
-  return from_hip(tern::launch_quantize(w, w_dtype == TERN_BF16, n, k, ldw, t, ldt, s,
+  return from_hip(tern::launch_quantize(w, w_dtype == TERN_BF16, n, k, ldw, t, ldt, s, nullptr, 0,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+tern_status tern_quantize_pack(const void* w, tern_dtype w_dtype, int64_t n, int64_t k,
+                               int64_t ldw, int8_t* t, int64_t ldt, uint8_t* p, int64_t ldp,
+                               float* s, void* stream) {
+  if (w_dtype != TERN_F32 && w_dtype != TERN_BF16) return TERN_ERR_DTYPE;
+  if (n < 0 || n > kMaxInt || k < 0 || k > TERN_QUANTIZE_MAX_K) return TERN_ERR_SHAPE;
+  if (n == 0) return TERN_OK;
+  if (k == 0) return TERN_ERR_SHAPE;
+  if (w == nullptr || p == nullptr || s == nullptr) return TERN_ERR_NULL;
+  if (ldw < k || (t != nullptr && ldt < k) || ldp < (k + 3) / 4) return TERN_ERR_STRIDE;
+  const uintptr_t esz = (w_dtype == TERN_F32) ? 4 : 2;
+  if (!aligned(w, esz) || !aligned(s, 4)) return TERN_ERR_ALIGN;
+  return from_hip(tern::launch_quantize(w, w_dtype == TERN_BF16, n, k, ldw, t, ldt, s, p, ldp,
                                         static_cast<hipStream_t>(stream)));
 }
 

@@ -11,8 +11,11 @@ namespace tern {
 // Launch geometry and the ld / alignment facts the launchers rely on are
 // established by the caller (api.hip); each launcher returns the HIP status of
 // its launch.
+// p == nullptr: codes to t only.  Otherwise the codes also go to p packed
+// (as launch_pack writes them), and t may be nullptr.
 hipError_t launch_quantize(const void* w, bool w_is_bf16, int64_t n, int64_t k, int64_t ldw,
-                           int8_t* t, int64_t ldt, float* s, hipStream_t stream);
+                           int8_t* t, int64_t ldt, float* s, uint8_t* p, int64_t ldp,
+                           hipStream_t stream);
 
 hipError_t launch_pack(const int8_t* t, int64_t n, int64_t k, int64_t ldt, uint8_t* p,
                        int64_t ldp, hipStream_t stream);

@@ -81,15 +81,22 @@ __device__ inline float scale_of(unsigned long long q, int E, int64_t k) {
   return static_cast<float>(ldexp(static_cast<double>(q), E - 48) / static_cast<double>(k));
 }
 
-template <typename TIn, int VEC, int CAP>
+// With PACK, the codes also go out packed four to a byte (weight k in bits
+// 2(k%4) .. 2(k%4)+1 of byte k/4 of row n of p, fields past k zero), exactly
+// as the pack kernel writes them, and t may be null (codes not written).
+template <typename TIn, int VEC, int CAP, bool PACK>
 __global__ __launch_bounds__(kThreads) void quantize_rows(const TIn* __restrict__ w, int64_t k,
                                                           int64_t ldw, int8_t* __restrict__ t,
-                                                          int64_t ldt, float* __restrict__ s) {
+                                                          int64_t ldt, float* __restrict__ s,
+                                                          uint8_t* __restrict__ p, int64_t ldp) {
   constexpr int kChunks = CAP / VEC;
   const int tid = threadIdx.x;
   const int64_t row = blockIdx.x;
   const TIn* wr = w + row * ldw;
-  int8_t* tr = t + row * ldt;
+  const bool write_t = !PACK || t != nullptr;
+  int8_t* tr = write_t ? t + row * ldt : nullptr;
+  uint8_t* pr = PACK ? p + row * ldp : nullptr;
+  const int64_t nbytes = (k + 3) / 4;
 
   uint32_t a[CAP];  // fp32 bit patterns, sign included
 #pragma unroll
@@ -165,6 +172,25 @@ __global__ __launch_bounds__(kThreads) void quantize_rows(const TIn* __restrict_
     int8_t code[VEC];
 #pragma unroll
     for (int v = 0; v < VEC; ++v) code[v] = ternary_code(a[c * VEC + v], scale);
+    if constexpr (PACK) {
+      if constexpr (VEC == 1) {
+        // Four consecutive weights belong to four neighbouring lanes (e0 % 4
+        // is tid % 4): OR their fields together, the first lane writes.
+        uint32_t b = (static_cast<uint32_t>(code[0]) & 3u) << (2 * (e0 & 3));
+        b |= __shfl_xor(b, 1, 64);
+        b |= __shfl_xor(b, 2, 64);
+        if ((e0 & 3) == 0 && e0 / 4 < nbytes) pr[e0 / 4] = static_cast<uint8_t>(b);
+      } else {
+#pragma unroll
+        for (int q = 0; q < VEC / 4; ++q) {
+          uint32_t b = 0;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) b |= (static_cast<uint32_t>(code[4 * q + v]) & 3u) << (2 * v);
+          if (e0 / 4 + q < nbytes) pr[e0 / 4 + q] = static_cast<uint8_t>(b);
+        }
+      }
+      if (!write_t) continue;
+    }
     if constexpr (VEC == 4) {
       if (e0 + 4 <= k) {
         uint32_t packed = (uint32_t(uint8_t(code[0]))) | (uint32_t(uint8_t(code[1])) << 8) |
@@ -190,15 +216,15 @@ __global__ __launch_bounds__(kThreads) void quantize_rows(const TIn* __restrict_
 }
 
 
-template <typename TIn, int VEC>
+template <typename TIn, int VEC, bool PACK>
 hipError_t launch_cap(const TIn* w, int64_t n, int64_t k, int64_t ldw, int8_t* t, int64_t ldt,
-                      float* s, hipStream_t stream) {
+                      float* s, uint8_t* p, int64_t ldp, hipStream_t stream) {
   const int64_t per_thread = (k + kThreads - 1) / kThreads;
   dim3 grid(static_cast<unsigned>(n)), block(kThreads);
 #define TERN_Q_LAUNCH(CAP)                                                                   \
   if (per_thread <= CAP) {                                                                   \
-    hipLaunchKernelGGL((quantize_rows<TIn, VEC, (CAP < VEC ? VEC : CAP)>), grid, block, 0, \
-                       stream, w, k, ldw, t, ldt, s);                                        \
+    hipLaunchKernelGGL((quantize_rows<TIn, VEC, (CAP < VEC ? VEC : CAP), PACK>), grid, block, \
+                       0, stream, w, k, ldw, t, ldt, s, p, ldp);                             \
     return hipGetLastError();                                                                \
   }
   TERN_Q_LAUNCH(8)
@@ -212,20 +238,32 @@ hipError_t launch_cap(const TIn* w, int64_t n, int64_t k, int64_t ldw, int8_t* t
 
 inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+template <bool PACK>
+hipError_t launch_variant(const void* w, bool w_is_bf16, int64_t n, int64_t k, int64_t ldw,
+                          int8_t* t, int64_t ldt, float* s, uint8_t* p, int64_t ldp,
+                          hipStream_t stream) {
+  // Vector loads (and vector stores of the codes) where the rows allow them.
+  const bool t_vec4 = t == nullptr || (aligned(t, 4) && ldt % 4 == 0);
+  const bool t_vec8 = t == nullptr || (aligned(t, 8) && ldt % 8 == 0);
+  if (!w_is_bf16) {
+    const float* wf = static_cast<const float*>(w);
+    if (aligned(w, 16) && ldw % 4 == 0 && t_vec4)
+      return launch_cap<float, 4, PACK>(wf, n, k, ldw, t, ldt, s, p, ldp, stream);
+    return launch_cap<float, 1, PACK>(wf, n, k, ldw, t, ldt, s, p, ldp, stream);
+  }
+  const uint16_t* wb = static_cast<const uint16_t*>(w);
+  if (aligned(w, 16) && ldw % 8 == 0 && t_vec8)
+    return launch_cap<uint16_t, 8, PACK>(wb, n, k, ldw, t, ldt, s, p, ldp, stream);
+  return launch_cap<uint16_t, 1, PACK>(wb, n, k, ldw, t, ldt, s, p, ldp, stream);
+}
+
 }  // namespace
 
 hipError_t launch_quantize(const void* w, bool w_is_bf16, int64_t n, int64_t k, int64_t ldw,
-                           int8_t* t, int64_t ldt, float* s, hipStream_t stream) {
-  if (!w_is_bf16) {
-    const float* wf = static_cast<const float*>(w);
-    if (aligned(w, 16) && ldw % 4 == 0 && aligned(t, 4) && ldt % 4 == 0)
-      return launch_cap<float, 4>(wf, n, k, ldw, t, ldt, s, stream);
-    return launch_cap<float, 1>(wf, n, k, ldw, t, ldt, s, stream);
-  }
-  const uint16_t* wb = static_cast<const uint16_t*>(w);
-  if (aligned(w, 16) && ldw % 8 == 0 && aligned(t, 8) && ldt % 8 == 0)
-    return launch_cap<uint16_t, 8>(wb, n, k, ldw, t, ldt, s, stream);
-  return launch_cap<uint16_t, 1>(wb, n, k, ldw, t, ldt, s, stream);
+                           int8_t* t, int64_t ldt, float* s, uint8_t* p, int64_t ldp,
+                           hipStream_t stream) {
+  if (p != nullptr) return launch_variant<true>(w, w_is_bf16, n, k, ldw, t, ldt, s, p, ldp, stream);
+  return launch_variant<false>(w, w_is_bf16, n, k, ldw, t, ldt, s, nullptr, 0, stream);
 }
 
 }  // namespace tern

@@ -33,6 +33,18 @@ def gpu_quantize_pack(w_cpu: torch.Tensor):
     return t, s, p
 
 
+def gpu_quantize_pack_fused(w_cpu: torch.Tensor, with_t: bool = True):
+    """GPU path through tern_quantize_pack: W -> (T or None, s, P) on the host."""
+    w = w_cpu.to(DEV)
+    n, k = w.shape
+    t = torch.empty((n, k), dtype=torch.int8, device=DEV) if with_t else None
+    s = torch.empty((n,), dtype=torch.float32, device=DEV)
+    p = torch.empty((n, tern.packed_row_bytes(k)), dtype=torch.uint8, device=DEV)
+    tern.tern_quantize_pack(w, t, p, s)
+    torch.cuda.synchronize()
+    return t, s, p
+
+
 def oracle_weights(w_cpu: torch.Tensor):
     if w_cpu.dtype == torch.bfloat16:
         t, s = oracle.oracle_quantize(tern_inputs.bf16_bits(w_cpu))
@@ -110,6 +122,11 @@ def check_layer(x_cpu: torch.Tensor, w_cpu: torch.Tensor, what: str, rows=None, 
     t_ref, s_ref, p_ref = oracle_weights(w_cpu)
     t_g, s_g, p_g = gpu_quantize_pack(w_cpu)
     assert_bitexact_weights(t_g, s_g, p_g, t_ref, s_ref, p_ref, what)
+    # the fused conversion writes the same scales and packed bytes
+    _, s_f, p_f = gpu_quantize_pack_fused(w_cpu, with_t=False)
+    assert torch.equal(s_f.cpu().view(torch.int32), s_g.cpu().view(torch.int32)), f"{what}: fused s"
+    assert torch.equal(p_f.cpu()[:, : p_ref.shape[1]], torch.from_numpy(p_ref)), f"{what}: fused p"
+    del s_f, p_f
     # the packed codes round-trip on the GPU
     back = tern.unpack(p_g, k)
     torch.cuda.synchronize()

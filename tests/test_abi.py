@@ -89,6 +89,30 @@ def test_quantize_validation():
     assert q(A, 0, 4, 64, 64, A, 64, A + 1, NULL) == tern.TERN_ERR_ALIGN
 
 
+def test_quantize_pack_validation():
+    q = lib.tern_quantize_pack
+
+    def call(w=A, dt=0, n=4, k=64, ldw=64, t=A, ldt=64, p=A, ldp=16, s=A):
+        return q(w, dt, n, k, ldw, t, ldt, p, ldp, s, NULL)
+
+    assert call(dt=7) == tern.TERN_ERR_DTYPE
+    assert call(n=-1) == tern.TERN_ERR_SHAPE
+    assert call(k=32769, ldw=32769, ldt=32769, ldp=8193) == tern.TERN_ERR_SHAPE
+    assert call(k=0) == tern.TERN_ERR_SHAPE
+    assert call(n=0, w=NULL, t=NULL, p=NULL, s=NULL) == tern.TERN_OK   # n == 0: no-op
+    for name in ("w", "p", "s"):
+        assert call(**{name: NULL}) == tern.TERN_ERR_NULL
+    assert call(ldw=63) == tern.TERN_ERR_STRIDE
+    assert call(ldt=63) == tern.TERN_ERR_STRIDE
+    # t NULL: ldt is ignored (strides are checked before alignment, so a
+    # rejected alignment shows that ldt = 0 passed)
+    assert call(t=NULL, ldt=0, s=A + 1) == tern.TERN_ERR_ALIGN
+    assert call(ldp=15) == tern.TERN_ERR_STRIDE                  # < ceil(k/4)
+    assert call(k=65, ldw=65, ldt=65, ldp=16) == tern.TERN_ERR_STRIDE
+    assert call(w=A + 2) == tern.TERN_ERR_ALIGN                  # fp32 needs 4 bytes
+    assert call(s=A + 1) == tern.TERN_ERR_ALIGN
+
+
 def test_pack_unpack_validation():
     for fn in (lib.tern_pack, lib.tern_unpack):
         assert fn(A, -1, 8, 8, A, 2, NULL) == tern.TERN_ERR_SHAPE

@@ -13,8 +13,8 @@ import torch
 import oracle
 import tern_inputs
 from parity import (DEV, assert_bitexact_weights, assert_within_tolerance, bf16_to_f64,
-                    check_layer, edge_indices, gemm_gpu, gpu_quantize_pack, log,
-                    oracle_weights, row_norms)
+                    check_layer, edge_indices, gemm_gpu, gpu_quantize_pack,
+                    gpu_quantize_pack_fused, log, oracle_weights, row_norms)
 
 pytestmark = pytest.mark.gpu
 tern = pytest.importorskip("ternary_weight_quantized_tern_amd")
@@ -34,6 +34,50 @@ def test_quantize_pack_random(n, k, dtype):
     t_ref, s_ref, p_ref = oracle_weights(w)
     t, s, p = gpu_quantize_pack(w)
     assert_bitexact_weights(t, s, p, t_ref, s_ref, p_ref, f"n={n} k={k}")
+
+
+@pytest.mark.parametrize("n,k", [(1, 1), (3, 5), (7, 64), (33, 257), (64, 3072), (5, 32768),
+                                 (300, 1000), (2, 12289)])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("with_t", [True, False])
+def test_quantize_pack_fused_random(n, k, dtype, with_t):
+    log(f"quantize_pack n={n} k={k} {dtype} with_t={with_t}")
+    _, w = tern_inputs.draw(1, k, n, seed=1000 * n + k + 1)
+    w = w.to(dtype)
+    t_ref, s_ref, p_ref = oracle_weights(w)
+    t, s, p = gpu_quantize_pack_fused(w, with_t)
+    if with_t:
+        assert_bitexact_weights(t, s, p, t_ref, s_ref, p_ref, f"fused n={n} k={k}")
+    else:
+        assert_bitexact_weights(torch.from_numpy(t_ref), s, p, t_ref, s_ref, p_ref,
+                                f"fused n={n} k={k}")
+
+
+@pytest.mark.parametrize("k", [1, 3, 4, 5, 17, 63, 65, 255, 1153])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_quantize_pack_fused_unaligned_rows(k, dtype):
+    # Row pitches that rule out vector loads and stores (the one-weight-per-
+    # thread path, where four lanes combine one packed byte); bytes past
+    # ceil(k/4) and codes past k must stay untouched.
+    n = 21
+    _, w = tern_inputs.draw(1, k, n, seed=500 + k)
+    w = w.to(dtype)
+    t_ref, s_ref, p_ref = oracle_weights(w)
+    big = torch.zeros((n, k + 3), dtype=dtype)
+    big[:, :k] = w
+    wg = big.to(DEV)[:, :k]                          # pitch k + 3: no 16-byte rows
+    nb = (k + 3) // 4
+    t = torch.full((n, k + 5), 7, dtype=torch.int8, device=DEV)
+    p = torch.full((n, nb + 9), 0xA5, dtype=torch.uint8, device=DEV)
+    s = torch.empty(n, device=DEV)
+    tern.tern_quantize_pack(wg, t[:, :k], p, s)
+    torch.cuda.synchronize()
+    th, ph = t.cpu().numpy(), p.cpu().numpy()
+    assert np.array_equal(th[:, :k], t_ref)
+    assert np.all(th[:, k:] == 7)
+    assert np.array_equal(ph[:, :nb], p_ref)
+    assert np.all(ph[:, nb:] == 0xA5)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
 
 
 def test_quantize_special_rows():
