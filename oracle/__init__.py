@@ -4,8 +4,11 @@ Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package.  The GPU library never does.
 """
 from .oracle import (  # noqa: F401
+    ACT_GELU_TANH,
+    ACT_NONE,
     build,
     library_path,
+    oracle_epilogue,
     oracle_gemm,
     oracle_pack,
     oracle_quantize,

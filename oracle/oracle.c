@@ -19,6 +19,9 @@
  *  - The layer output Y = (X . T^T) (.) s for unquantized bf16 activations
  *    ("1.58-bit FLUX", section 4, limitation on speed: activations are not
  *    quantized).
+ *  - An epilogue variant of that output: a per-channel bias and the
+ *    tanh-form GELU on a trailing range of columns (oracle_epilogue; not on
+ *    the pages: the activation of the FLUX MLP, the reading is stated there).
  *
  * Readings where the pages are silent (all listed in the design notes):
  *  - the mean is taken in 64-bit fixed point relative to the row's largest
@@ -231,3 +234,41 @@ int oracle_gemm(const uint16_t* x_bf16, int64_t m, int64_t k, int64_t ldx, const
   free(xd);
   return rc;
 }
+
+/*
+ * Epilogue variant of the layer: bias and activation after the scale.
+ *
+ *   y[m][n] <- f_n( y[m][n] + b[n] ),  f_n = GELU (tanh form) for n >= act_from
+ *                                       f_n = identity otherwise
+ *
+ * applied in place to an unrounded layer output from oracle_gemm, all in
+ * double.  The GELU in its tanh form (Hendrycks and Gimpel) is
+ *
+ *   gelu(z) = z/2 * (1 + tanh( sqrt(2/pi) * (z + 0.044715 z^3) )),
+ *
+ * the activation that FLUX's MLP applies after its up-projection.  The pages
+ * name no bias and no activation for the ternary layer; this variant is the
+ * reading used for the fused epilogues of the MLP up-projection and of the
+ * single-stream in-projection (activation on its MLP columns only).
+ * bias may be NULL (no bias); act is 0 (none) or 1 (GELU, tanh form).
+ */
+static double gelu_tanh(double z) {
+  const double pi = 3.14159265358979323846;
+  const double u = sqrt(2.0 / pi) * (z + 0.044715 * z * z * z);
+  return 0.5 * z * (1.0 + tanh(u));
+}
+
+int oracle_epilogue(double* y, int64_t m, int64_t n, int64_t ldy, const float* bias, int act,
+                    int64_t act_from) {
+  if (m < 0 || n < 0 || ldy < n || (act != 0 && act != 1) || act_from < 0 || act_from > n)
+    return ORACLE_BAD_ARG;
+  for (int64_t mm = 0; mm < m; ++mm)
+    for (int64_t nn = 0; nn < n; ++nn) {
+      double v = y[mm * ldy + nn];
+      if (bias) v += (double)bias[nn];
+      if (act == 1 && nn >= act_from) v = gelu_tanh(v);
+      y[mm * ldy + nn] = v;
+    }
+  return ORACLE_OK;
+}
+

@@ -53,7 +53,9 @@ def load(path: str | None = None):
     lib.oracle_pack.argtypes = [vp, i64, i64, i64, vp, i64]
     lib.oracle_unpack.argtypes = [vp, i64, i64, i64, vp, i64]
     lib.oracle_gemm.argtypes = [vp, i64, i64, i64, vp, i64, i64, vp, vp, i64, ctypes.c_int]
-    for f in (lib.oracle_quantize, lib.oracle_pack, lib.oracle_unpack, lib.oracle_gemm):
+    lib.oracle_epilogue.argtypes = [vp, i64, i64, i64, vp, ctypes.c_int, i64]
+    for f in (lib.oracle_quantize, lib.oracle_pack, lib.oracle_unpack, lib.oracle_gemm,
+              lib.oracle_epilogue):
         f.restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -131,3 +133,26 @@ def oracle_gemm(x_bf16_bits: np.ndarray, p: np.ndarray, s: np.ndarray, k: int | 
     _check(lib.oracle_gemm(_ptr(x), m, k, kx, _ptr(p), n, ldp, _ptr(s), _ptr(y), n, nthreads),
            "oracle_gemm")
     return y
+
+
+ACT_NONE = 0
+ACT_GELU_TANH = 1
+
+
+def oracle_epilogue(y: np.ndarray, bias: np.ndarray | None = None, act: int = ACT_NONE,
+                    act_from: int = 0, lib=None) -> np.ndarray:
+    """Bias and activation on an unrounded layer output (float64 ``[M, N]``):
+    ``f_n(y + b_n)`` with ``f_n`` the tanh-form GELU for ``n >= act_from`` when
+    ``act`` is ``ACT_GELU_TANH``, else the identity.  Returns a new array."""
+    lib = lib or load()
+    out = np.array(y, dtype=np.float64, order="C", copy=True)
+    m, n = out.shape
+    b = None
+    if bias is not None:
+        b = np.ascontiguousarray(bias, dtype=np.float32)
+        if b.shape != (n,):
+            raise ValueError("bias must have one entry per output column")
+    _check(lib.oracle_epilogue(_ptr(out), m, n, n, None if b is None else _ptr(b), int(act),
+                               int(act_from)), "oracle_epilogue")
+    return out
+

@@ -323,6 +323,61 @@ def test_gemm_thread_count_does_not_change_result():
 
 
 # --------------------------------------------------------------------------
+# epilogue variant: bias and the tanh-form GELU
+# --------------------------------------------------------------------------
+
+_Z_GRID = np.concatenate([np.linspace(-12.0, 12.0, 4801), [-40.0, -20.0, -1e-8, 0.0, 1e-8, 20.0, 40.0]])
+
+
+def _gelu_oracle(z):
+    return oracle.oracle_epilogue(np.asarray(z, np.float64)[None, :], None,
+                                  oracle.ACT_GELU_TANH, 0)[0]
+
+
+def test_epilogue_gelu_equals_torch_tanh_gelu():
+    # library routine: torch's GELU with approximate='tanh', in float64
+    ref = torch.nn.functional.gelu(torch.from_numpy(_Z_GRID), approximate="tanh").numpy()
+    got = _gelu_oracle(_Z_GRID)
+    assert np.all(np.abs(got - ref) <= 1e-14 * np.maximum(1.0, np.abs(_Z_GRID)))
+
+
+def test_epilogue_gelu_close_to_exact_gelu():
+    # the tanh form approximates z * Phi(z) (Phi through math.erf) to a few 1e-4
+    exact = np.array([0.5 * z * (1.0 + math.erf(z / math.sqrt(2.0))) for z in _Z_GRID])
+    dev = np.abs(_gelu_oracle(_Z_GRID) - exact)
+    assert dev.max() < 1e-3
+    assert dev[np.abs(_Z_GRID) > 8].max() < 1e-12      # both saturate to 0 and z
+
+
+def test_epilogue_gelu_odd_part_is_identity():
+    # z/2 (1 + tanh u(z)) - (-z)/2 (1 + tanh u(-z)) = z for an odd u and tanh
+    z = _Z_GRID
+    assert np.all(np.abs(_gelu_oracle(z) - _gelu_oracle(-z) - z) <= 1e-15 * np.maximum(1, np.abs(z)))
+    assert _gelu_oracle(np.array([0.0]))[0] == 0.0
+
+
+def test_epilogue_bias_and_activated_columns():
+    rng = np.random.default_rng(3)
+    y = rng.normal(size=(5, 9)) * 3
+    b = rng.normal(size=9).astype(np.float32)
+    out = oracle.oracle_epilogue(y, b, oracle.ACT_GELU_TANH, 4)
+    z = y + b.astype(np.float64)
+    assert np.array_equal(out[:, :4], z[:, :4])                       # identity before act_from
+    ref = torch.nn.functional.gelu(torch.from_numpy(z[:, 4:]), approximate="tanh").numpy()
+    assert np.allclose(out[:, 4:], ref, rtol=0, atol=1e-14 * np.abs(z).max())
+    assert np.array_equal(oracle.oracle_epilogue(y, b, oracle.ACT_NONE, 0), z)
+    assert np.array_equal(oracle.oracle_epilogue(y, None, oracle.ACT_NONE, 0), y)
+    assert np.array_equal(oracle.oracle_epilogue(y, None, oracle.ACT_GELU_TANH, 9), y)
+
+
+def test_epilogue_rejects_bad_arguments():
+    y = np.zeros((2, 3))
+    for act, act_from in [(2, 0), (1, -1), (1, 4)]:
+        with pytest.raises(ValueError):
+            oracle.oracle_epilogue(y, None, act, act_from)
+
+
+# --------------------------------------------------------------------------
 # mutation check: the pins above must catch plausible mistakes in the oracle
 # --------------------------------------------------------------------------
 
@@ -342,6 +397,11 @@ MUTANTS = {
                               "unsigned code = (j->p[(n ^ 1) % (j->n_end > 0 ? j->n_end : 1) * j->ldp + kk / 4]"),
     "gemm_x_transposed_index": ("const double* xr = j->xd + mm * j->k;",
                                 "const double* xr = j->xd + (mm % 2) * j->k;"),
+    "gelu_cubic_coefficient": ("(z + 0.044715 * z * z * z)", "(z + 0.04715 * z * z * z)"),
+    "gelu_missing_half": ("return 0.5 * z * (1.0 + tanh(u));", "return z * (1.0 + tanh(u));"),
+    "gelu_inverted_sqrt": ("sqrt(2.0 / pi)", "sqrt(pi / 2.0)"),
+    "epilogue_act_from_off_by_one": ("nn >= act_from", "nn > act_from"),
+    "epilogue_bias_dropped": ("if (bias) v += (double)bias[nn];", "if (bias) v += 0.0;"),
 }
 
 PIN_TESTS = [
@@ -351,6 +411,8 @@ PIN_TESTS = [
     test_quantize_fixed_point_of_scaled_ternary, test_quantize_mean_is_correctly_rounded_exact_mean,
     test_quantize_gaussian_statistics, test_gemm_sign_sum_identity_exact,
     test_gemm_equals_float64_matmul_on_exact_inputs, test_gemm_against_numpy_on_random_data,
+    test_epilogue_gelu_equals_torch_tanh_gelu, test_epilogue_gelu_close_to_exact_gelu,
+    test_epilogue_gelu_odd_part_is_identity, test_epilogue_bias_and_activated_columns,
 ]
 
 
