@@ -21,8 +21,8 @@
  *    NULL is the default stream) and returns after enqueueing.  Faults inside
  *    a kernel surface at the caller's next synchronisation with that stream.
  *  - Arguments are validated on the host, before anything is enqueued, in
- *    this order: dtype, sizes, (no-op check), null pointers, leading
- *    dimensions, alignment.  A call whose output is empty (a zero size) is a
+ *    this order: dtype or activation kind, sizes, (no-op check), null
+ *    pointers, leading dimensions, alignment.  A call whose output is empty (a zero size) is a
  *    no-op that returns TERN_OK without touching any pointer.
  *  - A kernel launch that the HIP runtime rejects returns TERN_ERR_HIP.
  *  - Outputs must not overlap inputs.  Calls are re-entrant and thread-safe.
@@ -45,7 +45,8 @@ typedef enum {
   TERN_ERR_ALIGN = 3,  /* a pointer or leading dimension breaks an alignment rule */
   TERN_ERR_STRIDE = 4, /* a leading dimension is too short for its row, or too long */
   TERN_ERR_DTYPE = 5,  /* unknown element type */
-  TERN_ERR_HIP = 6     /* the HIP runtime rejected a launch */
+  TERN_ERR_HIP = 6,    /* the HIP runtime rejected a launch */
+  TERN_ERR_ARG = 7     /* an argument is outside its set of allowed values */
 } tern_status;
 
 typedef enum { TERN_F32 = 0, TERN_BF16 = 1 } tern_dtype;
@@ -157,6 +158,36 @@ tern_status tern_unpack(const uint8_t* p, int64_t n, int64_t k, int64_t ldp, int
 tern_status tern_gemm(const void* x_bf16, int64_t m, int64_t k, int64_t ldx, const uint8_t* p,
                       int64_t n, int64_t ldp, const float* s, void* y_bf16, int64_t ldy,
                       void* stream);
+
+/* Activation of the fused epilogue of tern_gemm_ex. */
+typedef enum { TERN_ACT_NONE = 0, TERN_ACT_GELU_TANH = 1 } tern_act;
+
+/*
+ * tern_gemm_ex: tern_gemm with a fused bias and activation, for the layers
+ * that the ternary linear feeds in a diffusion transformer: the MLP
+ * up-projection followed by GELU, and the single-stream in-projection whose
+ * trailing (MLP) columns are followed by GELU.  The pages give the layer
+ * without either ("1.58-bit FLUX", section 1 and section 4); the activation is
+ * the tanh form of GELU (Hendrycks and Gimpel),
+ *   gelu(z) = z/2 * (1 + tanh(sqrt(2/pi) * (z + 0.044715 z^3))).
+ *
+ *   Y[m][n] = bf16( f_n( fp32(acc[m][n] * s[n]) + b[n] ) )
+ *
+ * with acc as in tern_gemm, b[n] = bias[n] (0 when bias is NULL), the sum in
+ * fp32, and f_n = gelu evaluated in fp32 (accurate to a few units in the
+ * last place) when act = TERN_ACT_GELU_TANH and n >= act_from, else the
+ * identity.  tern_gemm_ex(..., NULL, TERN_ACT_NONE, 0, ...) is tern_gemm.
+ *
+ *   bias      NULL or [n] fp32, 4-byte aligned (else TERN_ERR_ALIGN)
+ *   act       TERN_ACT_NONE or TERN_ACT_GELU_TANH (else TERN_ERR_ARG)
+ *   act_from  with TERN_ACT_GELU_TANH: 0 <= act_from <= n (else TERN_ERR_ARG);
+ *             ignored with TERN_ACT_NONE
+ * All other arguments, sizes and rules as tern_gemm; k == 0 writes
+ * bf16(f_n(b[n])).
+ */
+tern_status tern_gemm_ex(const void* x_bf16, int64_t m, int64_t k, int64_t ldx, const uint8_t* p,
+                         int64_t n, int64_t ldp, const float* s, const float* bias, tern_act act,
+                         int64_t act_from, void* y_bf16, int64_t ldy, void* stream);
 
 /* Static, never-NULL description of a status code. */
 const char* tern_status_string(tern_status status);

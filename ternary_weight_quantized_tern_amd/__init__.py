@@ -7,8 +7,11 @@ fails if the library has not been built: there is no CPU fallback.
 from ._binding import (  # noqa: F401
     EXPORTED,
     LIB_PATH,
+    TERN_ACT_GELU_TANH,
+    TERN_ACT_NONE,
     TERN_BF16,
     TERN_ERR_ALIGN,
+    TERN_ERR_ARG,
     TERN_ERR_DTYPE,
     TERN_ERR_HIP,
     TERN_ERR_NULL,
@@ -24,6 +27,7 @@ from ._binding import (  # noqa: F401
     packed_row_bytes,
     quantize,
     tern_gemm,
+    tern_gemm_ex,
     tern_pack,
     tern_quantize,
     tern_quantize_pack,

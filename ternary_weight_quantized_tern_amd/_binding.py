@@ -25,12 +25,15 @@ TERN_ERR_ALIGN = 3
 TERN_ERR_STRIDE = 4
 TERN_ERR_DTYPE = 5
 TERN_ERR_HIP = 6
+TERN_ERR_ARG = 7
+TERN_ACT_NONE = 0
+TERN_ACT_GELU_TANH = 1
 TERN_F32 = 0
 TERN_BF16 = 1
 TERN_QUANTIZE_MAX_K = 32768
 
 EXPORTED = ("tern_quantize", "tern_quantize_pack", "tern_pack", "tern_unpack", "tern_gemm",
-            "tern_status_string")
+            "tern_gemm_ex", "tern_status_string")
 
 
 class TernError(RuntimeError):
@@ -53,7 +56,10 @@ def _load(path: str):
     lib.tern_pack.argtypes = [vp, i64, i64, i64, vp, i64, vp]
     lib.tern_unpack.argtypes = [vp, i64, i64, i64, vp, i64, vp]
     lib.tern_gemm.argtypes = [vp, i64, i64, i64, vp, i64, i64, vp, vp, i64, vp]
-    for name in ("tern_quantize", "tern_quantize_pack", "tern_pack", "tern_unpack", "tern_gemm"):
+    lib.tern_gemm_ex.argtypes = [vp, i64, i64, i64, vp, i64, i64, vp, vp, ctypes.c_int, i64, vp,
+                                 i64, vp]
+    for name in ("tern_quantize", "tern_quantize_pack", "tern_pack", "tern_unpack", "tern_gemm",
+                 "tern_gemm_ex"):
         getattr(lib, name).restype = ctypes.c_int
     lib.tern_status_string.argtypes = [ctypes.c_int]
     lib.tern_status_string.restype = ctypes.c_char_p
@@ -184,6 +190,33 @@ def tern_gemm(x: torch.Tensor, p: torch.Tensor, s: torch.Tensor, y: torch.Tensor
         raise ValueError("shapes must be x [m, k], p [n, >=k/4], s [n], y [m, >=n]")
     _check("tern_gemm", _lib.tern_gemm(x.data_ptr(), m, k, ldx, p.data_ptr(), n, ldp,
                                        s.data_ptr(), y.data_ptr(), ldy, _stream(stream)))
+
+
+def tern_gemm_ex(x: torch.Tensor, p: torch.Tensor, s: torch.Tensor, y: torch.Tensor,
+                 bias: torch.Tensor | None = None, act: int = TERN_ACT_NONE, act_from: int = 0,
+                 k: int | None = None, stream=None) -> None:
+    """``tern_gemm`` with a fused epilogue: ``y = bf16(f_n(x . T^T * s + bias))``,
+    ``f_n`` the tanh-form GELU for columns ``n >= act_from`` when ``act`` is
+    ``TERN_ACT_GELU_TANH``, else the identity; ``bias`` fp32 [n] or None."""
+    ldx = _mat(x, "x", (torch.bfloat16,))
+    ldp = _mat(p, "p", (torch.uint8,))
+    ldy = _mat(y, "y", (torch.bfloat16,))
+    _vec(s, "s", torch.float32)
+    m = x.shape[0]
+    k = x.shape[1] if k is None else int(k)
+    n = p.shape[0]
+    if k > x.shape[1] or p.shape[1] < k // 4 or s.shape[0] != n or tuple(y.shape[:1]) != (m,) \
+            or y.shape[1] < n:
+        raise ValueError("shapes must be x [m, k], p [n, >=k/4], s [n], y [m, >=n]")
+    b_ptr = None
+    if bias is not None:
+        _vec(bias, "bias", torch.float32)
+        if bias.shape[0] != n:
+            raise ValueError("bias must be [n]")
+        b_ptr = bias.data_ptr()
+    _check("tern_gemm_ex", _lib.tern_gemm_ex(x.data_ptr(), m, k, ldx, p.data_ptr(), n, ldp,
+                                             s.data_ptr(), b_ptr, int(act), int(act_from),
+                                             y.data_ptr(), ldy, _stream(stream)))
 
 
 # ---------------------------------------------------------------------------

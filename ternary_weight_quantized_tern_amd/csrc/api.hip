@@ -69,9 +69,11 @@ tern_status tern_unpack(const uint8_t* p, int64_t n, int64_t k, int64_t ldp, int
   return from_hip(tern::launch_unpack(p, n, k, ldp, t, ldt, static_cast<hipStream_t>(stream)));
 }
 
-tern_status tern_gemm(const void* x_bf16, int64_t m, int64_t k, int64_t ldx, const uint8_t* p,
-                      int64_t n, int64_t ldp, const float* s, void* y_bf16, int64_t ldy,
-                      void* stream) {
+namespace {
+
+tern_status gemm_common(const void* x_bf16, int64_t m, int64_t k, int64_t ldx, const uint8_t* p,
+                        int64_t n, int64_t ldp, const float* s, const float* bias,
+                        int64_t act_from, void* y_bf16, int64_t ldy, void* stream) {
   if (m < 0 || n < 0 || k < 0 || m > kMaxInt || n > kMaxInt || k > kMaxInt - 63 || k % 64 != 0)
     return TERN_ERR_SHAPE;
   if (((m + 255) / 256) * ((n + 255) / 256) > kMaxInt) return TERN_ERR_SHAPE;
@@ -80,11 +82,28 @@ tern_status tern_gemm(const void* x_bf16, int64_t m, int64_t k, int64_t ldx, con
   if (ldx < k || ldp < k / 4 || ldy < n) return TERN_ERR_STRIDE;
   if (ldx > kGemmMaxLdx || ldp > kGemmMaxLdp || ldy > kMaxInt) return TERN_ERR_STRIDE;
   if (!aligned(x_bf16, 16) || ldx % 8 != 0 || !aligned(p, 16) || ldp % 16 != 0 ||
-      !aligned(y_bf16, 2) || !aligned(s, 4))
+      !aligned(y_bf16, 2) || !aligned(s, 4) || !aligned(bias, 4))
     return TERN_ERR_ALIGN;
   return from_hip(tern::launch_gemm(static_cast<const uint16_t*>(x_bf16), m, k, ldx, p, n, ldp, s,
-                                    static_cast<uint16_t*>(y_bf16), ldy,
+                                    bias, act_from, static_cast<uint16_t*>(y_bf16), ldy,
                                     static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+tern_status tern_gemm(const void* x_bf16, int64_t m, int64_t k, int64_t ldx, const uint8_t* p,
+                      int64_t n, int64_t ldp, const float* s, void* y_bf16, int64_t ldy,
+                      void* stream) {
+  return gemm_common(x_bf16, m, k, ldx, p, n, ldp, s, nullptr, n, y_bf16, ldy, stream);
+}
+
+tern_status tern_gemm_ex(const void* x_bf16, int64_t m, int64_t k, int64_t ldx, const uint8_t* p,
+                         int64_t n, int64_t ldp, const float* s, const float* bias, tern_act act,
+                         int64_t act_from, void* y_bf16, int64_t ldy, void* stream) {
+  if (act != TERN_ACT_NONE && act != TERN_ACT_GELU_TANH) return TERN_ERR_ARG;
+  if (act == TERN_ACT_GELU_TANH && (act_from < 0 || act_from > n)) return TERN_ERR_ARG;
+  return gemm_common(x_bf16, m, k, ldx, p, n, ldp, s, bias,
+                     act == TERN_ACT_GELU_TANH ? act_from : n, y_bf16, ldy, stream);
 }
 
 const char* tern_status_string(tern_status status) {
@@ -96,6 +115,7 @@ const char* tern_status_string(tern_status status) {
     case TERN_ERR_STRIDE: return "TERN_ERR_STRIDE: a leading dimension is too short or too long";
     case TERN_ERR_DTYPE: return "TERN_ERR_DTYPE: unknown element type";
     case TERN_ERR_HIP: return "TERN_ERR_HIP: the HIP runtime rejected a launch";
+    case TERN_ERR_ARG: return "TERN_ERR_ARG: an argument is outside its set of allowed values";
   }
   return "unknown tern_status";
 }

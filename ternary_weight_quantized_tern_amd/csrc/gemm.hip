@@ -146,13 +146,15 @@ struct TileCfg {
 // LDS by the time the previous tile's epilogue ends.  Tile boundaries must
 // fall between iterations of the kRing-step unrolled loop: PERSIST requires
 // (k / 64) % kRing == 0.  Without PERSIST each workgroup computes tile b
-// only, for any k that is a multiple of 64.
-template <int BM, int BN, int WAVES_M, int GM, bool PERSIST, int WPE>
+// only, for any k that is a multiple of 64.  With EPI the epilogue adds
+// bias[n] (when bias is not null) and applies the tanh-form GELU to columns
+// n >= act_from; without it, bias and act_from are not read.
+template <int BM, int BN, int WAVES_M, int GM, bool PERSIST, int WPE, bool EPI>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
                        const uint8_t* __restrict__ p, int n, int ldp,
-                       const float* __restrict__ s, uint16_t* __restrict__ y, int ldy,
-                       int tiles_m, int tiles_n, int y_flags) {
+                       const float* __restrict__ s, const float* __restrict__ bias, int act_from,
+                       uint16_t* __restrict__ y, int ldy, int tiles_m, int tiles_n, int y_flags) {
 #if defined(__HIP_DEVICE_COMPILE__)
   // (The body uses LDS address-space casts that only the device pass accepts.)
   using C = TileCfg<BM, BN, WAVES_M>;
@@ -438,6 +440,16 @@ void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
 #pragma unroll
       for (int j = 0; j < kTN; ++j)
         sc[j] = *reinterpret_cast<const f32x4_t*>(s + col0 + 16 * j + 4 * g) * 0.5f;
+      const bool act_all = col0 >= act_from;
+      const bool act_none = col0 + C::kWN <= act_from;
+      f32x4_t bsv[EPI ? kTN : 1];
+      if constexpr (EPI) {
+#pragma unroll
+        for (int j = 0; j < kTN; ++j)
+          bsv[j] = bias != nullptr
+                       ? *reinterpret_cast<const f32x4_t*>(bias + col0 + 16 * j + 4 * g)
+                       : f32x4_t{};
+      }
       uint32_t rd_off[kStores], st_off[kStores];
 #pragma unroll
       for (int q = 0; q < kStores; ++q) {
@@ -474,6 +486,26 @@ void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
         }
 #pragma unroll
         for (int jj = 0; jj < kEpiJ; ++jj) v[jj] *= sc[jp + jj];
+        if constexpr (EPI) {
+#pragma unroll
+          for (int jj = 0; jj < kEpiJ; ++jj) v[jj] += bsv[jp + jj];
+          // The activated columns start at act_from: all of the wave's
+          // columns, none of them (no GELU), or a boundary inside them.
+          if (act_all) {
+#pragma unroll
+            for (int jj = 0; jj < kEpiJ; ++jj)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v[jj][e] = gelu_tanh_f32(v[jj][e]);
+          } else if (!act_none) {
+#pragma unroll
+            for (int jj = 0; jj < kEpiJ; ++jj) {
+              const int c0 = col0 + 16 * (jp + jj) + 4 * g;
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (c0 + e >= act_from) v[jj][e] = gelu_tanh_f32(v[jj][e]);
+            }
+          }
+        }
 #pragma unroll
         for (int jj = 0; jj < kEpiJ; ++jj) {
           out[jj][0] = pack_bf16x2(v[jj][0], v[jj][1]);
@@ -509,12 +541,24 @@ void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
         float sc[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) sc[e] = (ng + e < n) ? s[ng + e] : 0.0f;
+        float bv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if constexpr (EPI) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) bv[e] = (bias != nullptr && ng + e < n) ? bias[ng + e] : 0.0f;
+        }
 #pragma unroll
         for (int i = 0; i < kTM; ++i) {
           const int mg = m0 + wm * C::kWM + 16 * i + l16;
           __bf16 b[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) b[e] = static_cast<__bf16>((acc[j][i][e] * sc[e]) * 0.5f);
+          for (int e = 0; e < 4; ++e) {
+            float z = (acc[j][i][e] * sc[e]) * 0.5f;
+            if constexpr (EPI) {
+              z += bv[e];
+              if (ng + e >= act_from) z = gelu_tanh_f32(z);
+            }
+            b[e] = static_cast<__bf16>(z);
+          }
           if (mg >= m) continue;
           uint16_t* yr = y + static_cast<int64_t>(mg) * ldy + ng;
           if ((y_flags & 1) && ng + 4 <= n) {
@@ -607,13 +651,18 @@ void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-// k == 0: the sum is empty, so Y = bf16(0 * s) = 0.
-__global__ void fill_zero_bf16(uint16_t* y, int m, int n, int ldy) {
+// k == 0: the sum is empty, so Y = bf16(f(0 * s + b)): zero, or the
+// epilogue applied to the bias alone.
+__global__ void fill_empty_sum(uint16_t* y, int m, int n, int ldy, const float* bias,
+                               int act_from) {
   const int64_t total = static_cast<int64_t>(m) * n;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
        i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
     const int64_t r = i / n;
-    y[r * ldy + (i - r * n)] = 0;
+    const int c = static_cast<int>(i - r * n);
+    float z = bias != nullptr ? bias[c] : 0.0f;
+    if (c >= act_from) z = gelu_tanh_f32(z);
+    y[r * ldy + c] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(z));
   }
 }
 
@@ -623,55 +672,46 @@ __global__ void fill_zero_bf16(uint16_t* y, int m, int n, int ldy) {
 constexpr int kPersistentGrid = 256;
 constexpr int64_t kSmallMaxM = 32;
 
-template <int BM, int BN, int WAVES_M, int GM, int WPE>
+template <int BM, int BN, int WAVES_M, int GM, int WPE, bool EPI>
 hipError_t launch_tiles(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const uint8_t* p,
-                        int64_t n, int64_t ldp, const float* s, uint16_t* y, int64_t ldy,
-                        hipStream_t stream) {
+                        int64_t n, int64_t ldp, const float* s, const float* bias, int act_from,
+                        uint16_t* y, int64_t ldy, hipStream_t stream) {
   const int tiles_m = static_cast<int>((m + BM - 1) / BM);
   const int tiles_n = static_cast<int>((n + BN - 1) / BN);
   const int64_t tiles = static_cast<int64_t>(tiles_m) * tiles_n;
   const int stages = static_cast<int>(k / kBK);
   // Bit 0: 8-byte stores of Y; bit 1: 16-byte stores of Y, 16-byte loads of
-  // the scales and 32-bit offsets within 16 rows of Y.
+  // the scales (and of the bias) and 32-bit offsets within 16 rows of Y.
   const int y_flags =
       (((reinterpret_cast<uintptr_t>(y) & 7) == 0 && ldy % 4 == 0) ? 1 : 0) |
       (((reinterpret_cast<uintptr_t>(y) & 15) == 0 && ldy % 8 == 0 && ldy < (int64_t{1} << 27) &&
-        (reinterpret_cast<uintptr_t>(s) & 15) == 0) ? 2 : 0);
+        (reinterpret_cast<uintptr_t>(s) & 15) == 0 &&
+        (reinterpret_cast<uintptr_t>(bias) & 15) == 0) ? 2 : 0);
   // The persistent kernel takes whole tiles only (its epilogue has no edge
   // handling) and needs the ring stream to restart at a tile boundary.
   if constexpr (WPE == 1) {
     if (stages % 6 == 0 && tiles > kPersistentGrid && m % BM == 0 && n % BN == 0 &&
         (y_flags & 2)) {
-      hipLaunchKernelGGL((gemm_ternary_mfma<BM, BN, WAVES_M, GM, true, WPE>),
+      hipLaunchKernelGGL((gemm_ternary_mfma<BM, BN, WAVES_M, GM, true, WPE, EPI>),
                          dim3(kPersistentGrid), dim3(kThreads), 0, stream, x,
                          static_cast<int>(m), static_cast<int>(k), static_cast<int>(ldx), p,
-                         static_cast<int>(n), static_cast<int>(ldp), s, y, static_cast<int>(ldy),
-                         tiles_m, tiles_n, y_flags);
+                         static_cast<int>(n), static_cast<int>(ldp), s, bias, act_from, y,
+                         static_cast<int>(ldy), tiles_m, tiles_n, y_flags);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((gemm_ternary_mfma<BM, BN, WAVES_M, GM, false, WPE>),
+  hipLaunchKernelGGL((gemm_ternary_mfma<BM, BN, WAVES_M, GM, false, WPE, EPI>),
                      dim3(static_cast<unsigned>(tiles)), dim3(kThreads), 0, stream, x,
                      static_cast<int>(m), static_cast<int>(k), static_cast<int>(ldx), p,
-                     static_cast<int>(n), static_cast<int>(ldp), s, y, static_cast<int>(ldy),
-                     tiles_m, tiles_n, y_flags);
+                     static_cast<int>(n), static_cast<int>(ldp), s, bias, act_from, y,
+                     static_cast<int>(ldy), tiles_m, tiles_n, y_flags);
   return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_gemm(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const uint8_t* p,
-                       int64_t n, int64_t ldp, const float* s, uint16_t* y, int64_t ldy,
-                       hipStream_t stream) {
-  if (k == 0) {
-    int64_t blocks = (m * n + 255) / 256;
-    if (blocks > 65536) blocks = 65536;
-    hipLaunchKernelGGL(fill_zero_bf16, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
-                       y, static_cast<int>(m), static_cast<int>(n), static_cast<int>(ldy));
-    return hipGetLastError();
-  }
-  // A few tokens: the weight stream dominates; see gemm_small.hip.
-  if (m <= kSmallMaxM) return launch_gemm_small(x, m, k, ldx, p, n, ldp, s, y, ldy, stream);
+template <bool EPI>
+hipError_t launch_big(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const uint8_t* p,
+                      int64_t n, int64_t ldp, const float* s, const float* bias, int act_from,
+                      uint16_t* y, int64_t ldy, hipStream_t stream) {
   // Layers with at least one 144 x 384 tile per CU use the big tile (one
   // workgroup per CU, 147 KiB of LDS).  Smaller layers that 64 x 576 tiles
   // cut into exactly one tile per CU use those (wave tile 64 x 144, still on
@@ -680,12 +720,38 @@ hipError_t launch_gemm(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, con
   // whichever still gives two tiles per CU, so that every CU has work.
   const auto tiles = [&](int64_t bm, int64_t bn) { return ((m + bm - 1) / bm) * ((n + bn - 1) / bn); };
   if (tiles(144, 384) >= kPersistentGrid)
-    return launch_tiles<144, 384, 1, 4, 1>(x, m, k, ldx, p, n, ldp, s, y, ldy, stream);
+    return launch_tiles<144, 384, 1, 4, 1, EPI>(x, m, k, ldx, p, n, ldp, s, bias, act_from, y,
+                                                ldy, stream);
   if (m % 64 == 0 && n % 576 == 0 && tiles(64, 576) == kPersistentGrid)
-    return launch_tiles<64, 576, 1, 4, 1>(x, m, k, ldx, p, n, ldp, s, y, ldy, stream);
+    return launch_tiles<64, 576, 1, 4, 1, EPI>(x, m, k, ldx, p, n, ldp, s, bias, act_from, y,
+                                               ldy, stream);
   if (tiles(64, 256) >= 2 * kPersistentGrid)
-    return launch_tiles<64, 256, 1, 4, 2>(x, m, k, ldx, p, n, ldp, s, y, ldy, stream);
-  return launch_tiles<64, 128, 1, 4, 2>(x, m, k, ldx, p, n, ldp, s, y, ldy, stream);
+    return launch_tiles<64, 256, 1, 4, 2, EPI>(x, m, k, ldx, p, n, ldp, s, bias, act_from, y,
+                                               ldy, stream);
+  return launch_tiles<64, 128, 1, 4, 2, EPI>(x, m, k, ldx, p, n, ldp, s, bias, act_from, y, ldy,
+                                             stream);
+}
+
+}  // namespace
+
+hipError_t launch_gemm(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const uint8_t* p,
+                       int64_t n, int64_t ldp, const float* s, const float* bias,
+                       int64_t act_from, uint16_t* y, int64_t ldy, hipStream_t stream) {
+  const int af = static_cast<int>(act_from);
+  if (k == 0) {
+    int64_t blocks = (m * n + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(fill_empty_sum, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
+                       y, static_cast<int>(m), static_cast<int>(n), static_cast<int>(ldy), bias,
+                       af);
+    return hipGetLastError();
+  }
+  const bool epi = bias != nullptr || act_from < n;
+  // A few tokens: the weight stream dominates; see gemm_small.hip.
+  if (m <= kSmallMaxM)
+    return launch_gemm_small(x, m, k, ldx, p, n, ldp, s, bias, act_from, y, ldy, stream);
+  if (epi) return launch_big<true>(x, m, k, ldx, p, n, ldp, s, bias, af, y, ldy, stream);
+  return launch_big<false>(x, m, k, ldx, p, n, ldp, s, nullptr, af, y, ldy, stream);
 }
 
 }  // namespace tern

@@ -68,4 +68,18 @@ __device__ inline void mfma16(f32x4_t& acc, const bf16x8_t& a, const bf16x8_t& b
   }
 }
 
+// The tanh form of GELU (Hendrycks and Gimpel) in fp32:
+//   gelu(z) = z/2 (1 + tanh u),  u = sqrt(2/pi) (z + 0.044715 z^3).
+// Since (1 + tanh u)/2 = 1/(1 + e^(-2u)), gelu(z) = z / (1 + e^(-2u)): the
+// denominator is at least 1 (no cancellation for negative z), e^(-2u) = 2^a
+// with a = z (A + B z^2), A = -2 sqrt(2/pi) log2 e, B = 0.044715 A, and an
+// overflow to +inf gives the limit 0.  Five VALU instructions, the hardware
+// exp2 and one hardware reciprocal.
+__device__ inline float gelu_tanh_f32(float z) {
+  constexpr float kA = -2.302208198144325f;    // -2 sqrt(2/pi) log2(e)
+  constexpr float kB = -0.1029432395800235f;   // 0.044715 kA
+  const float a = z * __builtin_fmaf(kB, z * z, kA);
+  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(a));
+}
+
 }  // namespace tern

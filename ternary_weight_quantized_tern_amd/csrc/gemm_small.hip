@@ -39,11 +39,14 @@ constexpr uint32_t kOutOfRange = 0x80000000u;
 
 // R MFMA row blocks (m <= 16 R), B blocks of 16 output channels per
 // workgroup (every wave covers all of them for its K chunks, so one X operand
-// serves B MFMAs), DEPTH chunks in flight per wave.
-template <int R, int B, int DEPTH>
+// serves B MFMAs), DEPTH chunks in flight per wave.  With EPI the epilogue
+// adds bias[n] (when bias is not null) and applies the tanh-form GELU to
+// columns n >= act_from.
+template <int R, int B, int DEPTH, bool EPI>
 __global__ __launch_bounds__(kSmallThreads) void gemm_ternary_small(
     const uint16_t* __restrict__ x, int m, int k, int ldx, const uint8_t* __restrict__ p, int n,
-    int ldp, const float* __restrict__ s, uint16_t* __restrict__ y, int ldy, int y_vec_ok) {
+    int ldp, const float* __restrict__ s, const float* __restrict__ bias, int act_from,
+    uint16_t* __restrict__ y, int ldy, int y_vec_ok) {
   __shared__ f32x4_t red[kSmallThreads / 64 - 1][B][R][64];
 
   const int tid = threadIdx.x;
@@ -113,6 +116,16 @@ __global__ __launch_bounds__(kSmallThreads) void gemm_ternary_small(
       const int nc = n0 + 16 * bl + 4 * g + e;
       sc[bl][e] = nc < n ? s[nc] * 0.5f : 0.0f;
     }
+  float bsv[EPI ? B : 1][4];
+  if constexpr (EPI) {
+#pragma unroll
+    for (int bl = 0; bl < B; ++bl)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int nc = n0 + 16 * bl + 4 * g + e;
+        bsv[bl][e] = (bias != nullptr && nc < n) ? bias[nc] : 0.0f;
+      }
+  }
 
   f32x4_t acc[B][R];
 #pragma unroll
@@ -177,7 +190,14 @@ __global__ __launch_bounds__(kSmallThreads) void gemm_ternary_small(
     if (token >= m) continue;
     __bf16 o[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) o[e] = static_cast<__bf16>(v[e] * sc[bl][e]);
+    for (int e = 0; e < 4; ++e) {
+      float z = v[e] * sc[bl][e];
+      if constexpr (EPI) {
+        z += bsv[bl][e];
+        if (nb + e >= act_from) z = gelu_tanh_f32(z);
+      }
+      o[e] = static_cast<__bf16>(z);
+    }
     uint16_t* yr = y + static_cast<int64_t>(token) * ldy + nb;
     if (y_vec_ok && nb + 4 <= n) {
       u32x2_t q;
@@ -195,24 +215,25 @@ __global__ __launch_bounds__(kSmallThreads) void gemm_ternary_small(
   }
 }
 
-template <int R, int B, int DEPTH>
+template <int R, int B, int DEPTH, bool EPI>
 hipError_t launch_small(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const uint8_t* p,
-                        int64_t n, int64_t ldp, const float* s, uint16_t* y, int64_t ldy,
-                        hipStream_t stream) {
+                        int64_t n, int64_t ldp, const float* s, const float* bias, int act_from,
+                        uint16_t* y, int64_t ldy, hipStream_t stream) {
   const int64_t blocks = (n + 16 * B - 1) / (16 * B);
   const int y_vec_ok = ((reinterpret_cast<uintptr_t>(y) & 7) == 0) && (ldy % 4 == 0);
-  hipLaunchKernelGGL((gemm_ternary_small<R, B, DEPTH>), dim3(static_cast<unsigned>(blocks)),
+  hipLaunchKernelGGL((gemm_ternary_small<R, B, DEPTH, EPI>), dim3(static_cast<unsigned>(blocks)),
                      dim3(kSmallThreads), 0, stream, x, static_cast<int>(m), static_cast<int>(k),
-                     static_cast<int>(ldx), p, static_cast<int>(n), static_cast<int>(ldp), s, y,
-                     static_cast<int>(ldy), y_vec_ok);
+                     static_cast<int>(ldx), p, static_cast<int>(n), static_cast<int>(ldp), s, bias,
+                     act_from, y, static_cast<int>(ldy), y_vec_ok);
   return hipGetLastError();
 }
 
-}  // namespace
 
-hipError_t launch_gemm_small(const uint16_t* x, int64_t m, int64_t k, int64_t ldx,
-                             const uint8_t* p, int64_t n, int64_t ldp, const float* s,
-                             uint16_t* y, int64_t ldy, hipStream_t stream) {
+template <bool EPI>
+hipError_t launch_small_any(const uint16_t* x, int64_t m, int64_t k, int64_t ldx,
+                            const uint8_t* p, int64_t n, int64_t ldp, const float* s,
+                            const float* bias, int act_from, uint16_t* y, int64_t ldy,
+                            hipStream_t stream) {
   // Channel blocks per workgroup.  The weight stream is latency-bound: every
   // CU keeps a fixed number of bytes in flight per workgroup, and a CU that
   // holds two workgroups finishes them well after the CUs that hold one.  So
@@ -231,16 +252,37 @@ hipError_t launch_gemm_small(const uint16_t* x, int64_t m, int64_t k, int64_t ld
       best_cost = cost;
     }
   }
-#define TERN_SMALL(R, DEPTH6, DEPTH3, DEPTH2, DEPTH1)                                            \
-  switch (best) {                                                                                \
-    case 6: return launch_small<R, 6, DEPTH6>(x, m, k, ldx, p, n, ldp, s, y, ldy, stream);       \
-    case 3: return launch_small<R, 3, DEPTH3>(x, m, k, ldx, p, n, ldp, s, y, ldy, stream);       \
-    case 2: return launch_small<R, 2, DEPTH2>(x, m, k, ldx, p, n, ldp, s, y, ldy, stream);       \
-    default: return launch_small<R, 1, DEPTH1>(x, m, k, ldx, p, n, ldp, s, y, ldy, stream);      \
+#define TERN_SMALL(R, DEPTH6, DEPTH3, DEPTH2, DEPTH1)                                           \
+  switch (best) {                                                                               \
+    case 6:                                                                                     \
+      return launch_small<R, 6, DEPTH6, EPI>(x, m, k, ldx, p, n, ldp, s, bias, act_from, y, ldy, \
+                                             stream);                                           \
+    case 3:                                                                                     \
+      return launch_small<R, 3, DEPTH3, EPI>(x, m, k, ldx, p, n, ldp, s, bias, act_from, y, ldy, \
+                                             stream);                                           \
+    case 2:                                                                                     \
+      return launch_small<R, 2, DEPTH2, EPI>(x, m, k, ldx, p, n, ldp, s, bias, act_from, y, ldy, \
+                                             stream);                                           \
+    default:                                                                                    \
+      return launch_small<R, 1, DEPTH1, EPI>(x, m, k, ldx, p, n, ldp, s, bias, act_from, y, ldy, \
+                                             stream);                                           \
   }
   if (m <= 16) TERN_SMALL(1, 3, 3, 4, 4)
   TERN_SMALL(2, 2, 2, 2, 2)
 #undef TERN_SMALL
+}
+
+}  // namespace
+
+hipError_t launch_gemm_small(const uint16_t* x, int64_t m, int64_t k, int64_t ldx,
+                             const uint8_t* p, int64_t n, int64_t ldp, const float* s,
+                             const float* bias, int64_t act_from, uint16_t* y, int64_t ldy,
+                             hipStream_t stream) {
+  if (bias != nullptr || act_from < n)
+    return launch_small_any<true>(x, m, k, ldx, p, n, ldp, s, bias, static_cast<int>(act_from), y,
+                                  ldy, stream);
+  return launch_small_any<false>(x, m, k, ldx, p, n, ldp, s, nullptr, static_cast<int>(act_from),
+                                 y, ldy, stream);
 }
 
 }  // namespace tern

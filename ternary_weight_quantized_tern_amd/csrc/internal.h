@@ -23,13 +23,16 @@ hipError_t launch_pack(const int8_t* t, int64_t n, int64_t k, int64_t ldt, uint8
 hipError_t launch_unpack(const uint8_t* p, int64_t n, int64_t k, int64_t ldp, int8_t* t,
                          int64_t ldt, hipStream_t stream);
 
+// bias: nullptr or [n]; act_from in [0, n]: the tanh-form GELU is applied to
+// columns >= act_from (act_from == n: no activation).
 hipError_t launch_gemm(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const uint8_t* p,
-                       int64_t n, int64_t ldp, const float* s, uint16_t* y, int64_t ldy,
-                       hipStream_t stream);
+                       int64_t n, int64_t ldp, const float* s, const float* bias,
+                       int64_t act_from, uint16_t* y, int64_t ldy, hipStream_t stream);
 
 // m <= 32 (called by launch_gemm).
 hipError_t launch_gemm_small(const uint16_t* x, int64_t m, int64_t k, int64_t ldx,
                              const uint8_t* p, int64_t n, int64_t ldp, const float* s,
-                             uint16_t* y, int64_t ldy, hipStream_t stream);
+                             const float* bias, int64_t act_from, uint16_t* y, int64_t ldy,
+                             hipStream_t stream);
 
 }  // namespace tern

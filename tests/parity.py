@@ -154,3 +154,90 @@ def check_layer(x_cpu: torch.Tensor, w_cpu: torch.Tensor, what: str, rows=None, 
             worst = max(worst, assert_within_tolerance(yh[:, cols], y_ref, s_ref[cols], xnorm,
                                                        what + " (cols)"))
     return worst
+
+
+# ---------------------------------------------------------------------------
+# fused epilogue (tern_gemm_ex): bias and the tanh-form GELU
+# ---------------------------------------------------------------------------
+
+# Lipschitz bound of the tanh-form GELU (its slope peaks at about 1.13).
+GELU_LIP = 1.2
+# fp32 rounding of the product and of the bias add, relative to |z| + |b|.
+EPI_ADD_TOL = 1e-5
+
+
+def gemm_ex_gpu(x_cpu, p_gpu, s_gpu, k, bias_cpu=None, act=0, act_from=0):
+    x = x_cpu.to(DEV)
+    y = torch.empty((x.shape[0], p_gpu.shape[0]), dtype=torch.bfloat16, device=DEV)
+    b = None if bias_cpu is None else torch.from_numpy(np.ascontiguousarray(bias_cpu)).to(DEV)
+    tern.tern_gemm_ex(x, p_gpu, s_gpu, y, b, act, act_from, k)
+    torch.cuda.synchronize()
+    return y
+
+
+def assert_within_tolerance_ex(y_gpu, y_lin_ref, s, xnorm, bias, act, act_from, cols=None,
+                               what=""):
+    """Epilogue output against oracle_epilogue of the unrounded linear output.
+
+    z_ref = y_lin_ref + b.  The GPU forms z in fp32 from an fp32 sum, so
+    |z - z_ref| <= 1e-3 s_n ||x_m|| (the slack of the plain layer) + 1e-5
+    (|z_ref| + |b_n|) (fp32 product and add); the GELU is Lipschitz with
+    constant below 1.2, and the bf16 rounding of y is covered by 8e-3 |y_ref|.
+    ``cols`` are the output-column indices of y_gpu's columns (for act_from)."""
+    n_cols = y_lin_ref.shape[1]
+    cols = np.arange(n_cols) if cols is None else np.asarray(cols)
+    b = np.zeros(n_cols) if bias is None else np.asarray(bias, np.float64)
+    z_ref = y_lin_ref + b[None, :]
+    act_on = (cols >= act_from) if act == oracle.ACT_GELU_TANH else np.zeros(n_cols, bool)
+    # oracle_epilogue applies act to its own column indices: pass the mask as act_from 0
+    # on the activated subset
+    y_ref = z_ref.copy()
+    if act_on.any():
+        y_ref[:, act_on] = oracle.oracle_epilogue(z_ref[:, act_on], None, oracle.ACT_GELU_TANH, 0)
+    lip = np.where(act_on, GELU_LIP, 1.0)[None, :]
+    bound = (REL_TOL * np.abs(y_ref)
+             + lip * (NORM_TOL * s.astype(np.float64)[None, :] * xnorm[:, None]
+                      + EPI_ADD_TOL * (np.abs(z_ref) + np.abs(b)[None, :])))
+    err = np.abs(y_gpu - y_ref)
+    bad = err > bound
+    if np.any(bad) or not np.all(np.isfinite(y_gpu)):
+        idx = np.argwhere(bad | ~np.isfinite(y_gpu))
+        r, c = idx[0]
+        raise AssertionError(
+            f"{what}: {len(idx)} of {y_ref.size} outputs outside tolerance; first at (m={r}, "
+            f"col={cols[c]}): gpu={y_gpu[r, c]!r} ref={y_ref[r, c]!r} bound={bound[r, c]!r}")
+    return float(np.max(err / np.maximum(bound, 1e-300)))
+
+
+def check_layer_ex(x_cpu, w_cpu, bias, act, act_from, what, rows=None, cols=None,
+                   full=False):
+    """tern_gemm_ex on every element (``full``) or on rows x all columns and all
+    rows x columns; weights from the GPU quantizer (bit-exact against the
+    oracle's, checked by check_layer elsewhere)."""
+    m, k = x_cpu.shape
+    t_ref, s_ref, p_ref = oracle_weights(w_cpu)
+    _, s_g, p_g = gpu_quantize_pack(w_cpu)
+    y = gemm_ex_gpu(x_cpu, p_g, s_g, k, bias, act, act_from)
+    yh = bf16_to_f64(y)
+    xb = tern_inputs.bf16_bits(x_cpu)
+    xnorm = row_norms(xb)
+    bias32 = None if bias is None else np.asarray(bias, np.float32)
+    worst = 0.0
+    if full:
+        y_lin = oracle.oracle_gemm(xb, p_ref, s_ref, k=k)
+        worst = assert_within_tolerance_ex(yh, y_lin, s_ref, xnorm, bias32, act, act_from,
+                                           what=what)
+    else:
+        if rows is not None:
+            y_lin = oracle.oracle_gemm(xb[rows], p_ref, s_ref, k=k)
+            worst = max(worst, assert_within_tolerance_ex(yh[rows], y_lin, s_ref, xnorm[rows],
+                                                          bias32, act, act_from,
+                                                          what=what + " (rows)"))
+        if cols is not None:
+            y_lin = oracle.oracle_gemm(xb, p_ref[cols], s_ref[cols], k=k)
+            worst = max(worst, assert_within_tolerance_ex(
+                yh[:, cols], y_lin, s_ref[cols], xnorm,
+                None if bias32 is None else bias32[cols], act, act_from, cols=cols,
+                what=what + " (cols)"))
+    return worst
+

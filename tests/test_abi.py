@@ -59,7 +59,7 @@ def test_header_compiles_as_c_and_matches_enum_values(tmp_path):
 
 def test_status_strings():
     seen = set()
-    for code in range(7):
+    for code in range(8):
         sstr = tern.tern_status_string(code)
         assert sstr and sstr not in seen
         seen.add(sstr)
@@ -154,6 +154,29 @@ def test_gemm_validation():
     assert call(ldp=40) == tern.TERN_ERR_ALIGN
     assert call(y=A + 1) == tern.TERN_ERR_ALIGN
     assert call(s=A + 2) == tern.TERN_ERR_ALIGN
+
+
+def test_gemm_ex_validation():
+    g = lib.tern_gemm_ex
+    ok = dict(x=A, m=8, k=128, ldx=128, p=A, n=16, ldp=32, s=A, b=A, act=1, af=0, y=A, ldy=16)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return g(a["x"], a["m"], a["k"], a["ldx"], a["p"], a["n"], a["ldp"], a["s"], a["b"],
+                 a["act"], a["af"], a["y"], a["ldy"], NULL)
+
+    assert call(act=2) == tern.TERN_ERR_ARG
+    assert call(act=2, m=-1) == tern.TERN_ERR_ARG              # the kind is checked first
+    assert call(af=-1) == tern.TERN_ERR_ARG
+    assert call(af=17) == tern.TERN_ERR_ARG                    # act_from > n
+    assert call(act=0, af=99, ldx=120) == tern.TERN_ERR_STRIDE  # act_from ignored without act
+    assert call(m=-1) == tern.TERN_ERR_SHAPE
+    assert call(k=100, ldx=128) == tern.TERN_ERR_SHAPE
+    assert call(m=0, x=NULL, p=NULL, s=NULL, y=NULL) == tern.TERN_OK
+    for name in ("x", "p", "s", "y"):
+        assert call(**{name: NULL}) == tern.TERN_ERR_NULL
+    assert call(b=A + 2) == tern.TERN_ERR_ALIGN               # bias needs 4 bytes
+    assert call(b=A + 4, x=A + 8) == tern.TERN_ERR_ALIGN
 
 
 def test_binding_refuses_cpu_tensors():

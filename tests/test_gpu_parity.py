@@ -12,8 +12,9 @@ import torch
 
 import oracle
 import tern_inputs
-from parity import (DEV, assert_bitexact_weights, assert_within_tolerance, bf16_to_f64,
-                    check_layer, edge_indices, gemm_gpu, gpu_quantize_pack,
+from parity import (DEV, assert_bitexact_weights, assert_within_tolerance,
+                    assert_within_tolerance_ex, bf16_to_f64, check_layer, check_layer_ex,
+                    edge_indices, gemm_ex_gpu, gemm_gpu, gpu_quantize_pack,
                     gpu_quantize_pack_fused, log, oracle_weights, row_norms)
 
 pytestmark = pytest.mark.gpu
@@ -224,6 +225,110 @@ def test_gemm_error_status_through_binding():
     with pytest.raises(tern.TernError) as e:
         tern.tern_gemm(x, p, s, y, 100)
     assert e.value.status == tern.TERN_ERR_SHAPE
+
+
+# ---------------------------------------------------------------------------
+# fused epilogue: bias and tanh-form GELU (tern_gemm_ex)
+# ---------------------------------------------------------------------------
+
+def _bias(n, seed):
+    return (np.random.default_rng(seed).normal(size=n) * 0.5).astype(np.float32)
+
+
+EPI_VARIANTS = {            # (bias?, act, act_from as a function of n)
+    "bias": (True, tern.TERN_ACT_NONE, lambda n: 0),
+    "gelu": (False, tern.TERN_ACT_GELU_TANH, lambda n: 0),
+    "bias_gelu_from_mid": (True, tern.TERN_ACT_GELU_TANH, lambda n: n // 3 + 1),
+}
+
+EPI_SHAPES = [
+    (8, 256, 100), (24, 320, 210), (3, 1088, 24536),   # few-token kernel (R = 1, 2; B = 6)
+    (300, 320, 520), (513, 192, 700),                  # 64 x 128 tiles
+    (1100, 128, 7500),                                 # 64 x 256 tiles
+    (1024, 192, 9216),                                 # 64 x 576 tiles
+]
+
+
+@pytest.mark.parametrize("m,k,n", EPI_SHAPES)
+@pytest.mark.parametrize("variant", list(EPI_VARIANTS))
+def test_gemm_ex_all_elements(m, k, n, variant):
+    log(f"gemm_ex {variant} m={m} k={k} n={n}")
+    has_bias, act, af = EPI_VARIANTS[variant]
+    x, w = tern_inputs.draw(m, k, n, seed=m * 131 + k * 7 + n + 11,
+                            x_dist="student_t3" if m % 2 else "normal")
+    bias = _bias(n, m + n) if has_bias else None
+    check_layer_ex(x, w, bias, act, af(n), f"gemm_ex {variant} {m}x{k}x{n}", full=True)
+
+
+@pytest.mark.parametrize("m,k,n", [(4608, 384, 9216), (4608, 448, 9216)])
+def test_gemm_ex_big_tiles_sampled(m, k, n):
+    # 144 x 384 tiles: persistent (k = 384) and one tile per workgroup (k = 448)
+    log(f"gemm_ex big m={m} k={k} n={n}")
+    x, w = tern_inputs.draw(m, k, n, seed=k + 3)
+    rows = edge_indices(m, extra=64, seed=k)
+    cols = edge_indices(n, extra=64, seed=k + 1)
+    check_layer_ex(x, w, _bias(n, k), tern.TERN_ACT_GELU_TANH, 3001, f"gemm_ex big k={k}",
+                   rows=rows, cols=cols)
+
+
+@pytest.mark.parametrize("m,k,n", [(4608, 384, 9216), (300, 320, 520), (8, 256, 100)])
+def test_gemm_ex_without_epilogue_is_gemm(m, k, n):
+    x, w = tern_inputs.draw(m, k, n, seed=m + k + n)
+    _, s, p = gpu_quantize_pack(w)
+    y0 = gemm_gpu(x, p, s, k)
+    y1 = gemm_ex_gpu(x, p, s, k, None, tern.TERN_ACT_NONE, 0)
+    y2 = gemm_ex_gpu(x, p, s, k, None, tern.TERN_ACT_GELU_TANH, n)   # empty activated range
+    assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
+    assert torch.equal(y0.view(torch.int16), y2.view(torch.int16))
+
+
+def test_gemm_ex_k_zero_is_epilogue_of_bias():
+    m, n = 6, 50
+    bias = _bias(n, 1)
+    x = torch.zeros((m, 64), dtype=torch.bfloat16)
+    p = torch.zeros((n, 16), dtype=torch.uint8, device=DEV)
+    s = torch.ones(n, device=DEV)
+    y = gemm_ex_gpu(x, p, s, 0, bias, tern.TERN_ACT_GELU_TANH, 17)
+    ref = oracle.oracle_epilogue(np.zeros((m, n)), bias, oracle.ACT_GELU_TANH, 17)
+    yh = bf16_to_f64(y)
+    assert np.all(np.abs(yh - ref) <= 8e-3 * np.abs(ref) + 1e-6)
+
+
+def test_gemm_ex_error_status():
+    x = torch.zeros((4, 64), dtype=torch.bfloat16, device=DEV)
+    p = torch.zeros((8, 16), dtype=torch.uint8, device=DEV)
+    s = torch.ones(8, device=DEV)
+    y = torch.empty((4, 8), dtype=torch.bfloat16, device=DEV)
+    for act, af, code in [(5, 0, tern.TERN_ERR_ARG), (tern.TERN_ACT_GELU_TANH, -1, tern.TERN_ERR_ARG),
+                          (tern.TERN_ACT_GELU_TANH, 9, tern.TERN_ERR_ARG)]:
+        with pytest.raises(tern.TernError) as e:
+            tern.tern_gemm_ex(x, p, s, y, None, act, af)
+        assert e.value.status == code
+    b = torch.zeros(9, device=DEV)[1:]                 # 4-byte aligned, not 16: still accepted
+    tern.tern_gemm_ex(x, p, s, y, b, tern.TERN_ACT_GELU_TANH, 0)
+    torch.cuda.synchronize()
+
+
+def test_workload_flux_mlp_up_gelu():
+    layer = tern_inputs.WORKLOADS["flux_mlp"][0]
+    log(f"workload {layer.name} + GELU m={layer.m} k={layer.k} n={layer.n}")
+    x, w = tern_inputs.draw_layer(layer)
+    rows = edge_indices(layer.m, extra=96, seed=layer.seed)
+    cols = edge_indices(layer.n, extra=96, seed=layer.seed + 1)
+    check_layer_ex(x, w, None, tern.TERN_ACT_GELU_TANH, 0, layer.name + " + GELU",
+                   rows=rows, cols=cols)
+
+
+def test_workload_flux_single_stream_in_proj_bias_gelu_mlp_part():
+    # GELU on the MLP columns only (the first 3 * 3072 columns are Q, K, V)
+    layer = tern_inputs.WORKLOADS["flux_single_stream"][0]
+    log(f"workload {layer.name} + bias + GELU[9216:] m={layer.m} k={layer.k} n={layer.n}")
+    x, w = tern_inputs.draw_layer(layer)
+    rows = edge_indices(layer.m, extra=64, seed=layer.seed)
+    cols = np.unique(np.concatenate([edge_indices(layer.n, extra=96, seed=layer.seed + 1),
+                                     np.arange(9200, 9232)]))
+    check_layer_ex(x, w, _bias(layer.n, 5), tern.TERN_ACT_GELU_TANH, 9216,
+                   layer.name + " + bias + GELU[9216:]", rows=rows, cols=cols)
 
 
 # ---------------------------------------------------------------------------
