@@ -2,17 +2,19 @@
 """Throughput of the 1.58-bit linear layer on one MI355X.
 
 One step is one pass of the whole path over one layer's synthetic inputs,
-already resident in HBM: tern_quantize (fp32 weights -> codes + scales),
-tern_pack, tern_unpack, and tern_gemm (bf16 X times the packed ternary
-weights, fused scale epilogue).  The reported value is whole-step throughput
+already resident in HBM: tern_quantize_pack (fp32 weights -> codes, scales
+and packed bytes in one pass), tern_unpack, and tern_gemm (bf16 X times the
+packed ternary weights, fused scale epilogue); --separate-quantize runs
+tern_quantize and tern_pack as two calls instead.  The reported value is whole-step throughput
 in effective TFLOP/s, 2*M*N*K per step; the roofline object describes the
 dominant kernel (tern_gemm) measured with HIP events on the stream it is
 launched on; the CPU baseline is the oracle timed on this host on a bounded
 sample of the same step.
 
 After the timed steps, every layer shape of the five workloads is timed on its
-own ("rows"): tern_gemm per launch, as effective TFLOP/s, GB/s and the
-fraction of the bound that applies (MFMA or HBM).  The two few-token layers
+own ("rows"): tern_gemm per launch, and tern_gemm_ex with the bias and GELU
+of the layers that have them, as effective TFLOP/s, GB/s and the fraction of
+the bound that applies (MFMA or HBM).  The two few-token layers
 cycle through a pool of distinct packed weights larger than every cache, so
 that each launch streams its weights from HBM.
 
@@ -144,24 +146,45 @@ def roofline_of(flops, byts, seconds):
 
 
 def time_rows(tern, tern_inputs, torch, dev, reps, pool_mib):
-    """tern_gemm alone on every layer shape of the workloads (layer 0 inputs of
-    each shape).  Few-token shapes cycle through a pool of distinct packed
-    weights of at least pool_mib MiB (seeded normal weights quantized on the
-    GPU), one launch per pool entry."""
+    """The layer on every layer shape of the workloads (layer 0 inputs of each
+    shape): tern_gemm, and tern_gemm_ex where the layer's consumer applies a
+    bias and the tanh-form GELU (the MLP up-projections; the single-stream
+    in-projection, whose GELU covers only its MLP columns from 9216 on).
+    Few-token shapes cycle through a pool of distinct packed weights of at
+    least pool_mib MiB (seeded normal weights quantized on the GPU), one
+    launch per pool entry."""
     import statistics
-    shapes = [("single", tern_inputs.WORKLOADS["single"][0]),
-              ("flux_qkv", tern_inputs.WORKLOADS["flux_qkv"][0]),
-              ("flux_mlp.up", tern_inputs.WORKLOADS["flux_mlp"][0]),
-              ("flux_mlp.down", tern_inputs.WORKLOADS["flux_mlp"][1]),
-              ("flux_single_stream.in_proj", tern_inputs.WORKLOADS["flux_single_stream"][0]),
-              ("flux_single_stream.out_proj", tern_inputs.WORKLOADS["flux_single_stream"][1])]
-    shapes += [(l.name, l) for l in tern_inputs.WORKLOADS["dit"]]
+    W = tern_inputs.WORKLOADS
+    shapes = [("single", W["single"][0], None),
+              ("flux_qkv", W["flux_qkv"][0], None),
+              ("flux_mlp.up", W["flux_mlp"][0], None),
+              ("flux_mlp.up+gelu", W["flux_mlp"][0], (False, 0)),
+              ("flux_mlp.down", W["flux_mlp"][1], None),
+              ("flux_single_stream.in_proj", W["flux_single_stream"][0], None),
+              ("flux_single_stream.in_proj+bias+gelu[9216:]", W["flux_single_stream"][0],
+               (True, 9216)),
+              ("flux_single_stream.out_proj", W["flux_single_stream"][1], None)]
+    for l in W["dit"]:
+        shapes.append((l.name, l, None))
+        if ".up." in l.name:
+            shapes.append((l.name + "+bias+gelu", l, (True, 0)))
     rows = []
-    for name, layer in shapes:
+    for name, layer, epi in shapes:
         x, w = tern_inputs.draw_layer(layer)
         xd = x.to(dev)
         ldp = tern.packed_row_bytes(layer.k)
         y = torch.empty((layer.m, layer.n), dtype=torch.bfloat16, device=dev)
+        if epi is None:
+            def launch(p_i, s_i, xd=xd, y=y, k=layer.k):
+                tern.tern_gemm(xd, p_i, s_i, y, k)
+        else:
+            bias = None
+            if epi[0]:
+                gb = torch.Generator().manual_seed(layer.seed + 7)
+                bias = (torch.randn(layer.n, generator=gb) * 0.02).to(dev)
+
+            def launch(p_i, s_i, xd=xd, y=y, k=layer.k, bias=bias, act_from=epi[1]):
+                tern.tern_gemm_ex(xd, p_i, s_i, y, bias, tern.TERN_ACT_GELU_TANH, act_from, k)
         pool = layer.m <= 64 and layer.n * layer.k >= (1 << 20)
         if pool:
             per = layer.n * ldp + 4 * layer.n
@@ -182,7 +205,7 @@ def time_rows(tern, tern_inputs, torch, dev, reps, pool_mib):
             launches = reps
         for i in range(min(5, launches)):
             p_i, s_i = operands[i % len(operands)]
-            tern.tern_gemm(xd, p_i, s_i, y, layer.k)
+            launch(p_i, s_i)
         torch.cuda.synchronize()
         # Per-launch durations with events around each launch (they include
         # the host's submission gaps), and the same launches captured in a
@@ -192,7 +215,7 @@ def time_rows(tern, tern_inputs, torch, dev, reps, pool_mib):
         for i in range(launches):
             p_i, s_i = operands[i % len(operands)]
             ev[i][0].record()
-            tern.tern_gemm(xd, p_i, s_i, y, layer.k)
+            launch(p_i, s_i)
             ev[i][1].record()
         torch.cuda.synchronize()
         d = [a.elapsed_time(b) * 1e-3 for a, b in ev]
@@ -200,12 +223,12 @@ def time_rows(tern, tern_inputs, torch, dev, reps, pool_mib):
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
-            tern.tern_gemm(xd, operands[0][0], operands[0][1], y, layer.k)
+            launch(*operands[0])
         torch.cuda.current_stream().wait_stream(side)
         with torch.cuda.graph(graph):
             for i in range(launches):
                 p_i, s_i = operands[i % len(operands)]
-                tern.tern_gemm(xd, p_i, s_i, y, layer.k)
+                launch(p_i, s_i)
         graph.replay()
         torch.cuda.synchronize()
         g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -218,13 +241,18 @@ def time_rows(tern, tern_inputs, torch, dev, reps, pool_mib):
         med = statistics.median(d)
         flops = 2 * layer.m * layer.n * layer.k
         byts = gemm_alg_bytes(layer.m, layer.k, layer.n)
+        if epi is not None and epi[0]:
+            byts += 4 * layer.n  # the fp32 bias
         # The table's rate is the back-to-back (graph) time per launch unless
         # the event-bracketed median is lower.
         t = min(per_launch, med)
         row = {"layer": name, "m": layer.m, "k": layer.k, "n": layer.n,
                "launches": launches, "us_per_launch": t * 1e6,
                "graph_us_per_launch": per_launch * 1e6, "event_median_us": med * 1e6,
-               "event_min_us": min(d) * 1e6, "alg_flops": flops, "alg_bytes": byts}
+               "event_min_us": min(d) * 1e6, "alg_flops": flops, "alg_bytes": byts,
+               "entry": "tern_gemm" if epi is None else "tern_gemm_ex"}
+        if epi is not None:
+            row["epilogue"] = {"bias": bool(epi[0]), "act": "gelu_tanh", "act_from": epi[1]}
         row.update(roofline_of(flops, byts, t))
         if pool:
             row["weight_pool_mib"] = round(launches * per / 2**20, 1)
@@ -381,13 +409,30 @@ def main():
         torch.cuda.synchronize()
         kern_ms["tern_quantize"] = e[0].elapsed_time(e[1]) / reps
         kern_ms["tern_pack"] = e[1].elapsed_time(e[2]) / reps
+    # The fused conversion from bf16 weights (the 16-bit checkpoints the pages
+    # start from), on the first layer's weights rounded to bf16, same timing.
+    reps = 10
+    b0, l0 = bufs[0], layers[0]
+    w16 = b0["w"].to(torch.bfloat16)
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    tern.tern_gemm(b0["x"], b0["p"], b0["s"], b0["y"], l0.k)
+    e[0].record()
+    for _ in range(reps):
+        tern.tern_quantize_pack(w16, b0["t"], b0["p"], b0["s"])
+    e[1].record()
+    torch.cuda.synchronize()
+    kern_ms["tern_quantize_pack.bf16_w"] = e[0].elapsed_time(e[1]) / reps
+    del w16
 
     kernels = {}
     for nm in kern_ms:
         d = {"avg_ms": kern_ms[nm]}
         if nm in ("tern_quantize", "tern_pack"):
             d["in_step"] = bool(args.separate_quantize)
-        if nm == "tern_quantize_pack":
+        if nm == "tern_quantize_pack.bf16_w":
+            d["in_step"] = False
+            byts = l0.n * l0.k * 2 + l0.n * l0.k + l0.n * ((l0.k + 3) // 4) + 4 * l0.n
+        elif nm == "tern_quantize_pack":
             byts = sum(l.n * l.k * 4 + l.n * l.k + l.n * ((l.k + 3) // 4) + 4 * l.n
                        for l in layers) / len(layers)
         elif nm == "tern_quantize":

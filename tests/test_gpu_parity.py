@@ -26,7 +26,8 @@ tern = pytest.importorskip("ternary_weight_quantized_tern_amd")
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("n,k", [(1, 1), (3, 5), (7, 64), (33, 257), (64, 3072), (5, 32768),
-                                 (300, 1000), (2, 12289)])
+                                 (300, 1000), (2, 12289), (9, 3071), (6, 3073), (11, 1152),
+                                 (7, 4000)])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_quantize_pack_random(n, k, dtype):
     log(f"quantize n={n} k={k} {dtype}")
@@ -38,7 +39,8 @@ def test_quantize_pack_random(n, k, dtype):
 
 
 @pytest.mark.parametrize("n,k", [(1, 1), (3, 5), (7, 64), (33, 257), (64, 3072), (5, 32768),
-                                 (300, 1000), (2, 12289)])
+                                 (300, 1000), (2, 12289), (9, 3071), (6, 3073), (11, 1152),
+                                 (7, 4000)])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("with_t", [True, False])
 def test_quantize_pack_fused_random(n, k, dtype, with_t):
