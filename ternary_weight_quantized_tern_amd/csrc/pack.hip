@@ -8,13 +8,16 @@
 //
 // Both kernels are HBM-bound streams.  One thread handles one 16-weight group
 // (16 int8 <-> one 32-bit word of codes) with 16-byte int8 accesses when the
-// row pointer allows it; a grid-stride loop covers any n x k.
+// row pointer allows it; a grid-stride loop covers any n x k.  The flat group
+// index is split into (row, group) with 32-bit arithmetic whenever every index
+// the loop forms fits in 32 bits (all practical layer shapes), else 64-bit.
 #include "internal.h"
 
 namespace tern {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int64_t kMaxBlocks = 256 * 64;  // fills 256 CUs many times over
 
 __device__ inline bool aligned_dev(const void* p, uintptr_t a) {
   return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
@@ -34,16 +37,18 @@ __device__ inline uint32_t unpack4(uint32_t b) {
   return __builtin_amdgcn_perm(0u, 0xFFFE0100u, sel);
 }
 
+template <typename IDX>
 __global__ __launch_bounds__(kThreads) void pack_kernel(const int8_t* __restrict__ t, int64_t n,
                                                         int64_t k, int64_t ldt,
                                                         uint8_t* __restrict__ p, int64_t ldp) {
   const int64_t nbytes = (k + 3) / 4;
   const int64_t groups = (nbytes + 3) / 4;  // 16 weights per group
   const int64_t total = n * groups;
-  for (int64_t idx = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; idx < total;
-       idx += static_cast<int64_t>(gridDim.x) * kThreads) {
-    const int64_t row = idx / groups;
-    const int64_t g = idx - row * groups;
+  const IDX groups_i = static_cast<IDX>(groups);
+  for (IDX idx = static_cast<IDX>(blockIdx.x) * kThreads + threadIdx.x; idx < static_cast<IDX>(total);
+       idx += static_cast<IDX>(gridDim.x) * kThreads) {
+    const int64_t row = static_cast<int64_t>(idx / groups_i);
+    const int64_t g = static_cast<int64_t>(idx - static_cast<IDX>(row) * groups_i);
     const int64_t k0 = g * 16;
     const int8_t* src = t + row * ldt + k0;
     uint32_t d[4];
@@ -77,16 +82,18 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const int8_t* __restrict
   }
 }
 
+template <typename IDX>
 __global__ __launch_bounds__(kThreads) void unpack_kernel(const uint8_t* __restrict__ p, int64_t n,
                                                           int64_t k, int64_t ldp,
                                                           int8_t* __restrict__ t, int64_t ldt) {
   const int64_t nbytes = (k + 3) / 4;
   const int64_t groups = (nbytes + 3) / 4;
   const int64_t total = n * groups;
-  for (int64_t idx = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; idx < total;
-       idx += static_cast<int64_t>(gridDim.x) * kThreads) {
-    const int64_t row = idx / groups;
-    const int64_t g = idx - row * groups;
+  const IDX groups_i = static_cast<IDX>(groups);
+  for (IDX idx = static_cast<IDX>(blockIdx.x) * kThreads + threadIdx.x; idx < static_cast<IDX>(total);
+       idx += static_cast<IDX>(gridDim.x) * kThreads) {
+    const int64_t row = static_cast<int64_t>(idx / groups_i);
+    const int64_t g = static_cast<int64_t>(idx - static_cast<IDX>(row) * groups_i);
     const uint8_t* src = p + row * ldp + 4 * g;
     uint32_t word = 0;
     if (4 * g + 4 <= nbytes && aligned_dev(src, 4)) {
@@ -113,10 +120,15 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(const uint8_t* __restr
 
 inline unsigned grid_for(int64_t work_items) {
   int64_t blocks = (work_items + kThreads - 1) / kThreads;
-  const int64_t cap = 256 * 64;  // enough workgroups to fill 256 CUs many times over
-  if (blocks > cap) blocks = cap;
+  if (blocks > kMaxBlocks) blocks = kMaxBlocks;
   if (blocks < 1) blocks = 1;
   return static_cast<unsigned>(blocks);
+}
+
+// The loop's indices stay below total + (grid size) * kThreads, the grid
+// being at most kMaxBlocks workgroups.
+inline bool fits_u32(int64_t total) {
+  return total + kMaxBlocks * kThreads < (int64_t(1) << 32);
 }
 
 }  // namespace
@@ -124,16 +136,22 @@ inline unsigned grid_for(int64_t work_items) {
 hipError_t launch_pack(const int8_t* t, int64_t n, int64_t k, int64_t ldt, uint8_t* p,
                        int64_t ldp, hipStream_t stream) {
   const int64_t groups = ((k + 3) / 4 + 3) / 4;
-  hipLaunchKernelGGL(pack_kernel, dim3(grid_for(n * groups)), dim3(kThreads), 0, stream, t, n, k,
-                     ldt, p, ldp);
+  const dim3 grid(grid_for(n * groups));
+  if (fits_u32(n * groups))
+    hipLaunchKernelGGL(pack_kernel<uint32_t>, grid, dim3(kThreads), 0, stream, t, n, k, ldt, p, ldp);
+  else
+    hipLaunchKernelGGL(pack_kernel<uint64_t>, grid, dim3(kThreads), 0, stream, t, n, k, ldt, p, ldp);
   return hipGetLastError();
 }
 
 hipError_t launch_unpack(const uint8_t* p, int64_t n, int64_t k, int64_t ldp, int8_t* t,
                          int64_t ldt, hipStream_t stream) {
   const int64_t groups = ((k + 3) / 4 + 3) / 4;
-  hipLaunchKernelGGL(unpack_kernel, dim3(grid_for(n * groups)), dim3(kThreads), 0, stream, p, n,
-                     k, ldp, t, ldt);
+  const dim3 grid(grid_for(n * groups));
+  if (fits_u32(n * groups))
+    hipLaunchKernelGGL(unpack_kernel<uint32_t>, grid, dim3(kThreads), 0, stream, p, n, k, ldp, t, ldt);
+  else
+    hipLaunchKernelGGL(unpack_kernel<uint64_t>, grid, dim3(kThreads), 0, stream, p, n, k, ldp, t, ldt);
   return hipGetLastError();
 }
 

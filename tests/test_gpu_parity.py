@@ -137,6 +137,33 @@ def test_pack_unpack_ragged(k):
     assert np.all(th[:, k:] == 77)
 
 
+@pytest.mark.parametrize("k", [16, 16384, 16400, 50001, 65536])
+def test_pack_unpack_segments_vector_pitches(k):
+    # Rows of one to four 16384-weight segments with 16-byte row pitches (the
+    # vector paths), ragged last groups, and a row count that is not a
+    # multiple of anything; bytes and codes past the row stay untouched.
+    n = 7
+    t = tern_inputs.random_ternary(n, k, seed=k + 11).numpy()
+    p_ref = oracle.oracle_pack(t)
+    nb = (k + 3) // 4
+    ldp = (nb + 15) // 16 * 16 + 16
+    ldt = (k + 15) // 16 * 16 + 16
+    tpad = np.full((n, ldt), 5, dtype=np.int8)
+    tpad[:, :k] = t
+    tg = torch.from_numpy(tpad).to(DEV)[:, :k]
+    p = torch.full((n, ldp), 0xA5, dtype=torch.uint8, device=DEV)
+    tern.tern_pack(tg, p, k)
+    tout = torch.full((n, ldt), 77, dtype=torch.int8, device=DEV)
+    tern.tern_unpack(p, tout[:, :k], k)
+    torch.cuda.synchronize()
+    ph = p.cpu().numpy()
+    assert np.array_equal(ph[:, :nb], p_ref)
+    assert np.all(ph[:, nb:] == 0xA5)
+    th = tout.cpu().numpy()
+    assert np.array_equal(th[:, :k], t)
+    assert np.all(th[:, k:] == 77)
+
+
 def test_unpack_all_byte_values():
     allb = np.tile(np.arange(256, dtype=np.uint8), (3, 1))      # [3, 256] -> k = 1024
     t_ref = oracle.oracle_unpack(allb, 1024)
