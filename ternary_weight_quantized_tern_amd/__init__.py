@@ -23,9 +23,11 @@ from ._binding import (  # noqa: F401
     TernError,
     library,
     linear,
+    linear_ex,
     pack,
     packed_row_bytes,
     quantize,
+    quantize_pack,
     tern_gemm,
     tern_gemm_ex,
     tern_pack,

@@ -244,6 +244,17 @@ def pack(t: torch.Tensor, stream=None) -> torch.Tensor:
     return p
 
 
+def quantize_pack(w: torch.Tensor, with_codes: bool = False, stream=None):
+    """Full-precision weights ``w`` [n, k] -> ``(p, s)`` (packed codes and
+    scales) in one pass, or ``(t, p, s)`` with the int8 codes as well."""
+    n, k = w.shape
+    p = torch.zeros((n, packed_row_bytes(k)), dtype=torch.uint8, device=w.device)
+    s = torch.empty((n,), dtype=torch.float32, device=w.device)
+    t = torch.empty((n, k), dtype=torch.int8, device=w.device) if with_codes else None
+    tern_quantize_pack(w, t, p, s, stream)
+    return (t, p, s) if with_codes else (p, s)
+
+
 def unpack(p: torch.Tensor, k: int, stream=None) -> torch.Tensor:
     t = torch.empty((p.shape[0], k), dtype=torch.int8, device=p.device)
     tern_unpack(p, t, k, stream)
@@ -254,4 +265,14 @@ def linear(x: torch.Tensor, p: torch.Tensor, s: torch.Tensor, stream=None) -> to
     """Ternary linear layer: bf16 ``x`` [m, k] -> bf16 [m, n]."""
     y = torch.empty((x.shape[0], p.shape[0]), dtype=torch.bfloat16, device=x.device)
     tern_gemm(x, p, s, y, None, stream)
+    return y
+
+
+def linear_ex(x: torch.Tensor, p: torch.Tensor, s: torch.Tensor, bias: torch.Tensor | None = None,
+              gelu_from: int | None = None, stream=None) -> torch.Tensor:
+    """The layer with a fused epilogue: plus ``bias`` (fp32 [n]) if given, then
+    the tanh-form GELU on output columns ``>= gelu_from`` if given."""
+    y = torch.empty((x.shape[0], p.shape[0]), dtype=torch.bfloat16, device=x.device)
+    act = TERN_ACT_NONE if gelu_from is None else TERN_ACT_GELU_TANH
+    tern_gemm_ex(x, p, s, y, bias, act, 0 if gelu_from is None else int(gelu_from), None, stream)
     return y

@@ -323,6 +323,30 @@ def test_gemm_ex_k_zero_is_epilogue_of_bias():
     assert np.all(np.abs(yh - ref) <= 8e-3 * np.abs(ref) + 1e-6)
 
 
+def test_allocating_conveniences():
+    # quantize_pack and linear_ex allocate their outputs and call the same
+    # entry points: results bit-identical to the explicit calls.
+    x, w = tern_inputs.draw(64, 256, 96, seed=9)
+    xd, wd = x.to(DEV), w.to(DEV)
+    t, s = tern.quantize(wd)
+    p = tern.pack(t)
+    p2, s2 = tern.quantize_pack(wd)
+    t3, p3, s3 = tern.quantize_pack(wd, with_codes=True)
+    b = (torch.randn(96, generator=torch.Generator().manual_seed(5)) * 0.1).to(DEV)
+    y = tern.linear_ex(xd, p, s, bias=b, gelu_from=32)
+    y_ref = torch.empty_like(y)
+    tern.tern_gemm_ex(xd, p, s, y_ref, b, tern.TERN_ACT_GELU_TANH, 32)
+    y0 = tern.linear_ex(xd, p, s)
+    torch.cuda.synchronize()
+    nb = (256 + 3) // 4
+    assert torch.equal(p2[:, :nb], p[:, :nb]) and torch.equal(p3[:, :nb], p[:, :nb])
+    assert torch.equal(t3, t)
+    assert torch.equal(s2.view(torch.int32), s.view(torch.int32))
+    assert torch.equal(s3.view(torch.int32), s.view(torch.int32))
+    assert torch.equal(y, y_ref)
+    assert torch.equal(y0, tern.linear(xd, p, s))
+
+
 def test_gemm_ex_error_status():
     x = torch.zeros((4, 64), dtype=torch.bfloat16, device=DEV)
     p = torch.zeros((8, 16), dtype=torch.uint8, device=DEV)
