@@ -10,7 +10,10 @@ from .oracle import (  # noqa: F401
     library_path,
     oracle_epilogue,
     oracle_gemm,
+    oracle_gemm_dx,
     oracle_pack,
+    oracle_pack_transposed,
     oracle_quantize,
+    oracle_scale_grad,
     oracle_unpack,
 )

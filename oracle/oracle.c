@@ -22,6 +22,12 @@
  *  - An epilogue variant of that output: a per-channel bias and the
  *    tanh-form GELU on a trailing range of columns (oracle_epilogue; not on
  *    the pages: the activation of the FLUX MLP, the reading is stated there).
+ *  - The gradient of the layer with respect to its input, for training the
+ *    ternary weights in the loop ("TerDiT", abstract: quantization-aware
+ *    training of ternary DiTs; the pages give no formula): with
+ *    Y = (X . T^T) (.) s, dX = (dY (.) s) . T.  oracle_scale_grad forms the
+ *    scaled gradient u = bf16(dY (.) s) as a bf16 operand, oracle_gemm_dx the
+ *    unrounded sum over n of u . T (T in the forward's packed layout).
  *
  * Readings where the pages are silent (all listed in the design notes):
  *  - the mean is taken in 64-bit fixed point relative to the row's largest
@@ -272,3 +278,104 @@ int oracle_epilogue(double* y, int64_t m, int64_t n, int64_t ldy, const float* b
   return ORACLE_OK;
 }
 
+/*
+ * Scaled output gradient, the operand of the input gradient:
+ *
+ *   u[m][n] = bf16( fp32(dy[m][n]) * s[n] )
+ *
+ * one IEEE single-precision product (round to nearest even), then one
+ * rounding to bf16, to nearest with ties to even.  The bf16 rounding keeps
+ * the upper 16 bits of the single-precision pattern after adding 0x7FFF plus
+ * the lowest kept bit (finite values; a carry into the exponent is the
+ * correct rounding up, to infinity at the top).
+ */
+static uint16_t float_to_bf16_rne(float f) {
+  uint32_t b;
+  memcpy(&b, &f, sizeof b);
+  const uint32_t lsb = (b >> 16) & 1u;
+  return (uint16_t)((b + 0x7FFFu + lsb) >> 16);
+}
+
+int oracle_scale_grad(const uint16_t* dy, int64_t m, int64_t n, int64_t lddy, const float* s,
+                      uint16_t* u, int64_t ldu) {
+  if (m < 0 || n < 0 || lddy < n || ldu < n) return ORACLE_BAD_ARG;
+  for (int64_t mm = 0; mm < m; ++mm)
+    for (int64_t nn = 0; nn < n; ++nn) {
+      const float prod = bf16_bits_to_float(dy[mm * lddy + nn]) * s[nn];
+      u[mm * ldu + nn] = float_to_bf16_rne(prod);
+    }
+  return ORACLE_OK;
+}
+
+/*
+ * Input gradient, unrounded: dx[m][k] = sum_{n ascending} u[m][n] * T[n][k],
+ * u the bf16 scaled gradient widened exactly, T decoded from the forward's
+ * packed bytes (row n, packed along k), the sum in double.  Threads split the
+ * output columns k; each thread decodes, for its columns, the whole column of
+ * T once and runs it against every gradient row.
+ */
+typedef struct {
+  const double* ud;  /* m x n, widened scaled gradient */
+  int64_t m, n;
+  const uint8_t* p;
+  int64_t ldp;
+  double* dx;
+  int64_t lddx;
+  int64_t k_begin, k_end;
+} dx_job;
+
+static void* dx_worker(void* arg) {
+  dx_job* j = (dx_job*)arg;
+  int8_t* tcol = (int8_t*)malloc((size_t)(j->n > 0 ? j->n : 1));
+  if (!tcol) return (void*)1;
+  for (int64_t kk = j->k_begin; kk < j->k_end; ++kk) {
+    for (int64_t nn = 0; nn < j->n; ++nn) {
+      unsigned code = (j->p[nn * j->ldp + kk / 4] >> (2 * (kk % 4))) & 3u;
+      tcol[nn] = (int8_t)decode_code(code);
+    }
+    for (int64_t mm = 0; mm < j->m; ++mm) {
+      const double* ur = j->ud + mm * j->n;
+      double acc = 0.0;
+      for (int64_t nn = 0; nn < j->n; ++nn) acc += ur[nn] * (double)tcol[nn];
+      j->dx[mm * j->lddx + kk] = acc;
+    }
+  }
+  free(tcol);
+  return NULL;
+}
+
+int oracle_gemm_dx(const uint16_t* u, int64_t m, int64_t n, int64_t ldu, const uint8_t* p,
+                   int64_t k, int64_t ldp, double* dx, int64_t lddx, int nthreads) {
+  if (m < 0 || n < 0 || k < 0 || ldu < n || ldp < (k + 3) / 4 || lddx < k) return ORACLE_BAD_ARG;
+  if (m == 0 || k == 0) return ORACLE_OK;
+  double* ud = (double*)malloc((size_t)(m * (n > 0 ? n : 1)) * sizeof(double));
+  if (!ud) return ORACLE_BAD_ARG;
+  for (int64_t mm = 0; mm < m; ++mm)
+    for (int64_t nn = 0; nn < n; ++nn) ud[mm * n + nn] = (double)bf16_bits_to_float(u[mm * ldu + nn]);
+
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > k) nthreads = (int)k;
+  pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nthreads);
+  dx_job* jobs = (dx_job*)malloc(sizeof(dx_job) * (size_t)nthreads);
+  int rc = ORACLE_OK;
+  if (!th || !jobs) rc = ORACLE_BAD_ARG;
+  int started = 0;
+  for (int i = 0; rc == ORACLE_OK && i < nthreads; ++i) {
+    dx_job jb = {ud, m, n, p, ldp, dx, lddx, k * i / nthreads, k * (i + 1) / nthreads};
+    jobs[i] = jb;
+    if (pthread_create(&th[i], NULL, dx_worker, &jobs[i]) != 0) {
+      rc = ORACLE_BAD_ARG;
+      break;
+    }
+    ++started;
+  }
+  for (int i = 0; i < started; ++i) {
+    void* ret = NULL;
+    pthread_join(th[i], &ret);
+    if (ret != NULL) rc = ORACLE_BAD_ARG;
+  }
+  free(jobs);
+  free(th);
+  free(ud);
+  return rc;
+}

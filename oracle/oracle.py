@@ -54,8 +54,10 @@ def load(path: str | None = None):
     lib.oracle_unpack.argtypes = [vp, i64, i64, i64, vp, i64]
     lib.oracle_gemm.argtypes = [vp, i64, i64, i64, vp, i64, i64, vp, vp, i64, ctypes.c_int]
     lib.oracle_epilogue.argtypes = [vp, i64, i64, i64, vp, ctypes.c_int, i64]
+    lib.oracle_scale_grad.argtypes = [vp, i64, i64, i64, vp, vp, i64]
+    lib.oracle_gemm_dx.argtypes = [vp, i64, i64, i64, vp, i64, i64, vp, i64, ctypes.c_int]
     for f in (lib.oracle_quantize, lib.oracle_pack, lib.oracle_unpack, lib.oracle_gemm,
-              lib.oracle_epilogue):
+              lib.oracle_epilogue, lib.oracle_scale_grad, lib.oracle_gemm_dx):
         f.restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -156,3 +158,43 @@ def oracle_epilogue(y: np.ndarray, bias: np.ndarray | None = None, act: int = AC
                                int(act_from)), "oracle_epilogue")
     return out
 
+
+def oracle_pack_transposed(p: np.ndarray, n: int, k: int, lib=None) -> np.ndarray:
+    """The codes of packed weights ``p`` (rows n, packed along k) packed along n
+    instead: uint8 ``[K, ceil(N/4)]`` whose row k holds T[0..N-1, k]."""
+    t = oracle_unpack(np.ascontiguousarray(p)[:n], k, lib=lib)
+    return oracle_pack(np.ascontiguousarray(t.T), lib=lib)
+
+
+def oracle_scale_grad(dy_bf16_bits: np.ndarray, s: np.ndarray, lib=None) -> np.ndarray:
+    """``u = bf16(fp32(dy) * s_n)`` (single-precision product, then round to
+    nearest even) as uint16 bf16 bit patterns ``[M, N]``."""
+    lib = lib or load()
+    dy = np.ascontiguousarray(dy_bf16_bits, dtype=np.uint16)
+    s = np.ascontiguousarray(s, dtype=np.float32)
+    m, n = dy.shape
+    if s.shape != (n,):
+        raise ValueError("s must have one entry per gradient column")
+    u = np.empty((m, n), np.uint16)
+    _check(lib.oracle_scale_grad(_ptr(dy), m, n, n, _ptr(s), _ptr(u), n), "oracle_scale_grad")
+    return u
+
+
+def oracle_gemm_dx(u_bf16_bits: np.ndarray, p: np.ndarray, k: int, n: int | None = None,
+                   nthreads: int | None = None, lib=None) -> np.ndarray:
+    """Unrounded input gradient ``dx[m,k] = sum_n u[m,n] * T[n,k]`` in float64
+    ``[M, K]``; ``p`` the forward's packed weights (rows n, packed along k)."""
+    lib = lib or load()
+    u = np.ascontiguousarray(u_bf16_bits, dtype=np.uint16)
+    p = np.ascontiguousarray(p, dtype=np.uint8)
+    m, nu = u.shape
+    n = nu if n is None else n
+    if p.shape[0] < n:
+        raise ValueError("p must have a row per gradient column")
+    ldp = p.shape[1]
+    dx = np.empty((m, k), np.float64)
+    if nthreads is None:
+        nthreads = len(os.sched_getaffinity(0))
+    _check(lib.oracle_gemm_dx(_ptr(u), m, n, nu, _ptr(p), k, ldp, _ptr(dx), k, nthreads),
+           "oracle_gemm_dx")
+    return dx

@@ -378,6 +378,83 @@ def test_epilogue_rejects_bad_arguments():
 
 
 # --------------------------------------------------------------------------
+# input gradient: u = bf16(dy * s), dx = u . T, and the transposed packing
+# --------------------------------------------------------------------------
+
+def _bf16_bits(a):
+    return tern_inputs.bf16_bits(torch.as_tensor(a, dtype=torch.float32).to(torch.bfloat16))
+
+
+def _from_bf16_bits(b):
+    return (np.asarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def test_scale_grad_matches_torch_single_product_then_bf16():
+    # library routine: torch's float32 product, then its round-to-nearest-even
+    # conversion to bfloat16
+    g = torch.Generator().manual_seed(21)
+    dy = (torch.randn(37, 53, generator=g) * 3).to(torch.bfloat16)
+    s = torch.rand(53, generator=g) * 0.05 + 1e-4
+    ref = tern_inputs.bf16_bits((dy.float() * s).to(torch.bfloat16))
+    got = oracle.oracle_scale_grad(tern_inputs.bf16_bits(dy), s.numpy())
+    assert np.array_equal(got, ref)
+
+
+def test_scale_grad_ties_to_even():
+    # 1 * (1 + 2^-8) lies half-way between bf16 1 and 1 + 2^-7: the even one (1);
+    # 1 * (1 + 3 * 2^-8) half-way between 1 + 2^-7 and 1 + 2^-6: the even one
+    # (1 + 2^-6); -1 * (1 + 2^-8) rounds to -1 likewise
+    dy = _bf16_bits([[1.0, 1.0, -1.0, 2.0]])
+    s = np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, 1 + 2.0 ** -8, 0.75], np.float32)
+    got = oracle.oracle_scale_grad(dy, s)
+    assert got.tolist() == [[0x3F80, 0x3F82, 0xBF80, 0x3FC0]]
+
+
+def test_gemm_dx_adjoint_of_the_layer_exact():
+    # <dY, X T^T (.) s> = <(dY (.) s) T, X> exactly, with small integer X and
+    # dY and power-of-two scales (every product and sum exact in double)
+    rng = np.random.default_rng(8)
+    m, k, n = 7, 72, 40
+    x = rng.integers(-4, 5, size=(m, k)).astype(np.float32)
+    dy = rng.integers(-3, 4, size=(m, n)).astype(np.float32)
+    s = (2.0 ** rng.integers(-3, 4, size=n)).astype(np.float32)
+    t = rng.integers(-1, 2, size=(n, k)).astype(np.int8)
+    p = oracle.oracle_pack(t)
+    y = oracle.oracle_gemm(_bf16_bits(x), p, s)
+    u = oracle.oracle_scale_grad(_bf16_bits(dy), s)
+    assert np.array_equal(_from_bf16_bits(u), dy.astype(np.float64) * s)
+    dx = oracle.oracle_gemm_dx(u, p, k)
+    assert float((dy.astype(np.float64) * y).sum()) == float((dx * x.astype(np.float64)).sum())
+
+
+def test_gemm_dx_equals_numpy_matmul():
+    # exact on small-integer operands; to rounding on random bf16 operands
+    rng = np.random.default_rng(9)
+    m, k, n = 5, 33, 70
+    t = rng.integers(-1, 2, size=(n, k)).astype(np.int8)
+    p = oracle.oracle_pack(t)
+    ui = rng.integers(-8, 9, size=(m, n)).astype(np.float32)
+    dx = oracle.oracle_gemm_dx(_bf16_bits(ui), p, k)
+    assert np.array_equal(dx, ui.astype(np.float64) @ t.astype(np.float64))
+    ur = _bf16_bits(rng.normal(size=(m, n)))
+    dx = oracle.oracle_gemm_dx(ur, p, k)
+    assert np.allclose(dx, _from_bf16_bits(ur) @ t.astype(np.float64), rtol=1e-12, atol=1e-12)
+
+
+def test_pack_transposed_worked_example():
+    # T (5 x 2): column 0 = (1, 0, -1, 1, -1) -> codes 01 00 11 01 | 11 ->
+    # bytes 0x71 0x03; column 1 = (-1, 1, 0, 1, -1) -> 11 01 00 01 | 11 ->
+    # bytes 0x47 0x03
+    t = np.array([[1, -1], [0, 1], [-1, 0], [1, 1], [-1, -1]], np.int8)
+    pt = oracle.oracle_pack_transposed(oracle.oracle_pack(t), 5, 2)
+    assert pt.tolist() == [[0x71, 0x03], [0x47, 0x03]]
+    rng = np.random.default_rng(10)
+    t = rng.integers(-1, 2, size=(37, 29)).astype(np.int8)
+    pt = oracle.oracle_pack_transposed(oracle.oracle_pack(t), 37, 29)
+    assert np.array_equal(oracle.oracle_unpack(pt, 37), t.T)
+
+
+# --------------------------------------------------------------------------
 # mutation check: the pins above must catch plausible mistakes in the oracle
 # --------------------------------------------------------------------------
 
@@ -402,6 +479,16 @@ MUTANTS = {
     "gelu_inverted_sqrt": ("sqrt(2.0 / pi)", "sqrt(pi / 2.0)"),
     "epilogue_act_from_off_by_one": ("nn >= act_from", "nn > act_from"),
     "epilogue_bias_dropped": ("if (bias) v += (double)bias[nn];", "if (bias) v += 0.0;"),
+    "scale_grad_truncates": ("(b + 0x7FFFu + lsb) >> 16", "b >> 16"),
+    "scale_grad_ties_away": ("(b + 0x7FFFu + lsb) >> 16", "(b + 0x8000u) >> 16"),
+    "scale_grad_unscaled": ("bf16_bits_to_float(dy[mm * lddy + nn]) * s[nn]",
+                            "bf16_bits_to_float(dy[mm * lddy + nn])"),
+    "dx_drops_last_n": ("for (int64_t nn = 0; nn < j->n; ++nn) acc +=",
+                        "for (int64_t nn = 0; nn + 1 < j->n; ++nn) acc +="),
+    "dx_wrong_column": ("(j->p[nn * j->ldp + kk / 4] >> (2 * (kk % 4)))",
+                        "(j->p[nn * j->ldp + (kk ^ 1) / 4] >> (2 * ((kk ^ 1) % 4)))"),
+    "dx_wrong_row": ("const double* ur = j->ud + mm * j->n;",
+                     "const double* ur = j->ud + ((mm + 1) % j->m) * j->n;"),
 }
 
 PIN_TESTS = [
@@ -413,6 +500,9 @@ PIN_TESTS = [
     test_gemm_equals_float64_matmul_on_exact_inputs, test_gemm_against_numpy_on_random_data,
     test_epilogue_gelu_equals_torch_tanh_gelu, test_epilogue_gelu_close_to_exact_gelu,
     test_epilogue_gelu_odd_part_is_identity, test_epilogue_bias_and_activated_columns,
+    test_scale_grad_matches_torch_single_product_then_bf16, test_scale_grad_ties_to_even,
+    test_gemm_dx_adjoint_of_the_layer_exact, test_gemm_dx_equals_numpy_matmul,
+    test_pack_transposed_worked_example,
 ]
 
 
