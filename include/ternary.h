@@ -192,6 +192,62 @@ tern_status tern_gemm_ex(const void* x_bf16, int64_t m, int64_t k, int64_t ldx, 
 /* Static, never-NULL description of a status code. */
 const char* tern_status_string(tern_status status);
 
+/*
+ * Training in the loop ("TerDiT: Ternary Diffusion Models with Transformers",
+ * abstract: quantization-aware training of ternary DiT weights; the pages
+ * give no formula).  For the layer Y = (X . T^T) (.) s the gradient with
+ * respect to its input is dX = (dY (.) s) . T, a ternary GEMM that contracts
+ * over the output channels n.  The codes are used packed along n for it.
+ */
+
+/*
+ * tern_pack_transposed: the codes of packed weights re-packed along n.
+ *
+ *   p   [n, ldp] uint8 input, packed as tern_pack writes it for a row length
+ *       k (row n holds T[n][0..k-1])
+ *   pt  [k, ldpt] uint8 output: row k holds T[0..n-1][k], four codes per
+ *       byte, code n in bits 2(n%4) .. 2(n%4)+1 of byte n/4 (the tern_pack
+ *       layout with the roles of n and k exchanged); fields past n in the
+ *       last byte are 00, bytes from ceil(n/4) to ldpt-1 are left untouched
+ * Sizes: 0 <= n, k <= 2^31 - 1 (else TERN_ERR_SHAPE); a zero size is a no-op.
+ * ldp >= ceil(k/4), ldpt >= ceil(n/4) (else TERN_ERR_STRIDE).  p and pt must
+ * not be NULL (TERN_ERR_NULL).
+ */
+tern_status tern_pack_transposed(const uint8_t* p, int64_t n, int64_t k, int64_t ldp, uint8_t* pt,
+                                 int64_t ldpt, void* stream);
+
+/*
+ * tern_gemm_dx: the input gradient of the ternary layer.
+ *
+ *   u[m][j]  = bf16( fp32(dy[m][j]) * s[j] )          (round to nearest even)
+ *   dx[m][c] = bf16( sum_j u[m][j] * T[j][c] )
+ *
+ * the sum over the n output channels j of the forward layer in fp32 in an
+ * unspecified order, with one round-to-nearest-even conversion at the end.
+ *
+ *   dy  [m, lddy] bf16 gradient of the layer's output Y (m tokens, n channels)
+ *   pt  [k, ldpt] the layer's codes packed along n, as tern_pack_transposed
+ *       writes them (k = the layer's input width)
+ *   s   [n] fp32 the layer's per-channel scales
+ *   u   [m, ldu] bf16 workspace, owned by the caller and overwritten with the
+ *       scaled gradient (it may be read afterwards)
+ *   dx  [m, lddx] bf16 output; columns >= k untouched
+ * Sizes: m, n, k >= 0 and n % 64 == 0 (else TERN_ERR_SHAPE); m == 0 or
+ * k == 0 is a no-op; n == 0 writes zeros.  m, k <= 2^31 - 1,
+ * n <= 2^31 - 64, ceil(m/256) * ceil(k/256) <= 2^31 - 1.
+ * lddy >= n, ldu >= n, ldpt >= n/4, lddx >= k, and ldu < 2^23, ldpt < 2^24,
+ * lddx < 2^31 (else TERN_ERR_STRIDE).  pt and dx must not be NULL, nor dy, s
+ * and u unless n == 0 (TERN_ERR_NULL).  Alignment (else TERN_ERR_ALIGN): u
+ * and pt 16-byte aligned, ldu % 8 == 0, ldpt % 16 == 0; dy and dx 2-byte
+ * aligned; s 4-byte aligned; with n == 0 the rules on dy, s, u and ldu (not
+ * read then) do not apply.  u must not overlap dy, pt, s or dx.  Two
+ * launches on `stream`: the scaling, then the product (the kernels of
+ * tern_gemm with unit scales).
+ */
+tern_status tern_gemm_dx(const void* dy_bf16, int64_t m, int64_t n, int64_t lddy,
+                         const uint8_t* pt, int64_t k, int64_t ldpt, const float* s,
+                         void* u_bf16, int64_t ldu, void* dx_bf16, int64_t lddx, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -23,14 +23,18 @@ from ._binding import (  # noqa: F401
     TernError,
     library,
     linear,
+    linear_dx,
     linear_ex,
     pack,
+    pack_transposed,
     packed_row_bytes,
     quantize,
     quantize_pack,
     tern_gemm,
+    tern_gemm_dx,
     tern_gemm_ex,
     tern_pack,
+    tern_pack_transposed,
     tern_quantize,
     tern_quantize_pack,
     tern_status_string,

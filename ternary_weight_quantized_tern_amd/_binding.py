@@ -33,7 +33,7 @@ TERN_BF16 = 1
 TERN_QUANTIZE_MAX_K = 32768
 
 EXPORTED = ("tern_quantize", "tern_quantize_pack", "tern_pack", "tern_unpack", "tern_gemm",
-            "tern_gemm_ex", "tern_status_string")
+            "tern_gemm_ex", "tern_pack_transposed", "tern_gemm_dx", "tern_status_string")
 
 
 class TernError(RuntimeError):
@@ -58,8 +58,10 @@ def _load(path: str):
     lib.tern_gemm.argtypes = [vp, i64, i64, i64, vp, i64, i64, vp, vp, i64, vp]
     lib.tern_gemm_ex.argtypes = [vp, i64, i64, i64, vp, i64, i64, vp, vp, ctypes.c_int, i64, vp,
                                  i64, vp]
+    lib.tern_pack_transposed.argtypes = [vp, i64, i64, i64, vp, i64, vp]
+    lib.tern_gemm_dx.argtypes = [vp, i64, i64, i64, vp, i64, i64, vp, vp, i64, vp, i64, vp]
     for name in ("tern_quantize", "tern_quantize_pack", "tern_pack", "tern_unpack", "tern_gemm",
-                 "tern_gemm_ex"):
+                 "tern_gemm_ex", "tern_pack_transposed", "tern_gemm_dx"):
         getattr(lib, name).restype = ctypes.c_int
     lib.tern_status_string.argtypes = [ctypes.c_int]
     lib.tern_status_string.restype = ctypes.c_char_p
@@ -219,6 +221,40 @@ def tern_gemm_ex(x: torch.Tensor, p: torch.Tensor, s: torch.Tensor, y: torch.Ten
                                              y.data_ptr(), ldy, _stream(stream)))
 
 
+def tern_pack_transposed(p: torch.Tensor, pt: torch.Tensor, n: int | None = None,
+                         k: int | None = None, stream=None) -> None:
+    """Re-pack the codes of ``p`` uint8 [n, >=ceil(k/4)] (packed along k) along n
+    into ``pt`` uint8 [k, >=ceil(n/4)]; n defaults to p's rows, k to pt's rows."""
+    ldp = _mat(p, "p", (torch.uint8,))
+    ldpt = _mat(pt, "pt", (torch.uint8,))
+    n = p.shape[0] if n is None else int(n)
+    k = pt.shape[0] if k is None else int(k)
+    if n > p.shape[0] or k > pt.shape[0] or p.shape[1] < (k + 3) // 4 or pt.shape[1] < (n + 3) // 4:
+        raise ValueError("p must be [>=n, >=ceil(k/4)] and pt [>=k, >=ceil(n/4)]")
+    _check("tern_pack_transposed",
+           _lib.tern_pack_transposed(p.data_ptr(), n, k, ldp, pt.data_ptr(), ldpt, _stream(stream)))
+
+
+def tern_gemm_dx(dy: torch.Tensor, pt: torch.Tensor, s: torch.Tensor, u: torch.Tensor,
+                 dx: torch.Tensor, k: int | None = None, stream=None) -> None:
+    """Input gradient of the layer: ``u = bf16(dy * s)`` into the workspace ``u``
+    (bf16 [m, >=n]), then ``dx = bf16(u . T)`` with ``pt`` the codes packed
+    along n (uint8 [k, >=n/4]); dy bf16 [m, n], s fp32 [n], dx bf16 [m, >=k]."""
+    lddy = _mat(dy, "dy", (torch.bfloat16,))
+    ldpt = _mat(pt, "pt", (torch.uint8,))
+    ldu = _mat(u, "u", (torch.bfloat16,))
+    lddx = _mat(dx, "dx", (torch.bfloat16,))
+    _vec(s, "s", torch.float32)
+    m, n = dy.shape
+    k = pt.shape[0] if k is None else int(k)
+    if (s.shape[0] != n or k > pt.shape[0] or pt.shape[1] < n // 4 or tuple(u.shape[:1]) != (m,)
+            or u.shape[1] < n or tuple(dx.shape[:1]) != (m,) or dx.shape[1] < k):
+        raise ValueError("shapes must be dy [m, n], pt [>=k, >=n/4], s [n], u [m, >=n], dx [m, >=k]")
+    _check("tern_gemm_dx", _lib.tern_gemm_dx(dy.data_ptr(), m, n, lddy, pt.data_ptr(), k, ldpt,
+                                             s.data_ptr(), u.data_ptr(), ldu, dx.data_ptr(), lddx,
+                                             _stream(stream)))
+
+
 # ---------------------------------------------------------------------------
 # allocating conveniences (torch allocates the outputs; the library computes)
 # ---------------------------------------------------------------------------
@@ -276,3 +312,20 @@ def linear_ex(x: torch.Tensor, p: torch.Tensor, s: torch.Tensor, bias: torch.Ten
     act = TERN_ACT_NONE if gelu_from is None else TERN_ACT_GELU_TANH
     tern_gemm_ex(x, p, s, y, bias, act, 0 if gelu_from is None else int(gelu_from), None, stream)
     return y
+
+
+def pack_transposed(p: torch.Tensor, n: int, k: int, stream=None) -> torch.Tensor:
+    """The codes of packed weights ``p`` (n rows, row length k) packed along n:
+    uint8 [k, ceil(n/4) rounded up to 16]."""
+    pt = torch.zeros((k, packed_row_bytes(n)), dtype=torch.uint8, device=p.device)
+    tern_pack_transposed(p, pt, n, k, stream)
+    return pt
+
+
+def linear_dx(dy: torch.Tensor, pt: torch.Tensor, s: torch.Tensor, k: int, stream=None):
+    """Input gradient ``bf16((dy * s) . T)`` [m, k] of the layer; ``pt`` from
+    pack_transposed.  Allocates the bf16 workspace for the scaled gradient."""
+    u = torch.empty_like(dy, memory_format=torch.contiguous_format)
+    dx = torch.empty((dy.shape[0], k), dtype=torch.bfloat16, device=dy.device)
+    tern_gemm_dx(dy, pt, s, u, dx, k, stream)
+    return dx

@@ -106,6 +106,46 @@ tern_status tern_gemm_ex(const void* x_bf16, int64_t m, int64_t k, int64_t ldx, 
                      act == TERN_ACT_GELU_TANH ? act_from : n, y_bf16, ldy, stream);
 }
 
+tern_status tern_pack_transposed(const uint8_t* p, int64_t n, int64_t k, int64_t ldp, uint8_t* pt,
+                                 int64_t ldpt, void* stream) {
+  if (n < 0 || k < 0 || n > kMaxInt || k > kMaxInt) return TERN_ERR_SHAPE;
+  if (n == 0 || k == 0) return TERN_OK;
+  if (p == nullptr || pt == nullptr) return TERN_ERR_NULL;
+  if (ldp < (k + 3) / 4 || ldpt < (n + 3) / 4) return TERN_ERR_STRIDE;
+  return from_hip(
+      tern::launch_pack_transposed(p, n, k, ldp, pt, ldpt, static_cast<hipStream_t>(stream)));
+}
+
+tern_status tern_gemm_dx(const void* dy_bf16, int64_t m, int64_t n, int64_t lddy,
+                         const uint8_t* pt, int64_t k, int64_t ldpt, const float* s,
+                         void* u_bf16, int64_t ldu, void* dx_bf16, int64_t lddx, void* stream) {
+  // The product is the layer's GEMM with the roles renamed: u [m, n] is the
+  // activation operand, pt (rows k, packed along n) the weights, n the
+  // contraction and k the output width; unit scales.
+  if (m < 0 || n < 0 || k < 0 || m > kMaxInt || k > kMaxInt || n > kMaxInt - 63 || n % 64 != 0)
+    return TERN_ERR_SHAPE;
+  if (((m + 255) / 256) * ((k + 255) / 256) > kMaxInt) return TERN_ERR_SHAPE;
+  if (m == 0 || k == 0) return TERN_OK;
+  // With n == 0 the gradient, the scales and the workspace are not read.
+  if (pt == nullptr || dx_bf16 == nullptr ||
+      (n > 0 && (dy_bf16 == nullptr || s == nullptr || u_bf16 == nullptr)))
+    return TERN_ERR_NULL;
+  if (lddy < n || ldu < n || ldpt < n / 4 || lddx < k) return TERN_ERR_STRIDE;
+  if ((n > 0 && ldu > kGemmMaxLdx) || ldpt > kGemmMaxLdp || lddx > kMaxInt) return TERN_ERR_STRIDE;
+  if (!aligned(pt, 16) || ldpt % 16 != 0 || !aligned(dx_bf16, 2)) return TERN_ERR_ALIGN;
+  if (n > 0 && (!aligned(dy_bf16, 2) || !aligned(u_bf16, 16) || ldu % 8 != 0 || !aligned(s, 4)))
+    return TERN_ERR_ALIGN;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  uint16_t* u = static_cast<uint16_t*>(u_bf16);
+  if (n > 0) {
+    const hipError_t e =
+        tern::launch_scale_grad(static_cast<const uint16_t*>(dy_bf16), m, n, lddy, s, u, ldu, st);
+    if (e != hipSuccess) return TERN_ERR_HIP;
+  }
+  return from_hip(tern::launch_gemm(u, m, n, ldu, pt, k, ldpt, nullptr, nullptr, k,
+                                    static_cast<uint16_t*>(dx_bf16), lddx, st));
+}
+
 const char* tern_status_string(tern_status status) {
   switch (status) {
     case TERN_OK: return "TERN_OK: success";

@@ -439,7 +439,8 @@ void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
       f32x4_t sc[kTN];
 #pragma unroll
       for (int j = 0; j < kTN; ++j)
-        sc[j] = *reinterpret_cast<const f32x4_t*>(s + col0 + 16 * j + 4 * g) * 0.5f;
+        sc[j] = s != nullptr ? *reinterpret_cast<const f32x4_t*>(s + col0 + 16 * j + 4 * g) * 0.5f
+                             : f32x4_t{0.5f, 0.5f, 0.5f, 0.5f};
       const bool act_all = col0 >= act_from;
       const bool act_none = col0 + C::kWN <= act_from;
       f32x4_t bsv[EPI ? kTN : 1];
@@ -540,7 +541,7 @@ void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
         const int ng = n0 + wn * C::kWN + 16 * j + 4 * g;
         float sc[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sc[e] = (ng + e < n) ? s[ng + e] : 0.0f;
+        for (int e = 0; e < 4; ++e) sc[e] = (ng + e < n) ? (s != nullptr ? s[ng + e] : 1.0f) : 0.0f;
         float bv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         if constexpr (EPI) {
 #pragma unroll
@@ -601,6 +602,11 @@ void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
   lds_barrier();
   TERN_GEMM_READ_A(lds0)
   decode_lo_all();
+  // The first MFMA reads wa right after this decode: two wait states (the
+  // schedule of the loop keeps every other decode far from its MFMA).
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 1");
+  __builtin_amdgcn_sched_barrier(0);
 
   if constexpr (PERSIST) {
     for (int t = 0; t < my_tiles; ++t) {

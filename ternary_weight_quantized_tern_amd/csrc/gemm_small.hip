@@ -114,7 +114,7 @@ __global__ __launch_bounds__(kSmallThreads) void gemm_ternary_small(
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int nc = n0 + 16 * bl + 4 * g + e;
-      sc[bl][e] = nc < n ? s[nc] * 0.5f : 0.0f;
+      sc[bl][e] = nc < n ? (s != nullptr ? s[nc] : 1.0f) * 0.5f : 0.0f;
     }
   float bsv[EPI ? B : 1][4];
   if constexpr (EPI) {

@@ -23,7 +23,8 @@ hipError_t launch_pack(const int8_t* t, int64_t n, int64_t k, int64_t ldt, uint8
 hipError_t launch_unpack(const uint8_t* p, int64_t n, int64_t k, int64_t ldp, int8_t* t,
                          int64_t ldt, hipStream_t stream);
 
-// bias: nullptr or [n]; act_from in [0, n]: the tanh-form GELU is applied to
+// s: [n], or nullptr for unit scales (the input-gradient product); bias:
+// nullptr or [n]; act_from in [0, n]: the tanh-form GELU is applied to
 // columns >= act_from (act_from == n: no activation).
 hipError_t launch_gemm(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const uint8_t* p,
                        int64_t n, int64_t ldp, const float* s, const float* bias,
@@ -34,5 +35,13 @@ hipError_t launch_gemm_small(const uint16_t* x, int64_t m, int64_t k, int64_t ld
                              const uint8_t* p, int64_t n, int64_t ldp, const float* s,
                              const float* bias, int64_t act_from, uint16_t* y, int64_t ldy,
                              hipStream_t stream);
+
+// Codes of p (rows n, packed along k) packed along n into pt (rows k).
+hipError_t launch_pack_transposed(const uint8_t* p, int64_t n, int64_t k, int64_t ldp,
+                                  uint8_t* pt, int64_t ldpt, hipStream_t stream);
+
+// u = bf16(fp32(dy) * s[col]) for an m x n bf16 matrix.
+hipError_t launch_scale_grad(const uint16_t* dy, int64_t m, int64_t n, int64_t lddy,
+                             const float* s, uint16_t* u, int64_t ldu, hipStream_t stream);
 
 }  // namespace tern

@@ -241,3 +241,57 @@ def check_layer_ex(x_cpu, w_cpu, bias, act, act_from, what, rows=None, cols=None
                 what=what + " (cols)"))
     return worst
 
+
+# ---------------------------------------------------------------------------
+# input gradient (tern_gemm_dx) and the codes packed along n
+# ---------------------------------------------------------------------------
+
+def draw_grad(m: int, n: int, seed: int) -> torch.Tensor:
+    """Seeded bf16 output gradient dY [m, n] ~ N(0, 1) (CPU)."""
+    g = torch.Generator().manual_seed(int(seed))
+    return torch.randn(m, n, generator=g).to(torch.bfloat16)
+
+
+def check_dx(dy_cpu: torch.Tensor, w_cpu: torch.Tensor, what: str, rows=None, cols=None,
+             full=False):
+    """tern_gemm_dx on the GPU against the oracle: the weights are quantized and
+    packed on the GPU (bit-exact against the oracle), re-packed along n by
+    tern_pack_transposed (bit-exact), the scaled gradient u compared bit for
+    bit, and dx within |dx - dx_ref| <= 8e-3 |dx_ref| + 1e-3 ||u_m||_2 on every
+    element (``full``) or on rows x all columns and all rows x columns."""
+    m, n = dy_cpu.shape
+    k = w_cpu.shape[1]
+    t_ref, s_ref, p_ref = oracle_weights(w_cpu)
+    t, s, p = gpu_quantize_pack(w_cpu)
+    assert_bitexact_weights(t, s, p, t_ref, s_ref, p_ref, what + " (weights)")
+    pt = tern.pack_transposed(p, n, k)
+    pt_ref = oracle.oracle_pack_transposed(p_ref, n, k)
+    nb = (n + 3) // 4
+    assert np.array_equal(pt.cpu().numpy()[:, :nb], pt_ref), what + " (transposed packing)"
+    dyd = dy_cpu.to(DEV)
+    u = torch.empty((m, n), dtype=torch.bfloat16, device=DEV)
+    dx = torch.empty((m, k), dtype=torch.bfloat16, device=DEV)
+    tern.tern_gemm_dx(dyd, pt, s, u, dx, k)
+    torch.cuda.synchronize()
+    dyb = tern_inputs.bf16_bits(dy_cpu)
+    u_ref = oracle.oracle_scale_grad(dyb, s_ref)
+    assert np.array_equal(tern_inputs.bf16_bits(u.cpu()), u_ref), what + " (scaled gradient)"
+    unorm = row_norms(u_ref)
+    dxh = bf16_to_f64(dx)
+    ones = np.ones(k, np.float32)
+    if full or (rows is None and cols is None):
+        ref = oracle.oracle_gemm_dx(u_ref, p_ref, k)
+        return assert_within_tolerance(dxh, ref, ones, unorm, what)
+    worst = 0.0
+    if rows is not None:
+        ref = oracle.oracle_gemm_dx(u_ref[rows], p_ref, k)
+        worst = max(worst, assert_within_tolerance(dxh[rows], ref, ones, unorm[rows],
+                                                   what + " (rows)"))
+    if cols is not None:
+        # columns c of dx need column c of T: the codes of the chosen columns,
+        # re-packed as a narrower layer
+        t_cols = np.ascontiguousarray(t_ref[:, cols])
+        ref = oracle.oracle_gemm_dx(u_ref, oracle.oracle_pack(t_cols), len(cols))
+        worst = max(worst, assert_within_tolerance(dxh[:, cols], ref, ones[: len(cols)], unorm,
+                                                   what + " (cols)"))
+    return worst

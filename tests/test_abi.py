@@ -179,6 +179,52 @@ def test_gemm_ex_validation():
     assert call(b=A + 4, x=A + 8) == tern.TERN_ERR_ALIGN
 
 
+def test_pack_transposed_validation():
+    f = lib.tern_pack_transposed
+    assert f(A, -1, 8, 2, A, 2, NULL) == tern.TERN_ERR_SHAPE
+    assert f(A, 8, 2 ** 31, 2 ** 29, A, 2, NULL) == tern.TERN_ERR_SHAPE
+    assert f(NULL, 0, 8, 2, NULL, 2, NULL) == tern.TERN_OK
+    assert f(NULL, 8, 0, 2, NULL, 2, NULL) == tern.TERN_OK
+    assert f(NULL, 8, 8, 2, A, 2, NULL) == tern.TERN_ERR_NULL
+    assert f(A, 8, 8, 2, NULL, 2, NULL) == tern.TERN_ERR_NULL
+    assert f(A, 9, 9, 2, A, 3, NULL) == tern.TERN_ERR_STRIDE     # ldp < ceil(k/4)
+    assert f(A, 9, 9, 3, A, 2, NULL) == tern.TERN_ERR_STRIDE     # ldpt < ceil(n/4)
+
+
+def test_gemm_dx_validation():
+    g = lib.tern_gemm_dx
+    ok = dict(dy=A, m=8, n=128, lddy=128, pt=A, k=16, ldpt=32, s=A, u=A, ldu=128, dx=A, lddx=16)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return g(a["dy"], a["m"], a["n"], a["lddy"], a["pt"], a["k"], a["ldpt"], a["s"], a["u"],
+                 a["ldu"], a["dx"], a["lddx"], NULL)
+
+    assert call(m=-1) == tern.TERN_ERR_SHAPE
+    assert call(n=100, lddy=128, ldu=128) == tern.TERN_ERR_SHAPE   # n % 64 != 0
+    assert call(k=2 ** 31) == tern.TERN_ERR_SHAPE
+    assert call(m=0, dy=NULL, pt=NULL, s=NULL, u=NULL, dx=NULL) == tern.TERN_OK
+    assert call(k=0, dy=NULL, pt=NULL, s=NULL, u=NULL, dx=NULL) == tern.TERN_OK
+    for name in ("dy", "pt", "s", "u", "dx"):
+        assert call(**{name: NULL}) == tern.TERN_ERR_NULL
+    assert call(n=0, pt=NULL) == tern.TERN_ERR_NULL
+    assert call(n=0, dx=NULL) == tern.TERN_ERR_NULL
+    assert call(n=0, dy=NULL, s=NULL, u=NULL, lddx=15) == tern.TERN_ERR_STRIDE  # not read at n = 0
+    assert call(lddy=120) == tern.TERN_ERR_STRIDE
+    assert call(ldu=120) == tern.TERN_ERR_STRIDE
+    assert call(ldpt=16) == tern.TERN_ERR_STRIDE                  # < n/4
+    assert call(lddx=15) == tern.TERN_ERR_STRIDE
+    assert call(ldu=1 << 23) == tern.TERN_ERR_STRIDE
+    assert call(ldpt=1 << 24) == tern.TERN_ERR_STRIDE
+    assert call(u=A + 8) == tern.TERN_ERR_ALIGN
+    assert call(ldu=132) == tern.TERN_ERR_ALIGN
+    assert call(pt=A + 4) == tern.TERN_ERR_ALIGN
+    assert call(ldpt=40) == tern.TERN_ERR_ALIGN
+    assert call(dy=A + 1) == tern.TERN_ERR_ALIGN
+    assert call(dx=A + 1) == tern.TERN_ERR_ALIGN
+    assert call(s=A + 2) == tern.TERN_ERR_ALIGN
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     x = torch.zeros(4, 64, dtype=torch.bfloat16)

@@ -14,8 +14,8 @@ import oracle
 import tern_inputs
 from parity import (DEV, assert_bitexact_weights, assert_within_tolerance,
                     assert_within_tolerance_ex, bf16_to_f64, check_layer, check_layer_ex,
-                    edge_indices, gemm_ex_gpu, gemm_gpu, gpu_quantize_pack,
-                    gpu_quantize_pack_fused, log, oracle_weights, row_norms)
+                    check_dx, draw_grad, edge_indices, gemm_ex_gpu, gemm_gpu,
+                    gpu_quantize_pack, gpu_quantize_pack_fused, log, oracle_weights, row_norms)
 
 pytestmark = pytest.mark.gpu
 tern = pytest.importorskip("ternary_weight_quantized_tern_amd")
@@ -422,3 +422,85 @@ def test_workload_flux_single_stream(block):
     layers = tern_inputs.WORKLOADS["flux_single_stream"]
     for layer in layers[2 * block: 2 * block + 2]:
         _run_workload_layer(layer, n_extra=64)
+
+
+# ---------------------------------------------------------------------------
+# input gradient: tern_pack_transposed and tern_gemm_dx
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,k", [(1, 1), (5, 2), (37, 29), (128, 128), (129, 257), (300, 515),
+                                 (4608, 1152)])
+@pytest.mark.parametrize("aligned", [True, False])
+def test_pack_transposed(n, k, aligned):
+    log(f"pack_transposed n={n} k={k} aligned={aligned}")
+    t = tern_inputs.random_ternary(n, k, seed=n * 7 + k).numpy()
+    p_ref = oracle.oracle_pack(t)
+    pt_ref = oracle.oracle_pack_transposed(p_ref, n, k)
+    kb, nb = (k + 3) // 4, (n + 3) // 4
+    ldp = (kb + 15) // 16 * 16 if aligned else kb + 3
+    ldpt = (nb + 15) // 16 * 16 + 16 if aligned else nb + 5
+    ph = np.zeros((n, ldp), np.uint8)
+    ph[:, :kb] = p_ref
+    p = torch.from_numpy(ph).to(DEV)
+    pt = torch.full((k, ldpt), 0xA5, dtype=torch.uint8, device=DEV)
+    tern.tern_pack_transposed(p, pt, n, k)
+    torch.cuda.synchronize()
+    got = pt.cpu().numpy()
+    assert np.array_equal(got[:, :nb], pt_ref)
+    assert np.all(got[:, nb:] == 0xA5)                 # bytes past ceil(n/4) untouched
+
+
+@pytest.mark.parametrize("m,n,k", [(37, 128, 90), (300, 256, 515), (33, 64, 1), (8, 448, 200),
+                                   (1, 64, 64), (130, 192, 2048), (517, 320, 384)])
+def test_gemm_dx_all_elements(m, n, k):
+    log(f"gemm_dx m={m} n={n} k={k}")
+    _, w = tern_inputs.draw(1, k, n, seed=m + 3 * n + 7 * k)
+    check_dx(draw_grad(m, n, seed=m * n + k), w, f"dx m={m} n={n} k={k}", full=True)
+
+
+def test_gemm_dx_n_zero_writes_zeros():
+    dy = torch.empty((5, 0), dtype=torch.bfloat16, device=DEV)
+    pt = torch.zeros((64, 16), dtype=torch.uint8, device=DEV)
+    s = torch.empty(0, device=DEV)
+    u = torch.empty((5, 0), dtype=torch.bfloat16, device=DEV)
+    dx = torch.full((5, 64), 3.0, dtype=torch.bfloat16, device=DEV)
+    tern.tern_gemm_dx(dy, pt, s, u, dx, 64)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dx).item() == 0
+
+
+def test_gemm_dx_error_status_and_convenience():
+    dy = torch.zeros((4, 100), dtype=torch.bfloat16, device=DEV)      # n % 64 != 0
+    pt = torch.zeros((8, 32), dtype=torch.uint8, device=DEV)
+    s = torch.ones(100, device=DEV)
+    u = torch.empty_like(dy)
+    dx = torch.empty((4, 8), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(tern.TernError) as e:
+        tern.tern_gemm_dx(dy, pt, s, u, dx, 8)
+    assert e.value.status == tern.TERN_ERR_SHAPE
+    # linear_dx allocates the workspace and calls the same entry point
+    dyc = draw_grad(40, 128, seed=5)
+    _, w = tern_inputs.draw(1, 96, 128, seed=6)
+    t, s, p = gpu_quantize_pack(w)
+    pt = tern.pack_transposed(p, 128, 96)
+    dyd = dyc.to(DEV)
+    u = torch.empty_like(dyd)
+    dx_ref = torch.empty((40, 96), dtype=torch.bfloat16, device=DEV)
+    tern.tern_gemm_dx(dyd, pt, s, u, dx_ref, 96)
+    dx = tern.linear_dx(dyd, pt, s, 96)
+    torch.cuda.synchronize()
+    assert torch.equal(dx, dx_ref)
+
+
+@pytest.mark.parametrize("layer", ["dit.up.m2048", "flux_qkv", "flux_mlp.up"])
+def test_workload_dx(layer):
+    # the input gradients of the layers at full size: every weight and the
+    # whole scaled gradient bit-exact, dx on tile-edge and sampled rows and
+    # columns
+    lyr = {l.name: l for wl in tern_inputs.WORKLOADS.values() for l in wl}[layer]
+    log(f"dx workload {layer} m={lyr.m} n={lyr.n} k={lyr.k}")
+    _, w = tern_inputs.draw_layer(lyr)
+    dy = draw_grad(lyr.m, lyr.n, seed=lyr.seed + 500)
+    rows = edge_indices(lyr.m, extra=24, seed=1)[:64]
+    cols = edge_indices(lyr.k, extra=24, seed=2)[:96]
+    check_dx(dy, w, f"dx {layer}", rows=rows, cols=cols)
