@@ -14,7 +14,8 @@ sample of the same step.
 After the timed steps, every layer shape of the five workloads is timed on its
 own ("rows"): tern_gemm per launch, and tern_gemm_ex with the bias and GELU
 of the layers that have them, as effective TFLOP/s, GB/s and the fraction of
-the bound that applies (MFMA or HBM).  The two few-token layers
+the bound that applies (MFMA or HBM); "dx_rows" time the input gradient
+(tern_gemm_dx, tern_pack_transposed) on the backward shapes.  The two few-token layers
 cycle through a pool of distinct packed weights larger than every cache, so
 that each launch streams its weights from HBM.
 
@@ -55,7 +56,10 @@ def parse():
                     help="also run a device copy of this size (for counter calibration)")
     ap.add_argument("--gemm-only-reps", type=int, default=0,
                     help="after the steps, launch tern_gemm alone this many times (profiling)")
-    ap.add_argument("--no-rows", action="store_true", help="skip the per-layer-shape table")
+    ap.add_argument("--no-rows", action="store_true", help="skip the per-layer-shape tables")
+    ap.add_argument("--rows", choices=("all", "fwd", "dx"), default="all",
+                    help="which per-layer-shape tables to time: the forward layer, the input "
+                         "gradient, or both")
     ap.add_argument("--separate-quantize", action="store_true",
                     help="run quantize and pack as two calls in the step instead of the fused pass")
     ap.add_argument("--row-reps", type=int, default=30, help="timed launches per row")
@@ -265,6 +269,70 @@ def time_rows(tern, tern_inputs, torch, dev, reps, pool_mib):
     return rows
 
 
+def time_graph(torch, fn, launches):
+    """Seconds per call of fn() with `launches` calls captured in one HIP graph
+    and replayed back to back (after one eager warm-up call on a side stream)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(launches):
+            fn()
+    graph.replay()
+    torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record()
+    graph.replay()
+    g1.record()
+    torch.cuda.synchronize()
+    del graph
+    return g0.elapsed_time(g1) * 1e-3 / launches
+
+
+def time_dx_rows(tern, tern_inputs, torch, dev, reps):
+    """The input gradient of the layer, dX = bf16((dY * s) . T), on the backward
+    shapes of the DiT and FLUX layers (dY [m, n] of the forward's output, dX
+    [m, k]): tern_gemm_dx (the scaling pass and the ternary GEMM over n), and
+    tern_pack_transposed of the layer's codes.  Seeded normal weights quantized
+    on the GPU, dY ~ N(0, 1) in bf16; graph-replayed launches."""
+    names = ["dit.up.m2048", "dit.down.m2048", "flux_qkv", "flux_mlp.up", "flux_mlp.down"]
+    layers = {l.name: l for wl in tern_inputs.WORKLOADS.values() for l in wl}
+    rows = []
+    for name in names:
+        layer = layers[name]
+        m, k, n = layer.m, layer.k, layer.n
+        _, w = tern_inputs.draw_layer(layer)
+        p, s = tern.quantize_pack(w.to(dev))
+        pt = torch.zeros((k, tern.packed_row_bytes(n)), dtype=torch.uint8, device=dev)
+        g = torch.Generator(device=dev).manual_seed(layer.seed + 500)
+        dy = torch.randn((m, n), generator=g, device=dev).to(torch.bfloat16)
+        u = torch.empty_like(dy)
+        dx = torch.empty((m, k), dtype=torch.bfloat16, device=dev)
+        tern.tern_pack_transposed(p, pt, n, k)
+        t_pt = time_graph(torch, lambda: tern.tern_pack_transposed(p, pt, n, k), reps)
+        t_dx = time_graph(torch, lambda: tern.tern_gemm_dx(dy, pt, s, u, dx, k), reps)
+        flops = 2 * m * n * k
+        # algorithmic bytes: dY, the codes, the scales and dX (the bf16 workspace
+        # u, written once and read once, is the implementation's own traffic)
+        byts = 2 * m * n + n * k // 4 + 4 * n + 2 * m * k
+        row = {"layer": name + ".dx", "m": m, "n": n, "k": k, "us_per_launch": t_dx * 1e6,
+               "alg_flops": flops, "alg_bytes": byts, "workspace_bytes": 4 * m * n,
+               "entry": "tern_gemm_dx",
+               "pack_transposed_us": t_pt * 1e6,
+               "pack_transposed_gbs": 2 * (n * k // 4) / t_pt / 1e9}
+        row.update(roofline_of(flops, byts, t_dx))
+        rows.append(row)
+        print(f"# dx row {name}: {t_dx * 1e6:.1f} us per launch, {row['tflops']:.0f} TFLOP/s, "
+              f"{row['pct_roofline']:.1f}% of roofline; pack_transposed {t_pt * 1e6:.1f} us",
+              file=sys.stderr, flush=True)
+        del p, s, pt, dy, u, dx
+        torch.cuda.empty_cache()
+    return rows
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -464,10 +532,13 @@ def main():
         torch.cuda.synchronize()
         print(f"# copy calibration: {nbytes} bytes read and written", file=sys.stderr)
 
-    rows = None
-    if not args.no_rows:
+    rows = dx_rows = None
+    if not args.no_rows and args.rows in ("all", "fwd"):
         print("# timing tern_gemm on every layer shape", file=sys.stderr, flush=True)
         rows = time_rows(tern, tern_inputs, torch, dev, args.row_reps, args.pool_mib)
+    if not args.no_rows and args.rows in ("all", "dx"):
+        print("# timing the input gradient on the backward shapes", file=sys.stderr, flush=True)
+        dx_rows = time_dx_rows(tern, tern_inputs, torch, dev, args.row_reps)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -496,6 +567,7 @@ def main():
         "cpu_baseline": cpu,
         "kernels": kernels,
         "rows": rows,
+        "dx_rows": dx_rows,
         "peaks": {"bf16_mfma_tflops": PEAK_BF16_TFLOPS, "hbm_gbs": PEAK_HBM_GBS},
     }
     print(json.dumps(out), flush=True)

@@ -119,86 +119,105 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(const uint8_t* __restr
 }
 
 // Transposed packing: the codes of p (row n, packed along k) packed along n
-// into pt (row k holds T[0..n-1][k]).  A workgroup moves a 128 (n) x 128 (k)
-// tile: each thread loads 16 bytes of one row of p (64 codes) into LDS; then
-// thread (c, q) takes byte column c (codes k = 4c .. 4c+3) of tile rows
-// 16q .. 16q+15, splits the 16 bytes by field with shifts and masks, gathers
-// the four 2-bit fields of each 4-byte group into one byte with a byte dot
-// product against (1, 4, 16, 64), and writes 4 bytes (16 codes along n) into
-// each of the rows 4c .. 4c+3 of pt.  Rows of the tile past n read as zero, so
-// the fields past n in the last byte of a pt row are zero.
-constexpr int kTT = 128;         // tile edge, in codes
-constexpr int kTB = kTT / 4;     // tile edge of p, in bytes
-constexpr int kTPitch = kTB + 4; // LDS row pitch (bytes)
+// into pt (row k holds T[0..n-1][k]).  A workgroup moves a tile of 128 rows
+// of p by 128 bytes (512 codes), so that it reads whole 128-byte lines (a
+// narrower tile leaves each line to several workgroups, which the round-robin
+// placement puts on different XCDs, each fetching the line into its own L2).
+// Load: 16-byte pieces of the tile rows into LDS (eight threads per row).
+// Transpose: work item (c, q) takes byte column c (codes k = 4c .. 4c+3) of
+// tile rows 16q .. 16q+15, splits the 16 bytes by field with shifts and
+// masks, gathers the four 2-bit fields of each 4-byte group into one byte
+// with a byte dot product against (1, 4, 16, 64), and writes 4 bytes (16 codes
+// along n) into each of the rows 4c .. 4c+3 of pt.  Rows of the tile past n
+// read as zero, so the fields past n in the last byte of a pt row are zero.
+constexpr int kTRows = 128;            // rows of p (codes along n) per tile
+constexpr int kTBytes = 128;           // bytes of p per tile row (512 codes along k)
+constexpr int kTPitch = kTBytes + 4;   // LDS row pitch (bytes)
+constexpr int kTLoads = kTRows * kTBytes / 16 / kThreads;       // 16-byte loads per thread
+constexpr int kTGroups = kTRows / 16;                            // 16-row groups per tile
+constexpr int kTItems = (kTBytes * kTGroups) / kThreads;        // (c, q) items per thread
+static_assert(kTLoads * kThreads * 16 == kTRows * kTBytes && kTItems * kThreads == kTBytes * kTGroups,
+              "whole loads and items per thread");
 
 __global__ __launch_bounds__(kThreads) void pack_transposed_kernel(
     const uint8_t* __restrict__ p, int64_t n, int64_t k, int64_t ldp, uint8_t* __restrict__ pt,
     int64_t ldpt, int64_t tiles_k, bool p_vec, bool pt_vec) {
-  __shared__ __attribute__((aligned(16))) uint8_t tile[kTT * kTPitch];
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kTRows * kTPitch];
   const int64_t in_bytes = (k + 3) / 4;   // bytes of a p row
   const int64_t out_bytes = (n + 3) / 4;  // bytes of a pt row
-  const int64_t tiles = ((n + kTT - 1) / kTT) * tiles_k;
+  const int64_t tiles = ((n + kTRows - 1) / kTRows) * tiles_k;
   const int t = threadIdx.x;
   for (int64_t b = blockIdx.x; b < tiles; b += gridDim.x) {
     const int64_t tn = b / tiles_k;
-    const int64_t n0 = tn * kTT;
-    const int64_t k0 = (b - tn * tiles_k) * kTT;
-    // Load: thread t takes 16 bytes of row n0 + t/2, byte columns 16 (t % 2) ...
-    {
-      const int r = t >> 1;
-      const int c0 = 16 * (t & 1);
-      const int64_t col = k0 / 4 + c0;  // byte column in p
-      uint32_t w[4] = {0u, 0u, 0u, 0u};
+    const int64_t n0 = tn * kTRows;
+    const int64_t kb0 = (b - tn * tiles_k) * kTBytes;  // first byte column of p
+    uint32_t w[kTLoads][4];
+#pragma unroll
+    for (int i = 0; i < kTLoads; ++i) {
+      const int id = i * kThreads + t;
+      const int r = id / (kTBytes / 16);
+      const int64_t col = kb0 + 16 * (id % (kTBytes / 16));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[i][e] = 0u;
       if (n0 + r < n) {
         const uint8_t* src = p + (n0 + r) * ldp + col;
         if (p_vec && col + 16 <= in_bytes) {
           const uint4 v = *reinterpret_cast<const uint4*>(src);
-          w[0] = v.x;
-          w[1] = v.y;
-          w[2] = v.z;
-          w[3] = v.w;
+          w[i][0] = v.x;
+          w[i][1] = v.y;
+          w[i][2] = v.z;
+          w[i][3] = v.w;
         } else {
 #pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (col + i < in_bytes) w[i / 4] |= static_cast<uint32_t>(src[i]) << (8 * (i % 4));
+          for (int e = 0; e < 16; ++e)
+            if (col + e < in_bytes) w[i][e / 4] |= static_cast<uint32_t>(src[e]) << (8 * (e % 4));
         }
       }
-      __syncthreads();  // the previous tile's reads are done
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<uint32_t*>(&tile[r * kTPitch + c0 + 4 * i]) = w[i];
-      __syncthreads();
     }
-    // Transpose: thread (c, q) = (t / 8, t % 8).
-    const int c = t >> 3;
-    const int q = t & 7;
-    uint32_t d[4];  // byte i of d[j]: tile row 16 q + 4 j + i, byte column c
+    __syncthreads();  // the previous tile's reads are done
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint32_t v = 0;
+    for (int i = 0; i < kTLoads; ++i) {
+      const int id = i * kThreads + t;
+      const int r = id / (kTBytes / 16);
+      const int c0 = 16 * (id % (kTBytes / 16));
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        v |= static_cast<uint32_t>(tile[(16 * q + 4 * j + i) * kTPitch + c]) << (8 * i);
-      d[j] = v;
+      for (int e = 0; e < 4; ++e)
+        *reinterpret_cast<uint32_t*>(&tile[r * kTPitch + c0 + 4 * e]) = w[i][e];
     }
+    __syncthreads();
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      const int64_t row = k0 + 4 * c + f;  // row of pt (code column k of p)
-      if (row >= k) break;
-      uint32_t o = 0;
+    for (int it = 0; it < kTItems; ++it) {
+      const int id = it * kThreads + t;
+      const int c = id / kTGroups;  // byte column of the tile
+      const int q = id % kTGroups;  // 16-row group
+      uint32_t d[4];  // byte i of d[j]: tile row 16 q + 4 j + i, byte column c
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint32_t fields = (d[j] >> (2 * f)) & 0x03030303u;
-        o |= __builtin_amdgcn_udot4(fields, 0x40100401u, 0u, false) << (8 * j);
-      }
-      const int64_t byte0 = n0 / 4 + 4 * q;
-      uint8_t* dst = pt + row * ldpt + byte0;
-      if (pt_vec && byte0 + 4 <= out_bytes) {
-        *reinterpret_cast<uint32_t*>(dst) = o;
-      } else {
+        uint32_t v = 0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (byte0 + j < out_bytes) dst[j] = static_cast<uint8_t>(o >> (8 * j));
+        for (int i = 0; i < 4; ++i)
+          v |= static_cast<uint32_t>(tile[(16 * q + 4 * j + i) * kTPitch + c]) << (8 * i);
+        d[j] = v;
+      }
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        const int64_t row = 4 * (kb0 + c) + f;  // row of pt (code column k of p)
+        if (row >= k) break;
+        uint32_t o = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t fields = (d[j] >> (2 * f)) & 0x03030303u;
+          o |= __builtin_amdgcn_udot4(fields, 0x40100401u, 0u, false) << (8 * j);
+        }
+        const int64_t byte0 = n0 / 4 + 4 * q;
+        uint8_t* dst = pt + row * ldpt + byte0;
+        if (pt_vec && byte0 + 4 <= out_bytes) {
+          *reinterpret_cast<uint32_t*>(dst) = o;
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (byte0 + j < out_bytes) dst[j] = static_cast<uint8_t>(o >> (8 * j));
+        }
       }
     }
   }
@@ -243,8 +262,8 @@ hipError_t launch_unpack(const uint8_t* p, int64_t n, int64_t k, int64_t ldp, in
 
 hipError_t launch_pack_transposed(const uint8_t* p, int64_t n, int64_t k, int64_t ldp,
                                   uint8_t* pt, int64_t ldpt, hipStream_t stream) {
-  const int64_t tiles_k = (k + kTT - 1) / kTT;
-  int64_t tiles = ((n + kTT - 1) / kTT) * tiles_k;
+  const int64_t tiles_k = ((k + 3) / 4 + kTBytes - 1) / kTBytes;
+  int64_t tiles = ((n + kTRows - 1) / kTRows) * tiles_k;
   if (tiles > kMaxBlocks) tiles = kMaxBlocks;
   const bool p_vec = reinterpret_cast<uintptr_t>(p) % 16 == 0 && ldp % 16 == 0;
   const bool pt_vec = reinterpret_cast<uintptr_t>(pt) % 4 == 0 && ldpt % 4 == 0;
