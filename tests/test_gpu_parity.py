@@ -424,6 +424,87 @@ def test_workload_flux_single_stream(block):
         _run_workload_layer(layer, n_extra=64)
 
 
+def test_kernel_configurations_agree_bitwise():
+    # Every tiled kernel feeds an output the same MFMA sequence over k (k-blocks
+    # of 32 in ascending order into one accumulator), so the persistent 144 x 384
+    # kernel (whose LDS ring streams across tiles), the one-tile-per-workgroup
+    # 144 x 384 kernel, the 64 x 576 kernel and the 64 x 128 kernel (two
+    # workgroups per CU) must give bit-identical outputs on the same operands.
+    # A race in any of the LDS pipelines shows up as a mismatch here.
+    m, k, n = 4608, 3072, 9216
+    x, w = tern_inputs.draw(m, k, n, seed=77)
+    t, s, p = gpu_quantize_pack(w)
+    xd = x.to(DEV)
+
+    def run(mm, nn):
+        y = torch.empty((mm, nn), dtype=torch.bfloat16, device=DEV)
+        tern.tern_gemm(xd[:mm], p[:nn], s[:nn], y, k)
+        return y
+
+    full = run(m, n)            # persistent 144 x 384 (768 tiles)
+    a = run(2048, n)            # 144 x 384, one tile per workgroup (m % 144 != 0)
+    b = run(2048, 4608)         # 64 x 576 (exactly 256 tiles)
+    c = run(512, n)             # 64 x 128, two workgroups per CU
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), full[:2048].view(torch.int16))
+    assert torch.equal(b.view(torch.int16), full[:2048, :4608].view(torch.int16))
+    assert torch.equal(c.view(torch.int16), full[:512].view(torch.int16))
+
+
+def test_hip_graph_replays_match_eager():
+    # The entry points launch kernels only (no memset or copy nodes), so a
+    # captured graph must reproduce the eager results on every replay, with
+    # other eager work and synchronizations between the replays.
+    m, k, n = 300, 512, 640
+    x, w = tern_inputs.draw(m, k, n, seed=88)
+    dy = draw_grad(m, n, seed=89)
+    xd, wd, dyd = x.to(DEV), w.to(DEV), dy.to(DEV)
+    ldp, ldpt = tern.packed_row_bytes(k), tern.packed_row_bytes(n)
+    bias = (torch.randn(n, generator=torch.Generator().manual_seed(90)) * 0.1).to(DEV)
+
+    def buffers():
+        return dict(t=torch.zeros((n, k), dtype=torch.int8, device=DEV),
+                    p=torch.zeros((n, ldp), dtype=torch.uint8, device=DEV),
+                    s=torch.zeros(n, device=DEV),
+                    tu=torch.zeros((n, k), dtype=torch.int8, device=DEV),
+                    pt=torch.zeros((k, ldpt), dtype=torch.uint8, device=DEV),
+                    y=torch.zeros((m, n), dtype=torch.bfloat16, device=DEV),
+                    ye=torch.zeros((m, n), dtype=torch.bfloat16, device=DEV),
+                    u=torch.zeros((m, n), dtype=torch.bfloat16, device=DEV),
+                    dx=torch.zeros((m, k), dtype=torch.bfloat16, device=DEV))
+
+    def work(b):
+        tern.tern_quantize_pack(wd, b["t"], b["p"], b["s"])
+        tern.tern_unpack(b["p"], b["tu"], k)
+        tern.tern_gemm(xd, b["p"], b["s"], b["y"], k)
+        tern.tern_gemm_ex(xd, b["p"], b["s"], b["ye"], bias, tern.TERN_ACT_GELU_TANH, 100, k)
+        tern.tern_pack_transposed(b["p"], b["pt"], n, k)
+        tern.tern_gemm_dx(dyd, b["pt"], b["s"], b["u"], b["dx"], k)
+
+    eager = buffers()
+    work(eager)
+    torch.cuda.synchronize()
+    cap = buffers()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        work(cap)                                  # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        work(cap)
+    for r in range(3):
+        for v in cap.values():
+            v.zero_()                               # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name in eager:
+            assert torch.equal(cap[name].view(torch.uint8), eager[name].view(torch.uint8)), \
+                f"replay {r}: {name} differs from the eager result"
+    del graph
+
+
 # ---------------------------------------------------------------------------
 # input gradient: tern_pack_transposed and tern_gemm_dx
 # ---------------------------------------------------------------------------
