@@ -388,14 +388,15 @@ def test_workload_flux_single_stream_in_proj_bias_gelu_mlp_part():
 # the five workloads at full size
 # ---------------------------------------------------------------------------
 
-def _run_workload_layer(layer, n_extra=192):
+def _run_workload_layer(layer, n_extra=192, full=None):
     log(f"workload layer {layer.name} m={layer.m} k={layer.k} n={layer.n} seed={layer.seed}")
     x, w = tern_inputs.draw_layer(layer)
     rows = edge_indices(layer.m, extra=n_extra, seed=layer.seed)
     cols = edge_indices(layer.n, extra=n_extra, seed=layer.seed + 1)
-    full = layer.m * layer.n * layer.k <= 2 ** 26
+    if full is None:
+        full = layer.m * layer.n * layer.k <= 2 ** 26
     worst = check_layer(x, w, layer.name, rows=rows, cols=cols, full=full,
-                        repeat_check=(layer.seed % 7 == 0))
+                        repeat_check=(layer.seed % 7 == 0 or layer.name == "flux_qkv"))
     log(f"  ok, worst error / bound = {worst:.3f}")
 
 
@@ -419,9 +420,11 @@ def test_workload_dit(i):
 
 @pytest.mark.parametrize("block", range(38))
 def test_workload_flux_single_stream(block):
+    # every element of the first, middle and last block; tile-edge and
+    # sampled rows and columns of the others
     layers = tern_inputs.WORKLOADS["flux_single_stream"]
     for layer in layers[2 * block: 2 * block + 2]:
-        _run_workload_layer(layer, n_extra=64)
+        _run_workload_layer(layer, n_extra=64, full=block in (0, 18, 37))
 
 
 def test_kernel_configurations_agree_bitwise():
