@@ -149,7 +149,7 @@ tern_status tern_unpack(const uint8_t* p, int64_t n, int64_t k, int64_t ldp, int
  *   y  [m, ldy] bf16 output; columns >= n untouched
  * Sizes: m, n, k >= 0 and k % 64 == 0 (else TERN_ERR_SHAPE); m == 0 or
  * n == 0 is a no-op; k == 0 writes zeros.  m, n <= 2^31 - 1,
- * k <= 2^31 - 64 and ceil(m/256) * ceil(n/256) <= 2^31 - 1.
+ * k <= 2^31 - 64 and ceil(m/64) * ceil(n/128) <= 2^31 - 1.
  * ldx >= k, ldp >= k/4, ldy >= n, and ldx < 2^23, ldp < 2^24, ldy < 2^31
  * (else TERN_ERR_STRIDE).
  * Alignment (else TERN_ERR_ALIGN): x and p 16-byte aligned, ldx % 8 == 0,
@@ -234,7 +234,7 @@ tern_status tern_pack_transposed(const uint8_t* p, int64_t n, int64_t k, int64_t
  *   dx  [m, lddx] bf16 output; columns >= k untouched
  * Sizes: m, n, k >= 0 and n % 64 == 0 (else TERN_ERR_SHAPE); m == 0 or
  * k == 0 is a no-op; n == 0 writes zeros.  m, k <= 2^31 - 1,
- * n <= 2^31 - 64, ceil(m/256) * ceil(k/256) <= 2^31 - 1.
+ * n <= 2^31 - 64, ceil(m/64) * ceil(k/128) <= 2^31 - 1.
  * lddy >= n, ldu >= n, ldpt >= n/4, lddx >= k, and ldu < 2^23, ldpt < 2^24,
  * lddx < 2^31 (else TERN_ERR_STRIDE).  pt and dx must not be NULL, nor dy, s
  * and u unless n == 0 (TERN_ERR_NULL).  Alignment (else TERN_ERR_ALIGN): u

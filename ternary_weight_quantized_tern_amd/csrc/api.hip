@@ -76,7 +76,8 @@ tern_status gemm_common(const void* x_bf16, int64_t m, int64_t k, int64_t ldx, c
                         int64_t act_from, void* y_bf16, int64_t ldy, void* stream) {
   if (m < 0 || n < 0 || k < 0 || m > kMaxInt || n > kMaxInt || k > kMaxInt - 63 || k % 64 != 0)
     return TERN_ERR_SHAPE;
-  if (((m + 255) / 256) * ((n + 255) / 256) > kMaxInt) return TERN_ERR_SHAPE;
+  // The smallest tile is 64 x 128: the tile count must fit the grid.
+  if (((m + 63) / 64) * ((n + 127) / 128) > kMaxInt) return TERN_ERR_SHAPE;
   if (m == 0 || n == 0) return TERN_OK;
   if (x_bf16 == nullptr || p == nullptr || s == nullptr || y_bf16 == nullptr) return TERN_ERR_NULL;
   if (ldx < k || ldp < k / 4 || ldy < n) return TERN_ERR_STRIDE;
@@ -124,7 +125,7 @@ tern_status tern_gemm_dx(const void* dy_bf16, int64_t m, int64_t n, int64_t lddy
   // contraction and k the output width; unit scales.
   if (m < 0 || n < 0 || k < 0 || m > kMaxInt || k > kMaxInt || n > kMaxInt - 63 || n % 64 != 0)
     return TERN_ERR_SHAPE;
-  if (((m + 255) / 256) * ((k + 255) / 256) > kMaxInt) return TERN_ERR_SHAPE;
+  if (((m + 63) / 64) * ((k + 127) / 128) > kMaxInt) return TERN_ERR_SHAPE;
   if (m == 0 || k == 0) return TERN_OK;
   // With n == 0 the gradient, the scales and the workspace are not read.
   if (pt == nullptr || dx_bf16 == nullptr ||

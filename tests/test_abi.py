@@ -139,6 +139,7 @@ def test_gemm_validation():
     assert call(m=-1) == tern.TERN_ERR_SHAPE
     assert call(k=100, ldx=128) == tern.TERN_ERR_SHAPE        # k % 64 != 0
     assert call(n=2 ** 31) == tern.TERN_ERR_SHAPE
+    assert call(m=2 ** 30, n=2 ** 20, ldy=2 ** 20) == tern.TERN_ERR_SHAPE  # 2^24 * 2^13 tiles
     assert call(m=0, x=NULL, p=NULL, s=NULL, y=NULL) == tern.TERN_OK
     assert call(n=0, x=NULL, p=NULL, s=NULL, y=NULL) == tern.TERN_OK
     for name in ("x", "p", "s", "y"):
