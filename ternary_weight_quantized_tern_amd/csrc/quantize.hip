@@ -12,7 +12,8 @@
 // the two reductions (max |w|, then the integer sum) are wave butterflies,
 // combined across the row's waves through LDS when R > 1; then the codes are
 // written, as int8 and/or packed four to a byte.  Per weight: 4 (or 2) bytes
-// read, 1 byte (and/or 1/4 byte) written, and about ten VALU instructions:
+// read, 1 byte (and/or 1/4 byte) written, and about fourteen VALU instructions
+// (per-row reductions and addressing included):
 //  - max |w| as the larger of the signed and the unsigned maximum of the bit
 //    patterns (one 3-way max per two weights each);
 //  - the fixed-point term floor(|w| * 2^(48 - E)) is an exact fp32 scaling
