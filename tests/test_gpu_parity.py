@@ -576,6 +576,42 @@ def test_gemm_dx_error_status_and_convenience():
     assert torch.equal(dx, dx_ref)
 
 
+@pytest.mark.parametrize("m,n,k", [(9, 128, 77), (300, 192, 260)])
+def test_gemm_dx_strided_views(m, n, k):
+    # dY, the workspace and dX as views into wider rows (pitches n + 25,
+    # n + 8 and k + 40): the few-token and the tiled GEMM paths, and the
+    # scaling pass's element-wise path (dY's odd pitch rules out its 16-byte
+    # accesses)
+    _, w = tern_inputs.draw(1, k, n, seed=m + n + k)
+    dy = draw_grad(m, n, seed=3 * m + n)
+    t_ref, s_ref, p_ref = oracle_weights(w)
+    t, s, p = gpu_quantize_pack(w)
+    pt = tern.pack_transposed(p, n, k)
+    dyw = torch.zeros((m, n + 25), dtype=torch.bfloat16)
+    dyw[:, :n] = dy
+    dyd = dyw.to(DEV)[:, :n]
+    u = torch.zeros((m, n + 8), dtype=torch.bfloat16, device=DEV)[:, :n]
+    dxw = torch.full((m, k + 40), 5.0, dtype=torch.bfloat16, device=DEV)
+    tern.tern_gemm_dx(dyd, pt, s, u, dxw[:, :k], k)
+    torch.cuda.synchronize()
+    u_ref = oracle.oracle_scale_grad(tern_inputs.bf16_bits(dy), s_ref)
+    assert np.array_equal(tern_inputs.bf16_bits(u.cpu().contiguous()), u_ref)
+    dx_ref = oracle.oracle_gemm_dx(u_ref, p_ref, k)
+    assert_within_tolerance(bf16_to_f64(dxw[:, :k].contiguous()), dx_ref, np.ones(k, np.float32),
+                            row_norms(u_ref), f"dx strided m={m}")
+    assert torch.all(dxw[:, k:] == 5.0)          # columns past k untouched
+
+
+@pytest.mark.parametrize("m,k,n,act_from", [(5, 256, 77, 37), (20, 192, 333, 200),
+                                            (31, 128, 40, 0)])
+def test_gemm_ex_few_tokens_ragged_activation_boundary(m, k, n, act_from):
+    # the few-token kernel with n not a multiple of 16 and the activated
+    # columns starting inside a 16-channel block
+    x, w = tern_inputs.draw(m, k, n, seed=m * 11 + n)
+    check_layer_ex(x, w, _bias(n, m), tern.TERN_ACT_GELU_TANH, act_from,
+                   f"ex few tokens m={m} n={n} from {act_from}", full=True)
+
+
 @pytest.mark.parametrize("layer", ["dit.up.m2048", "flux_qkv", "flux_mlp.up"])
 def test_workload_dx(layer):
     # the input gradients of the layers at full size: every weight and the
