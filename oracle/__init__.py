@@ -10,10 +10,13 @@ from .oracle import (  # noqa: F401
     library_path,
     oracle_epilogue,
     oracle_gemm,
+    oracle_gemm_a8,
     oracle_gemm_dx,
     oracle_pack,
+    oracle_pack_a8,
     oracle_pack_transposed,
     oracle_quantize,
+    oracle_quantize_act,
     oracle_scale_grad,
     oracle_unpack,
 )

@@ -22,6 +22,14 @@
  *  - An epilogue variant of that output: a per-channel bias and the
  *    tanh-form GELU on a trailing range of columns (oracle_epilogue; not on
  *    the pages: the activation of the FLUX MLP, the reading is stated there).
+ *  - An 8-bit-activation variant of the layer (W1.58-A8; "1.58-bit FLUX",
+ *    section 4 names unquantized activations as the reason its latency did
+ *    not improve; the pages give no activation quantizer): each token's
+ *    activations are scaled by 127 / max|x| and rounded to int8
+ *    (oracle_quantize_act), and the layer is s_n * (max|x_m| / 127) times the
+ *    exact integer sum of q . T (oracle_gemm_a8).  oracle_pack_a8 writes the
+ *    codes with the four 2-bit fields of each 4-code group of every 16-code
+ *    word exchanged across groups (a 4 x 4 transposition of the fields).
  *  - The gradient of the layer with respect to its input, for training the
  *    ternary weights in the loop ("TerDiT", abstract: quantization-aware
  *    training of ternary DiTs; the pages give no formula): with
@@ -378,4 +386,89 @@ int oracle_gemm_dx(const uint16_t* u, int64_t m, int64_t n, int64_t ldu, const u
   free(th);
   free(ud);
   return rc;
+}
+
+/*
+ * Per-token activation quantization to int8 (absmax):
+ *
+ *   g_m = max_k |x[m][k]|   (bf16 values, exact in fp32)
+ *   q[m][k] = rint( fp32(x[m][k] * fp32(127 / g_m)) )   (ties to even)
+ *   xs[m] = fp32(g_m / 127)
+ *
+ * each division and product one IEEE single-precision operation; a row of
+ * zeros gives q = 0 and xs = 0.  |x| <= g gives |x * (127 / g)| <= 127 (1 +
+ * 2^-23)^2 < 127.5, so q lies in [-127, 127].
+ */
+int oracle_quantize_act(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, int8_t* q,
+                        int64_t ldq, float* xs) {
+  if (m < 0 || k < 0 || ldx < k || ldq < k) return ORACLE_BAD_ARG;
+  for (int64_t mm = 0; mm < m; ++mm) {
+    float g = 0.0f;
+    for (int64_t kk = 0; kk < k; ++kk) {
+      const float a = fabsf(bf16_bits_to_float(x[mm * ldx + kk]));
+      if (a > g) g = a;
+    }
+    if (g == 0.0f) {
+      for (int64_t kk = 0; kk < k; ++kk) q[mm * ldq + kk] = 0;
+      xs[mm] = 0.0f;
+      continue;
+    }
+    const float inv = 127.0f / g;
+    for (int64_t kk = 0; kk < k; ++kk) {
+      const float v = bf16_bits_to_float(x[mm * ldx + kk]) * inv;
+      q[mm * ldq + kk] = (int8_t)rintf(v);
+    }
+    xs[mm] = g / 127.0f;
+  }
+  return ORACLE_OK;
+}
+
+/*
+ * The 8-bit-activation layer, unrounded:
+ *   y[m][n] = s_n * xs_m * sum_k q[m][k] * T[n][k]
+ * with the sum exact in 64-bit integers (ascending k) and the two scale
+ * products in double.
+ */
+int oracle_gemm_a8(const int8_t* q, int64_t m, int64_t k, int64_t ldq, const float* xs,
+                   const uint8_t* p, int64_t n, int64_t ldp, const float* s, double* y,
+                   int64_t ldy) {
+  if (m < 0 || n < 0 || k < 0 || ldq < k || ldp < (k + 3) / 4 || ldy < n) return ORACLE_BAD_ARG;
+  int8_t* trow = (int8_t*)malloc((size_t)(k > 0 ? k : 1));
+  if (!trow) return ORACLE_BAD_ARG;
+  for (int64_t nn = 0; nn < n; ++nn) {
+    for (int64_t kk = 0; kk < k; ++kk) {
+      unsigned code = (p[nn * ldp + kk / 4] >> (2 * (kk % 4))) & 3u;
+      trow[kk] = (int8_t)decode_code(code);
+    }
+    for (int64_t mm = 0; mm < m; ++mm) {
+      int64_t acc = 0;
+      for (int64_t kk = 0; kk < k; ++kk) acc += (int64_t)q[mm * ldq + kk] * trow[kk];
+      y[mm * ldy + nn] = (double)s[nn] * (double)xs[mm] * (double)acc;
+    }
+  }
+  free(trow);
+  return ORACLE_OK;
+}
+
+/*
+ * Field-transposed packing for the 8-bit-activation layer: in every 32-bit
+ * word of a packed row (codes 16 w .. 16 w + 15 of the row), field 4 i + j
+ * (bits 2(4i+j) .. 2(4i+j)+1) holds code 4 j + i of the word.  Rows are whole
+ * words (k % 16 == 0); bytes k/4 .. ldp8 - 1 of an output row are not written.
+ */
+int oracle_pack_a8(const uint8_t* p, int64_t n, int64_t k, int64_t ldp, uint8_t* p8,
+                   int64_t ldp8) {
+  const int64_t nb = k / 4;
+  if (n < 0 || k < 0 || k % 16 != 0 || ldp < nb || ldp8 < nb) return ORACLE_BAD_ARG;
+  for (int64_t nn = 0; nn < n; ++nn) {
+    for (int64_t b = 0; b < nb; ++b) p8[nn * ldp8 + b] = 0;
+    for (int64_t c = 0; c < k; ++c) {
+      const int64_t w = c / 16, f = c % 16;     /* code f of word w */
+      const int64_t i = f % 4, j = f / 4;       /* code 4 j + i -> field 4 i + j */
+      const unsigned code = (p[nn * ldp + c / 4] >> (2 * (c % 4))) & 3u;
+      const int64_t field = 16 * w + 4 * i + j;
+      p8[nn * ldp8 + field / 4] |= (uint8_t)(code << (2 * (field % 4)));
+    }
+  }
+  return ORACLE_OK;
 }

@@ -56,8 +56,12 @@ def load(path: str | None = None):
     lib.oracle_epilogue.argtypes = [vp, i64, i64, i64, vp, ctypes.c_int, i64]
     lib.oracle_scale_grad.argtypes = [vp, i64, i64, i64, vp, vp, i64]
     lib.oracle_gemm_dx.argtypes = [vp, i64, i64, i64, vp, i64, i64, vp, i64, ctypes.c_int]
+    lib.oracle_quantize_act.argtypes = [vp, i64, i64, i64, vp, i64, vp]
+    lib.oracle_gemm_a8.argtypes = [vp, i64, i64, i64, vp, vp, i64, i64, vp, vp, i64]
+    lib.oracle_pack_a8.argtypes = [vp, i64, i64, i64, vp, i64]
     for f in (lib.oracle_quantize, lib.oracle_pack, lib.oracle_unpack, lib.oracle_gemm,
-              lib.oracle_epilogue, lib.oracle_scale_grad, lib.oracle_gemm_dx):
+              lib.oracle_epilogue, lib.oracle_scale_grad, lib.oracle_gemm_dx,
+              lib.oracle_quantize_act, lib.oracle_gemm_a8, lib.oracle_pack_a8):
         f.restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -198,3 +202,42 @@ def oracle_gemm_dx(u_bf16_bits: np.ndarray, p: np.ndarray, k: int, n: int | None
     _check(lib.oracle_gemm_dx(_ptr(u), m, n, nu, _ptr(p), k, ldp, _ptr(dx), k, nthreads),
            "oracle_gemm_dx")
     return dx
+
+
+def oracle_quantize_act(x_bf16_bits: np.ndarray, lib=None):
+    """Per-token absmax int8 activations: ``(q int8 [M, K], xs float32 [M])``."""
+    lib = lib or load()
+    x = np.ascontiguousarray(x_bf16_bits, dtype=np.uint16)
+    m, k = x.shape
+    q = np.empty((m, k), np.int8)
+    xs = np.empty((m,), np.float32)
+    _check(lib.oracle_quantize_act(_ptr(x), m, k, k, _ptr(q), k, _ptr(xs)), "oracle_quantize_act")
+    return q, xs
+
+
+def oracle_gemm_a8(q: np.ndarray, xs: np.ndarray, p: np.ndarray, s: np.ndarray, lib=None):
+    """Unrounded 8-bit-activation layer ``s_n * xs_m * sum_k q[m,k] T[n,k]``
+    in float64 ``[M, N]`` (the integer sum exact)."""
+    lib = lib or load()
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    xs = np.ascontiguousarray(xs, dtype=np.float32)
+    p = np.ascontiguousarray(p, dtype=np.uint8)
+    s = np.ascontiguousarray(s, dtype=np.float32)
+    m, k = q.shape
+    n, ldp = p.shape
+    y = np.empty((m, n), np.float64)
+    _check(lib.oracle_gemm_a8(_ptr(q), m, k, k, _ptr(xs), _ptr(p), n, ldp, _ptr(s), _ptr(y), n),
+           "oracle_gemm_a8")
+    return y
+
+
+def oracle_pack_a8(p: np.ndarray, k: int, lib=None) -> np.ndarray:
+    """Field-transposed packing of the codes of ``p`` (row length k, a
+    multiple of 16): ``[N, k / 4]`` uint8."""
+    lib = lib or load()
+    p = np.ascontiguousarray(p, dtype=np.uint8)
+    n, ldp = p.shape
+    nb = k // 4
+    out = np.empty((n, nb), np.uint8)
+    _check(lib.oracle_pack_a8(_ptr(p), n, k, ldp, _ptr(out), nb), "oracle_pack_a8")
+    return out

@@ -455,6 +455,114 @@ def test_pack_transposed_worked_example():
 
 
 # --------------------------------------------------------------------------
+# 8-bit activations (per-token absmax) and the W1.58-A8 layer
+# --------------------------------------------------------------------------
+
+def _rne_int(fr: Fraction) -> int:
+    """Round a rational to the nearest integer, ties to even, exactly."""
+    f = math.floor(fr)
+    d = fr - f
+    if d > Fraction(1, 2) or (d == Fraction(1, 2) and f % 2 == 1):
+        return f + 1
+    return f
+
+
+def test_quantize_act_worked_examples():
+    # row 0: max 2 -> 127/2 = 63.5; 1 * 63.5 = 63.5 is a tie -> 64 (even),
+    #        0.5 * 63.5 = 31.75 -> 32; scale 2/127
+    # row 1: max 127/64 -> 127/max = 64 exactly; 0.5078125 * 64 = 32.5 -> 32
+    #        (even), -0.5234375 * 64 = -33.5 -> -34 (even), 1/64 * 64 = 1;
+    #        scale (127/64)/127 = 1/64
+    # row 2: zeros -> codes 0, scale 0
+    x = torch.tensor([[1.0, -2.0, 0.5, 0.0],
+                      [1.984375, 0.5078125, -0.5234375, 0.015625],
+                      [0.0, 0.0, 0.0, 0.0]]).to(torch.bfloat16)
+    assert torch.equal(x.float(), torch.tensor([[1.0, -2.0, 0.5, 0.0],
+                                                [1.984375, 0.5078125, -0.5234375, 0.015625],
+                                                [0.0, 0.0, 0.0, 0.0]]))   # all exact in bf16
+    q, xs = oracle.oracle_quantize_act(tern_inputs.bf16_bits(x))
+    assert q.tolist() == [[64, -127, 32, 0], [127, 32, -34, 1], [0, 0, 0, 0]]
+    assert xs.tolist() == [float(np.float32(2.0 / 127.0)), 0.015625, 0.0]
+
+
+def test_quantize_act_matches_exact_rational_rounding():
+    # q = round(127 x / max|x|) away from the few products that fall within
+    # fp32 rounding of a half-integer; the scale is the correctly rounded
+    # fp32 quotient max|x| / 127
+    g = torch.Generator().manual_seed(91)
+    x = (torch.randn(12, 200, generator=g) * torch.logspace(-3, 2, 12)[:, None]).to(torch.bfloat16)
+    x[3, 17] = -x[3].abs().max() * 1.5   # a negative maximum
+    xb = tern_inputs.bf16_bits(x)
+    q, xs = oracle.oracle_quantize_act(xb)
+    xv = _bf16_values(xb)
+    checked = 0
+    for m in range(12):
+        gm = max(Fraction(abs(float(v))) for v in xv[m])
+        assert xs[m] == _rn32(gm / 127)
+        assert int(np.abs(q[m]).max()) == 127
+        for kk in range(200):
+            e = Fraction(float(xv[m, kk])) * 127 / gm
+            frac = abs(e - math.floor(e) - Fraction(1, 2))
+            if frac > Fraction(1, 10**5):
+                assert q[m, kk] == _rne_int(e), (m, kk)
+                checked += 1
+    assert checked > 0.99 * 12 * 200
+
+
+def test_quantize_act_power_of_two_invariance_and_sign():
+    x, _ = tern_inputs.draw(9, 160, 4, seed=93)
+    q, xs = oracle.oracle_quantize_act(tern_inputs.bf16_bits(x))
+    q2, xs2 = oracle.oracle_quantize_act(tern_inputs.bf16_bits(x * 4))
+    qn, xsn = oracle.oracle_quantize_act(tern_inputs.bf16_bits(-x))
+    assert np.array_equal(q, q2) and np.array_equal(xs2, xs * 4)
+    assert np.array_equal(qn, -q) and np.array_equal(xsn, xs)
+
+
+def test_gemm_a8_integer_activations_equal_bf16_layer():
+    # integer activations in [-127, 127] with a 127 in every row quantize to
+    # themselves with scale 1, so the A8 layer equals the bf16 layer exactly
+    rng = np.random.default_rng(95)
+    m, k, n = 6, 64, 11
+    xi = rng.integers(-127, 128, size=(m, k)).astype(np.float32)
+    xi[np.arange(m), rng.integers(0, k, size=m)] = 127.0
+    xb = tern_inputs.bf16_bits(torch.from_numpy(xi).to(torch.bfloat16))
+    t = rng.integers(-1, 2, size=(n, k)).astype(np.int8)
+    s = rng.uniform(0.01, 0.1, size=n).astype(np.float32)
+    p = oracle.oracle_pack(t)
+    q, xs = oracle.oracle_quantize_act(xb)
+    assert np.array_equal(q, xi.astype(np.int8)) and np.all(xs == 1.0)
+    assert np.array_equal(oracle.oracle_gemm_a8(q, xs, p, s), oracle.oracle_gemm(xb, p, s))
+
+
+def test_gemm_a8_equals_numpy_integer_matmul():
+    x, w = tern_inputs.draw(7, 192, 21, seed=97, x_dist="student_t3")
+    t, s = oracle.oracle_quantize(w.numpy())
+    q, xs = oracle.oracle_quantize_act(tern_inputs.bf16_bits(x))
+    y = oracle.oracle_gemm_a8(q, xs, oracle.oracle_pack(t), s)
+    acc = q.astype(np.int64) @ t.astype(np.int64).T
+    ref = s.astype(np.float64)[None, :] * xs.astype(np.float64)[:, None] * acc
+    assert np.array_equal(y, ref)
+
+
+def test_pack_a8_worked_example_and_involution():
+    # codes of one word: t = 1 0 -1 1 | 0 1 1 -1 | -1 -1 0 0 | 1 1 1 0; field
+    # 4i + j holds code 4j + i: fields 0-3 = codes 0, 4, 8, 12 = 1, 0, -1, 1
+    # -> 01 00 11 01 (LSB first) = 0x71; fields 4-7 = codes 1, 5, 9, 13 = 0, 1,
+    # -1, 1 -> 0x74; fields 8-11 = codes 2, 6, 10, 14 = -1, 1, 0, 1 -> 0x47;
+    # fields 12-15 = codes 3, 7, 11, 15 = 1, -1, 0, 0 -> 0x0D
+    t = np.array([[1, 0, -1, 1, 0, 1, 1, -1, -1, -1, 0, 0, 1, 1, 1, 0]], np.int8)
+    p = oracle.oracle_pack(t)
+    assert oracle.oracle_pack_a8(p, 16).tolist() == [[0x71, 0x74, 0x47, 0x0D]]
+    # the field transposition is its own inverse
+    tt = tern_inputs.random_ternary(13, 96, seed=99).numpy()
+    pp = oracle.oracle_pack(tt)
+    p8 = oracle.oracle_pack_a8(pp, 96)
+    assert np.array_equal(oracle.oracle_pack_a8(p8, 96), pp[:, :24])
+    with pytest.raises(ValueError):
+        oracle.oracle_pack_a8(pp, 88)    # not whole 16-code words
+
+
+# --------------------------------------------------------------------------
 # mutation check: the pins above must catch plausible mistakes in the oracle
 # --------------------------------------------------------------------------
 
@@ -489,6 +597,17 @@ MUTANTS = {
                         "(j->p[nn * j->ldp + (kk ^ 1) / 4] >> (2 * ((kk ^ 1) % 4)))"),
     "dx_wrong_row": ("const double* ur = j->ud + mm * j->n;",
                      "const double* ur = j->ud + ((mm + 1) % j->m) * j->n;"),
+    "act_ties_away": ("q[mm * ldq + kk] = (int8_t)rintf(v);", "q[mm * ldq + kk] = (int8_t)roundf(v);"),
+    "act_range_128": ("const float inv = 127.0f / g;", "const float inv = 128.0f / g;"),
+    "act_scale_inverted": ("xs[mm] = g / 127.0f;", "xs[mm] = 127.0f / g;"),
+    "act_max_skips_first": ("for (int64_t kk = 0; kk < k; ++kk) {\n      const float a = fabsf",
+                            "for (int64_t kk = 1; kk < k; ++kk) {\n      const float a = fabsf"),
+    "a8_no_token_scale": ("(double)s[nn] * (double)xs[mm] * (double)acc",
+                          "(double)s[nn] * (double)acc"),
+    "a8_wrong_weight_index": ("acc += (int64_t)q[mm * ldq + kk] * trow[kk];",
+                              "acc += (int64_t)q[mm * ldq + kk] * trow[k - 1 - kk];"),
+    "pack_a8_untransposed": ("const int64_t field = 16 * w + 4 * i + j;",
+                             "const int64_t field = 16 * w + 4 * j + i;"),
 }
 
 PIN_TESTS = [
@@ -502,7 +621,11 @@ PIN_TESTS = [
     test_epilogue_gelu_odd_part_is_identity, test_epilogue_bias_and_activated_columns,
     test_scale_grad_matches_torch_single_product_then_bf16, test_scale_grad_ties_to_even,
     test_gemm_dx_adjoint_of_the_layer_exact, test_gemm_dx_equals_numpy_matmul,
-    test_pack_transposed_worked_example,
+    test_pack_transposed_worked_example, test_quantize_act_worked_examples,
+    test_quantize_act_matches_exact_rational_rounding,
+    test_quantize_act_power_of_two_invariance_and_sign,
+    test_gemm_a8_integer_activations_equal_bf16_layer, test_gemm_a8_equals_numpy_integer_matmul,
+    test_pack_a8_worked_example_and_involution,
 ]
 
 
