@@ -248,6 +248,85 @@ tern_status tern_gemm_dx(const void* dy_bf16, int64_t m, int64_t n, int64_t lddy
                          const uint8_t* pt, int64_t k, int64_t ldpt, const float* s,
                          void* u_bf16, int64_t ldu, void* dx_bf16, int64_t lddx, void* stream);
 
+/*
+ * 8-bit activations (W1.58-A8).  "1.58-bit FLUX" (section 4, limitation on
+ * speed) names the unquantized activations as the reason its latency barely
+ * improved, and gives no activation quantizer.  These calls use absmax
+ * quantization per token (the BitNet b1.58 family the paper follows,
+ * section 1), with the ternary weights unchanged, on the int8 matrix cores.
+ */
+
+/*
+ * tern_quantize_act: per-token int8 activations.
+ *
+ *   g_m      = max_k |x[m][k]|
+ *   q[m][k]  = rint( fp32( x[m][k] * fp32(127 / g_m) ) )   (ties to even)
+ *   xs[m]    = fp32( g_m / 127 )
+ *
+ * with both quotients correctly rounded to fp32; |q| <= 127.  A row of zeros
+ * (or k == 0) gives q = 0 and xs = 0.
+ *
+ *   x   [m, ldx] bf16 activations
+ *   q   [m, ldq] int8 output codes; columns >= k untouched
+ *   xs  [m] fp32 output per-token scales
+ * Sizes: 0 <= m, k <= 2^31 - 1 (else TERN_ERR_SHAPE); m == 0 is a no-op;
+ * k == 0 writes xs only (x and q are not read and may be NULL).  ldx >= k,
+ * ldq >= k (else TERN_ERR_STRIDE).  Alignment (else TERN_ERR_ALIGN): x 2-byte
+ * aligned, xs 4-byte aligned.
+ */
+tern_status tern_quantize_act(const void* x_bf16, int64_t m, int64_t k, int64_t ldx, int8_t* q,
+                              int64_t ldq, float* xs, void* stream);
+
+/*
+ * tern_pack_a8: packed codes re-arranged for tern_gemm_a8.  Within every
+ * 32-bit little-endian word of a row (codes 16 w .. 16 w + 15), field 4 i + j
+ * (bits 2(4i+j) .. 2(4i+j)+1) of the output holds code 4 j + i of the word:
+ * the 2-bit fields transposed as a 4 x 4 matrix.  The arrangement is its
+ * own inverse.
+ *
+ *   p   [n, ldp] uint8, packed as tern_pack writes it for a row length k
+ *   p8  [n, ldp8] uint8 output; bytes k/4 .. ldp8 - 1 of a row untouched.
+ *       p8 == p with ldp8 == ldp converts in place; otherwise the two must
+ *       not overlap.
+ * Sizes: 0 <= n, k <= 2^31 - 1 and k % 16 == 0 (else TERN_ERR_SHAPE); a zero
+ * size is a no-op.  ldp, ldp8 >= k/4 (else TERN_ERR_STRIDE).  Alignment
+ * (else TERN_ERR_ALIGN): p and p8 4-byte aligned, ldp % 4 == 0,
+ * ldp8 % 4 == 0.
+ */
+tern_status tern_pack_a8(const uint8_t* p, int64_t n, int64_t k, int64_t ldp, uint8_t* p8,
+                         int64_t ldp8, void* stream);
+
+/*
+ * tern_gemm_a8: the ternary layer on int8 activations.
+ *
+ *   Y[m][n] = bf16( f_n( fp32( fp32(acc[m][n]) * fp32(s[n] / 64) ) * xs[m] + b[n] ) ),
+ *   acc[m][n] = 64 * sum_k q[m][k] * T[n][k]       (exact int32)
+ *
+ * with T decoded from p8, one round-to-nearest-even conversion to bf16, b and
+ * f_n as in tern_gemm_ex (bias NULL and TERN_ACT_NONE: the plain layer).  The
+ * fp32 steps are exact but for at most three roundings of 2^-24 relative
+ * (acc converted, the two products) before the bf16 rounding.
+ *
+ *   q    [m, ldq] int8 activations, as tern_quantize_act writes them
+ *   xs   [m] fp32 per-token scales, as tern_quantize_act writes them
+ *   p8   [n, ldp8] codes arranged by tern_pack_a8 for a row length k
+ *   s    [n] fp32 per-output-channel scales
+ *   bias, act, act_from   as tern_gemm_ex
+ *   y    [m, ldy] bf16 output; columns >= n untouched
+ * Sizes: m, n, k >= 0 and k % 128 == 0 (else TERN_ERR_SHAPE); m == 0 or
+ * n == 0 is a no-op; k == 0 writes bf16(f_n(b[n])).  m, n <= 2^31 - 1,
+ * k <= 2^18 (the int32 sums cannot overflow) and
+ * ceil(m/64) * ceil(n/128) <= 2^31 - 1.
+ * ldq >= k, ldp8 >= k/4, ldy >= n, and ldq < 2^24, ldp8 < 2^24, ldy < 2^31
+ * (else TERN_ERR_STRIDE).  Alignment (else TERN_ERR_ALIGN): q and p8 16-byte
+ * aligned, ldq % 16 == 0, ldp8 % 16 == 0; y 2-byte aligned; xs, s and bias
+ * 4-byte aligned.
+ */
+tern_status tern_gemm_a8(const int8_t* q, int64_t m, int64_t k, int64_t ldq, const float* xs,
+                         const uint8_t* p8, int64_t n, int64_t ldp8, const float* s,
+                         const float* bias, tern_act act, int64_t act_from, void* y_bf16,
+                         int64_t ldy, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -33,7 +33,8 @@ TERN_BF16 = 1
 TERN_QUANTIZE_MAX_K = 32768
 
 EXPORTED = ("tern_quantize", "tern_quantize_pack", "tern_pack", "tern_unpack", "tern_gemm",
-            "tern_gemm_ex", "tern_pack_transposed", "tern_gemm_dx", "tern_status_string")
+            "tern_gemm_ex", "tern_pack_transposed", "tern_gemm_dx", "tern_quantize_act",
+            "tern_pack_a8", "tern_gemm_a8", "tern_status_string")
 
 
 class TernError(RuntimeError):
@@ -60,8 +61,13 @@ def _load(path: str):
                                  i64, vp]
     lib.tern_pack_transposed.argtypes = [vp, i64, i64, i64, vp, i64, vp]
     lib.tern_gemm_dx.argtypes = [vp, i64, i64, i64, vp, i64, i64, vp, vp, i64, vp, i64, vp]
+    lib.tern_quantize_act.argtypes = [vp, i64, i64, i64, vp, i64, vp, vp]
+    lib.tern_pack_a8.argtypes = [vp, i64, i64, i64, vp, i64, vp]
+    lib.tern_gemm_a8.argtypes = [vp, i64, i64, i64, vp, vp, i64, i64, vp, vp, ctypes.c_int, i64,
+                                 vp, i64, vp]
     for name in ("tern_quantize", "tern_quantize_pack", "tern_pack", "tern_unpack", "tern_gemm",
-                 "tern_gemm_ex", "tern_pack_transposed", "tern_gemm_dx"):
+                 "tern_gemm_ex", "tern_pack_transposed", "tern_gemm_dx", "tern_quantize_act",
+                 "tern_pack_a8", "tern_gemm_a8"):
         getattr(lib, name).restype = ctypes.c_int
     lib.tern_status_string.argtypes = [ctypes.c_int]
     lib.tern_status_string.restype = ctypes.c_char_p
@@ -255,6 +261,63 @@ def tern_gemm_dx(dy: torch.Tensor, pt: torch.Tensor, s: torch.Tensor, u: torch.T
                                              _stream(stream)))
 
 
+def tern_quantize_act(x: torch.Tensor, q: torch.Tensor, xs: torch.Tensor, k: int | None = None,
+                      stream=None) -> None:
+    """Per-token int8 activations of bf16 ``x`` [m, k]: codes into ``q`` int8
+    [m, >=k], scales max|x|/127 into ``xs`` fp32 [m]."""
+    ldx = _mat(x, "x", (torch.bfloat16,))
+    ldq = _mat(q, "q", (torch.int8,))
+    _vec(xs, "xs", torch.float32)
+    m = x.shape[0]
+    k = x.shape[1] if k is None else int(k)
+    if k > x.shape[1] or tuple(q.shape[:1]) != (m,) or q.shape[1] < k or xs.shape[0] != m:
+        raise ValueError("shapes must be x [m, k], q [m, >=k], xs [m]")
+    _check("tern_quantize_act", _lib.tern_quantize_act(x.data_ptr(), m, k, ldx, q.data_ptr(), ldq,
+                                                       xs.data_ptr(), _stream(stream)))
+
+
+def tern_pack_a8(p: torch.Tensor, p8: torch.Tensor, k: int, n: int | None = None,
+                 stream=None) -> None:
+    """Arrange the codes of ``p`` uint8 [n, >=k/4] for the int8 GEMM into
+    ``p8`` uint8 [n, >=k/4] (k % 16 == 0); ``p8`` may be ``p`` itself."""
+    ldp = _mat(p, "p", (torch.uint8,))
+    ldp8 = _mat(p8, "p8", (torch.uint8,))
+    n = p.shape[0] if n is None else int(n)
+    k = int(k)
+    if n > p.shape[0] or n > p8.shape[0] or p.shape[1] < k // 4 or p8.shape[1] < k // 4:
+        raise ValueError("p and p8 must be [>=n, >=k/4]")
+    _check("tern_pack_a8", _lib.tern_pack_a8(p.data_ptr(), n, k, ldp, p8.data_ptr(), ldp8,
+                                             _stream(stream)))
+
+
+def tern_gemm_a8(q: torch.Tensor, xs: torch.Tensor, p8: torch.Tensor, s: torch.Tensor,
+                 y: torch.Tensor, bias: torch.Tensor | None = None, act: int = TERN_ACT_NONE,
+                 act_from: int = 0, k: int | None = None, stream=None) -> None:
+    """The layer on int8 activations: ``y = bf16(f_n(s_n * xs_m * (q . T^T) +
+    bias))`` with ``q`` int8 [m, k], ``xs`` fp32 [m], ``p8`` from tern_pack_a8,
+    ``s`` fp32 [n], bias and act as ``tern_gemm_ex``."""
+    ldq = _mat(q, "q", (torch.int8,))
+    ldp8 = _mat(p8, "p8", (torch.uint8,))
+    ldy = _mat(y, "y", (torch.bfloat16,))
+    _vec(xs, "xs", torch.float32)
+    _vec(s, "s", torch.float32)
+    m = q.shape[0]
+    k = q.shape[1] if k is None else int(k)
+    n = p8.shape[0]
+    if k > q.shape[1] or xs.shape[0] != m or p8.shape[1] < k // 4 or s.shape[0] != n \
+            or tuple(y.shape[:1]) != (m,) or y.shape[1] < n:
+        raise ValueError("shapes must be q [m, k], xs [m], p8 [n, >=k/4], s [n], y [m, >=n]")
+    b_ptr = None
+    if bias is not None:
+        _vec(bias, "bias", torch.float32)
+        if bias.shape[0] != n:
+            raise ValueError("bias must be [n]")
+        b_ptr = bias.data_ptr()
+    _check("tern_gemm_a8", _lib.tern_gemm_a8(q.data_ptr(), m, k, ldq, xs.data_ptr(), p8.data_ptr(),
+                                             n, ldp8, s.data_ptr(), b_ptr, int(act), int(act_from),
+                                             y.data_ptr(), ldy, _stream(stream)))
+
+
 # ---------------------------------------------------------------------------
 # allocating conveniences (torch allocates the outputs; the library computes)
 # ---------------------------------------------------------------------------
@@ -329,3 +392,33 @@ def linear_dx(dy: torch.Tensor, pt: torch.Tensor, s: torch.Tensor, k: int, strea
     dx = torch.empty((dy.shape[0], k), dtype=torch.bfloat16, device=dy.device)
     tern_gemm_dx(dy, pt, s, u, dx, k, stream)
     return dx
+
+
+def quantize_act(x: torch.Tensor, stream=None):
+    """Return ``(q, xs)``: int8 codes [m, k] (rows 16-byte aligned) and fp32
+    per-token scales [m] of bf16 activations ``x`` [m, k]."""
+    m, k = x.shape
+    q = torch.empty((m, (k + 15) // 16 * 16), dtype=torch.int8, device=x.device)[:, :k]
+    xs = torch.empty((m,), dtype=torch.float32, device=x.device)
+    tern_quantize_act(x, q, xs, None, stream)
+    return q, xs
+
+
+def pack_a8(p: torch.Tensor, k: int, stream=None) -> torch.Tensor:
+    """Packed weights ``p`` (row length k) arranged for the int8 GEMM (same shape)."""
+    p8 = torch.zeros_like(p)
+    tern_pack_a8(p, p8, k, None, stream)
+    return p8
+
+
+def linear_a8(x: torch.Tensor, p8: torch.Tensor, s: torch.Tensor, bias: torch.Tensor | None = None,
+              gelu_from: int | None = None, stream=None) -> torch.Tensor:
+    """The layer with 8-bit activations: bf16 ``x`` [m, k] quantized per token,
+    then the int8 GEMM with ``p8`` from pack_a8 (and the optional fused bias and
+    GELU of linear_ex).  Returns bf16 [m, n]."""
+    q, xs = quantize_act(x, stream)
+    y = torch.empty((x.shape[0], p8.shape[0]), dtype=torch.bfloat16, device=x.device)
+    act = TERN_ACT_NONE if gelu_from is None else TERN_ACT_GELU_TANH
+    tern_gemm_a8(q, xs, p8, s, y, bias, act, 0 if gelu_from is None else int(gelu_from), None,
+                 stream)
+    return y

@@ -147,6 +147,52 @@ tern_status tern_gemm_dx(const void* dy_bf16, int64_t m, int64_t n, int64_t lddy
                                     static_cast<uint16_t*>(dx_bf16), lddx, st));
 }
 
+tern_status tern_quantize_act(const void* x_bf16, int64_t m, int64_t k, int64_t ldx, int8_t* q,
+                              int64_t ldq, float* xs, void* stream) {
+  if (m < 0 || k < 0 || m > kMaxInt || k > kMaxInt) return TERN_ERR_SHAPE;
+  if (m == 0) return TERN_OK;
+  if (xs == nullptr || (k > 0 && (x_bf16 == nullptr || q == nullptr))) return TERN_ERR_NULL;
+  if (ldx < k || ldq < k) return TERN_ERR_STRIDE;
+  if (!aligned(x_bf16, 2) || !aligned(xs, 4)) return TERN_ERR_ALIGN;
+  return from_hip(tern::launch_quantize_act(static_cast<const uint16_t*>(x_bf16), m, k, ldx, q,
+                                            ldq, xs, static_cast<hipStream_t>(stream)));
+}
+
+tern_status tern_pack_a8(const uint8_t* p, int64_t n, int64_t k, int64_t ldp, uint8_t* p8,
+                         int64_t ldp8, void* stream) {
+  if (n < 0 || k < 0 || n > kMaxInt || k > kMaxInt || k % 16 != 0) return TERN_ERR_SHAPE;
+  if (n == 0 || k == 0) return TERN_OK;
+  if (p == nullptr || p8 == nullptr) return TERN_ERR_NULL;
+  if (ldp < k / 4 || ldp8 < k / 4) return TERN_ERR_STRIDE;
+  if (!aligned(p, 4) || !aligned(p8, 4) || ldp % 4 != 0 || ldp8 % 4 != 0) return TERN_ERR_ALIGN;
+  return from_hip(tern::launch_pack_a8(p, n, k, ldp, p8, ldp8, static_cast<hipStream_t>(stream)));
+}
+
+tern_status tern_gemm_a8(const int8_t* q, int64_t m, int64_t k, int64_t ldq, const float* xs,
+                         const uint8_t* p8, int64_t n, int64_t ldp8, const float* s,
+                         const float* bias, tern_act act, int64_t act_from, void* y_bf16,
+                         int64_t ldy, void* stream) {
+  if (act != TERN_ACT_NONE && act != TERN_ACT_GELU_TANH) return TERN_ERR_ARG;
+  if (act == TERN_ACT_GELU_TANH && (act_from < 0 || act_from > n)) return TERN_ERR_ARG;
+  // |sum| <= 127 * 64 * k < 2^31 for k <= 2^18.
+  if (m < 0 || n < 0 || k < 0 || m > kMaxInt || n > kMaxInt || k > (int64_t(1) << 18) ||
+      k % 128 != 0)
+    return TERN_ERR_SHAPE;
+  if (((m + 63) / 64) * ((n + 127) / 128) > kMaxInt) return TERN_ERR_SHAPE;
+  if (m == 0 || n == 0) return TERN_OK;
+  if (q == nullptr || xs == nullptr || p8 == nullptr || s == nullptr || y_bf16 == nullptr)
+    return TERN_ERR_NULL;
+  if (ldq < k || ldp8 < k / 4 || ldy < n) return TERN_ERR_STRIDE;
+  if (ldq > kGemmMaxLdp || ldp8 > kGemmMaxLdp || ldy > kMaxInt) return TERN_ERR_STRIDE;
+  if (!aligned(q, 16) || ldq % 16 != 0 || !aligned(p8, 16) || ldp8 % 16 != 0 ||
+      !aligned(y_bf16, 2) || !aligned(xs, 4) || !aligned(s, 4) || !aligned(bias, 4))
+    return TERN_ERR_ALIGN;
+  return from_hip(tern::launch_gemm_a8(q, m, k, ldq, xs, p8, n, ldp8, s, bias,
+                                       act == TERN_ACT_GELU_TANH ? act_from : n,
+                                       static_cast<uint16_t*>(y_bf16), ldy,
+                                       static_cast<hipStream_t>(stream)));
+}
+
 const char* tern_status_string(tern_status status) {
   switch (status) {
     case TERN_OK: return "TERN_OK: success";

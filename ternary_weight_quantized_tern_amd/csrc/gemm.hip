@@ -49,7 +49,6 @@ namespace tern {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBK = 64;                       // K per pipeline stage
 // s_waitcnt for this wave: vector-memory counter <= N and, with LGKM0, all
 // LDS operations complete.  (lgkmcnt saturates at 15 outstanding operations:
 // keeping at most one batch of operand reads in flight lets the compiler's
@@ -116,7 +115,11 @@ __device__ inline uint32_t pack_bf16x2(float a, float b) {
 // groups, so a ds_read_b128 of 64 lanes takes the minimum four passes.
 __device__ inline uint32_t xswz(uint32_t r) { return (r >> 1) & 7u; }
 
-template <int BM, int BN, int WAVES_M>
+// A8: int8 activations (one byte per element) with the int8 matrix cores
+// (v_mfma_i32_16x16x64_i8, K = 128 per stage); otherwise bf16 activations
+// with the bf16 matrix cores (K = 64 per stage).  An X row is 128 bytes of a
+// stage either way; a weight row is 16 bytes (64 codes) or 32 bytes (128).
+template <int BM, int BN, int WAVES_M, bool A8>
 struct TileCfg {
   static constexpr int kWavesM = WAVES_M;          // waves along M
   static constexpr int kWavesN = 4 / WAVES_M;      // waves along N
@@ -124,8 +127,11 @@ struct TileCfg {
   static constexpr int kWN = BN / kWavesN;         // wave tile rows (N)
   static constexpr int kTM = kWM / 16;             // 16x16 MFMA tiles per wave along M
   static constexpr int kTN = kWN / 16;             // ... along N
-  static constexpr int kXBytes = BM * kBK * 2;     // X bytes per stage (128 per row)
-  static constexpr int kPBytes = BN * kBK / 4;     // packed weight bytes per stage (16 per row)
+  static constexpr int kXElem = A8 ? 1 : 2;        // bytes per X element
+  static constexpr int kBK = A8 ? 128 : 64;        // K per pipeline stage
+  static constexpr int kPRow = kBK / 4;            // packed weight bytes per row per stage
+  static constexpr int kXBytes = BM * 128;         // X bytes per stage (128 per row)
+  static constexpr int kPBytes = BN * kPRow;       // packed weight bytes per stage
   static constexpr int kStage = kXBytes + kPBytes;
   static constexpr int kXInstr = kXBytes / 1024;   // 1 KiB DMA instructions per stage: X
   static constexpr int kPInstr = kPBytes / 1024;   // ... packed weights
@@ -138,28 +144,30 @@ struct TileCfg {
   static_assert((kWM * 128) % 1024 == 0 || kWavesM == 1, "row swizzle period");
 };
 
-// Y tile kernel.  With PERSIST, workgroup b computes tiles b, b + G, b + 2G,
+// Y tile kernel (A8: int8 X with a per-row scale xs, weights in the
+// field-transposed packing; otherwise bf16 X, xs not read).  With PERSIST, workgroup b computes tiles b, b + G, b + 2G,
 // ... of the XCD-aware order (G = gridDim.x, a multiple of 8, so that all of
 // a workgroup's tiles stay on its XCD), and the K steps of consecutive tiles
 // form one stream through the LDS ring: the requests run kRing-1 steps ahead
 // of the MFMAs and cross into the next tile, so a tile's first stages are in
 // LDS by the time the previous tile's epilogue ends.  Tile boundaries must
 // fall between iterations of the kRing-step unrolled loop: PERSIST requires
-// (k / 64) % kRing == 0.  Without PERSIST each workgroup computes tile b
-// only, for any k that is a multiple of 64.  With EPI the epilogue adds
+// (k / kBK) % kRing == 0.  Without PERSIST each workgroup computes tile b
+// only, for any k that is a multiple of 64 (128 with A8).  With EPI the epilogue adds
 // bias[n] (when bias is not null) and applies the tanh-form GELU to columns
 // n >= act_from; without it, bias and act_from are not read.
-template <int BM, int BN, int WAVES_M, int GM, bool PERSIST, int WPE, bool EPI>
+template <int BM, int BN, int WAVES_M, int GM, bool PERSIST, int WPE, bool EPI, bool A8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
-void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
-                       const uint8_t* __restrict__ p, int n, int ldp,
+void gemm_ternary_mfma(const uint8_t* __restrict__ x, int m, int k, int ldx,
+                       const float* __restrict__ xs, const uint8_t* __restrict__ p, int n, int ldp,
                        const float* __restrict__ s, const float* __restrict__ bias, int act_from,
                        uint16_t* __restrict__ y, int ldy, int tiles_m, int tiles_n, int y_flags) {
 #if defined(__HIP_DEVICE_COMPILE__)
   // (The body uses LDS address-space casts that only the device pass accepts.)
-  using C = TileCfg<BM, BN, WAVES_M>;
+  using C = TileCfg<BM, BN, WAVES_M, A8>;
   constexpr int kTM = C::kTM;
   constexpr int kTN = C::kTN;
+  const int ldxb = ldx * C::kXElem;  // X pitch in bytes (< 2^24, checked by the host)
   // One LDS object per ring stage, so that the compiler tracks each stage's
   // DMA writes separately.  kRing = 6 stages: one being read, one being read
   // next, four in flight.
@@ -175,7 +183,7 @@ void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
   const int grid = gridDim.x;
   const int bid = blockIdx.x;
   const int my_tiles = PERSIST ? (num_tiles - bid + grid - 1) / grid : 1;
-  const int stages = k / kBK;
+  const int stages = k / C::kBK;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -200,8 +208,9 @@ void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
     tile_coords(t, m0, n0);
     const int rows_m = (m - m0) < BM ? (m - m0) : BM;
     const int rows_n = (n - n0) < BN ? (n - n0) : BN;
-    xr = make_rsrc(x + static_cast<int64_t>(m0) * ldx,
-                   static_cast<uint32_t>((static_cast<int64_t>(rows_m - 1) * ldx + k) * 2));
+    xr = make_rsrc(x + static_cast<int64_t>(m0) * ldxb,
+                   static_cast<uint32_t>(static_cast<int64_t>(rows_m - 1) * ldxb +
+                                         static_cast<int64_t>(k) * C::kXElem));
     pr = make_rsrc(p + static_cast<int64_t>(n0) * ldp,
                    static_cast<uint32_t>(static_cast<int64_t>(rows_n - 1) * ldp + k / 4));
   };
@@ -211,7 +220,8 @@ void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
   // same number of them.  X load q fills
   // LDS bytes [1024 q, +1024): rows 8 q + lane/8, slot lane%8, which holds
   // logical chunk (lane%8) ^ xswz(row).  Weight load p fills [kXBytes +
-  // 1024 p, +1024): rows 64 p + lane, 16 bytes each.
+  // 1024 p, +1024): rows 64 p + lane, 16 bytes each (A8: rows 32 p + lane/2,
+  // half lane%2 of their 32 bytes).
   uint32_t dma_voff[C::kLoads];
   uint32_t dma_lds[C::kLoads];
   bool dma_is_x[C::kLoads];
@@ -223,8 +233,12 @@ void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
     if (dma_is_x[q]) {
       const uint32_t r = 8u * gi + (lane >> 3);
       const uint32_t c = (lane & 7) ^ xswz(r);
-      dma_voff[q] = (r * static_cast<uint32_t>(ldx) + 8u * c) * 2u;
+      dma_voff[q] = r * static_cast<uint32_t>(ldxb) + 16u * c;
       dma_lds[q] = 1024u * gi;
+    } else if constexpr (A8) {
+      const uint32_t r = 32u * (gi - C::kXInstr) + (lane >> 1);
+      dma_voff[q] = r * static_cast<uint32_t>(ldp) + 16u * (lane & 1);
+      dma_lds[q] = C::kXBytes + 1024u * (gi - C::kXInstr);
     } else {
       const uint32_t r = 64u * (gi - C::kXInstr) + lane;
       dma_voff[q] = r * static_cast<uint32_t>(ldp);
@@ -243,33 +257,37 @@ void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
   __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                 \
       (STAGE) < stages ? (dma_is_x[Q] ? (XR) : (PR)) : null_rsrc,                          \
       (lds_void_t*)(&BUF[dma_lds[Q]]), 16, dma_voff[Q],                                    \
-      ((STAGE) < stages ? (STAGE) : 0) * (dma_is_x[Q] ? kBK * 2 : kBK / 4), 0, 0);
+      ((STAGE) < stages ? (STAGE) : 0) * (dma_is_x[Q] ? 128 : C::kPRow), 0, 0);
 #define TERN_GEMM_ISSUE(BUF, XR, PR, STAGE) \
   _Pragma("unroll") for (int q = 0; q < C::kLoads; ++q) TERN_GEMM_DMA(BUF, XR, PR, STAGE, q)
 
   // MFMA operand reads.  Block b of a step covers, for the lanes of k-group
   // g, k = 16 g + 8 b .. 16 g + 8 b + 7 of the step: X chunk 2 g + b of row
   // (wm*kWM + 16 i + l16), and codes 8 b .. 8 b + 7 of 32-bit word g of
-  // weight row (wn*kWN + 16 j + l16).
+  // weight row (wn*kWN + 16 j + l16).  A8: k = 32 g + 16 b .. 32 g + 16 b +
+  // 15: the same X chunk (16 int8 values) and all 16 codes of word 2 g + b.
   const uint32_t x_row0 = static_cast<uint32_t>(wm * C::kWM + l16);
   const uint32_t xo0 = x_row0 * 128u + ((static_cast<uint32_t>(2 * g + 0) ^ xswz(x_row0)) << 4);
   const uint32_t xo1 = x_row0 * 128u + ((static_cast<uint32_t>(2 * g + 1) ^ xswz(x_row0)) << 4);
-  const uint32_t po = C::kXBytes + static_cast<uint32_t>(wn * C::kWN + l16) * 16u + 4u * g;
+  const uint32_t po = C::kXBytes + static_cast<uint32_t>(wn * C::kWN + l16) * C::kPRow +
+                      (A8 ? 8u : 4u) * g;
   static_assert(C::kWM % 16 == 0, "xswz(row + 16 i) == xswz(row)");
 
+  // (A8: the int32 sums live in the same accumulator registers, as bits.)
+  using PwT = std::conditional_t<A8, u32x2_t, uint32_t>;
   f32x4_t acc[kTN][kTM];
-  uint32_t pw[kTN], tq[kTN][4];
+  PwT pw[kTN];
+  uint32_t tq[kTN][4];
   u32x4_t wa[kTN], wb[kTN];
-  bf16x8_t xa[kTM], xb[kTM];
+  u32x4_t xa[kTM], xb[kTM];
 
   // Operand reads out of ring stage BUF: the 32-bit code words of every
   // weight tile (READ_PW), the X chunks of k-block 0 (READ_XA) and of k-block
   // 1 (READ_XB); READ_A is all of a step's words and k-block 0 chunks.
-#define TERN_GEMM_READ_PW(BUF, J) pw[J] = *reinterpret_cast<const uint32_t*>(&BUF[po + (J) * 256]);
-#define TERN_GEMM_READ_XA(BUF, I) \
-  xa[I] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(&BUF[xo0 + (I) * 2048]));
-#define TERN_GEMM_READ_XB(BUF, I) \
-  xb[I] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(&BUF[xo1 + (I) * 2048]));
+#define TERN_GEMM_READ_PW(BUF, J) \
+  pw[J] = *reinterpret_cast<const PwT*>(&BUF[po + (J) * (16 * C::kPRow)]);
+#define TERN_GEMM_READ_XA(BUF, I) xa[I] = *reinterpret_cast<const u32x4_t*>(&BUF[xo0 + (I) * 2048]);
+#define TERN_GEMM_READ_XB(BUF, I) xb[I] = *reinterpret_cast<const u32x4_t*>(&BUF[xo1 + (I) * 2048]);
 #define TERN_GEMM_READ_A(BUF)                                         \
   _Pragma("unroll") for (int j = 0; j < kTN; ++j) TERN_GEMM_READ_PW(BUF, j) \
   _Pragma("unroll") for (int i = 0; i < kTM; ++i) TERN_GEMM_READ_XA(BUF, i)
@@ -299,11 +317,19 @@ void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
   // codes 8h + 2q and 8h + 2q + 1.  Lo units 0..3 build tq[j], 4..5 the
   // k-block 0 operand wa[j] (codes 0..7); the hi units build wb[j] (codes
   // 8..15) out of the same tq[j] in the next half step.
-  constexpr int kLoUnits = 6;
-  constexpr int kHiUnits = 2;
+  //
+  // A8: the words are in the field-transposed packing (field 4 i + j holds
+  // code 4 j + i), so (w << (6 - 2r)) & 0xC0C0C0C0 is operand register r
+  // itself: byte b holds code 4 r + b as the int8 value 0 / +64 / -64.  Lo
+  // unit r builds register r of wa[j] out of the first word, hi unit r
+  // register r of wb[j] out of the second.
+  constexpr int kLoUnits = A8 ? 4 : 6;
+  constexpr int kHiUnits = A8 ? 4 : 2;
   auto lo_unit = [&](int j, int u) {
     constexpr uint32_t kTop2 = 0xC0C0C0C0u;
-    if (u < 4) {
+    if constexpr (A8) {
+      wa[j][u] = (pw[j][0] << (6 - 2 * u)) & kTop2;
+    } else if (u < 4) {
       tq[j][u] = (pw[j] << (6 - 2 * u)) & kTop2;
     } else {
       const uint32_t sel = u == 4 ? 0x040C000Cu : 0x050C010Cu;
@@ -312,9 +338,13 @@ void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
     }
   };
   auto hi_unit = [&](int j, int u) {
-    const uint32_t sel = u == 0 ? 0x060C020Cu : 0x070C030Cu;
-    wb[j][2 * u] = __builtin_amdgcn_perm(tq[j][1], tq[j][0], sel);
-    wb[j][2 * u + 1] = __builtin_amdgcn_perm(tq[j][3], tq[j][2], sel);
+    if constexpr (A8) {
+      wb[j][u] = (pw[j][1] << (6 - 2 * u)) & 0xC0C0C0C0u;
+    } else {
+      const uint32_t sel = u == 0 ? 0x060C020Cu : 0x070C030Cu;
+      wb[j][2 * u] = __builtin_amdgcn_perm(tq[j][1], tq[j][0], sel);
+      wb[j][2 * u + 1] = __builtin_amdgcn_perm(tq[j][3], tq[j][2], sel);
+    }
   };
   auto decode_lo_all = [&]() {  // the first step's wa
 #pragma unroll
@@ -368,8 +398,7 @@ void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
 #define TERN_GEMM_HALF_A(CUR, ZERO)                                                     \
   _Pragma("unroll") for (int t = 0; t < kSlotsA; ++t) {                                 \
     if (t < kSlots)                                                                     \
-      mfma16<ZERO::value, kPad>(acc[t / kTM][t % kTM],                                  \
-                                __builtin_bit_cast(bf16x8_t, wa[t / kTM]), xa[t % kTM]);  \
+      mfma_op<A8, ZERO::value, kPad>(acc[t / kTM][t % kTM], wa[t / kTM], xa[t % kTM]);  \
     if (t < kTM) TERN_GEMM_READ_XB(CUR, t)                                              \
     _Pragma("unroll") for (int u = t * kUpsA; u < (t + 1) * kUpsA && u < kUnitsA; ++u)  \
       hi_unit(u / kHiUnits, u % kHiUnits);                                              \
@@ -382,8 +411,7 @@ void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
     lds_barrier();                                                                       \
     _Pragma("unroll") for (int t = 0; t < kSlotsB; ++t) {                                \
       if (t < kSlots)                                                                    \
-        mfma16<false, kPad>(acc[t / kTM][t % kTM],                                       \
-                            __builtin_bit_cast(bf16x8_t, wb[t / kTM]), xb[t % kTM]);     \
+        mfma_op<A8, false, kPad>(acc[t / kTM][t % kTM], wb[t / kTM], xb[t % kTM]);       \
       if (t < kTN) {                                                                     \
         TERN_GEMM_READ_PW(NXT, t)                                                        \
       } else if (t < kTN + C::kLoads) {                                                  \
@@ -402,7 +430,8 @@ void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
   // Epilogue of tile t.  For MFMA tile (j, i) the lane holds output channels
   // n = wn*kWN + 16 j + 4 g + e (e = 0..3) of token m = wm*kWM + 16 i + l16.
   // The decode produced 2 T, so y = bf16(fp32(acc * s) * 0.5), which equals
-  // bf16(fp32(acc / 2 * s)) exactly.
+  // bf16(fp32(acc / 2 * s)) exactly.  A8: the decode produced 64 T and the
+  // sum is an int32, so y = bf16(fp32(fp32(acc) * fp32(s / 64)) * xs[m]).
   //
   // Whole tiles with a 16-byte aligned Y and scale vector go through LDS:
   // each wave writes 16 of its rows at a time, kEpiJ MFMA tiles (16 kEpiJ
@@ -422,6 +451,15 @@ void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
     return best;
   }();
   constexpr bool kEpiLds = kEpiJ > 0;
+  // The decode's factor (2 or 64), removed exactly, and the accumulator as
+  // fp32 (A8: the int32 sum converted, exact below 2^24).
+  constexpr float kDecode = A8 ? 0.015625f : 0.5f;
+  auto acc_value = [](const f32x4_t& a) -> f32x4_t {
+    if constexpr (A8)
+      return __builtin_convertvector(__builtin_bit_cast(i32x4_t, a), f32x4_t);
+    else
+      return a;
+  };
   static_assert(kEpiLds || !PERSIST, "the persistent kernel stores through LDS");
   auto epilogue = [&](int t) {
     acc_ready();
@@ -439,8 +477,14 @@ void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
       f32x4_t sc[kTN];
 #pragma unroll
       for (int j = 0; j < kTN; ++j)
-        sc[j] = s != nullptr ? *reinterpret_cast<const f32x4_t*>(s + col0 + 16 * j + 4 * g) * 0.5f
-                             : f32x4_t{0.5f, 0.5f, 0.5f, 0.5f};
+        sc[j] = s != nullptr ? *reinterpret_cast<const f32x4_t*>(s + col0 + 16 * j + 4 * g) * kDecode
+                             : f32x4_t{kDecode, kDecode, kDecode, kDecode};
+      // A8: the scale of each of the lane's tokens (the tile is whole).
+      float xsv[A8 ? kTM : 1];
+      if constexpr (A8) {
+#pragma unroll
+        for (int i = 0; i < kTM; ++i) xsv[i] = xs[m0 + wm * C::kWM + 16 * i + l16];
+      }
       const bool act_all = col0 >= act_from;
       const bool act_none = col0 + C::kWN <= act_from;
       f32x4_t bsv[EPI ? kTN : 1];
@@ -483,10 +527,14 @@ void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
 #pragma unroll
         for (int jj = 0; jj < kEpiJ; ++jj) {
           asm volatile("" : "+a"(acc[jp + jj][i]));
-          v[jj] = acc[jp + jj][i];
+          v[jj] = acc_value(acc[jp + jj][i]);
         }
 #pragma unroll
         for (int jj = 0; jj < kEpiJ; ++jj) v[jj] *= sc[jp + jj];
+        if constexpr (A8) {
+#pragma unroll
+          for (int jj = 0; jj < kEpiJ; ++jj) v[jj] *= xsv[i];
+        }
         if constexpr (EPI) {
 #pragma unroll
           for (int jj = 0; jj < kEpiJ; ++jj) v[jj] += bsv[jp + jj];
@@ -542,6 +590,10 @@ void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
         float sc[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) sc[e] = (ng + e < n) ? (s != nullptr ? s[ng + e] : 1.0f) : 0.0f;
+        if constexpr (A8) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sc[e] *= kDecode;
+        }
         float bv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         if constexpr (EPI) {
 #pragma unroll
@@ -550,10 +602,13 @@ void gemm_ternary_mfma(const uint16_t* __restrict__ x, int m, int k, int ldx,
 #pragma unroll
         for (int i = 0; i < kTM; ++i) {
           const int mg = m0 + wm * C::kWM + 16 * i + l16;
+          const f32x4_t av = acc_value(acc[j][i]);
+          float xsm = 0.0f;
+          if constexpr (A8) xsm = mg < m ? xs[mg] : 0.0f;
           __bf16 b[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            float z = (acc[j][i][e] * sc[e]) * 0.5f;
+            float z = A8 ? (av[e] * sc[e]) * xsm : (av[e] * sc[e]) * 0.5f;
             if constexpr (EPI) {
               z += bv[e];
               if (ng + e >= act_from) z = gelu_tanh_f32(z);
@@ -678,14 +733,16 @@ __global__ void fill_empty_sum(uint16_t* y, int m, int n, int ldy, const float* 
 constexpr int kPersistentGrid = 256;
 constexpr int64_t kSmallMaxM = 32;
 
-template <int BM, int BN, int WAVES_M, int GM, int WPE, bool EPI>
-hipError_t launch_tiles(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const uint8_t* p,
-                        int64_t n, int64_t ldp, const float* s, const float* bias, int act_from,
-                        uint16_t* y, int64_t ldy, hipStream_t stream) {
+template <int BM, int BN, int WAVES_M, int GM, int WPE, bool EPI, bool A8 = false>
+hipError_t launch_tiles(const void* x, int64_t m, int64_t k, int64_t ldx, const float* xs,
+                        const uint8_t* p, int64_t n, int64_t ldp, const float* s,
+                        const float* bias, int act_from, uint16_t* y, int64_t ldy,
+                        hipStream_t stream) {
   const int tiles_m = static_cast<int>((m + BM - 1) / BM);
   const int tiles_n = static_cast<int>((n + BN - 1) / BN);
   const int64_t tiles = static_cast<int64_t>(tiles_m) * tiles_n;
-  const int stages = static_cast<int>(k / kBK);
+  const int stages = static_cast<int>(k / TileCfg<BM, BN, WAVES_M, A8>::kBK);
+  const uint8_t* xb = static_cast<const uint8_t*>(x);
   // Bit 0: 8-byte stores of Y; bit 1: 16-byte stores of Y, 16-byte loads of
   // the scales (and of the bias) and 32-bit offsets within 16 rows of Y.
   const int y_flags =
@@ -698,17 +755,17 @@ hipError_t launch_tiles(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, co
   if constexpr (WPE == 1) {
     if (stages % 6 == 0 && tiles > kPersistentGrid && m % BM == 0 && n % BN == 0 &&
         (y_flags & 2)) {
-      hipLaunchKernelGGL((gemm_ternary_mfma<BM, BN, WAVES_M, GM, true, WPE, EPI>),
-                         dim3(kPersistentGrid), dim3(kThreads), 0, stream, x,
-                         static_cast<int>(m), static_cast<int>(k), static_cast<int>(ldx), p,
+      hipLaunchKernelGGL((gemm_ternary_mfma<BM, BN, WAVES_M, GM, true, WPE, EPI, A8>),
+                         dim3(kPersistentGrid), dim3(kThreads), 0, stream, xb,
+                         static_cast<int>(m), static_cast<int>(k), static_cast<int>(ldx), xs, p,
                          static_cast<int>(n), static_cast<int>(ldp), s, bias, act_from, y,
                          static_cast<int>(ldy), tiles_m, tiles_n, y_flags);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((gemm_ternary_mfma<BM, BN, WAVES_M, GM, false, WPE, EPI>),
-                     dim3(static_cast<unsigned>(tiles)), dim3(kThreads), 0, stream, x,
-                     static_cast<int>(m), static_cast<int>(k), static_cast<int>(ldx), p,
+  hipLaunchKernelGGL((gemm_ternary_mfma<BM, BN, WAVES_M, GM, false, WPE, EPI, A8>),
+                     dim3(static_cast<unsigned>(tiles)), dim3(kThreads), 0, stream, xb,
+                     static_cast<int>(m), static_cast<int>(k), static_cast<int>(ldx), xs, p,
                      static_cast<int>(n), static_cast<int>(ldp), s, bias, act_from, y,
                      static_cast<int>(ldy), tiles_m, tiles_n, y_flags);
   return hipGetLastError();
@@ -726,16 +783,32 @@ hipError_t launch_big(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, cons
   // whichever still gives two tiles per CU, so that every CU has work.
   const auto tiles = [&](int64_t bm, int64_t bn) { return ((m + bm - 1) / bm) * ((n + bn - 1) / bn); };
   if (tiles(144, 384) >= kPersistentGrid)
-    return launch_tiles<144, 384, 1, 4, 1, EPI>(x, m, k, ldx, p, n, ldp, s, bias, act_from, y,
-                                                ldy, stream);
+    return launch_tiles<144, 384, 1, 4, 1, EPI>(x, m, k, ldx, nullptr, p, n, ldp, s, bias,
+                                                act_from, y, ldy, stream);
   if (m % 64 == 0 && n % 576 == 0 && tiles(64, 576) == kPersistentGrid)
-    return launch_tiles<64, 576, 1, 4, 1, EPI>(x, m, k, ldx, p, n, ldp, s, bias, act_from, y,
-                                               ldy, stream);
+    return launch_tiles<64, 576, 1, 4, 1, EPI>(x, m, k, ldx, nullptr, p, n, ldp, s, bias,
+                                               act_from, y, ldy, stream);
   if (tiles(64, 256) >= 2 * kPersistentGrid)
-    return launch_tiles<64, 256, 1, 4, 2, EPI>(x, m, k, ldx, p, n, ldp, s, bias, act_from, y,
-                                               ldy, stream);
-  return launch_tiles<64, 128, 1, 4, 2, EPI>(x, m, k, ldx, p, n, ldp, s, bias, act_from, y, ldy,
-                                             stream);
+    return launch_tiles<64, 256, 1, 4, 2, EPI>(x, m, k, ldx, nullptr, p, n, ldp, s, bias,
+                                               act_from, y, ldy, stream);
+  return launch_tiles<64, 128, 1, 4, 2, EPI>(x, m, k, ldx, nullptr, p, n, ldp, s, bias, act_from,
+                                             y, ldy, stream);
+}
+
+template <bool EPI>
+hipError_t launch_big_a8(const int8_t* q, int64_t m, int64_t k, int64_t ldq, const float* xs,
+                         const uint8_t* p8, int64_t n, int64_t ldp8, const float* s,
+                         const float* bias, int act_from, uint16_t* y, int64_t ldy,
+                         hipStream_t stream) {
+  // The int8 stage holds K = 128: 144 x 256 tiles fill six ring stages
+  // (156 KiB of LDS) and cut M = 4608 and every FLUX width into whole tiles;
+  // smaller layers use 64 x 128 tiles, two workgroups per CU.
+  const auto tiles = [&](int64_t bm, int64_t bn) { return ((m + bm - 1) / bm) * ((n + bn - 1) / bn); };
+  if (tiles(144, 256) >= kPersistentGrid)
+    return launch_tiles<144, 256, 1, 4, 1, EPI, true>(q, m, k, ldq, xs, p8, n, ldp8, s, bias,
+                                                      act_from, y, ldy, stream);
+  return launch_tiles<64, 128, 1, 4, 2, EPI, true>(q, m, k, ldq, xs, p8, n, ldp8, s, bias,
+                                                   act_from, y, ldy, stream);
 }
 
 }  // namespace
@@ -758,6 +831,24 @@ hipError_t launch_gemm(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, con
     return launch_gemm_small(x, m, k, ldx, p, n, ldp, s, bias, act_from, y, ldy, stream);
   if (epi) return launch_big<true>(x, m, k, ldx, p, n, ldp, s, bias, af, y, ldy, stream);
   return launch_big<false>(x, m, k, ldx, p, n, ldp, s, nullptr, af, y, ldy, stream);
+}
+
+hipError_t launch_gemm_a8(const int8_t* q, int64_t m, int64_t k, int64_t ldq, const float* xs,
+                          const uint8_t* p8, int64_t n, int64_t ldp8, const float* s,
+                          const float* bias, int64_t act_from, uint16_t* y, int64_t ldy,
+                          hipStream_t stream) {
+  const int af = static_cast<int>(act_from);
+  if (k == 0) {
+    int64_t blocks = (m * n + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(fill_empty_sum, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
+                       y, static_cast<int>(m), static_cast<int>(n), static_cast<int>(ldy), bias,
+                       af);
+    return hipGetLastError();
+  }
+  if (bias != nullptr || act_from < n)
+    return launch_big_a8<true>(q, m, k, ldq, xs, p8, n, ldp8, s, bias, af, y, ldy, stream);
+  return launch_big_a8<false>(q, m, k, ldq, xs, p8, n, ldp8, s, nullptr, af, y, ldy, stream);
 }
 
 }  // namespace tern

@@ -1,6 +1,6 @@
 // Device helpers shared by the ternary GEMM kernels (gemm.hip, gemm_small.hip):
 // vector types, raw buffer resources, the 2-bit code -> bf16 decode and the
-// tied-accumulator bf16 MFMA.  Internal to libternary.
+// tied-accumulator bf16 and int8 MFMAs.  Internal to libternary.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -10,6 +10,7 @@ namespace tern {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(4))) int i32x4_t;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
 typedef __attribute__((ext_vector_type(2))) unsigned u32x2_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -66,6 +67,31 @@ __device__ inline void mfma16(f32x4_t& acc, const bf16x8_t& a, const bf16x8_t& b
   } else {
     asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
   }
+}
+
+// One v_mfma_i32_16x16x64_i8 (16 int8 values per lane and operand, exact
+// int32 sums), tied like mfma16.  The accumulator registers are declared
+// fp32 and hold the int32 sums as bit patterns; the same hazard rule holds.
+template <bool ZERO, bool PAD = true>
+__device__ inline void mfma_i8(f32x4_t& acc, const u32x4_t& a, const u32x4_t& b) {
+  if constexpr (ZERO && PAD) {
+    asm volatile("s_nop 1\n\tv_mfma_i32_16x16x64_i8 %0, %1, %2, 0" : "=a"(acc) : "v"(a), "v"(b));
+  } else if constexpr (ZERO) {
+    asm volatile("v_mfma_i32_16x16x64_i8 %0, %1, %2, 0" : "=a"(acc) : "v"(a), "v"(b));
+  } else if constexpr (PAD) {
+    asm volatile("s_nop 1\n\tv_mfma_i32_16x16x64_i8 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  } else {
+    asm volatile("v_mfma_i32_16x16x64_i8 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  }
+}
+
+// The MFMA of an operand kind: int8 (A8) or bf16, operands as raw registers.
+template <bool A8, bool ZERO, bool PAD>
+__device__ inline void mfma_op(f32x4_t& acc, const u32x4_t& a, const u32x4_t& b) {
+  if constexpr (A8)
+    mfma_i8<ZERO, PAD>(acc, a, b);
+  else
+    mfma16<ZERO, PAD>(acc, __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b));
 }
 
 // The tanh form of GELU (Hendrycks and Gimpel) in fp32:

@@ -44,4 +44,19 @@ hipError_t launch_pack_transposed(const uint8_t* p, int64_t n, int64_t k, int64_
 hipError_t launch_scale_grad(const uint16_t* dy, int64_t m, int64_t n, int64_t lddy,
                              const float* s, uint16_t* u, int64_t ldu, hipStream_t stream);
 
+// Per-token int8 activations: q = rint(x * (127 / max|x|)), xs = max|x| / 127.
+hipError_t launch_quantize_act(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, int8_t* q,
+                               int64_t ldq, float* xs, hipStream_t stream);
+
+// Codes of p (k % 16 == 0) in the field-transposed packing of the int8 GEMM.
+hipError_t launch_pack_a8(const uint8_t* p, int64_t n, int64_t k, int64_t ldp, uint8_t* p8,
+                          int64_t ldp8, hipStream_t stream);
+
+// y = bf16(f(s[n] * xs[m] * (q . T^T) + bias)), k % 128 == 0, weights in the
+// field-transposed packing; bias and act_from as for launch_gemm.
+hipError_t launch_gemm_a8(const int8_t* q, int64_t m, int64_t k, int64_t ldq, const float* xs,
+                          const uint8_t* p8, int64_t n, int64_t ldp8, const float* s,
+                          const float* bias, int64_t act_from, uint16_t* y, int64_t ldy,
+                          hipStream_t stream);
+
 }  // namespace tern

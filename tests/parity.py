@@ -176,7 +176,7 @@ def gemm_ex_gpu(x_cpu, p_gpu, s_gpu, k, bias_cpu=None, act=0, act_from=0):
 
 
 def assert_within_tolerance_ex(y_gpu, y_lin_ref, s, xnorm, bias, act, act_from, cols=None,
-                               what=""):
+                               what="", rel_tol=REL_TOL, norm_tol=NORM_TOL):
     """Epilogue output against oracle_epilogue of the unrounded linear output.
 
     z_ref = y_lin_ref + b.  The GPU forms z in fp32 from an fp32 sum, so
@@ -195,8 +195,8 @@ def assert_within_tolerance_ex(y_gpu, y_lin_ref, s, xnorm, bias, act, act_from, 
     if act_on.any():
         y_ref[:, act_on] = oracle.oracle_epilogue(z_ref[:, act_on], None, oracle.ACT_GELU_TANH, 0)
     lip = np.where(act_on, GELU_LIP, 1.0)[None, :]
-    bound = (REL_TOL * np.abs(y_ref)
-             + lip * (NORM_TOL * s.astype(np.float64)[None, :] * xnorm[:, None]
+    bound = (rel_tol * np.abs(y_ref)
+             + lip * (norm_tol * s.astype(np.float64)[None, :] * xnorm[:, None]
                       + EPI_ADD_TOL * (np.abs(z_ref) + np.abs(b)[None, :])))
     err = np.abs(y_gpu - y_ref)
     bad = err > bound
@@ -294,4 +294,105 @@ def check_dx(dy_cpu: torch.Tensor, w_cpu: torch.Tensor, what: str, rows=None, co
         ref = oracle.oracle_gemm_dx(u_ref, oracle.oracle_pack(t_cols), len(cols))
         worst = max(worst, assert_within_tolerance(dxh[:, cols], ref, ones[: len(cols)], unorm,
                                                    what + " (cols)"))
+    return worst
+
+
+# ---------------------------------------------------------------------------
+# 8-bit activations (tern_quantize_act, tern_pack_a8, tern_gemm_a8)
+# ---------------------------------------------------------------------------
+
+# The int8 sum is exact; fp32(acc) and the two fp32 products add at most
+# three roundings of 2^-24 relative, then one bf16 rounding (at most 2^-8
+# relative): |y - y_ref| <= (2^-8 + 2^-21) |y_ref|.
+A8_REL_TOL = 2.0 ** -8 + 2.0 ** -21
+
+
+def quantize_act_gpu(x_cpu: torch.Tensor):
+    q, xs = tern.quantize_act(x_cpu.to(DEV))
+    torch.cuda.synchronize()
+    return q, xs
+
+
+def assert_act_bitexact(q_gpu, xs_gpu, q_ref, xs_ref, what=""):
+    qg = q_gpu.cpu().numpy()
+    xg = xs_gpu.cpu().numpy()
+    bad_q = int(np.count_nonzero(qg != q_ref))
+    bad_s = int(np.count_nonzero(xg.view(np.uint32) != xs_ref.view(np.uint32)))
+    if bad_q or bad_s:
+        idx = np.argwhere(qg != q_ref)
+        first = f"; first code at {tuple(idx[0])}: gpu {qg[tuple(idx[0])]} ref " \
+                f"{q_ref[tuple(idx[0])]}" if len(idx) else ""
+        raise AssertionError(f"{what}: {bad_q} codes and {bad_s} scales differ{first}")
+
+
+def gemm_a8_gpu(q_gpu, xs_gpu, p8_gpu, s_gpu, k, bias_cpu=None, act=0, act_from=0):
+    y = torch.empty((q_gpu.shape[0], p8_gpu.shape[0]), dtype=torch.bfloat16, device=DEV)
+    b = None if bias_cpu is None else torch.from_numpy(np.ascontiguousarray(bias_cpu)).to(DEV)
+    tern.tern_gemm_a8(q_gpu, xs_gpu, p8_gpu, s_gpu, y, b, act, act_from, k)
+    torch.cuda.synchronize()
+    return y
+
+
+def assert_within_tolerance_a8(y_gpu, y_ref, what=""):
+    bound = A8_REL_TOL * np.abs(y_ref)
+    err = np.abs(y_gpu - y_ref)
+    bad = err > bound
+    if np.any(bad) or not np.all(np.isfinite(y_gpu)):
+        idx = np.argwhere(bad | ~np.isfinite(y_gpu))
+        r, c = idx[0]
+        raise AssertionError(
+            f"{what}: {len(idx)} of {y_ref.size} outputs outside tolerance; first at (m={r}, n={c}):"
+            f" gpu={y_gpu[r, c]!r} ref={y_ref[r, c]!r} bound={bound[r, c]!r}")
+    return float(np.max(err / np.maximum(bound, 1e-300)))
+
+
+def check_layer_a8(x_cpu, w_cpu, what, rows=None, cols=None, full=False, bias=None, act=0,
+                   act_from=0, repeat_check=False):
+    """The A8 layer end to end on the GPU (quantize and pack the weights,
+    arrange them with tern_pack_a8, quantize the activations, the int8 GEMM)
+    against the oracle: weights, arranged codes and activations bit-exact;
+    the output within A8_REL_TOL (with the epilogue's terms for bias / GELU)
+    on every element (``full``) or on rows x all columns and all rows x
+    ``cols``."""
+    m, k = x_cpu.shape
+    t_ref, s_ref, p_ref = oracle_weights(w_cpu)
+    t_g, s_g, p_g = gpu_quantize_pack(w_cpu)
+    assert_bitexact_weights(t_g, s_g, p_g, t_ref, s_ref, p_ref, what)
+    del t_g
+    p8_ref = oracle.oracle_pack_a8(p_ref, k)
+    p8_g = tern.pack_a8(p_g, k)
+    torch.cuda.synchronize()
+    assert torch.equal(p8_g.cpu()[:, : k // 4], torch.from_numpy(p8_ref)), f"{what}: pack_a8"
+    xb = tern_inputs.bf16_bits(x_cpu)
+    q_ref, xs_ref = oracle.oracle_quantize_act(xb)
+    q_g, xs_g = quantize_act_gpu(x_cpu)
+    assert_act_bitexact(q_g, xs_g, q_ref, xs_ref, what)
+    y = gemm_a8_gpu(q_g, xs_g, p8_g, s_g, k, bias, act, act_from)
+    if repeat_check:
+        y2 = gemm_a8_gpu(q_g, xs_g, p8_g, s_g, k, bias, act, act_from)
+        assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), f"{what}: not deterministic"
+    yh = bf16_to_f64(y)
+    epi = bias is not None or act != 0
+    bias32 = None if bias is None else np.asarray(bias, np.float32)
+    zero = np.zeros(m)
+
+    def compare(yg, q_sel, xs_sel, col_sel, tag):
+        p_sel = p_ref if col_sel is None else p_ref[col_sel]
+        s_sel = s_ref if col_sel is None else s_ref[col_sel]
+        y_lin = oracle.oracle_gemm_a8(q_sel, xs_sel, p_sel, s_sel)
+        if not epi:
+            return assert_within_tolerance_a8(yg, y_lin, what + tag)
+        b_sel = None if bias32 is None else (bias32 if col_sel is None else bias32[col_sel])
+        return assert_within_tolerance_ex(yg, y_lin, s_sel, zero[: yg.shape[0]], b_sel, act,
+                                          act_from, cols=col_sel, what=what + tag,
+                                          rel_tol=A8_REL_TOL, norm_tol=0.0)
+
+    worst = 0.0
+    if full:
+        worst = compare(yh, q_ref, xs_ref, None, "")
+    else:
+        if rows is not None:
+            worst = max(worst, compare(yh[rows], q_ref[rows], xs_ref[rows], None, " (rows)"))
+        if cols is not None:
+            worst = max(worst, compare(yh[:, cols], q_ref, xs_ref, cols, " (cols)"))
     return worst

@@ -24,7 +24,7 @@ def declared_functions():
     with open(HEADER) as f:
         text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(tern_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(tern_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_boundary():
@@ -34,7 +34,7 @@ def test_header_declares_the_boundary():
 def test_library_exports_every_declared_symbol():
     out = subprocess.run(["nm", "-D", "--defined-only", tern.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
-    exported = set(re.findall(r"\bT (tern_[a-z_]+)\b", out))
+    exported = set(re.findall(r"\bT (tern_[a-z0-9_]+)\b", out))
     for name in declared_functions():
         assert name in exported, name
         assert hasattr(lib, name)
@@ -224,6 +224,80 @@ def test_gemm_dx_validation():
     assert call(dy=A + 1) == tern.TERN_ERR_ALIGN
     assert call(dx=A + 1) == tern.TERN_ERR_ALIGN
     assert call(s=A + 2) == tern.TERN_ERR_ALIGN
+
+
+def test_quantize_act_validation():
+    f = lib.tern_quantize_act
+    ok = dict(x=A, m=8, k=64, ldx=64, q=A, ldq=64, xs=A)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["x"], a["m"], a["k"], a["ldx"], a["q"], a["ldq"], a["xs"], NULL)
+
+    assert call(m=-1) == tern.TERN_ERR_SHAPE
+    assert call(k=2 ** 31) == tern.TERN_ERR_SHAPE
+    assert call(m=0, x=NULL, q=NULL, xs=NULL) == tern.TERN_OK
+    for name in ("x", "q", "xs"):
+        assert call(**{name: NULL}) == tern.TERN_ERR_NULL
+    assert call(k=0, x=NULL, q=NULL, xs=NULL) == tern.TERN_ERR_NULL   # xs is written
+    assert call(k=0, x=NULL, q=NULL, ldx=0, ldq=0, xs=A + 1) == tern.TERN_ERR_ALIGN  # x, q not read
+    assert call(ldx=63) == tern.TERN_ERR_STRIDE
+    assert call(ldq=63) == tern.TERN_ERR_STRIDE
+    assert call(x=A + 1) == tern.TERN_ERR_ALIGN
+    assert call(xs=A + 2) == tern.TERN_ERR_ALIGN
+
+
+def test_pack_a8_validation():
+    f = lib.tern_pack_a8
+    assert f(A, -1, 16, 4, A, 4, NULL) == tern.TERN_ERR_SHAPE
+    assert f(A, 8, 24, 8, A, 8, NULL) == tern.TERN_ERR_SHAPE      # k % 16 != 0
+    assert f(A, 8, 2 ** 31, 2 ** 29, A, 2 ** 29, NULL) == tern.TERN_ERR_SHAPE
+    assert f(NULL, 0, 16, 4, NULL, 4, NULL) == tern.TERN_OK
+    assert f(NULL, 8, 0, 4, NULL, 4, NULL) == tern.TERN_OK
+    assert f(NULL, 8, 16, 4, A, 4, NULL) == tern.TERN_ERR_NULL
+    assert f(A, 8, 16, 4, NULL, 4, NULL) == tern.TERN_ERR_NULL
+    assert f(A, 8, 32, 4, A, 8, NULL) == tern.TERN_ERR_STRIDE     # ldp < k/4
+    assert f(A, 8, 32, 8, A, 4, NULL) == tern.TERN_ERR_STRIDE     # ldp8 < k/4
+    assert f(A + 2, 8, 16, 4, A, 4, NULL) == tern.TERN_ERR_ALIGN
+    assert f(A, 8, 16, 4, A + 2, 4, NULL) == tern.TERN_ERR_ALIGN
+    assert f(A, 8, 16, 6, A, 4, NULL) == tern.TERN_ERR_ALIGN
+    assert f(A, 8, 16, 4, A, 6, NULL) == tern.TERN_ERR_ALIGN
+
+
+def test_gemm_a8_validation():
+    g = lib.tern_gemm_a8
+    ok = dict(q=A, m=8, k=128, ldq=128, xs=A, p=A, n=16, ldp=32, s=A, b=NULL, act=0, af=0, y=A,
+              ldy=16)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return g(a["q"], a["m"], a["k"], a["ldq"], a["xs"], a["p"], a["n"], a["ldp"], a["s"],
+                 a["b"], a["act"], a["af"], a["y"], a["ldy"], NULL)
+
+    assert call(act=2) == tern.TERN_ERR_ARG
+    assert call(act=1, af=17) == tern.TERN_ERR_ARG
+    assert call(act=1, af=-1, m=-1) == tern.TERN_ERR_ARG         # the kind is checked first
+    assert call(m=-1) == tern.TERN_ERR_SHAPE
+    assert call(k=64, ldq=128) == tern.TERN_ERR_SHAPE            # k % 128 != 0
+    assert call(k=2 ** 18 + 128, ldq=2 ** 18 + 128, ldp=2 ** 16 + 32) == tern.TERN_ERR_SHAPE
+    assert call(m=2 ** 30, n=2 ** 20, ldy=2 ** 20) == tern.TERN_ERR_SHAPE
+    assert call(m=0, q=NULL, xs=NULL, p=NULL, s=NULL, y=NULL) == tern.TERN_OK
+    assert call(n=0, q=NULL, xs=NULL, p=NULL, s=NULL, y=NULL) == tern.TERN_OK
+    for name in ("q", "xs", "p", "s", "y"):
+        assert call(**{name: NULL}) == tern.TERN_ERR_NULL
+    assert call(ldq=112) == tern.TERN_ERR_STRIDE
+    assert call(ldp=16) == tern.TERN_ERR_STRIDE                   # < k/4
+    assert call(ldy=15) == tern.TERN_ERR_STRIDE
+    assert call(ldq=1 << 24) == tern.TERN_ERR_STRIDE
+    assert call(ldp=1 << 24) == tern.TERN_ERR_STRIDE
+    assert call(q=A + 8) == tern.TERN_ERR_ALIGN
+    assert call(ldq=136) == tern.TERN_ERR_ALIGN
+    assert call(p=A + 4) == tern.TERN_ERR_ALIGN
+    assert call(ldp=40) == tern.TERN_ERR_ALIGN
+    assert call(y=A + 1) == tern.TERN_ERR_ALIGN
+    assert call(xs=A + 2) == tern.TERN_ERR_ALIGN
+    assert call(s=A + 2) == tern.TERN_ERR_ALIGN
+    assert call(b=A + 2) == tern.TERN_ERR_ALIGN
 
 
 def test_binding_refuses_cpu_tensors():

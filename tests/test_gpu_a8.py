@@ -1,0 +1,267 @@
+"""GPU parity of the 8-bit-activation layer (tern_quantize_act, tern_pack_a8,
+tern_gemm_a8) against the CPU oracle, through the C-ABI.
+
+Bars: activation codes, per-token scales and arranged weight codes bit-exact;
+the layer output within (2^-8 + 2^-21) |y_ref| of the oracle's unrounded
+double result (the int32 sum is exact, so only fp32 and bf16 roundings
+remain), and bit-exact where every fp32 step is exact (power-of-two scales).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tern_inputs
+from parity import (DEV, assert_act_bitexact, bf16_to_f64, check_layer_a8, edge_indices,
+                    gemm_a8_gpu, log, quantize_act_gpu)
+import ternary_weight_quantized_tern_amd as tern
+
+pytestmark = pytest.mark.gpu
+
+
+def _x(m, k, seed, dist="normal"):
+    x, _ = tern_inputs.draw(m, k, 1, seed=seed, x_dist=dist)
+    return x
+
+
+# ---------------------------------------------------------------------------
+# per-token activation codes
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("m,k", [(1, 64), (7, 3072), (5, 1000), (3, 1001), (4, 8), (2, 1),
+                                 (70, 520), (9, 32768), (1030, 136)])
+@pytest.mark.parametrize("dist", ["normal", "student_t3"])
+def test_quantize_act_bitexact(m, k, dist):
+    log(f"quantize_act m={m} k={k} {dist}")
+    x = _x(m, k, seed=m * 7 + k, dist=dist)
+    # rows over many magnitudes, a row of zeros, a row with a negative maximum
+    x = (x.float() * torch.logspace(-4, 3, m)[:, None]).to(torch.bfloat16)
+    if m > 2:
+        x[1] = 0
+        x[2, k // 2] = -x[2].float().abs().max().to(torch.bfloat16) * 2
+    q_ref, xs_ref = oracle.oracle_quantize_act(tern_inputs.bf16_bits(x))
+    q, xs = quantize_act_gpu(x)
+    assert_act_bitexact(q, xs, q_ref, xs_ref, f"m={m} k={k}")
+
+
+def test_quantize_act_ties_and_extremes():
+    # 127/max exact (max = 127/64 -> 64): x * 64 lands on half-integers, which
+    # round to even; the maximum maps to +-127
+    vals = torch.tensor([127 / 64, -127 / 64] + [(j + 0.5) / 64 for j in range(-60, 60)])
+    x = vals.repeat(3, 2)[:, :240].to(torch.bfloat16)
+    q_ref, xs_ref = oracle.oracle_quantize_act(tern_inputs.bf16_bits(x))
+    q, xs = quantize_act_gpu(x)
+    assert_act_bitexact(q, xs, q_ref, xs_ref, "ties")
+    assert int(q.abs().max()) == 127
+
+
+def test_quantize_act_strided_views_and_k_zero():
+    big = _x(40, 700, seed=11)
+    x = big[3:33, 5:605]                       # row pitch 700, unaligned start: scalar path
+    q_store = torch.full((30, 640), 55, dtype=torch.int8, device=DEV)
+    xs = torch.empty(30, dtype=torch.float32, device=DEV)
+    tern.tern_quantize_act(big.to(DEV)[3:33, 5:605], q_store, xs)
+    torch.cuda.synchronize()
+    q_ref, xs_ref = oracle.oracle_quantize_act(tern_inputs.bf16_bits(x.contiguous()))
+    assert_act_bitexact(q_store[:, :600], xs, q_ref, xs_ref, "strided")
+    assert bool((q_store[:, 600:] == 55).all()), "columns past k were written"
+    # k == 0: scales 0, codes untouched
+    xs0 = torch.full((4,), 7.0, device=DEV)
+    q0 = torch.full((4, 16), 3, dtype=torch.int8, device=DEV)
+    tern.tern_quantize_act(torch.empty((4, 16), dtype=torch.bfloat16, device=DEV), q0, xs0, k=0)
+    torch.cuda.synchronize()
+    assert xs0.cpu().tolist() == [0.0] * 4 and bool((q0 == 3).all())
+
+
+# ---------------------------------------------------------------------------
+# arranged weight codes
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,k", [(9216, 3072), (37, 48), (5, 16), (300, 1152), (64, 12288)])
+def test_pack_a8_bitexact(n, k):
+    t = tern_inputs.random_ternary(n, k, seed=n + k).numpy()
+    p_ref = oracle.oracle_pack(t)
+    p8_ref = oracle.oracle_pack_a8(p_ref, k)
+    p = torch.zeros((n, tern.packed_row_bytes(k)), dtype=torch.uint8)
+    p[:, : p_ref.shape[1]] = torch.from_numpy(p_ref)
+    p = p.to(DEV)
+    p8 = tern.pack_a8(p, k)
+    torch.cuda.synchronize()
+    assert torch.equal(p8.cpu()[:, : k // 4], torch.from_numpy(p8_ref))
+    # in place, and back again (the arrangement is its own inverse)
+    tern.tern_pack_a8(p8, p8, k)
+    torch.cuda.synchronize()
+    assert torch.equal(p8.cpu(), p.cpu())
+
+
+def test_pack_a8_unaligned_rows_scalar_path():
+    n, k = 21, 80                                  # 5 words per row, pitch 20 bytes
+    t = tern_inputs.random_ternary(n, k, seed=5).numpy()
+    p_ref = oracle.oracle_pack(t)
+    buf = torch.zeros(n * 20 + 4, dtype=torch.uint8)
+    view = buf[4:].view(n, 20)
+    view[:] = torch.from_numpy(p_ref)
+    dev = buf.to(DEV)
+    out = torch.full((n, 24), 0xAB, dtype=torch.uint8, device=DEV)
+    tern.tern_pack_a8(dev[4:].view(n, 20), out, k)
+    torch.cuda.synchronize()
+    assert torch.equal(out.cpu()[:, :20], torch.from_numpy(oracle.oracle_pack_a8(p_ref, k)))
+    assert bool((out[:, 20:] == 0xAB).all())
+
+
+# ---------------------------------------------------------------------------
+# the int8 GEMM
+# ---------------------------------------------------------------------------
+
+def _bf16_rne(v: np.ndarray) -> np.ndarray:
+    # every value here is an fp32 value (exact products of small powers of two
+    # and integers below 2^24), so the conversion through fp32 rounds once
+    return torch.from_numpy(v.astype(np.float32)).to(torch.bfloat16).double().numpy()
+
+
+@pytest.mark.parametrize("m,k,n", [(300, 384, 520), (4608, 3072, 3072), (4608, 1152, 3072),
+                                   (4600, 3072, 3000), (2304, 3072, 4608), (1, 128, 64),
+                                   (33, 256, 200)])
+def test_gemm_a8_power_of_two_scales_bitexact(m, k, n):
+    # q uniform on [-127, 127]; with s and xs powers of two every fp32 step is
+    # exact, so y must be the bf16 rounding of the exact result
+    log(f"gemm_a8 exact m={m} k={k} n={n}")
+    g = torch.Generator().manual_seed(m + 3 * k + 7 * n)
+    q = torch.randint(-127, 128, (m, k), generator=g, dtype=torch.int8)
+    xs = (2.0 ** torch.randint(-9, -3, (m,), generator=g)).float()
+    s = (2.0 ** torch.randint(-8, -2, (n,), generator=g)).float()
+    t = tern_inputs.random_ternary(n, k, seed=m + n).numpy()
+    p = oracle.oracle_pack(t)
+    p8 = oracle.oracle_pack_a8(p, k)
+    p8_dev = torch.zeros((n, tern.packed_row_bytes(k)), dtype=torch.uint8)
+    p8_dev[:, : k // 4] = torch.from_numpy(p8)
+    y = gemm_a8_gpu(q.to(DEV), xs.to(DEV), p8_dev.to(DEV), s.to(DEV), k)
+    yh = bf16_to_f64(y)
+    qn, xsn, sn = q.numpy(), xs.numpy(), s.numpy()
+    if m * n * k <= 2 ** 27:
+        rows, cols = np.arange(m), None
+    else:
+        rows, cols = edge_indices(m, tile=144, extra=48, seed=m), edge_indices(n, extra=48, seed=n)
+    # (the oracle's layer reads the plain packing p)
+    y_ref = oracle.oracle_gemm_a8(qn[rows], xsn[rows], p, sn)
+    assert np.array_equal(yh[rows], _bf16_rne(y_ref)), "rows differ"
+    if cols is not None:
+        y_ref_c = oracle.oracle_gemm_a8(qn, xsn, p[cols], sn[cols])
+        assert np.array_equal(yh[:, cols], _bf16_rne(y_ref_c)), "columns differ"
+
+
+@pytest.mark.parametrize("m,k,n", [(37, 256, 300), (300, 384, 520), (1, 128, 64),
+                                   (130, 1152, 1000), (64, 128, 128), (65, 640, 129)])
+def test_gemm_a8_layer_all_elements(m, k, n):
+    x, w = tern_inputs.draw(m, k, n, seed=17 * m + n, x_dist="student_t3")
+    worst = check_layer_a8(x, w, f"a8 m={m} k={k} n={n}", full=True)
+    log(f"  worst error / bound = {worst:.3f}")
+
+
+@pytest.mark.parametrize("m,k,n,act_from", [(300, 384, 520, 200), (37, 256, 300, 0),
+                                            (130, 1152, 1000, 1000), (20, 128, 333, 37)])
+def test_gemm_a8_epilogue_all_elements(m, k, n, act_from):
+    x, w = tern_inputs.draw(m, k, n, seed=m + 5 * n)
+    bias = np.random.default_rng(m).normal(0, 0.5, n).astype(np.float32)
+    worst = check_layer_a8(x, w, f"a8 epi m={m} n={n}", full=True, bias=bias,
+                           act=tern.TERN_ACT_GELU_TANH, act_from=act_from)
+    log(f"  worst error / bound = {worst:.3f}")
+
+
+def test_gemm_a8_epilogue_big_tiles_sampled():
+    m, k, n = 4608, 384, 9216
+    x, w = tern_inputs.draw(m, k, n, seed=77)
+    bias = np.random.default_rng(3).normal(0, 0.5, n).astype(np.float32)
+    rows = edge_indices(m, tile=144, extra=32, seed=1)
+    cols = np.unique(np.concatenate([edge_indices(n, extra=64, seed=2), np.arange(8990, 9010)]))
+    check_layer_a8(x, w, "a8 epi 4608x9216", rows=rows, cols=cols, bias=bias,
+                   act=tern.TERN_ACT_GELU_TANH, act_from=9000)
+
+
+def test_gemm_a8_k_zero_and_strided_operands():
+    # k == 0: bf16(gelu(bias))
+    n = 40
+    bias = torch.linspace(-2, 2, n)
+    y = torch.full((5, n), 9.0, dtype=torch.bfloat16, device=DEV)
+    tern.tern_gemm_a8(torch.empty((5, 128), dtype=torch.int8, device=DEV),
+                      torch.ones(5, device=DEV), torch.zeros((n, 32), dtype=torch.uint8, device=DEV),
+                      torch.ones(n, device=DEV), y, bias.to(DEV), tern.TERN_ACT_GELU_TANH, 0, k=0)
+    torch.cuda.synchronize()
+    ref = oracle.oracle_epilogue(np.zeros((5, n)), bias.numpy(), oracle.ACT_GELU_TANH, 0)
+    assert np.allclose(bf16_to_f64(y), ref, rtol=2.0 ** -8, atol=1e-6)
+    # views: q rows of pitch 400 bytes, y rows of pitch 310, p8 rows of 112 bytes
+    m, k, n = 70, 384, 300
+    x, w = tern_inputs.draw(m, k, n, seed=23)
+    t_ref, s_ref = oracle.oracle_quantize(w.numpy())
+    p_ref = oracle.oracle_pack(t_ref)
+    q_ref, xs_ref = oracle.oracle_quantize_act(tern_inputs.bf16_bits(x))
+    qb = torch.zeros((m, 400), dtype=torch.int8)
+    qb[:, :k] = torch.from_numpy(q_ref)
+    pb = torch.zeros((n, 112), dtype=torch.uint8)
+    pb[:, : k // 4] = torch.from_numpy(p_ref)
+    p8 = torch.zeros_like(pb).to(DEV)
+    tern.tern_pack_a8(pb.to(DEV), p8, k)
+    yb = torch.zeros((m, 310), dtype=torch.bfloat16, device=DEV)
+    tern.tern_gemm_a8(qb.to(DEV)[:, :k], torch.from_numpy(xs_ref).to(DEV), p8,
+                      torch.from_numpy(s_ref).to(DEV), yb[:, :n], k=k)
+    torch.cuda.synchronize()
+    y_ref = oracle.oracle_gemm_a8(q_ref, xs_ref, p_ref, s_ref)
+    from parity import assert_within_tolerance_a8
+    assert_within_tolerance_a8(bf16_to_f64(yb[:, :n]), y_ref, "strided")
+    assert bool((yb[:, n:] == 0).all())
+
+
+def test_gemm_a8_launch_paths_agree_bitwise():
+    # the persistent 144 x 256 kernel (whole tiles, 16-byte aligned y) and the
+    # one-tile-per-workgroup kernel with the direct epilogue (y misaligned)
+    # compute the same formula
+    m, k, n = 4608, 768, 3072
+    g = torch.Generator().manual_seed(5)
+    q = torch.randint(-127, 128, (m, k), generator=g, dtype=torch.int8).to(DEV)
+    xs = (torch.rand(m, generator=g) * 0.05).to(DEV)
+    s = (torch.rand(n, generator=g) * 0.05).to(DEV)
+    t = tern_inputs.random_ternary(n, k, seed=9).numpy()
+    p8 = torch.from_numpy(oracle.oracle_pack_a8(oracle.oracle_pack(t), k)).to(DEV)
+    y1 = torch.empty((m, n), dtype=torch.bfloat16, device=DEV)
+    tern.tern_gemm_a8(q, xs, p8, s, y1)
+    buf = torch.empty(m * n + 1, dtype=torch.bfloat16, device=DEV)
+    y2 = buf[1:].view(m, n)
+    tern.tern_gemm_a8(q, xs, p8, s, y2)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+def test_linear_a8_convenience_and_errors():
+    m, k, n = 50, 256, 96
+    x, w = tern_inputs.draw(m, k, n, seed=31)
+    p, s = tern.quantize_pack(w.to(DEV))
+    y = tern.linear_a8(x.to(DEV), tern.pack_a8(p, k), s)
+    torch.cuda.synchronize()
+    t_ref, s_ref = oracle.oracle_quantize(w.numpy())
+    q_ref, xs_ref = oracle.oracle_quantize_act(tern_inputs.bf16_bits(x))
+    from parity import assert_within_tolerance_a8
+    assert_within_tolerance_a8(bf16_to_f64(y), oracle.oracle_gemm_a8(
+        q_ref, xs_ref, oracle.oracle_pack(t_ref), s_ref), "linear_a8")
+    with pytest.raises(tern.TernError) as e:
+        tern.linear_a8(x[:, :192].contiguous().to(DEV), tern.pack_a8(p, k), s)   # k % 128 != 0
+    assert e.value.status == tern.TERN_ERR_SHAPE
+
+
+# ---------------------------------------------------------------------------
+# the workloads at full size
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,i", [("single", 0), ("flux_qkv", 0), ("flux_mlp", 0),
+                                    ("flux_mlp", 1), ("dit", 0), ("dit", 1), ("dit", 2)])
+def test_workload_a8(name, i):
+    layer = tern_inputs.WORKLOADS[name][i]
+    log(f"a8 workload {layer.name} m={layer.m} k={layer.k} n={layer.n}")
+    x, w = tern_inputs.draw_layer(layer)
+    full = layer.m * layer.n * layer.k <= 2 ** 26
+    rows = edge_indices(layer.m, tile=144, extra=96, seed=layer.seed)
+    cols = edge_indices(layer.n, extra=96, seed=layer.seed + 1)
+    worst = check_layer_a8(x, w, layer.name, rows=rows, cols=cols, full=full,
+                           repeat_check=layer.name == "flux_qkv")
+    log(f"  ok, worst error / bound = {worst:.3f}")
