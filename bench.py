@@ -15,7 +15,9 @@ After the timed steps, every layer shape of the five workloads is timed on its
 own ("rows"): tern_gemm per launch, and tern_gemm_ex with the bias and GELU
 of the layers that have them, as effective TFLOP/s, GB/s and the fraction of
 the bound that applies (MFMA or HBM); "dx_rows" time the input gradient
-(tern_gemm_dx, tern_pack_transposed) on the backward shapes.  The two few-token layers
+(tern_gemm_dx, tern_pack_transposed) on the backward shapes; "a8_rows" time
+the 8-bit-activation layer (tern_quantize_act, tern_gemm_a8) on the forward
+shapes against the int8 matrix peak.  The two few-token layers
 cycle through a pool of distinct packed weights larger than every cache, so
 that each launch streams its weights from HBM.
 
@@ -36,6 +38,7 @@ sys.path.insert(0, ROOT)
 METRIC = "tern_gemm effective TFLOP/s + % of MFMA/HBM roofline, FLUX linears M=4608"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak
+PEAK_I8_TOPS = 5000.0       # MI355X dense int8 matrix peak
 RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
 CSRC = os.path.join(ROOT, "ternary_weight_quantized_tern_amd", "csrc")
 GEMM_SRCS = [os.path.join(CSRC, f) for f in ("gemm.hip", "gemm_small.hip", "gemm_common.h")]
@@ -57,9 +60,9 @@ def parse():
     ap.add_argument("--gemm-only-reps", type=int, default=0,
                     help="after the steps, launch tern_gemm alone this many times (profiling)")
     ap.add_argument("--no-rows", action="store_true", help="skip the per-layer-shape tables")
-    ap.add_argument("--rows", choices=("all", "fwd", "dx"), default="all",
+    ap.add_argument("--rows", choices=("all", "fwd", "dx", "a8"), default="all",
                     help="which per-layer-shape tables to time: the forward layer, the input "
-                         "gradient, or both")
+                         "gradient, the 8-bit-activation layer, or all")
     ap.add_argument("--separate-quantize", action="store_true",
                     help="run quantize and pack as two calls in the step instead of the fused pass")
     ap.add_argument("--row-reps", type=int, default=30, help="timed launches per row")
@@ -333,6 +336,67 @@ def time_dx_rows(tern, tern_inputs, torch, dev, reps):
     return rows
 
 
+def time_a8_rows(tern, tern_inputs, torch, dev, reps):
+    """The 8-bit-activation layer on the forward shapes with at least 2048
+    tokens: tern_quantize_act (bf16 X -> int8 codes and per-token scales) and
+    tern_gemm_a8 (int8 matrix cores), each graph-replayed, and the two
+    together as the layer.  Rates against the int8 peak (5.0 POP/s) and the
+    bf16 peak (the unquantized layer's bound)."""
+    W = tern_inputs.WORKLOADS
+    shapes = [("flux_qkv", W["flux_qkv"][0], None),
+              ("flux_mlp.up", W["flux_mlp"][0], None),
+              ("flux_mlp.up+gelu", W["flux_mlp"][0], (False, 0)),
+              ("flux_mlp.down", W["flux_mlp"][1], None),
+              ("flux_single_stream.in_proj", W["flux_single_stream"][0], None),
+              ("flux_single_stream.out_proj", W["flux_single_stream"][1], None),
+              ("dit.up.m2048", W["dit"][0], None), ("dit.down.m2048", W["dit"][1], None)]
+    rows = []
+    for name, layer, epi in shapes:
+        m, k, n = layer.m, layer.k, layer.n
+        x, w = tern_inputs.draw_layer(layer)
+        xd = x.to(dev)
+        p, s = tern.quantize_pack(w.to(dev))
+        p8 = tern.pack_a8(p, k)
+        q, xs = tern.quantize_act(xd)
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        act = tern.TERN_ACT_NONE if epi is None else tern.TERN_ACT_GELU_TANH
+        af = 0 if epi is None else epi[1]
+
+        def gemm():
+            tern.tern_gemm_a8(q, xs, p8, s, y, None, act, af, k)
+
+        def quant():
+            tern.tern_quantize_act(xd, q, xs)
+
+        def layer_fn():
+            quant()
+            gemm()
+
+        t_g = time_graph(torch, gemm, reps)
+        t_q = time_graph(torch, quant, reps)
+        t_l = time_graph(torch, layer_fn, reps)
+        flops = 2 * m * n * k
+        byts = m * k + n * k // 4 + 4 * n + 4 * m + 2 * m * n
+        q_bytes = 2 * m * k + m * k + 4 * m
+        row = {"layer": name, "m": m, "k": k, "n": n, "entry": "tern_gemm_a8",
+               "us_per_launch": t_g * 1e6, "tops": flops / t_g / 1e12,
+               "pct_i8_peak": 100 * flops / t_g / 1e12 / PEAK_I8_TOPS,
+               "pct_bf16_peak": 100 * flops / t_g / 1e12 / PEAK_BF16_TFLOPS,
+               "gbs": byts / t_g / 1e9, "alg_flops": flops, "alg_bytes": byts,
+               "quantize_act_us": t_q * 1e6, "quantize_act_gbs": q_bytes / t_q / 1e9,
+               "layer_us": t_l * 1e6, "layer_tops": flops / t_l / 1e12}
+        if epi is not None:
+            row["epilogue"] = {"bias": False, "act": "gelu_tanh", "act_from": af}
+        rows.append(row)
+        print(f"# a8 row {name}: gemm {t_g * 1e6:.1f} us {row['tops']:.0f} TOP/s "
+              f"({row['pct_i8_peak']:.1f}% of int8 peak); quantize_act {t_q * 1e6:.1f} us "
+              f"{row['quantize_act_gbs']:.0f} GB/s; layer {t_l * 1e6:.1f} us",
+              file=sys.stderr, flush=True)
+        del p, p8, q, xs, y, xd
+        torch.cuda.empty_cache()
+    return rows
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -532,13 +596,17 @@ def main():
         torch.cuda.synchronize()
         print(f"# copy calibration: {nbytes} bytes read and written", file=sys.stderr)
 
-    rows = dx_rows = None
+    rows = dx_rows = a8_rows = None
     if not args.no_rows and args.rows in ("all", "fwd"):
         print("# timing tern_gemm on every layer shape", file=sys.stderr, flush=True)
         rows = time_rows(tern, tern_inputs, torch, dev, args.row_reps, args.pool_mib)
     if not args.no_rows and args.rows in ("all", "dx"):
         print("# timing the input gradient on the backward shapes", file=sys.stderr, flush=True)
         dx_rows = time_dx_rows(tern, tern_inputs, torch, dev, args.row_reps)
+    if not args.no_rows and args.rows in ("all", "a8"):
+        print("# timing the 8-bit-activation layer on the forward shapes", file=sys.stderr,
+              flush=True)
+        a8_rows = time_a8_rows(tern, tern_inputs, torch, dev, args.row_reps)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -568,7 +636,9 @@ def main():
         "kernels": kernels,
         "rows": rows,
         "dx_rows": dx_rows,
-        "peaks": {"bf16_mfma_tflops": PEAK_BF16_TFLOPS, "hbm_gbs": PEAK_HBM_GBS},
+        "a8_rows": a8_rows,
+        "peaks": {"bf16_mfma_tflops": PEAK_BF16_TFLOPS, "hbm_gbs": PEAK_HBM_GBS,
+                  "i8_mfma_tops": PEAK_I8_TOPS},
     }
     print(json.dumps(out), flush=True)
 

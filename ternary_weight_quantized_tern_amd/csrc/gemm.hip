@@ -801,9 +801,14 @@ hipError_t launch_big_a8(const int8_t* q, int64_t m, int64_t k, int64_t ldq, con
                          const float* bias, int act_from, uint16_t* y, int64_t ldy,
                          hipStream_t stream) {
   // The int8 stage holds K = 128: 144 x 256 tiles fill six ring stages
-  // (156 KiB of LDS) and cut M = 4608 and every FLUX width into whole tiles;
-  // smaller layers use 64 x 128 tiles, two workgroups per CU.
+  // (156 KiB of LDS) and cut M = 4608 and every FLUX width into whole tiles.
+  // Layers that 64 x 576 tiles (the same stage size) cut into exactly one
+  // tile per CU use those; smaller layers use 64 x 128 tiles, two workgroups
+  // per CU.
   const auto tiles = [&](int64_t bm, int64_t bn) { return ((m + bm - 1) / bm) * ((n + bn - 1) / bn); };
+  if (m % 64 == 0 && n % 576 == 0 && tiles(64, 576) == kPersistentGrid)
+    return launch_tiles<64, 576, 1, 4, 1, EPI, true>(q, m, k, ldq, xs, p8, n, ldp8, s, bias,
+                                                     act_from, y, ldy, stream);
   if (tiles(144, 256) >= kPersistentGrid)
     return launch_tiles<144, 256, 1, 4, 1, EPI, true>(q, m, k, ldq, xs, p8, n, ldp8, s, bias,
                                                       act_from, y, ldy, stream);

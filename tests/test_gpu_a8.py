@@ -180,6 +180,18 @@ def test_gemm_a8_epilogue_big_tiles_sampled():
                    act=tern.TERN_ACT_GELU_TANH, act_from=9000)
 
 
+def test_gemm_a8_one_tile_per_cu_epilogue_sampled():
+    # M = 2048, N = 4608: the 64 x 576 tiles, one per CU
+    m, k, n = 2048, 1152, 4608
+    x, w = tern_inputs.draw(m, k, n, seed=79, x_dist="student_t3")
+    bias = np.random.default_rng(4).normal(0, 0.5, n).astype(np.float32)
+    rows = edge_indices(m, tile=64, extra=32, seed=5)
+    cols = np.unique(np.concatenate([edge_indices(n, tile=576, extra=64, seed=6),
+                                     np.arange(2290, 2310)]))
+    check_layer_a8(x, w, "a8 epi 2048x4608", rows=rows, cols=cols, bias=bias,
+                   act=tern.TERN_ACT_GELU_TANH, act_from=2300)
+
+
 def test_gemm_a8_k_zero_and_strided_operands():
     # k == 0: bf16(gelu(bias))
     n = 40
