@@ -27,7 +27,7 @@
  *    not improve; the pages give no activation quantizer): each token's
  *    activations are scaled by 127 / max|x| and rounded to int8
  *    (oracle_quantize_act), and the layer is s_n * (max|x_m| / 127) times the
- *    exact integer sum of q . T (oracle_gemm_a8).  oracle_pack_a8 writes the
+ *    exact integer sum of q . T (oracle_gemm_a8); max|x| is floored at 1e-5.  oracle_pack_a8 writes the
  *    codes with the four 2-bit fields of each 4-code group of every 16-code
  *    word exchanged across groups (a 4 x 4 transposition of the fields).
  *  - The gradient of the layer with respect to its input, for training the
@@ -391,13 +391,16 @@ int oracle_gemm_dx(const uint16_t* u, int64_t m, int64_t n, int64_t ldu, const u
 /*
  * Per-token activation quantization to int8 (absmax):
  *
- *   g_m = max_k |x[m][k]|   (bf16 values, exact in fp32)
+ *   g_m = max(max_k |x[m][k]|, 1e-5f)   (bf16 values, exact in fp32)
  *   q[m][k] = rint( fp32(x[m][k] * fp32(127 / g_m)) )   (ties to even)
  *   xs[m] = fp32(g_m / 127)
  *
- * each division and product one IEEE single-precision operation; a row of
- * zeros gives q = 0 and xs = 0.  |x| <= g gives |x * (127 / g)| <= 127 (1 +
- * 2^-23)^2 < 127.5, so q lies in [-127, 127].
+ * each division and product one IEEE single-precision operation.  The floor
+ * 1e-5 (the fp32 value nearest to it) keeps 127 / g finite: without it the
+ * quotient overflows for rows whose largest magnitude is below 127 / FLT_MAX
+ * (about 3.7e-37), which bf16 can hold.  A row of zeros gives q = 0.
+ * |x| <= g gives |x * (127 / g)| <= 127 (1 + 2^-23)^2 < 127.5, so q lies in
+ * [-127, 127].
  */
 int oracle_quantize_act(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, int8_t* q,
                         int64_t ldq, float* xs) {
@@ -408,11 +411,7 @@ int oracle_quantize_act(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, in
       const float a = fabsf(bf16_bits_to_float(x[mm * ldx + kk]));
       if (a > g) g = a;
     }
-    if (g == 0.0f) {
-      for (int64_t kk = 0; kk < k; ++kk) q[mm * ldq + kk] = 0;
-      xs[mm] = 0.0f;
-      continue;
-    }
+    if (g < 1e-5f) g = 1e-5f;
     const float inv = 127.0f / g;
     for (int64_t kk = 0; kk < k; ++kk) {
       const float v = bf16_bits_to_float(x[mm * ldx + kk]) * inv;

@@ -24,6 +24,14 @@ int oracle_scale_grad(const uint16_t* dy, int64_t m, int64_t n, int64_t lddy, co
 int oracle_gemm_dx(const uint16_t* u, int64_t m, int64_t n, int64_t ldu, const uint8_t* p,
                    int64_t k, int64_t ldp, double* dx, int64_t lddx, int nthreads);
 
+int oracle_quantize_act(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, int8_t* q,
+                        int64_t ldq, float* xs);
+int oracle_gemm_a8(const int8_t* q, int64_t m, int64_t k, int64_t ldq, const float* xs,
+                   const uint8_t* p, int64_t n, int64_t ldp, const float* s, double* y,
+                   int64_t ldy);
+int oracle_pack_a8(const uint8_t* p, int64_t n, int64_t k, int64_t ldp, uint8_t* p8,
+                   int64_t ldp8);
+
 static uint32_t rng = 12345u;
 static uint32_t next(void) {
   rng = rng * 1664525u + 1013904223u;
@@ -56,6 +64,10 @@ static int run_shape(int64_t m, int64_t n, int64_t k, int64_t pad, int threads) 
   uint16_t* dy = malloc(sizeof(uint16_t) * (size_t)(m * ldd + 1));
   uint16_t* u = malloc(sizeof(uint16_t) * (size_t)(m * ldd + 1));
   double* dx = malloc(sizeof(double) * (size_t)(m * (k + pad) + 1));
+  int8_t* q = malloc((size_t)(m * ldx + 1));
+  float* xs = malloc(sizeof(float) * (size_t)(m + 1));
+  const int64_t k16 = k / 16 * 16, ldp8 = k16 / 4 + pad;
+  uint8_t* p8 = malloc((size_t)(n * ldp8 + 1));
   (void)ldpt;
   for (int64_t i = 0; i < n * ldw; ++i) {
     w[i] = frand() * 0.05f;
@@ -77,6 +89,10 @@ static int run_shape(int64_t m, int64_t n, int64_t k, int64_t pad, int threads) 
   rc |= oracle_epilogue(y, m, n, ldy, NULL, 0, 0);
   rc |= oracle_scale_grad(dy, m, n, ldd, s, u, ldd);
   rc |= oracle_gemm_dx(u, m, n, ldd, p, k, ldp, dx, k + pad, threads);
+  rc |= oracle_quantize_act(x, m, k, ldx, q, ldx, xs);
+  rc |= oracle_gemm_a8(q, m, k, ldx, xs, p, n, ldp, s, y, ldy);
+  rc |= oracle_pack_a8(p, n, k16, ldp, p8, ldp8);
+  free(q); free(xs); free(p8);
   free(w); free(wb); free(t); free(t2); free(s); free(p); free(x); free(y); free(bias);
   free(dy); free(u); free(dx);
   return rc;
@@ -96,6 +112,9 @@ int main(void) {
   CHECK(oracle_epilogue(NULL, 1, 2, 2, NULL, 2, 0) != 0);
   CHECK(oracle_scale_grad(NULL, 1, 4, 3, NULL, NULL, 4) != 0);
   CHECK(oracle_gemm_dx(NULL, 1, 4, 4, NULL, 8, 1, NULL, 8, 1) != 0);
+  CHECK(oracle_quantize_act(NULL, 1, 8, 7, NULL, 8, NULL) != 0);
+  CHECK(oracle_gemm_a8(NULL, 1, 8, 8, NULL, NULL, 2, 1, NULL, NULL, 2) != 0);
+  CHECK(oracle_pack_a8(NULL, 2, 24, 6, NULL, 6) != 0);             /* k % 16 != 0 */
   printf("oracle driver ok\n");
   return 0;
 }

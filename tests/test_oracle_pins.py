@@ -473,33 +473,43 @@ def test_quantize_act_worked_examples():
     # row 1: max 127/64 -> 127/max = 64 exactly; 0.5078125 * 64 = 32.5 -> 32
     #        (even), -0.5234375 * 64 = -33.5 -> -34 (even), 1/64 * 64 = 1;
     #        scale (127/64)/127 = 1/64
-    # row 2: zeros -> codes 0, scale 0
+    # row 2: zeros -> codes 0; the maximum is floored at fp32(1e-5), so the
+    #        scale is fp32(fp32(1e-5) / 127)
+    # row 3: max 2^-20 < 1e-5 -> floored: 127 / fp32(1e-5) = 12700000 in fp32,
+    #        2^-20 * 12700000 = 12.11... -> 12, -2^-21 * 12700000 = -6.06... -> -6
     x = torch.tensor([[1.0, -2.0, 0.5, 0.0],
                       [1.984375, 0.5078125, -0.5234375, 0.015625],
-                      [0.0, 0.0, 0.0, 0.0]]).to(torch.bfloat16)
+                      [0.0, 0.0, 0.0, 0.0],
+                      [2.0 ** -20, -(2.0 ** -21), 0.0, 0.0]]).to(torch.bfloat16)
     assert torch.equal(x.float(), torch.tensor([[1.0, -2.0, 0.5, 0.0],
                                                 [1.984375, 0.5078125, -0.5234375, 0.015625],
-                                                [0.0, 0.0, 0.0, 0.0]]))   # all exact in bf16
+                                                [0.0, 0.0, 0.0, 0.0],
+                                                [2.0 ** -20, -(2.0 ** -21), 0.0, 0.0]]))
     q, xs = oracle.oracle_quantize_act(tern_inputs.bf16_bits(x))
-    assert q.tolist() == [[64, -127, 32, 0], [127, 32, -34, 1], [0, 0, 0, 0]]
-    assert xs.tolist() == [float(np.float32(2.0 / 127.0)), 0.015625, 0.0]
+    assert q.tolist() == [[64, -127, 32, 0], [127, 32, -34, 1], [0, 0, 0, 0], [12, -6, 0, 0]]
+    floor = np.float32(1e-5)
+    assert xs.tolist() == [float(np.float32(2.0 / 127.0)), 0.015625,
+                           float(np.float32(float(floor) / 127.0)),
+                           float(np.float32(float(floor) / 127.0))]
 
 
 def test_quantize_act_matches_exact_rational_rounding():
-    # q = round(127 x / max|x|) away from the few products that fall within
-    # fp32 rounding of a half-integer; the scale is the correctly rounded
-    # fp32 quotient max|x| / 127
+    # q = round(127 x / g), g = max(max|x|, fp32(1e-5)), away from the few
+    # products that fall within fp32 rounding of a half-integer; the scale is
+    # the correctly rounded fp32 quotient g / 127
     g = torch.Generator().manual_seed(91)
     x = (torch.randn(12, 200, generator=g) * torch.logspace(-3, 2, 12)[:, None]).to(torch.bfloat16)
     x[3, 17] = -x[3].abs().max() * 1.5   # a negative maximum
+    x[5] = x[5] * 1e-4                   # a row below the floor
     xb = tern_inputs.bf16_bits(x)
     q, xs = oracle.oracle_quantize_act(xb)
     xv = _bf16_values(xb)
     checked = 0
+    floor = Fraction(float(np.float32(1e-5)))
     for m in range(12):
-        gm = max(Fraction(abs(float(v))) for v in xv[m])
+        gm = max(max(Fraction(abs(float(v))) for v in xv[m]), floor)
         assert xs[m] == _rn32(gm / 127)
-        assert int(np.abs(q[m]).max()) == 127
+        assert (int(np.abs(q[m]).max()) == 127) == (gm > floor)
         for kk in range(200):
             e = Fraction(float(xv[m, kk])) * 127 / gm
             frac = abs(e - math.floor(e) - Fraction(1, 2))

@@ -9,7 +9,11 @@ oracle's code:
   * a code is nonzero exactly when 2|w| > s, and then carries the sign of w
     (checked against exact rational arithmetic on the fp32 values);
   * packing and unpacking any {-1, 0, +1} matrix round-trips, and unpacking
-    any byte matrix and re-packing it gives back the bytes when no field is 10.
+    any byte matrix and re-packing it gives back the bytes when no field is 10;
+  * per-token int8 activations: codes lie in [-127, 127], a row whose
+    maximum is at least the floor 1e-5 reaches +-127 there, rounding preserves order and sign, the
+    codes are odd in x and permuting the row permutes them; the field
+    arrangement of the int8 layout applied twice gives back any bytes.
 """
 from __future__ import annotations
 
@@ -87,3 +91,40 @@ def test_pack_unpack_round_trip_any_shape(n, k, seed):
     if k % 4:
         b[:, -1] &= np.uint8((1 << (2 * (k % 4))) - 1)   # fields past k are 00
     assert np.array_equal(oracle.oracle_pack(oracle.oracle_unpack(b, k)), b)
+
+
+def _bf16_row(vals):
+    """bf16 bit patterns (the top halves of the fp32 encodings) and their values."""
+    bits = (np.array(vals, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    return bits[None, :], (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+@settings(**SETTINGS)
+@given(st.lists(st.floats(min_value=-3e4, max_value=3e4, allow_nan=False, width=32),
+                min_size=1, max_size=300), st.randoms(use_true_random=False))
+def test_quantize_act_range_order_sign_and_permutation(vals, rnd):
+    bits, x = _bf16_row(vals)
+    q, xs = oracle.oracle_quantize_act(bits)
+    q = q[0].astype(np.int64)
+    assert np.all(np.abs(q) <= 127)
+    g = float(np.max(np.abs(x)))
+    assert (int(np.max(np.abs(q))) == 127) == (g >= float(np.float32(1e-5)))
+    assert (xs[0] == np.float32(float(np.float32(1e-5)) / 127)) == (g <= float(np.float32(1e-5)))
+    order = np.argsort(x, kind="stable")
+    assert np.all(np.diff(q[order]) >= 0)                   # monotone in x
+    assert np.all(np.sign(q) * np.sign(x) >= 0)             # never the opposite sign
+    qn, _ = oracle.oracle_quantize_act(np.ascontiguousarray(bits ^ np.uint16(0x8000)))
+    assert np.array_equal(qn[0].astype(np.int64), -q)
+    perm = list(range(len(vals)))
+    rnd.shuffle(perm)
+    qp, xsp = oracle.oracle_quantize_act(np.ascontiguousarray(bits[:, perm]))
+    assert np.array_equal(qp[0].astype(np.int64), q[perm]) and xsp[0] == xs[0]
+
+
+@settings(**SETTINGS)
+@given(st.integers(min_value=1, max_value=9), st.integers(min_value=1, max_value=6),
+       st.integers(min_value=0, max_value=2 ** 32 - 1))
+def test_pack_a8_is_an_involution_on_any_bytes(n, words, seed):
+    p = np.random.default_rng(seed).integers(0, 256, size=(n, 4 * words)).astype(np.uint8)
+    p8 = oracle.oracle_pack_a8(p, 16 * words)
+    assert np.array_equal(oracle.oracle_pack_a8(p8, 16 * words), p)
