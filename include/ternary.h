@@ -259,12 +259,13 @@ tern_status tern_gemm_dx(const void* dy_bf16, int64_t m, int64_t n, int64_t lddy
 /*
  * tern_quantize_act: per-token int8 activations.
  *
- *   g_m      = max_k |x[m][k]|
+ *   g_m      = max( max_k |x[m][k]|, 1e-5f )
  *   q[m][k]  = rint( fp32( x[m][k] * fp32(127 / g_m) ) )   (ties to even)
  *   xs[m]    = fp32( g_m / 127 )
  *
- * with both quotients correctly rounded to fp32; |q| <= 127.  A row of zeros
- * (or k == 0) gives q = 0 and xs = 0.
+ * with both quotients correctly rounded to fp32; |q| <= 127.  The floor
+ * (the fp32 value nearest 1e-5) keeps 127 / g finite; a row of zeros gives
+ * q = 0 and xs = fp32(1e-5f / 127), and so does k == 0 for xs.
  *
  *   x   [m, ldx] bf16 activations
  *   q   [m, ldq] int8 output codes; columns >= k untouched

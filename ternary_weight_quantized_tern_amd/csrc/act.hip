@@ -5,10 +5,11 @@
 // quantization as the reason its latency barely improved; the pages define no
 // activation quantizer.  The plainest one, absmax per token (as in the BitNet
 // b1.58 family the paper builds on, section 1), is used here:
-//   g_m = max_k |x[m][k]|,  q[m][k] = rint(fp32(x[m][k] * fp32(127 / g_m))),
-//   xs[m] = fp32(g_m / 127),
-// with every quotient correctly rounded to fp32 and ties to even; a row of
-// zeros gives q = 0 and xs = 0.  |q| <= 127 follows from |x| <= g.
+//   g_m = max(max_k |x[m][k]|, 1e-5),
+//   q[m][k] = rint(fp32(x[m][k] * fp32(127 / g_m))),  xs[m] = fp32(g_m / 127),
+// with every quotient correctly rounded to fp32 and ties to even.  The floor
+// keeps 127 / g finite (it overflows fp32 below about 3.7e-37); a row of
+// zeros gives q = 0.  |q| <= 127 follows from |x| <= g.
 //
 // quantize_act: HBM-bound (2 bytes read, 1 written per element).  One wave
 // per token: a first pass over the row finds the absolute maximum (16-byte
@@ -82,12 +83,12 @@ __global__ __launch_bounds__(kThreads) void quantize_act_kernel(const uint16_t* 
       const uint32_t o = static_cast<uint32_t>(__shfl_xor(static_cast<int>(amax), off));
       amax = amax > o ? amax : o;
     }
-    const float g = __uint_as_float(amax << 16);
+    const float g = fmaxf(__uint_as_float(amax << 16), 1e-5f);
     // Correctly rounded fp32 quotients: the double quotient of two floats
     // rounded to float is the correctly rounded float quotient (53 >= 2 * 24 + 2).
-    const float inv = g > 0.0f ? static_cast<float>(127.0 / static_cast<double>(g)) : 0.0f;
+    const float inv = static_cast<float>(127.0 / static_cast<double>(g));
     if (lane == 0) xs[row] = static_cast<float>(static_cast<double>(g) / 127.0);
-    // Pass 2: the codes.  (inv = 0 for a zero row: every product is 0.)
+    // Pass 2: the codes.
     if constexpr (VEC) {
       for (int64_t c = 8 * lane; c < k; c += 512) {
         const uint4 v = *reinterpret_cast<const uint4*>(xr + c);

@@ -41,6 +41,10 @@ def test_quantize_act_bitexact(m, k, dist):
     if m > 2:
         x[1] = 0
         x[2, k // 2] = -x[2].float().abs().max().to(torch.bfloat16) * 2
+    if m > 3:
+        x[3] = (x[3].float() * 1e-9).to(torch.bfloat16)      # below the floor 1e-5
+    if m > 4:
+        x[4] = (x[4].float() * 1e-38).to(torch.bfloat16)     # 127 / max would overflow fp32
     q_ref, xs_ref = oracle.oracle_quantize_act(tern_inputs.bf16_bits(x))
     q, xs = quantize_act_gpu(x)
     assert_act_bitexact(q, xs, q_ref, xs_ref, f"m={m} k={k}")
@@ -67,12 +71,13 @@ def test_quantize_act_strided_views_and_k_zero():
     q_ref, xs_ref = oracle.oracle_quantize_act(tern_inputs.bf16_bits(x.contiguous()))
     assert_act_bitexact(q_store[:, :600], xs, q_ref, xs_ref, "strided")
     assert bool((q_store[:, 600:] == 55).all()), "columns past k were written"
-    # k == 0: scales 0, codes untouched
+    # k == 0: the floored scale fp32(1e-5) / 127, codes untouched
     xs0 = torch.full((4,), 7.0, device=DEV)
     q0 = torch.full((4, 16), 3, dtype=torch.int8, device=DEV)
     tern.tern_quantize_act(torch.empty((4, 16), dtype=torch.bfloat16, device=DEV), q0, xs0, k=0)
     torch.cuda.synchronize()
-    assert xs0.cpu().tolist() == [0.0] * 4 and bool((q0 == 3).all())
+    floor_scale = float(np.float32(float(np.float32(1e-5)) / 127))
+    assert xs0.cpu().tolist() == [floor_scale] * 4 and bool((q0 == 3).all())
 
 
 # ---------------------------------------------------------------------------
