@@ -12,9 +12,12 @@
 // zeros gives q = 0.  |q| <= 127 follows from |x| <= g.
 //
 // quantize_act: HBM-bound (2 bytes read, 1 written per element).  One wave
-// per token: a first pass over the row finds the absolute maximum (16-byte
-// loads, a butterfly over the wave), a second pass re-reads the row, which
-// the first pass has just brought into the cache, and writes the codes.
+// per token.  Rows of up to 16384 elements (with 16-byte aligned rows) are
+// read once into registers, 8 elements per lane per 1 KiB chunk of the row;
+// the absolute maximum comes from a butterfly over the wave and the codes
+// are written from the registers.  Other rows take two passes, the second
+// re-reading the row (from HBM at large sizes: with every CU streaming rows
+// the cache does not keep a row between the passes).
 //
 // pack_a8: the int8 MFMA operand of 16 codes is four registers of four
 // bytes in ascending k.  With the 2-bit fields of each 32-bit code word
@@ -106,6 +109,67 @@ __global__ __launch_bounds__(kThreads) void quantize_act_kernel(const uint16_t* 
   }
 }
 
+// The larger of the absolute values of the two bf16 halves of v, as a
+// 15-bit pattern (for finite values the pattern orders like the value).
+__device__ inline uint32_t abs2(uint32_t v) {
+  const uint32_t a = v & 0x7FFFu, b = (v >> 16) & 0x7FFFu;
+  return a > b ? a : b;
+}
+
+__device__ inline uint32_t wave_max(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint32_t o = static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), off));
+    v = v > o ? v : o;
+  }
+  return v;
+}
+
+// One pass: rows of at most 512 * CAP elements, x rows 16-byte aligned, q
+// rows 8-byte aligned, k % 8 == 0.  Chunk c of a row is elements 512 c ..
+// 512 c + 511; lane l holds elements 512 c + 8 l .. 512 c + 8 l + 7.
+template <int CAP>
+__global__ __launch_bounds__(kThreads) void quantize_act_regs_kernel(
+    const uint16_t* __restrict__ x, int64_t m, int k, int64_t ldx, int8_t* __restrict__ q,
+    int64_t ldq, float* __restrict__ xs) {
+  const int lane = threadIdx.x & 63;
+  for (int64_t row = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6); row < m;
+       row += static_cast<int64_t>(gridDim.x) * kWaves) {
+    const uint16_t* xr = x + row * ldx;
+    int8_t* qr = q + row * ldq;
+    uint4 v[CAP];
+#pragma unroll
+    for (int c = 0; c < CAP; ++c) {
+      const int e = 512 * c + 8 * lane;
+      v[c] = e < k ? *reinterpret_cast<const uint4*>(xr + e) : uint4{0u, 0u, 0u, 0u};
+    }
+    uint32_t amax = 0;
+#pragma unroll
+    for (int c = 0; c < CAP; ++c) {
+      const uint32_t a = abs2(v[c].x) > abs2(v[c].y) ? abs2(v[c].x) : abs2(v[c].y);
+      const uint32_t b = abs2(v[c].z) > abs2(v[c].w) ? abs2(v[c].z) : abs2(v[c].w);
+      const uint32_t ab = a > b ? a : b;
+      amax = amax > ab ? amax : ab;
+    }
+    amax = wave_max(amax);
+    const float g = fmaxf(__uint_as_float(amax << 16), 1e-5f);
+    const float inv = static_cast<float>(127.0 / static_cast<double>(g));
+    if (lane == 0) xs[row] = static_cast<float>(static_cast<double>(g) / 127.0);
+#pragma unroll
+    for (int c = 0; c < CAP; ++c) {
+      const int e = 512 * c + 8 * lane;
+      if (e < k) {
+        uint2 o;
+        o.x = pack_codes4(bf16_lo(v[c].x) * inv, bf16_hi(v[c].x) * inv, bf16_lo(v[c].y) * inv,
+                          bf16_hi(v[c].y) * inv);
+        o.y = pack_codes4(bf16_lo(v[c].z) * inv, bf16_hi(v[c].z) * inv, bf16_lo(v[c].w) * inv,
+                          bf16_hi(v[c].w) * inv);
+        *reinterpret_cast<uint2*>(qr + e) = o;
+      }
+    }
+  }
+}
+
 __device__ inline uint32_t transpose_fields(uint32_t w) {
   uint32_t t = ((w >> 12) ^ w) & 0x0000F0F0u;  // off-diagonal 2 x 2 blocks of fields
   w ^= t ^ (t << 12);
@@ -148,6 +212,26 @@ hipError_t launch_quantize_act(const uint16_t* x, int64_t m, int64_t k, int64_t 
                    reinterpret_cast<uintptr_t>(q) % 8 == 0 && ldq % 8 == 0;
   int64_t blocks = (m + kWaves - 1) / kWaves;
   if (blocks > kMaxBlocks) blocks = kMaxBlocks;
+  const dim3 grid(static_cast<unsigned>(blocks));
+  if (vec && k <= 16384) {
+    const int ki = static_cast<int>(k);
+    if (k <= 1024)
+      hipLaunchKernelGGL(quantize_act_regs_kernel<2>, grid, dim3(kThreads), 0, stream, x, m, ki,
+                         ldx, q, ldq, xs);
+    else if (k <= 2048)
+      hipLaunchKernelGGL(quantize_act_regs_kernel<4>, grid, dim3(kThreads), 0, stream, x, m, ki,
+                         ldx, q, ldq, xs);
+    else if (k <= 4096)
+      hipLaunchKernelGGL(quantize_act_regs_kernel<8>, grid, dim3(kThreads), 0, stream, x, m, ki,
+                         ldx, q, ldq, xs);
+    else if (k <= 8192)
+      hipLaunchKernelGGL(quantize_act_regs_kernel<16>, grid, dim3(kThreads), 0, stream, x, m, ki,
+                         ldx, q, ldq, xs);
+    else
+      hipLaunchKernelGGL(quantize_act_regs_kernel<32>, grid, dim3(kThreads), 0, stream, x, m, ki,
+                         ldx, q, ldq, xs);
+    return hipGetLastError();
+  }
   if (vec)
     hipLaunchKernelGGL(quantize_act_kernel<true>, dim3(static_cast<unsigned>(blocks)),
                        dim3(kThreads), 0, stream, x, m, k, ldx, q, ldq, xs);

@@ -31,7 +31,8 @@ def _x(m, k, seed, dist="normal"):
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("m,k", [(1, 64), (7, 3072), (5, 1000), (3, 1001), (4, 8), (2, 1),
-                                 (70, 520), (9, 32768), (1030, 136)])
+                                 (70, 520), (9, 32768), (1030, 136), (6, 15360), (5, 16384),
+                                 (5, 16392), (300, 12288), (7, 1032), (6, 4104)])
 @pytest.mark.parametrize("dist", ["normal", "student_t3"])
 def test_quantize_act_bitexact(m, k, dist):
     log(f"quantize_act m={m} k={k} {dist}")
