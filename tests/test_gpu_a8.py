@@ -251,6 +251,62 @@ def test_gemm_a8_launch_paths_agree_bitwise():
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
 
 
+def test_gemm_a8_max_k_sums_do_not_overflow():
+    # K = 2^18, the largest the entry point accepts: with every code at +-127
+    # and every weight +-1 the sums reach 127 * 2^18 (64x that in the kernel's
+    # int32 accumulator, just below 2^31); power-of-two scales keep every fp32
+    # step exact, so y must equal the bf16 rounding of the exact sum
+    m, k, n = 3, 2 ** 18, 128
+    q = torch.full((m, k), 127, dtype=torch.int8)
+    q[1] = -127
+    q[2, 1::2] = -127                    # alternating: the sum cancels to 0 for t = +1
+    t = np.ones((n, k), np.int8)
+    t[1::2] = -1                         # odd channels all -1
+    t[5, : k // 2] = 0                   # a channel half zero
+    p = oracle.oracle_pack(t)
+    p8 = torch.from_numpy(oracle.oracle_pack_a8(p, k))
+    xs = torch.tensor([2.0 ** -10, 2.0 ** -8, 2.0 ** -4])
+    s = torch.full((n,), 2.0 ** -6)
+    y = gemm_a8_gpu(q.to(DEV), xs.to(DEV), p8.to(DEV), s.to(DEV), k)
+    y_ref = oracle.oracle_gemm_a8(q.numpy(), xs.numpy(), p, s.numpy())
+    assert np.array_equal(bf16_to_f64(y), _bf16_rne(y_ref))
+    assert y_ref[0, 0] == 127 * k * 2.0 ** -16 and y_ref[1, 1] == 127 * k * 2.0 ** -14
+
+
+def test_a8_layer_in_a_hip_graph_matches_eager():
+    m, k, n = 300, 384, 520
+    x, w = tern_inputs.draw(m, k, n, seed=41)
+    xd = x.to(DEV)
+    p, s = tern.quantize_pack(w.to(DEV))
+    p8 = tern.pack_a8(p, k)
+    q = torch.empty((m, k), dtype=torch.int8, device=DEV)
+    xs = torch.empty(m, dtype=torch.float32, device=DEV)
+    y = torch.empty((m, n), dtype=torch.bfloat16, device=DEV)
+
+    def layer():
+        tern.tern_quantize_act(xd, q, xs)
+        tern.tern_gemm_a8(q, xs, p8, s, y)
+
+    layer()
+    torch.cuda.synchronize()
+    eager = y.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        layer()
+    for i in range(4):
+        y.zero_()
+        q.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), eager.view(torch.int16)), f"replay {i}"
+
+
 def test_linear_a8_convenience_and_errors():
     m, k, n = 50, 256, 96
     x, w = tern_inputs.draw(m, k, n, seed=31)
