@@ -40,6 +40,17 @@
 //    than CUs and K / 64 is a multiple of 6, 256 persistent workgroups walk
 //    the tiles with one unbroken DMA stream, hiding each tile's start-up
 //    latency behind the previous tile's last steps.
+//
+// The same kernel, with its A8 flag, is the layer on int8 activations (the
+// 8-bit-activation variant that "1.58-bit FLUX", section 4, names as the
+// missing piece for latency): v_mfma_i32_16x16x64_i8 takes 16 int8 values
+// per lane and operand where the bf16 instruction takes 8 bf16 values, so a
+// stage holds K = 128 with the same 128-byte X rows and 32-byte weight rows.
+// The weights come field-transposed (act.hip), which makes one shift and one
+// mask per operand register the whole decode; the exact int32 sums are
+// scaled by s[n] / 64 and the token's scale xs[m] in the epilogue.  Tiles
+// 144 x 256 (the six-stage ring then fills 156 KiB of LDS), 64 x 576 or
+// 64 x 128.
 #include <type_traits>
 
 #include "gemm_common.h"

@@ -14,8 +14,8 @@ import torch
 
 import oracle
 import tern_inputs
-from parity import (DEV, assert_act_bitexact, bf16_to_f64, check_layer_a8, edge_indices,
-                    gemm_a8_gpu, log, quantize_act_gpu)
+from parity import (DEV, assert_act_bitexact, assert_within_tolerance_a8, bf16_to_f64,
+                    check_layer_a8, edge_indices, gemm_a8_gpu, log, quantize_act_gpu)
 import ternary_weight_quantized_tern_amd as tern
 
 pytestmark = pytest.mark.gpu
@@ -226,7 +226,6 @@ def test_gemm_a8_k_zero_and_strided_operands():
                       torch.from_numpy(s_ref).to(DEV), yb[:, :n], k=k)
     torch.cuda.synchronize()
     y_ref = oracle.oracle_gemm_a8(q_ref, xs_ref, p_ref, s_ref)
-    from parity import assert_within_tolerance_a8
     assert_within_tolerance_a8(bf16_to_f64(yb[:, :n]), y_ref, "strided")
     assert bool((yb[:, n:] == 0).all())
 
@@ -315,7 +314,6 @@ def test_linear_a8_convenience_and_errors():
     torch.cuda.synchronize()
     t_ref, s_ref = oracle.oracle_quantize(w.numpy())
     q_ref, xs_ref = oracle.oracle_quantize_act(tern_inputs.bf16_bits(x))
-    from parity import assert_within_tolerance_a8
     assert_within_tolerance_a8(bf16_to_f64(y), oracle.oracle_gemm_a8(
         q_ref, xs_ref, oracle.oracle_pack(t_ref), s_ref), "linear_a8")
     with pytest.raises(tern.TernError) as e:
