@@ -336,12 +336,14 @@ def time_dx_rows(tern, tern_inputs, torch, dev, reps):
     return rows
 
 
-def time_a8_rows(tern, tern_inputs, torch, dev, reps):
-    """The 8-bit-activation layer on the forward shapes with at least 2048
-    tokens: tern_quantize_act (bf16 X -> int8 codes and per-token scales) and
-    tern_gemm_a8 (int8 matrix cores), each graph-replayed, and the two
-    together as the layer.  Rates against the int8 peak (5.0 POP/s) and the
-    bf16 peak (the unquantized layer's bound)."""
+def time_a8_rows(tern, tern_inputs, torch, dev, reps, pool_mib):
+    """The 8-bit-activation layer on the forward shapes: tern_quantize_act
+    (bf16 X -> int8 codes and per-token scales) and tern_gemm_a8, each
+    graph-replayed, and the two together as the layer.  Rates against the
+    int8 peak (5.0 POP/s) and the bf16 peak (the unquantized layer's bound).
+    The few-token shapes cycle through at least pool_mib MiB of copies of the
+    arranged weights, one launch per copy, so that every launch streams its
+    weights from HBM; their rate is also given in GB/s."""
     W = tern_inputs.WORKLOADS
     shapes = [("flux_qkv", W["flux_qkv"][0], None),
               ("flux_mlp.up", W["flux_mlp"][0], None),
@@ -349,7 +351,8 @@ def time_a8_rows(tern, tern_inputs, torch, dev, reps):
               ("flux_mlp.down", W["flux_mlp"][1], None),
               ("flux_single_stream.in_proj", W["flux_single_stream"][0], None),
               ("flux_single_stream.out_proj", W["flux_single_stream"][1], None),
-              ("dit.up.m2048", W["dit"][0], None), ("dit.down.m2048", W["dit"][1], None)]
+              ("dit.up.m2048", W["dit"][0], None), ("dit.down.m2048", W["dit"][1], None),
+              ("dit.up.m8", W["dit"][2], None), ("dit.down.m8", W["dit"][3], None)]
     rows = []
     for name, layer, epi in shapes:
         m, k, n = layer.m, layer.k, layer.n
@@ -362,8 +365,16 @@ def time_a8_rows(tern, tern_inputs, torch, dev, reps):
         act = tern.TERN_ACT_NONE if epi is None else tern.TERN_ACT_GELU_TANH
         af = 0 if epi is None else epi[1]
 
+        pool = m <= 64
+        p8s = [p8]
+        if pool:
+            count = max(1, -(-(pool_mib << 20) // (p8.numel() + 4 * n)))
+            p8s = [p8.clone() for _ in range(count)]
+        it = [0]
+
         def gemm():
-            tern.tern_gemm_a8(q, xs, p8, s, y, None, act, af, k)
+            tern.tern_gemm_a8(q, xs, p8s[it[0] % len(p8s)], s, y, None, act, af, k)
+            it[0] += 1
 
         def quant():
             tern.tern_quantize_act(xd, q, xs)
@@ -372,9 +383,10 @@ def time_a8_rows(tern, tern_inputs, torch, dev, reps):
             quant()
             gemm()
 
-        t_g = time_graph(torch, gemm, reps)
+        launches = len(p8s) if pool else reps
+        t_g = time_graph(torch, gemm, launches)
         t_q = time_graph(torch, quant, reps)
-        t_l = time_graph(torch, layer_fn, reps)
+        t_l = time_graph(torch, layer_fn, launches)
         flops = 2 * m * n * k
         byts = m * k + n * k // 4 + 4 * n + 4 * m + 2 * m * n
         q_bytes = 2 * m * k + m * k + 4 * m
@@ -387,12 +399,14 @@ def time_a8_rows(tern, tern_inputs, torch, dev, reps):
                "layer_us": t_l * 1e6, "layer_tops": flops / t_l / 1e12}
         if epi is not None:
             row["epilogue"] = {"bias": False, "act": "gelu_tanh", "act_from": af}
+        if pool:
+            row["weight_pool_mib"] = round(len(p8s) * (p8.numel() + 4 * n) / 2**20, 1)
         rows.append(row)
         print(f"# a8 row {name}: gemm {t_g * 1e6:.1f} us {row['tops']:.0f} TOP/s "
               f"({row['pct_i8_peak']:.1f}% of int8 peak); quantize_act {t_q * 1e6:.1f} us "
               f"{row['quantize_act_gbs']:.0f} GB/s; layer {t_l * 1e6:.1f} us",
               file=sys.stderr, flush=True)
-        del p, p8, q, xs, y, xd
+        del p, p8, p8s, q, xs, y, xd
         torch.cuda.empty_cache()
     return rows
 
@@ -606,7 +620,7 @@ def main():
     if not args.no_rows and args.rows in ("all", "a8"):
         print("# timing the 8-bit-activation layer on the forward shapes", file=sys.stderr,
               flush=True)
-        a8_rows = time_a8_rows(tern, tern_inputs, torch, dev, args.row_reps)
+        a8_rows = time_a8_rows(tern, tern_inputs, torch, dev, args.row_reps, args.pool_mib)
 
     cpu = None
     if not args.no_cpu_baseline:

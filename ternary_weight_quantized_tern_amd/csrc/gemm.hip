@@ -862,6 +862,9 @@ hipError_t launch_gemm_a8(const int8_t* q, int64_t m, int64_t k, int64_t ldq, co
                        af);
     return hipGetLastError();
   }
+  // A few tokens: the weight stream dominates; see gemm_small.hip.
+  if (m <= kSmallMaxM)
+    return launch_gemm_small_a8(q, m, k, ldq, xs, p8, n, ldp8, s, bias, act_from, y, ldy, stream);
   if (bias != nullptr || act_from < n)
     return launch_big_a8<true>(q, m, k, ldq, xs, p8, n, ldp8, s, bias, af, y, ldy, stream);
   return launch_big_a8<false>(q, m, k, ldq, xs, p8, n, ldp8, s, nullptr, af, y, ldy, stream);

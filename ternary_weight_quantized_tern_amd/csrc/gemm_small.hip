@@ -25,6 +25,14 @@
 //    is zero as well.
 //  * The four per-wave partial sums are added through LDS; wave 0 applies the
 //    fp32 channel scale and rounds once to bf16.
+//  * A8 (int8 activations, the 8-bit-activation variant of the layer): the
+//    weights come field-transposed, so one shift and one mask per register
+//    give the int8 operand of v_mfma_i32_16x16x64_i8; MFMA d of a chunk
+//    (d = 0..3) takes code word d of the lane's 16 bytes (codes 16 d .. 16 d
+//    + 15 of its 64) and the matching 16 int8 values of X.  The partial sums
+//    are exact int32 values and are added as integers; wave 0 converts the
+//    total once and applies s[n] / 64 and the token's scale xs[m], the
+//    formula of the tiled kernel, so both give the same bits.
 #include <type_traits>
 
 #include "gemm_common.h"
@@ -42,11 +50,14 @@ constexpr uint32_t kOutOfRange = 0x80000000u;
 // serves B MFMAs), DEPTH chunks in flight per wave.  With EPI the epilogue
 // adds bias[n] (when bias is not null) and applies the tanh-form GELU to
 // columns n >= act_from.
-template <int R, int B, int DEPTH, bool EPI>
+template <int R, int B, int DEPTH, bool EPI, bool A8 = false>
 __global__ __launch_bounds__(kSmallThreads) void gemm_ternary_small(
-    const uint16_t* __restrict__ x, int m, int k, int ldx, const uint8_t* __restrict__ p, int n,
-    int ldp, const float* __restrict__ s, const float* __restrict__ bias, int act_from,
-    uint16_t* __restrict__ y, int ldy, int y_vec_ok) {
+    const uint8_t* __restrict__ x, int m, int k, int ldx, const float* __restrict__ xs,
+    const uint8_t* __restrict__ p, int n, int ldp, const float* __restrict__ s,
+    const float* __restrict__ bias, int act_from, uint16_t* __restrict__ y, int ldy,
+    int y_vec_ok) {
+  constexpr int kXElem = A8 ? 1 : 2;          // bytes per X element
+  constexpr int kXPieces = A8 ? 4 : 8;        // 16-byte X pieces per chunk and lane
   __shared__ f32x4_t red[kSmallThreads / 64 - 1][B][R][64];
 
   const int tid = threadIdx.x;
@@ -59,8 +70,8 @@ __global__ __launch_bounds__(kSmallThreads) void gemm_ternary_small(
 
   const __amdgpu_buffer_rsrc_t prs = make_rsrc(
       p + static_cast<int64_t>(n0) * ldp, static_cast<uint32_t>((rows - 1) * ldp + k / 4));
-  const __amdgpu_buffer_rsrc_t xrs =
-      make_rsrc(x, static_cast<uint32_t>((static_cast<int64_t>(m) - 1) * ldx * 2 + k * 2));
+  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(
+      x, static_cast<uint32_t>(((static_cast<int64_t>(m) - 1) * ldx + k) * kXElem));
 
   const int chunks = (k + kChunk - 1) / kChunk;
   const int mine = (chunks - wave + 3) / 4;  // chunks wave, wave + 4, ...
@@ -69,10 +80,11 @@ __global__ __launch_bounds__(kSmallThreads) void gemm_ternary_small(
   const uint32_t p_off = static_cast<uint32_t>(r16 * ldp + 16 * g);
   uint32_t x_off[R];
 #pragma unroll
-  for (int b = 0; b < R; ++b) x_off[b] = static_cast<uint32_t>(((16 * b + r16) * ldx + 64 * g) * 2);
+  for (int b = 0; b < R; ++b)
+    x_off[b] = static_cast<uint32_t>(((16 * b + r16) * ldx + 64 * g) * kXElem);
 
   u32x4_t wq[DEPTH][B];
-  u32x4_t xq[DEPTH][R][8];
+  u32x4_t xq[DEPTH][R][kXPieces];
   // Each chunk's loads are issued as one group, in chunk order (the fences
   // keep the scheduler from interleaving groups), so that waiting for the
   // oldest chunk never waits for a younger one.
@@ -97,8 +109,8 @@ __global__ __launch_bounds__(kSmallThreads) void gemm_ternary_small(
 #pragma unroll
     for (int b = 0; b < R; ++b)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t xo = (x_off[b] + static_cast<uint32_t>((c * kChunk + 8 * j) * 2)) | oob;
+      for (int j = 0; j < kXPieces; ++j) {
+        const uint32_t xo = (x_off[b] + static_cast<uint32_t>(c * kChunk * kXElem + 16 * j)) | oob;
         xq[slot][b][j] =
             __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(xrs, xo, 0, 0));
       }
@@ -114,7 +126,7 @@ __global__ __launch_bounds__(kSmallThreads) void gemm_ternary_small(
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int nc = n0 + 16 * bl + 4 * g + e;
-      sc[bl][e] = nc < n ? (s != nullptr ? s[nc] : 1.0f) * 0.5f : 0.0f;
+      sc[bl][e] = nc < n ? (s != nullptr ? s[nc] : 1.0f) * (A8 ? 0.015625f : 0.5f) : 0.0f;
     }
   float bsv[EPI ? B : 1][4];
   if constexpr (EPI) {
@@ -133,6 +145,19 @@ __global__ __launch_bounds__(kSmallThreads) void gemm_ternary_small(
 #pragma unroll
     for (int b = 0; b < R; ++b) acc[bl][b] = f32x4_t{};
   auto compute = [&](int slot) {
+    if constexpr (A8) {
+#pragma unroll
+      for (int bl = 0; bl < B; ++bl)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          u32x4_t a;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) a[r] = (wq[slot][bl][d] << (6 - 2 * r)) & 0xC0C0C0C0u;
+#pragma unroll
+          for (int b = 0; b < R; ++b) mfma_i8<false>(acc[bl][b], a, xq[slot][b][d]);
+        }
+      return;
+    }
 #pragma unroll
     for (int bl = 0; bl < B; ++bl)
 #pragma unroll
@@ -183,15 +208,27 @@ __global__ __launch_bounds__(kSmallThreads) void gemm_ternary_small(
   const int nb = n0 + 16 * bl + 4 * g;  // output channels nb .. nb + 3 of this lane
 #pragma unroll
   for (int b = 0; b < R; ++b) {
-    f32x4_t v = acc[bl][b];
+    f32x4_t v;
+    if constexpr (A8) {
+      i32x4_t vi = __builtin_bit_cast(i32x4_t, acc[bl][b]);
 #pragma unroll
-    for (int w = 0; w < kSmallThreads / 64 - 1; ++w) v += red[w][bl][b][lane];
+      for (int w = 0; w < kSmallThreads / 64 - 1; ++w)
+        vi += __builtin_bit_cast(i32x4_t, red[w][bl][b][lane]);
+      v = __builtin_convertvector(vi, f32x4_t);
+    } else {
+      v = acc[bl][b];
+#pragma unroll
+      for (int w = 0; w < kSmallThreads / 64 - 1; ++w) v += red[w][bl][b][lane];
+    }
     const int token = 16 * b + r16;
     if (token >= m) continue;
+    float xsm = 1.0f;
+    if constexpr (A8) xsm = xs[token];
     __bf16 o[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       float z = v[e] * sc[bl][e];
+      if constexpr (A8) z *= xsm;
       if constexpr (EPI) {
         z += bsv[bl][e];
         if (nb + e >= act_from) z = gelu_tanh_f32(z);
@@ -215,22 +252,24 @@ __global__ __launch_bounds__(kSmallThreads) void gemm_ternary_small(
   }
 }
 
-template <int R, int B, int DEPTH, bool EPI>
-hipError_t launch_small(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const uint8_t* p,
-                        int64_t n, int64_t ldp, const float* s, const float* bias, int act_from,
-                        uint16_t* y, int64_t ldy, hipStream_t stream) {
+template <int R, int B, int DEPTH, bool EPI, bool A8>
+hipError_t launch_small(const void* x, int64_t m, int64_t k, int64_t ldx, const float* xs,
+                        const uint8_t* p, int64_t n, int64_t ldp, const float* s,
+                        const float* bias, int act_from, uint16_t* y, int64_t ldy,
+                        hipStream_t stream) {
   const int64_t blocks = (n + 16 * B - 1) / (16 * B);
   const int y_vec_ok = ((reinterpret_cast<uintptr_t>(y) & 7) == 0) && (ldy % 4 == 0);
-  hipLaunchKernelGGL((gemm_ternary_small<R, B, DEPTH, EPI>), dim3(static_cast<unsigned>(blocks)),
-                     dim3(kSmallThreads), 0, stream, x, static_cast<int>(m), static_cast<int>(k),
-                     static_cast<int>(ldx), p, static_cast<int>(n), static_cast<int>(ldp), s, bias,
-                     act_from, y, static_cast<int>(ldy), y_vec_ok);
+  hipLaunchKernelGGL((gemm_ternary_small<R, B, DEPTH, EPI, A8>), dim3(static_cast<unsigned>(blocks)),
+                     dim3(kSmallThreads), 0, stream, static_cast<const uint8_t*>(x),
+                     static_cast<int>(m), static_cast<int>(k), static_cast<int>(ldx), xs, p,
+                     static_cast<int>(n), static_cast<int>(ldp), s, bias, act_from, y,
+                     static_cast<int>(ldy), y_vec_ok);
   return hipGetLastError();
 }
 
 
-template <bool EPI>
-hipError_t launch_small_any(const uint16_t* x, int64_t m, int64_t k, int64_t ldx,
+template <bool EPI, bool A8 = false>
+hipError_t launch_small_any(const void* x, int64_t m, int64_t k, int64_t ldx, const float* xs,
                             const uint8_t* p, int64_t n, int64_t ldp, const float* s,
                             const float* bias, int act_from, uint16_t* y, int64_t ldy,
                             hipStream_t stream) {
@@ -255,17 +294,17 @@ hipError_t launch_small_any(const uint16_t* x, int64_t m, int64_t k, int64_t ldx
 #define TERN_SMALL(R, DEPTH6, DEPTH3, DEPTH2, DEPTH1)                                           \
   switch (best) {                                                                               \
     case 6:                                                                                     \
-      return launch_small<R, 6, DEPTH6, EPI>(x, m, k, ldx, p, n, ldp, s, bias, act_from, y, ldy, \
-                                             stream);                                           \
+      return launch_small<R, 6, DEPTH6, EPI, A8>(x, m, k, ldx, xs, p, n, ldp, s, bias, act_from, \
+                                                 y, ldy, stream);                                 \
     case 3:                                                                                     \
-      return launch_small<R, 3, DEPTH3, EPI>(x, m, k, ldx, p, n, ldp, s, bias, act_from, y, ldy, \
-                                             stream);                                           \
+      return launch_small<R, 3, DEPTH3, EPI, A8>(x, m, k, ldx, xs, p, n, ldp, s, bias, act_from, \
+                                                 y, ldy, stream);                                 \
     case 2:                                                                                     \
-      return launch_small<R, 2, DEPTH2, EPI>(x, m, k, ldx, p, n, ldp, s, bias, act_from, y, ldy, \
-                                             stream);                                           \
+      return launch_small<R, 2, DEPTH2, EPI, A8>(x, m, k, ldx, xs, p, n, ldp, s, bias, act_from, \
+                                                 y, ldy, stream);                                 \
     default:                                                                                    \
-      return launch_small<R, 1, DEPTH1, EPI>(x, m, k, ldx, p, n, ldp, s, bias, act_from, y, ldy, \
-                                             stream);                                           \
+      return launch_small<R, 1, DEPTH1, EPI, A8>(x, m, k, ldx, xs, p, n, ldp, s, bias, act_from, \
+                                                 y, ldy, stream);                                 \
   }
   if (m <= 16) TERN_SMALL(1, 3, 3, 4, 4)
   TERN_SMALL(2, 2, 2, 2, 2)
@@ -279,10 +318,21 @@ hipError_t launch_gemm_small(const uint16_t* x, int64_t m, int64_t k, int64_t ld
                              const float* bias, int64_t act_from, uint16_t* y, int64_t ldy,
                              hipStream_t stream) {
   if (bias != nullptr || act_from < n)
-    return launch_small_any<true>(x, m, k, ldx, p, n, ldp, s, bias, static_cast<int>(act_from), y,
-                                  ldy, stream);
-  return launch_small_any<false>(x, m, k, ldx, p, n, ldp, s, nullptr, static_cast<int>(act_from),
-                                 y, ldy, stream);
+    return launch_small_any<true>(x, m, k, ldx, nullptr, p, n, ldp, s, bias,
+                                  static_cast<int>(act_from), y, ldy, stream);
+  return launch_small_any<false>(x, m, k, ldx, nullptr, p, n, ldp, s, nullptr,
+                                 static_cast<int>(act_from), y, ldy, stream);
+}
+
+hipError_t launch_gemm_small_a8(const int8_t* q, int64_t m, int64_t k, int64_t ldq,
+                                const float* xs, const uint8_t* p8, int64_t n, int64_t ldp8,
+                                const float* s, const float* bias, int64_t act_from, uint16_t* y,
+                                int64_t ldy, hipStream_t stream) {
+  if (bias != nullptr || act_from < n)
+    return launch_small_any<true, true>(q, m, k, ldq, xs, p8, n, ldp8, s, bias,
+                                        static_cast<int>(act_from), y, ldy, stream);
+  return launch_small_any<false, true>(q, m, k, ldq, xs, p8, n, ldp8, s, nullptr,
+                                       static_cast<int>(act_from), y, ldy, stream);
 }
 
 }  // namespace tern

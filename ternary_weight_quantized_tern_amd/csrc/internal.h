@@ -44,6 +44,12 @@ hipError_t launch_pack_transposed(const uint8_t* p, int64_t n, int64_t k, int64_
 hipError_t launch_scale_grad(const uint16_t* dy, int64_t m, int64_t n, int64_t lddy,
                              const float* s, uint16_t* u, int64_t ldu, hipStream_t stream);
 
+// m <= 32 with int8 activations (called by launch_gemm_a8).
+hipError_t launch_gemm_small_a8(const int8_t* q, int64_t m, int64_t k, int64_t ldq,
+                                const float* xs, const uint8_t* p8, int64_t n, int64_t ldp8,
+                                const float* s, const float* bias, int64_t act_from, uint16_t* y,
+                                int64_t ldy, hipStream_t stream);
+
 // Per-token int8 activations: q = rint(x * (127 / max|x|)), xs = max|x| / 127.
 hipError_t launch_quantize_act(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, int8_t* q,
                                int64_t ldq, float* xs, hipStream_t stream);

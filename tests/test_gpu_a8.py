@@ -198,6 +198,34 @@ def test_gemm_a8_one_tile_per_cu_epilogue_sampled():
                    act=tern.TERN_ACT_GELU_TANH, act_from=2300)
 
 
+@pytest.mark.parametrize("m,k,n", [(32, 3072, 3072), (17, 256, 1000), (5, 4608, 1152),
+                                   (16, 1152, 4608), (2, 15360, 520)])
+def test_gemm_a8_few_tokens_all_elements(m, k, n):
+    x, w = tern_inputs.draw(m, k, n, seed=3 * m + n, x_dist="student_t3")
+    worst = check_layer_a8(x, w, f"a8 few m={m} k={k} n={n}", full=True)
+    log(f"  worst error / bound = {worst:.3f}")
+
+
+def test_gemm_a8_few_token_and_tiled_kernels_agree_bitwise():
+    # m = 32 runs the weight-streaming kernel, m = 33 the tiled one; both
+    # apply the same formula to the same exact int32 sums
+    k, n = 1152, 4608
+    g = torch.Generator().manual_seed(8)
+    q = torch.randint(-127, 128, (33, k), generator=g, dtype=torch.int8).to(DEV)
+    xs = (torch.rand(33, generator=g) * 0.05).to(DEV)
+    s = (torch.rand(n, generator=g) * 0.05).to(DEV)
+    t = tern_inputs.random_ternary(n, k, seed=12).numpy()
+    p8 = torch.from_numpy(oracle.oracle_pack_a8(oracle.oracle_pack(t), k)).to(DEV)
+    bias = torch.linspace(-1, 1, n).to(DEV)
+    for act, act_from, b in ((tern.TERN_ACT_NONE, 0, None), (tern.TERN_ACT_GELU_TANH, 1000, bias)):
+        y33 = torch.empty((33, n), dtype=torch.bfloat16, device=DEV)
+        y32 = torch.empty((32, n), dtype=torch.bfloat16, device=DEV)
+        tern.tern_gemm_a8(q, xs, p8, s, y33, b, act, act_from)
+        tern.tern_gemm_a8(q[:32], xs[:32], p8, s, y32, b, act, act_from)
+        torch.cuda.synchronize()
+        assert torch.equal(y32.view(torch.int16), y33[:32].view(torch.int16)), f"act={act}"
+
+
 def test_gemm_a8_k_zero_and_strided_operands():
     # k == 0: bf16(gelu(bias))
     n = 40
@@ -326,7 +354,8 @@ def test_linear_a8_convenience_and_errors():
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("name,i", [("single", 0), ("flux_qkv", 0), ("flux_mlp", 0),
-                                    ("flux_mlp", 1), ("dit", 0), ("dit", 1), ("dit", 2)])
+                                    ("flux_mlp", 1), ("dit", 0), ("dit", 1), ("dit", 2),
+                                    ("dit", 3)])
 def test_workload_a8(name, i):
     layer = tern_inputs.WORKLOADS[name][i]
     log(f"a8 workload {layer.name} m={layer.m} k={layer.k} n={layer.n}")
