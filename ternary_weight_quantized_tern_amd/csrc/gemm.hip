@@ -49,7 +49,7 @@
 // The weights come field-transposed (act.hip), which makes one shift and one
 // mask per operand register the whole decode; the exact int32 sums are
 // scaled by s[n] / 64 and the token's scale xs[m] in the epilogue.  Tiles
-// 144 x 256 (the six-stage ring then fills 156 KiB of LDS), 64 x 576 or
+// 144 x 384 in a four-stage ring (30 KiB stages), 64 x 576, 144 x 256 or
 // 64 x 128.
 #include <type_traits>
 
@@ -167,7 +167,8 @@ struct TileCfg {
 // only, for any k that is a multiple of 64 (128 with A8).  With EPI the epilogue adds
 // bias[n] (when bias is not null) and applies the tanh-form GELU to columns
 // n >= act_from; without it, bias and act_from are not read.
-template <int BM, int BN, int WAVES_M, int GM, bool PERSIST, int WPE, bool EPI, bool A8>
+template <int BM, int BN, int WAVES_M, int GM, bool PERSIST, int WPE, bool EPI, bool A8,
+          int RING = 6>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void gemm_ternary_mfma(const uint8_t* __restrict__ x, int m, int k, int ldx,
                        const float* __restrict__ xs, const uint8_t* __restrict__ p, int n, int ldp,
@@ -181,14 +182,16 @@ void gemm_ternary_mfma(const uint8_t* __restrict__ x, int m, int k, int ldx,
   const int ldxb = ldx * C::kXElem;  // X pitch in bytes (< 2^24, checked by the host)
   // One LDS object per ring stage, so that the compiler tracks each stage's
   // DMA writes separately.  kRing = 6 stages: one being read, one being read
-  // next, four in flight.
-  constexpr int kRing = 6;
+  // next, four in flight; or 4 (two in flight) where a stage is too large for
+  // six (the int8 144 x 384 tile: 30 KiB per stage).
+  constexpr int kRing = RING;
+  static_assert(RING == 6 || RING == 4, "ring of 6 or 4 stages");
   __shared__ __attribute__((aligned(1024))) uint8_t lds0[C::kStage];
   __shared__ __attribute__((aligned(1024))) uint8_t lds1[C::kStage];
   __shared__ __attribute__((aligned(1024))) uint8_t lds2[C::kStage];
   __shared__ __attribute__((aligned(1024))) uint8_t lds3[C::kStage];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds4[C::kStage];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds5[C::kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds4[RING == 6 ? C::kStage : 1];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds5[RING == 6 ? C::kStage : 1];
 
   const int num_tiles = tiles_m * tiles_n;
   const int grid = gridDim.x;
@@ -446,12 +449,13 @@ void gemm_ternary_mfma(const uint8_t* __restrict__ x, int m, int k, int ldx,
   //
   // Whole tiles with a 16-byte aligned Y and scale vector go through LDS:
   // each wave writes 16 of its rows at a time, kEpiJ MFMA tiles (16 kEpiJ
-  // columns) per pass, into its own part of ring stage lds5 (pitch kEpiPitch
+  // columns) per pass, into its own part of the ring's last stage (lds5, or
+  // lds3 in a four-stage ring; pitch kEpiPitch
   // bytes, conflict-free for the 8-byte writes) and stores them back as
   // 16-byte pieces of whole row segments (32 kEpiJ bytes per row), so that a
   // store instruction writes a few long contiguous runs instead of 16
   // scattered 32-byte ones.  kEpiJ is the largest divisor of kTN whose four
-  // staging areas fit one ring stage.  lds5 holds no live stage here: it held
+  // staging areas fit one ring stage.  That stage holds no live data here: it held
   // the tile's last stage (all reads of it end at the barrier below) and the
   // next request into it follows the next step's barrier.  Other tiles take
   // the direct path, with 8-byte stores where Y allows them.
@@ -578,12 +582,16 @@ void gemm_ternary_mfma(const uint8_t* __restrict__ x, int m, int k, int ldx,
       for (int p = 0; p < kPasses; ++p) {
 #pragma unroll
         for (int jj = 0; jj < kEpiJ; ++jj)
-          *reinterpret_cast<u32x2_t*>(&lds5[wr_off + 32 * jj]) = o[p % 2][jj];
+          if constexpr (RING == 6)
+            *reinterpret_cast<u32x2_t*>(&lds5[wr_off + 32 * jj]) = o[p % 2][jj];
+          else
+            *reinterpret_cast<u32x2_t*>(&lds3[wr_off + 32 * jj]) = o[p % 2][jj];
         u32x4_t v[kStores];
 #pragma unroll
         for (int q = 0; q < kStores; ++q)
           if (kChunks % 64 == 0 || lane + 64 * q < kChunks)
-            v[q] = *reinterpret_cast<const u32x4_t*>(&lds5[rd_off[q]]);
+            v[q] = RING == 6 ? *reinterpret_cast<const u32x4_t*>(&lds5[rd_off[q]])
+                             : *reinterpret_cast<const u32x4_t*>(&lds3[rd_off[q]]);
         if (p + 1 < kPasses) convert(p + 1, o[(p + 1) % 2]);
         uint16_t* const yi =
             yt + static_cast<int64_t>(16 * (p / kJPasses)) * ldy + 16 * kEpiJ * (p % kJPasses);
@@ -648,7 +656,7 @@ void gemm_ternary_mfma(const uint8_t* __restrict__ x, int m, int k, int ldx,
   // One unrolled iteration: steps st .. st + kRing - 1 out of ring stages 0 ..
   // kRing - 1.  The first request is stage st + kRing - 1 of this tile, the
   // others stages B0 .. B0 + kRing - 2 of the tile with resources BX, BP.
-#define TERN_GEMM_ITER(BX, BP, B0, ZERO)                                          \
+#define TERN_GEMM_ITER6(BX, BP, B0, ZERO)                                         \
   /* several statements: use inside braces */                                     \
   TERN_GEMM_STEP(lds0, lds1, lds5, cur_xr, cur_pr, st + kRing - 1, ZERO)          \
   TERN_GEMM_STEP(lds1, lds2, lds0, BX, BP, (B0), kAcc)                            \
@@ -656,14 +664,27 @@ void gemm_ternary_mfma(const uint8_t* __restrict__ x, int m, int k, int ldx,
   TERN_GEMM_STEP(lds3, lds4, lds2, BX, BP, (B0) + 2, kAcc)                        \
   TERN_GEMM_STEP(lds4, lds5, lds3, BX, BP, (B0) + 3, kAcc)                        \
   TERN_GEMM_STEP(lds5, lds0, lds4, BX, BP, (B0) + 4, kAcc)
+#define TERN_GEMM_ITER4(BX, BP, B0, ZERO)                                         \
+  TERN_GEMM_STEP(lds0, lds1, lds3, cur_xr, cur_pr, st + kRing - 1, ZERO)          \
+  TERN_GEMM_STEP(lds1, lds2, lds0, BX, BP, (B0), kAcc)                            \
+  TERN_GEMM_STEP(lds2, lds3, lds1, BX, BP, (B0) + 1, kAcc)                        \
+  TERN_GEMM_STEP(lds3, lds0, lds2, BX, BP, (B0) + 2, kAcc)
+#define TERN_GEMM_ITER(BX, BP, B0, ZERO)                                          \
+  if constexpr (RING == 6) {                                                      \
+    TERN_GEMM_ITER6(BX, BP, B0, ZERO)                                             \
+  } else {                                                                        \
+    TERN_GEMM_ITER4(BX, BP, B0, ZERO)                                             \
+  }
 
   __amdgpu_buffer_rsrc_t cur_xr, cur_pr;
   tile_rsrc(0, cur_xr, cur_pr);
   TERN_GEMM_ISSUE(lds0, cur_xr, cur_pr, 0)
   TERN_GEMM_ISSUE(lds1, cur_xr, cur_pr, 1)
   TERN_GEMM_ISSUE(lds2, cur_xr, cur_pr, 2)
-  TERN_GEMM_ISSUE(lds3, cur_xr, cur_pr, 3)
-  TERN_GEMM_ISSUE(lds4, cur_xr, cur_pr, 4)
+  if constexpr (RING == 6) {
+    TERN_GEMM_ISSUE(lds3, cur_xr, cur_pr, 3)
+    TERN_GEMM_ISSUE(lds4, cur_xr, cur_pr, 4)
+  }
   wait_vmcnt<(kRing - 2) * C::kLoads, true>();
   lds_barrier();
   TERN_GEMM_READ_A(lds0)
@@ -712,6 +733,8 @@ void gemm_ternary_mfma(const uint8_t* __restrict__ x, int m, int k, int ldx,
     epilogue(0);
   }
 #undef TERN_GEMM_ITER
+#undef TERN_GEMM_ITER6
+#undef TERN_GEMM_ITER4
 #undef TERN_GEMM_STEP
 #undef TERN_GEMM_HALF_A
 #undef TERN_GEMM_ISSUE
@@ -744,7 +767,7 @@ __global__ void fill_empty_sum(uint16_t* y, int m, int n, int ldy, const float* 
 constexpr int kPersistentGrid = 256;
 constexpr int64_t kSmallMaxM = 32;
 
-template <int BM, int BN, int WAVES_M, int GM, int WPE, bool EPI, bool A8 = false>
+template <int BM, int BN, int WAVES_M, int GM, int WPE, bool EPI, bool A8 = false, int RING = 6>
 hipError_t launch_tiles(const void* x, int64_t m, int64_t k, int64_t ldx, const float* xs,
                         const uint8_t* p, int64_t n, int64_t ldp, const float* s,
                         const float* bias, int act_from, uint16_t* y, int64_t ldy,
@@ -764,9 +787,9 @@ hipError_t launch_tiles(const void* x, int64_t m, int64_t k, int64_t ldx, const 
   // The persistent kernel takes whole tiles only (its epilogue has no edge
   // handling) and needs the ring stream to restart at a tile boundary.
   if constexpr (WPE == 1) {
-    if (stages % 6 == 0 && tiles > kPersistentGrid && m % BM == 0 && n % BN == 0 &&
+    if (stages % RING == 0 && tiles > kPersistentGrid && m % BM == 0 && n % BN == 0 &&
         (y_flags & 2)) {
-      hipLaunchKernelGGL((gemm_ternary_mfma<BM, BN, WAVES_M, GM, true, WPE, EPI, A8>),
+      hipLaunchKernelGGL((gemm_ternary_mfma<BM, BN, WAVES_M, GM, true, WPE, EPI, A8, RING>),
                          dim3(kPersistentGrid), dim3(kThreads), 0, stream, xb,
                          static_cast<int>(m), static_cast<int>(k), static_cast<int>(ldx), xs, p,
                          static_cast<int>(n), static_cast<int>(ldp), s, bias, act_from, y,
@@ -774,7 +797,7 @@ hipError_t launch_tiles(const void* x, int64_t m, int64_t k, int64_t ldx, const 
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((gemm_ternary_mfma<BM, BN, WAVES_M, GM, false, WPE, EPI, A8>),
+  hipLaunchKernelGGL((gemm_ternary_mfma<BM, BN, WAVES_M, GM, false, WPE, EPI, A8, RING>),
                      dim3(static_cast<unsigned>(tiles)), dim3(kThreads), 0, stream, xb,
                      static_cast<int>(m), static_cast<int>(k), static_cast<int>(ldx), xs, p,
                      static_cast<int>(n), static_cast<int>(ldp), s, bias, act_from, y,
@@ -811,15 +834,21 @@ hipError_t launch_big_a8(const int8_t* q, int64_t m, int64_t k, int64_t ldq, con
                          const uint8_t* p8, int64_t n, int64_t ldp8, const float* s,
                          const float* bias, int act_from, uint16_t* y, int64_t ldy,
                          hipStream_t stream) {
-  // The int8 stage holds K = 128: 144 x 256 tiles fill six ring stages
-  // (156 KiB of LDS) and cut M = 4608 and every FLUX width into whole tiles.
-  // Layers that 64 x 576 tiles (the same stage size) cut into exactly one
-  // tile per CU use those; smaller layers use 64 x 128 tiles, two workgroups
-  // per CU.
+  // The int8 stage holds K = 128.  Large layers use 144 x 384 tiles (the
+  // bf16 kernel's wave tile, 54 MFMAs per half step) in a four-stage ring of
+  // 30 KiB stages (120 KiB of LDS); two stages in flight cover the memory
+  // latency, since an int8 step does as many MFMAs as a bf16 one.  Layers
+  // that 64 x 576 tiles cut into exactly one tile per CU use those (six
+  // stages of 26 KiB); 144 x 256 tiles with six stages take the layers with
+  // fewer than 256 144 x 384 tiles but at least 256 of their own; smaller
+  // layers use 64 x 128 tiles, two workgroups per CU.
   const auto tiles = [&](int64_t bm, int64_t bn) { return ((m + bm - 1) / bm) * ((n + bn - 1) / bn); };
   if (m % 64 == 0 && n % 576 == 0 && tiles(64, 576) == kPersistentGrid)
     return launch_tiles<64, 576, 1, 4, 1, EPI, true>(q, m, k, ldq, xs, p8, n, ldp8, s, bias,
                                                      act_from, y, ldy, stream);
+  if (tiles(144, 384) >= kPersistentGrid)
+    return launch_tiles<144, 384, 1, 4, 1, EPI, true, 4>(q, m, k, ldq, xs, p8, n, ldp8, s, bias,
+                                                         act_from, y, ldy, stream);
   if (tiles(144, 256) >= kPersistentGrid)
     return launch_tiles<144, 256, 1, 4, 1, EPI, true>(q, m, k, ldq, xs, p8, n, ldp8, s, bias,
                                                       act_from, y, ldy, stream);

@@ -259,10 +259,10 @@ def test_gemm_a8_k_zero_and_strided_operands():
 
 
 def test_gemm_a8_launch_paths_agree_bitwise():
-    # the persistent 144 x 256 kernel (whole tiles, 16-byte aligned y) and the
-    # one-tile-per-workgroup kernel with the direct epilogue (y misaligned)
-    # compute the same formula
-    m, k, n = 4608, 768, 3072
+    # the persistent 144 x 384 kernel (whole tiles, 16-byte aligned y, K / 128
+    # a multiple of its four-stage ring) and the one-tile-per-workgroup kernel
+    # with the direct epilogue (y misaligned) compute the same formula
+    m, k, n = 4608, 1024, 4608
     g = torch.Generator().manual_seed(5)
     q = torch.randint(-127, 128, (m, k), generator=g, dtype=torch.int8).to(DEV)
     xs = (torch.rand(m, generator=g) * 0.05).to(DEV)
