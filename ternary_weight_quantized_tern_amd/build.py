@@ -40,27 +40,46 @@ def sources() -> list:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
+def _compile_one(src: str, obj: str, extra: list) -> None:
+    cmd = [hipcc()] + compile_flags() + extra + ["-c", "-o", obj, src]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {os.path.basename(src)} ({r.returncode}):\n{r.stderr}")
+
+
 def build_library(out: str = LIB_PATH, extra: list | None = None, verbose: bool = False) -> str:
-    """Compile all HIP sources into ``out`` (atomically replaced)."""
+    """Compile all HIP sources into ``out`` (atomically replaced).  Each source
+    is compiled to an object file of its own, in parallel, then linked."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    extra = list(extra or [])
+    srcs = sources()
     fd, tmp = tempfile.mkstemp(suffix=".so.tmp", dir=os.path.dirname(out))
     os.close(fd)
-    cmd = [hipcc()] + compile_flags() + (extra or []) + ["-shared", "-o", tmp] + sources()
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    try:
-        r = subprocess.run(cmd, capture_output=True, text=True)
-        if r.returncode != 0:
-            raise RuntimeError(f"hipcc failed ({r.returncode}):\n{r.stderr}")
-        # A kernel whose host stub was not emitted shows up as an undefined
-        # symbol only when the library is loaded: load it in a child process.
-        chk = subprocess.run([sys.executable, "-c", f"import ctypes; ctypes.CDLL({tmp!r})"],
-                             capture_output=True, text=True)
-        if chk.returncode != 0:
-            raise RuntimeError(f"built library does not load:\n{chk.stderr}")
-        os.replace(tmp, out)
-    finally:
-        if os.path.exists(tmp):
-            os.unlink(tmp)
+    with tempfile.TemporaryDirectory(prefix="tern_build_") as objdir:
+        objs = [os.path.join(objdir, os.path.basename(f) + ".o") for f in srcs]
+        if verbose:
+            print(" ".join([hipcc()] + compile_flags() + extra + ["-c", "<each of>"] + srcs),
+                  flush=True)
+        jobs = max(1, min(len(srcs), os.cpu_count() or 1))
+        try:
+            with ThreadPoolExecutor(max_workers=jobs) as pool:
+                for f in [pool.submit(_compile_one, s, o, extra) for s, o in zip(srcs, objs)]:
+                    f.result()
+            cmd = [hipcc()] + compile_flags() + extra + ["-shared", "-o", tmp] + objs
+            r = subprocess.run(cmd, capture_output=True, text=True)
+            if r.returncode != 0:
+                raise RuntimeError(f"link failed ({r.returncode}):\n{r.stderr}")
+            # A kernel whose host stub was not emitted shows up as an undefined
+            # symbol only when the library is loaded: load it in a child process.
+            chk = subprocess.run([sys.executable, "-c", f"import ctypes; ctypes.CDLL({tmp!r})"],
+                                 capture_output=True, text=True)
+            if chk.returncode != 0:
+                raise RuntimeError(f"built library does not load:\n{chk.stderr}")
+            os.replace(tmp, out)
+        finally:
+            if os.path.exists(tmp):
+                os.unlink(tmp)
     return out
 
 
