@@ -11,6 +11,7 @@ from .oracle import (  # noqa: F401
     oracle_epilogue,
     oracle_gemm,
     oracle_gemm_a8,
+    oracle_gemm_dw,
     oracle_gemm_dx,
     oracle_pack,
     oracle_pack_a8,

@@ -36,6 +36,10 @@
  *    Y = (X . T^T) (.) s, dX = (dY (.) s) . T.  oracle_scale_grad forms the
  *    scaled gradient u = bf16(dY (.) s) as a bf16 operand, oracle_gemm_dx the
  *    unrounded sum over n of u . T (T in the forward's packed layout).
+ *  - The gradient of the latent full-precision weights for that training,
+ *    under the straight-through reading (the quantizer passes the gradient
+ *    of the quantized weight s_n T_nk to the latent weight unchanged):
+ *    oracle_gemm_dw, dW = dY^T . X, unrounded.
  *
  * Readings where the pages are silent (all listed in the design notes):
  *  - the mean is taken in 64-bit fixed point relative to the row's largest
@@ -470,4 +474,90 @@ int oracle_pack_a8(const uint8_t* p, int64_t n, int64_t k, int64_t ldp, uint8_t*
     }
   }
   return ORACLE_OK;
+}
+
+/*
+ * Gradient of the latent full-precision weights, for quantization-aware
+ * training of the ternary layer ("TerDiT", abstract: ternary DiT weights
+ * trained in the loop; the pages give no formula).  The forward layer is
+ * Y = X . (s (.) T)^T, the quantized weight s_n T_nk standing in for the
+ * latent weight w_nk.  The reading used is the straight-through estimator
+ * that treats the quantizer as the identity in the backward pass, so the
+ * latent weight receives the gradient of the quantized one:
+ *
+ *   dw[n][k] = sum_{m ascending} dy[m][n] * x[m][k]
+ *
+ * dy (the gradient of Y, [m, n]) and x (the layer input, [m, k]) bf16,
+ * widened exactly, the products and the sum in double, unrounded.  Threads
+ * split the output rows n; each thread gathers the column dy[., n] once and
+ * runs it against every column of x.
+ */
+typedef struct {
+  const double* dyd;  /* n x m: the widened gradient, transposed */
+  const double* xd;   /* k x m: the widened input, transposed */
+  int64_t m, k;
+  double* dw;
+  int64_t lddw;
+  int64_t n_begin, n_end;
+} dw_job;
+
+static void* dw_worker(void* arg) {
+  dw_job* j = (dw_job*)arg;
+  for (int64_t nn = j->n_begin; nn < j->n_end; ++nn) {
+    const double* g = j->dyd + nn * j->m;
+    for (int64_t kk = 0; kk < j->k; ++kk) {
+      const double* xc = j->xd + kk * j->m;
+      double acc = 0.0;
+      for (int64_t mm = 0; mm < j->m; ++mm) acc += g[mm] * xc[mm];
+      j->dw[nn * j->lddw + kk] = acc;
+    }
+  }
+  return NULL;
+}
+
+int oracle_gemm_dw(const uint16_t* dy, int64_t m, int64_t n, int64_t lddy, const uint16_t* x,
+                   int64_t k, int64_t ldx, double* dw, int64_t lddw, int nthreads) {
+  if (m < 0 || n < 0 || k < 0 || lddy < n || ldx < k || lddw < k) return ORACLE_BAD_ARG;
+  if (n == 0 || k == 0) return ORACLE_OK;
+  const int64_t mm1 = m > 0 ? m : 1;
+  double* dyd = (double*)malloc((size_t)(n * mm1) * sizeof(double));
+  double* xd = (double*)malloc((size_t)(k * mm1) * sizeof(double));
+  if (!dyd || !xd) {
+    free(dyd);
+    free(xd);
+    return ORACLE_BAD_ARG;
+  }
+  for (int64_t mm = 0; mm < m; ++mm) {
+    for (int64_t nn = 0; nn < n; ++nn)
+      dyd[nn * m + mm] = (double)bf16_bits_to_float(dy[mm * lddy + nn]);
+    for (int64_t kk = 0; kk < k; ++kk)
+      xd[kk * m + mm] = (double)bf16_bits_to_float(x[mm * ldx + kk]);
+  }
+
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > n) nthreads = (int)n;
+  pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nthreads);
+  dw_job* jobs = (dw_job*)malloc(sizeof(dw_job) * (size_t)nthreads);
+  int rc = ORACLE_OK;
+  if (!th || !jobs) rc = ORACLE_BAD_ARG;
+  int started = 0;
+  for (int i = 0; rc == ORACLE_OK && i < nthreads; ++i) {
+    dw_job jb = {dyd, xd, m, k, dw, lddw, n * i / nthreads, n * (i + 1) / nthreads};
+    jobs[i] = jb;
+    if (pthread_create(&th[i], NULL, dw_worker, &jobs[i]) != 0) {
+      rc = ORACLE_BAD_ARG;
+      break;
+    }
+    ++started;
+  }
+  for (int i = 0; i < started; ++i) {
+    void* ret = NULL;
+    pthread_join(th[i], &ret);
+    if (ret != NULL) rc = ORACLE_BAD_ARG;
+  }
+  free(jobs);
+  free(th);
+  free(xd);
+  free(dyd);
+  return rc;
 }

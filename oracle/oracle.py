@@ -59,9 +59,11 @@ def load(path: str | None = None):
     lib.oracle_quantize_act.argtypes = [vp, i64, i64, i64, vp, i64, vp]
     lib.oracle_gemm_a8.argtypes = [vp, i64, i64, i64, vp, vp, i64, i64, vp, vp, i64]
     lib.oracle_pack_a8.argtypes = [vp, i64, i64, i64, vp, i64]
+    lib.oracle_gemm_dw.argtypes = [vp, i64, i64, i64, vp, i64, i64, vp, i64, ctypes.c_int]
     for f in (lib.oracle_quantize, lib.oracle_pack, lib.oracle_unpack, lib.oracle_gemm,
               lib.oracle_epilogue, lib.oracle_scale_grad, lib.oracle_gemm_dx,
-              lib.oracle_quantize_act, lib.oracle_gemm_a8, lib.oracle_pack_a8):
+              lib.oracle_quantize_act, lib.oracle_gemm_a8, lib.oracle_pack_a8,
+              lib.oracle_gemm_dw):
         f.restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -241,3 +243,23 @@ def oracle_pack_a8(p: np.ndarray, k: int, lib=None) -> np.ndarray:
     out = np.empty((n, nb), np.uint8)
     _check(lib.oracle_pack_a8(_ptr(p), n, k, ldp, _ptr(out), nb), "oracle_pack_a8")
     return out
+
+
+def oracle_gemm_dw(dy_bf16_bits: np.ndarray, x_bf16_bits: np.ndarray,
+                   nthreads: int | None = None, lib=None) -> np.ndarray:
+    """Unrounded latent-weight gradient ``dw[n,k] = sum_m dy[m,n] * x[m,k]`` in
+    float64 ``[N, K]`` (straight-through reading); ``dy`` ``[M, N]`` and ``x``
+    ``[M, K]`` as bf16 bit patterns."""
+    lib = lib or load()
+    dy = np.ascontiguousarray(dy_bf16_bits, dtype=np.uint16)
+    x = np.ascontiguousarray(x_bf16_bits, dtype=np.uint16)
+    m, n = dy.shape
+    mx, k = x.shape
+    if mx != m:
+        raise ValueError("dy and x must have the same number of rows (tokens)")
+    dw = np.empty((n, k), np.float64)
+    if nthreads is None:
+        nthreads = len(os.sched_getaffinity(0))
+    _check(lib.oracle_gemm_dw(_ptr(dy), m, n, n, _ptr(x), k, k, _ptr(dw), k, nthreads),
+           "oracle_gemm_dw")
+    return dw

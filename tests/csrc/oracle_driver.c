@@ -31,6 +31,8 @@ int oracle_gemm_a8(const int8_t* q, int64_t m, int64_t k, int64_t ldq, const flo
                    int64_t ldy);
 int oracle_pack_a8(const uint8_t* p, int64_t n, int64_t k, int64_t ldp, uint8_t* p8,
                    int64_t ldp8);
+int oracle_gemm_dw(const uint16_t* dy, int64_t m, int64_t n, int64_t lddy, const uint16_t* x,
+                   int64_t k, int64_t ldx, double* dw, int64_t lddw, int nthreads);
 
 static uint32_t rng = 12345u;
 static uint32_t next(void) {
@@ -68,6 +70,7 @@ static int run_shape(int64_t m, int64_t n, int64_t k, int64_t pad, int threads) 
   float* xs = malloc(sizeof(float) * (size_t)(m + 1));
   const int64_t k16 = k / 16 * 16, ldp8 = k16 / 4 + pad;
   uint8_t* p8 = malloc((size_t)(n * ldp8 + 1));
+  double* dw = malloc(sizeof(double) * (size_t)(n * (k + pad) + 1));
   (void)ldpt;
   for (int64_t i = 0; i < n * ldw; ++i) {
     w[i] = frand() * 0.05f;
@@ -92,7 +95,8 @@ static int run_shape(int64_t m, int64_t n, int64_t k, int64_t pad, int threads) 
   rc |= oracle_quantize_act(x, m, k, ldx, q, ldx, xs);
   rc |= oracle_gemm_a8(q, m, k, ldx, xs, p, n, ldp, s, y, ldy);
   rc |= oracle_pack_a8(p, n, k16, ldp, p8, ldp8);
-  free(q); free(xs); free(p8);
+  rc |= oracle_gemm_dw(dy, m, n, ldd, x, k, ldx, dw, k + pad, threads);
+  free(q); free(xs); free(p8); free(dw);
   free(w); free(wb); free(t); free(t2); free(s); free(p); free(x); free(y); free(bias);
   free(dy); free(u); free(dx);
   return rc;
@@ -115,6 +119,7 @@ int main(void) {
   CHECK(oracle_quantize_act(NULL, 1, 8, 7, NULL, 8, NULL) != 0);
   CHECK(oracle_gemm_a8(NULL, 1, 8, 8, NULL, NULL, 2, 1, NULL, NULL, 2) != 0);
   CHECK(oracle_pack_a8(NULL, 2, 24, 6, NULL, 6) != 0);             /* k % 16 != 0 */
+  CHECK(oracle_gemm_dw(NULL, 2, 4, 3, NULL, 8, 8, NULL, 8, 1) != 0); /* lddy < n */
   printf("oracle driver ok\n");
   return 0;
 }

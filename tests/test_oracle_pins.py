@@ -455,6 +455,60 @@ def test_pack_transposed_worked_example():
 
 
 # --------------------------------------------------------------------------
+# latent-weight gradient (straight-through reading): dW = dY^T . X
+# --------------------------------------------------------------------------
+
+def test_gemm_dw_worked_example():
+    # dy (3 tokens x 2 channels) = [[1, 2], [3, 4], [5, 6]], x (3 x 2) =
+    # [[1, 0], [0, 1], [1, 1]]: dw[n][k] = sum_m dy[m][n] x[m][k], by hand
+    # [[1 + 0 + 5, 0 + 3 + 5], [2 + 0 + 6, 0 + 4 + 6]] = [[6, 8], [8, 10]]
+    dy = np.array([[1, 2], [3, 4], [5, 6]], np.float32)
+    x = np.array([[1, 0], [0, 1], [1, 1]], np.float32)
+    dw = oracle.oracle_gemm_dw(_bf16_bits(dy), _bf16_bits(x))
+    assert dw.tolist() == [[6.0, 8.0], [8.0, 10.0]]
+
+
+def test_gemm_dw_adjoint_of_the_layer_exact():
+    # For Y = X . (s (.) T)^T, the directional derivative of <dY, Y> along the
+    # quantized weight V = s (.) T is <dY, X . V^T> = <dY, Y>; with the
+    # straight-through reading it must equal <dW, V>.  Small integers and
+    # power-of-two scales keep every product and sum exact in double, and Y
+    # comes from the forward layer's own oracle.
+    rng = np.random.default_rng(11)
+    m, k, n = 9, 40, 24
+    x = rng.integers(-4, 5, size=(m, k)).astype(np.float32)
+    dy = rng.integers(-3, 4, size=(m, n)).astype(np.float32)
+    s = (2.0 ** rng.integers(-3, 4, size=n)).astype(np.float32)
+    t = rng.integers(-1, 2, size=(n, k)).astype(np.int8)
+    y = oracle.oracle_gemm(_bf16_bits(x), oracle.oracle_pack(t), s)
+    dw = oracle.oracle_gemm_dw(_bf16_bits(dy), _bf16_bits(x))
+    v = s.astype(np.float64)[:, None] * t.astype(np.float64)
+    assert float((dw * v).sum()) == float((dy.astype(np.float64) * y).sum())
+    # and along an arbitrary integer direction V: <dW, V> = <dY, X V^T>
+    vv = rng.integers(-2, 3, size=(n, k)).astype(np.float64)
+    lhs = float((dw * vv).sum())
+    rhs = float((dy.astype(np.float64) * (x.astype(np.float64) @ vv.T)).sum())
+    assert lhs == rhs
+
+
+def test_gemm_dw_equals_numpy_matmul():
+    # exact on small-integer operands; to rounding on random bf16 operands,
+    # including a token count of one and an empty token range
+    rng = np.random.default_rng(12)
+    for m, n, k in ((7, 13, 19), (1, 5, 3), (64, 33, 17)):
+        dy = rng.integers(-8, 9, size=(m, n)).astype(np.float32)
+        x = rng.integers(-8, 9, size=(m, k)).astype(np.float32)
+        dw = oracle.oracle_gemm_dw(_bf16_bits(dy), _bf16_bits(x))
+        assert np.array_equal(dw, dy.T.astype(np.float64) @ x.astype(np.float64))
+    dyr = _bf16_bits(rng.normal(size=(50, 21)))
+    xr = _bf16_bits(rng.standard_t(3, size=(50, 30)))
+    dw = oracle.oracle_gemm_dw(dyr, xr)
+    assert np.allclose(dw, _from_bf16_bits(dyr).T @ _from_bf16_bits(xr), rtol=1e-12, atol=1e-12)
+    dw0 = oracle.oracle_gemm_dw(np.zeros((0, 4), np.uint16), np.zeros((0, 6), np.uint16))
+    assert dw0.shape == (4, 6) and not dw0.any()
+
+
+# --------------------------------------------------------------------------
 # 8-bit activations (per-token absmax) and the W1.58-A8 layer
 # --------------------------------------------------------------------------
 
@@ -618,6 +672,12 @@ MUTANTS = {
                               "acc += (int64_t)q[mm * ldq + kk] * trow[k - 1 - kk];"),
     "pack_a8_untransposed": ("const int64_t field = 16 * w + 4 * i + j;",
                              "const int64_t field = 16 * w + 4 * j + i;"),
+    "dw_drops_last_token": ("for (int64_t mm = 0; mm < j->m; ++mm) acc += g[mm] * xc[mm];",
+                            "for (int64_t mm = 0; mm + 1 < j->m; ++mm) acc += g[mm] * xc[mm];"),
+    "dw_wrong_gradient_column": ("dyd[nn * m + mm] = (double)bf16_bits_to_float(dy[mm * lddy + nn]);",
+                                 "dyd[nn * m + mm] = (double)bf16_bits_to_float(dy[mm * lddy + (n - 1 - nn)]);"),
+    "dw_wrong_input_column": ("const double* xc = j->xd + kk * j->m;",
+                              "const double* xc = j->xd + ((kk + 1) % j->k) * j->m;"),
 }
 
 PIN_TESTS = [
@@ -635,7 +695,8 @@ PIN_TESTS = [
     test_quantize_act_matches_exact_rational_rounding,
     test_quantize_act_power_of_two_invariance_and_sign,
     test_gemm_a8_integer_activations_equal_bf16_layer, test_gemm_a8_equals_numpy_integer_matmul,
-    test_pack_a8_worked_example_and_involution,
+    test_pack_a8_worked_example_and_involution, test_gemm_dw_worked_example,
+    test_gemm_dw_adjoint_of_the_layer_exact, test_gemm_dw_equals_numpy_matmul,
 ]
 
 

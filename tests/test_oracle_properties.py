@@ -13,7 +13,11 @@ oracle's code:
   * per-token int8 activations: codes lie in [-127, 127], a row whose
     maximum is at least the floor 1e-5 reaches +-127 there, rounding preserves order and sign, the
     codes are odd in x and permuting the row permutes them; the field
-    arrangement of the int8 layout applied twice gives back any bytes.
+    arrangement of the int8 layout applied twice gives back any bytes;
+  * the latent-weight gradient dW = dY^T . X is a sum over tokens, so
+    splitting the tokens into two batches gives the sum of the two batches'
+    gradients, and permuting the tokens changes nothing (exact with
+    small-integer operands).
 """
 from __future__ import annotations
 
@@ -128,3 +132,21 @@ def test_pack_a8_is_an_involution_on_any_bytes(n, words, seed):
     p = np.random.default_rng(seed).integers(0, 256, size=(n, 4 * words)).astype(np.uint8)
     p8 = oracle.oracle_pack_a8(p, 16 * words)
     assert np.array_equal(oracle.oracle_pack_a8(p8, 16 * words), p)
+
+
+@settings(**SETTINGS)
+@given(st.integers(min_value=1, max_value=40), st.integers(min_value=1, max_value=12),
+       st.integers(min_value=1, max_value=12), st.integers(min_value=0, max_value=2**31 - 1),
+       st.randoms(use_true_random=False))
+def test_gemm_dw_additive_over_token_batches(m, n, k, seed, rnd):
+    rng = np.random.default_rng(seed)
+    bits = lambda a: (a.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    dy = bits(rng.integers(-9, 10, size=(m, n)))
+    x = bits(rng.integers(-9, 10, size=(m, k)))
+    cut = rnd.randint(0, m)
+    whole = oracle.oracle_gemm_dw(dy, x)
+    parts = oracle.oracle_gemm_dw(dy[:cut], x[:cut]) + oracle.oracle_gemm_dw(dy[cut:], x[cut:])
+    assert np.array_equal(whole, parts)
+    perm = list(range(m))
+    rnd.shuffle(perm)
+    assert np.array_equal(oracle.oracle_gemm_dw(dy[perm], x[perm]), whole)
