@@ -1,34 +1,53 @@
 #!/usr/bin/env python3
 """Throughput of the 1.58-bit linear layer on one MI355X.
 
-One step is one pass of the whole path over one layer's synthetic inputs,
-already resident in HBM: tern_quantize_pack (fp32 weights -> codes, scales
-and packed bytes in one pass), tern_unpack, and tern_gemm (bf16 X times the
-packed ternary weights, fused scale epilogue); --separate-quantize runs
-tern_quantize and tern_pack as two calls instead.  The reported value is whole-step throughput
-in effective TFLOP/s, 2*M*N*K per step; the roofline object describes the
-dominant kernel (tern_gemm) measured with HIP events on the stream it is
-launched on; the CPU baseline is the oracle timed on this host on a bounded
-sample of the same step.
+One step is one pass of tern_gemm over every layer of the workload, inputs
+already resident in HBM (default workload flux_qkv: bf16 X [4608, 3072] times
+the packed ternary weights of a [9216, 3072] layer, fp32 per-channel scales,
+bf16 Y [4608, 9216] through the fused scale epilogue).  The reported value is
+tern_gemm's effective throughput, 2*M*N*K per step over the step time, in
+TFLOP/s.  The weights are converted once before the timed region
+(tern_quantize_pack: fp32 weights to codes, scales and packed bytes); the
+conversion entry points are timed on their own afterwards and reported in
+"kernels" with in_step false.  The roofline object describes tern_gemm,
+timed with HIP events on the stream it is launched on; the CPU baseline is the
+oracle timed on this host's cores on a bounded sample of the same step.
 
-After the timed steps, every layer shape of the five workloads is timed on its
-own ("rows"): tern_gemm per launch, and tern_gemm_ex with the bias and GELU
-of the layers that have them, as effective TFLOP/s, GB/s and the fraction of
-the bound that applies (MFMA or HBM); "dx_rows" time the input gradient
-(tern_gemm_dx, tern_pack_transposed) on the backward shapes; "a8_rows" time
-the 8-bit-activation layer (tern_quantize_act, tern_gemm_a8) on the forward
-shapes against the int8 matrix peak.  The two few-token layers
-cycle through a pool of distinct packed weights larger than every cache, so
-that each launch streams its weights from HBM.
+After the timed steps:
+  * "config3": the FLUX single-stream block set, 38 seeded (in-projection,
+    out-projection) pairs, 76 tern_gemm launches back to back, timed as a
+    whole sequence and per launch;
+  * "sweep": tern_gemm at M = 1, 8, 16, 32 tokens on the 16.5 MB packed
+    in-projection weight [21504, 3072], cycling a pool of distinct weights
+    larger than every cache, against the HBM peak;
+  * "rows": tern_gemm on every layer shape of the five workloads, and
+    tern_gemm_ex with the bias and GELU of the layers that have them;
+  * "dx_rows": the input gradient (tern_gemm_dx, tern_pack_transposed) on the
+    backward shapes; "a8_rows": the 8-bit-activation layer (tern_quantize_act,
+    tern_gemm_a8) on the forward shapes against the int8 matrix peak.
+Few-token rows cycle through a pool of distinct packed weights of at least
+--pool-mib MiB, so that each launch streams its weights from HBM.  Table rows
+are graph-replayed launches; each figure is the median over several replays.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload flux_qkv]
+
+Counter summaries: python bench.py --summarize-traffic FETCH_DIR WRITE_DIR
+BENCH_JSON [--workload W] reads two rocprofv3 --pmc runs of this script (one
+with FETCH_SIZE, one with WRITE_SIZE, both with --copy-calibration-mib) and
+the JSON line that the FETCH run printed, and writes
+profiles/tern_gemm_<W>_traffic.json: the HBM bytes per tern_gemm launch,
+scaled by what the counters read for the calibration copy, with the GEMM
+source digest recorded by the measured run itself.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -42,13 +61,14 @@ PEAK_I8_TOPS = 5000.0       # MI355X dense int8 matrix peak
 RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
 CSRC = os.path.join(ROOT, "ternary_weight_quantized_tern_amd", "csrc")
 GEMM_SRCS = [os.path.join(CSRC, f) for f in ("gemm.hip", "gemm_small.hip", "gemm_common.h")]
+W_STD = 0.02
 
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="flux_qkv")
     ap.add_argument("--layers", type=int, default=0,
                     help="use only the first L layers of a multi-layer workload (0 = all)")
@@ -57,17 +77,19 @@ def parse():
                     help="target CPU time of the oracle's layer-output sample")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a device copy of this size (for counter calibration)")
-    ap.add_argument("--gemm-only-reps", type=int, default=0,
-                    help="after the steps, launch tern_gemm alone this many times (profiling)")
-    ap.add_argument("--no-rows", action="store_true", help="skip the per-layer-shape tables")
-    ap.add_argument("--rows", choices=("all", "fwd", "dx", "a8"), default="all",
-                    help="which per-layer-shape tables to time: the forward layer, the input "
-                         "gradient, the 8-bit-activation layer, or all")
-    ap.add_argument("--separate-quantize", action="store_true",
-                    help="run quantize and pack as two calls in the step instead of the fused pass")
-    ap.add_argument("--row-reps", type=int, default=30, help="timed launches per row")
+    ap.add_argument("--no-rows", action="store_true",
+                    help="skip every table after the timed steps")
+    ap.add_argument("--rows", default="all",
+                    help="comma-separated tables to time after the steps: config3, sweep, fwd, "
+                         "dx, a8, or all")
+    ap.add_argument("--row-reps", type=int, default=30, help="launches per graph of a table row")
+    ap.add_argument("--replays", type=int, default=5, help="timed graph replays per table row")
     ap.add_argument("--pool-mib", type=int, default=1024,
                     help="packed-weight pool cycled by the few-token rows")
+    ap.add_argument("--summarize-traffic", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "BENCH_JSON"),
+                    help="write the traffic record from two counter runs (no GPU used)")
+    ap.add_argument("--traffic-out", default=None,
+                    help="where --summarize-traffic writes (default: profiles/)")
     return ap.parse_args()
 
 
@@ -84,10 +106,15 @@ def source_digest(paths=GEMM_SRCS):
     return h.hexdigest()
 
 
+def traffic_path(workload):
+    return os.path.join(ROOT, "profiles", f"tern_gemm_{workload}_traffic.json")
+
+
 def load_traffic(workload):
-    """HBM bytes per tern_gemm launch from committed counter summaries, if
-    they were taken on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", f"tern_gemm_{workload}_traffic.json")
+    """HBM bytes per tern_gemm launch from the committed counter record, if it
+    was measured on the current kernel sources (the record's digest is the one
+    the measured run printed)."""
+    path = traffic_path(workload)
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -97,13 +124,25 @@ def load_traffic(workload):
     return rec.get("hbm_bytes_per_launch")
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(layers, inputs, target_s):
-    """The oracle, as it stands, on this host: all weights of every layer go
-    through quantize, pack and unpack; the layer output is computed for a
-    leading sample of X rows and scaled to all M rows."""
+    """The oracle, as it stands, on all of this host's cores: the layer output
+    for a leading sample of X rows, scaled to all M rows (the step is the
+    layer, 2MNK per layer).  The weights are converted by the oracle first
+    (not timed into the value: the step does not convert weights either)."""
     import oracle
     import tern_inputs
-    cores = min(len(os.sched_getaffinity(0)), 16)
+    cores = len(os.sched_getaffinity(0))
     t_weights = 0.0
     t_gemm = 0.0
     rows_used = []
@@ -112,7 +151,6 @@ def cpu_baseline(layers, inputs, target_s):
         t0 = time.perf_counter()
         t_ref, s_ref = oracle.oracle_quantize(w.numpy())
         p_ref = oracle.oracle_pack(t_ref)
-        oracle.oracle_unpack(p_ref, layer.k)
         t_weights += time.perf_counter() - t0
         xb = tern_inputs.bf16_bits(x)
         pilot = min(8, layer.m)
@@ -128,16 +166,20 @@ def cpu_baseline(layers, inputs, target_s):
         t_gemm += dt * layer.m / rows
         rows_used.append(rows)
         flops += 2 * layer.m * layer.n * layer.k
-    t_step = t_weights + t_gemm
     return {
-        "value": flops / t_step / 1e12,
+        "value": flops / t_gemm / 1e12,
         "unit": "TFLOP/s",
         "cores": cores,
         "kind": "oracle",
-        "seconds_per_step_extrapolated": t_step,
-        "sample": (f"oracle quantize+pack+unpack on all weights ({t_weights:.2f} s), oracle layer "
-                   f"output on the first {rows_used} X rows of M={[l.m for l in layers]} "
-                   f"scaled to all rows; {cores} threads"),
+        "cpu_count": os.cpu_count(),
+        "affinity_cores": cores,
+        "cpu_model": cpu_model(),
+        "seconds_per_step_extrapolated": t_gemm,
+        "weight_conversion_seconds": t_weights,
+        "sample": (f"oracle layer output (fp64, scalar C, {cores} threads = all cores in this "
+                   f"process's affinity) on the first {rows_used} X rows of "
+                   f"M={[l.m for l in layers]}, scaled to all rows; the oracle's weight "
+                   f"conversion ({t_weights:.2f} s) is not in the value"),
     }
 
 
@@ -152,15 +194,67 @@ def roofline_of(flops, byts, seconds):
             "pct_roofline": 100 * t_ideal / seconds}
 
 
-def time_rows(tern, tern_inputs, torch, dev, reps, pool_mib):
+def time_graph(torch, fn, launches, replays):
+    """Seconds per call of fn() with `launches` calls captured in one HIP graph
+    and replayed back to back (after one eager warm-up call on a side stream
+    and one untimed replay): the median and the minimum over `replays` timed
+    replays."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(launches):
+            fn()
+    graph.replay()
+    torch.cuda.synchronize()
+    per = []
+    for _ in range(max(1, replays)):
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        graph.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        per.append(g0.elapsed_time(g1) * 1e-3 / launches)
+    del graph
+    return statistics.median(per), min(per)
+
+
+class Cycler:
+    """Calls fn(*operands[i]) for i = 0, 1, 2, ... cyclically."""
+
+    def __init__(self, fn, operands):
+        self.fn, self.operands, self.i = fn, operands, 0
+
+    def __call__(self):
+        self.fn(*self.operands[self.i % len(self.operands)])
+        self.i += 1
+
+
+def weight_pool(tern, torch, dev, n, k, seed, pool_mib):
+    """Distinct packed weights [n, k] (seeded N(0, 0.02^2) fp32 weights drawn on
+    the GPU and converted by tern_quantize_pack) totalling at least pool_mib
+    MiB, as (p, s) pairs."""
+    ldp = tern.packed_row_bytes(k)
+    per = n * ldp + 4 * n
+    count = max(1, -(-(pool_mib << 20) // per))
+    gen = torch.Generator(device=dev).manual_seed(int(seed))
+    ps = torch.zeros((count, n, ldp), dtype=torch.uint8, device=dev)
+    ss = torch.empty((count, n), dtype=torch.float32, device=dev)
+    for i in range(count):
+        wi = torch.randn((n, k), generator=gen, device=dev) * W_STD
+        tern.tern_quantize_pack(wi, None, ps[i], ss[i])
+        del wi
+    return [(ps[i], ss[i]) for i in range(count)], count * per
+
+
+def time_rows(tern, tern_inputs, torch, dev, reps, replays, pool_mib):
     """The layer on every layer shape of the workloads (layer 0 inputs of each
     shape): tern_gemm, and tern_gemm_ex where the layer's consumer applies a
     bias and the tanh-form GELU (the MLP up-projections; the single-stream
-    in-projection, whose GELU covers only its MLP columns from 9216 on).
-    Few-token shapes cycle through a pool of distinct packed weights of at
-    least pool_mib MiB (seeded normal weights quantized on the GPU), one
-    launch per pool entry."""
-    import statistics
+    in-projection, whose GELU covers only its MLP columns from 9216 on)."""
     W = tern_inputs.WORKLOADS
     shapes = [("single", W["single"][0], None),
               ("flux_qkv", W["flux_qkv"][0], None),
@@ -179,7 +273,6 @@ def time_rows(tern, tern_inputs, torch, dev, reps, pool_mib):
     for name, layer, epi in shapes:
         x, w = tern_inputs.draw_layer(layer)
         xd = x.to(dev)
-        ldp = tern.packed_row_bytes(layer.k)
         y = torch.empty((layer.m, layer.n), dtype=torch.bfloat16, device=dev)
         if epi is None:
             def launch(p_i, s_i, xd=xd, y=y, k=layer.k):
@@ -194,75 +287,27 @@ def time_rows(tern, tern_inputs, torch, dev, reps, pool_mib):
                 tern.tern_gemm_ex(xd, p_i, s_i, y, bias, tern.TERN_ACT_GELU_TANH, act_from, k)
         pool = layer.m <= 64 and layer.n * layer.k >= (1 << 20)
         if pool:
-            per = layer.n * ldp + 4 * layer.n
-            count = max(1, -(-(pool_mib << 20) // per))
-            gen = torch.Generator(device=dev).manual_seed(layer.seed)
-            ps = torch.empty((count, layer.n, ldp), dtype=torch.uint8, device=dev)
-            ss = torch.empty((count, layer.n), dtype=torch.float32, device=dev)
-            t = torch.empty((layer.n, layer.k), dtype=torch.int8, device=dev)
-            for i in range(count):
-                wi = torch.randn((layer.n, layer.k), generator=gen, device=dev) * tern_inputs.W_STD
-                tern.tern_quantize(wi, t, ss[i])
-                tern.tern_pack(t, ps[i], layer.k)
-            operands = [(ps[i], ss[i]) for i in range(count)]
-            launches = count
+            operands, pool_bytes = weight_pool(tern, torch, dev, layer.n, layer.k, layer.seed,
+                                               pool_mib)
+            launches = len(operands)
         else:
-            t, s = tern.quantize(w.to(dev))
-            operands = [(tern.pack(t), s)]
+            operands = [tern.quantize_pack(w.to(dev))]
             launches = reps
-        for i in range(min(5, launches)):
-            p_i, s_i = operands[i % len(operands)]
-            launch(p_i, s_i)
         torch.cuda.synchronize()
-        # Per-launch durations with events around each launch (they include
-        # the host's submission gaps), and the same launches captured in a
-        # HIP graph and replayed back to back (no host in the loop).
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(launches)]
-        for i in range(launches):
-            p_i, s_i = operands[i % len(operands)]
-            ev[i][0].record()
-            launch(p_i, s_i)
-            ev[i][1].record()
-        torch.cuda.synchronize()
-        d = [a.elapsed_time(b) * 1e-3 for a, b in ev]
-        graph = torch.cuda.CUDAGraph()
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            launch(*operands[0])
-        torch.cuda.current_stream().wait_stream(side)
-        with torch.cuda.graph(graph):
-            for i in range(launches):
-                p_i, s_i = operands[i % len(operands)]
-                launch(p_i, s_i)
-        graph.replay()
-        torch.cuda.synchronize()
-        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        g0.record()
-        graph.replay()
-        g1.record()
-        torch.cuda.synchronize()
-        per_launch = g0.elapsed_time(g1) * 1e-3 / launches
-        del graph
-        med = statistics.median(d)
+        t, t_min = time_graph(torch, Cycler(launch, operands), launches, replays)
         flops = 2 * layer.m * layer.n * layer.k
         byts = gemm_alg_bytes(layer.m, layer.k, layer.n)
         if epi is not None and epi[0]:
             byts += 4 * layer.n  # the fp32 bias
-        # The table's rate is the back-to-back (graph) time per launch unless
-        # the event-bracketed median is lower.
-        t = min(per_launch, med)
         row = {"layer": name, "m": layer.m, "k": layer.k, "n": layer.n,
-               "launches": launches, "us_per_launch": t * 1e6,
-               "graph_us_per_launch": per_launch * 1e6, "event_median_us": med * 1e6,
-               "event_min_us": min(d) * 1e6, "alg_flops": flops, "alg_bytes": byts,
+               "launches": launches, "us_per_launch": t * 1e6, "min_us_per_launch": t_min * 1e6,
+               "alg_flops": flops, "alg_bytes": byts,
                "entry": "tern_gemm" if epi is None else "tern_gemm_ex"}
         if epi is not None:
             row["epilogue"] = {"bias": bool(epi[0]), "act": "gelu_tanh", "act_from": epi[1]}
         row.update(roofline_of(flops, byts, t))
         if pool:
-            row["weight_pool_mib"] = round(launches * per / 2**20, 1)
+            row["weight_pool_mib"] = round(pool_bytes / 2**20, 1)
         rows.append(row)
         print(f"# row {name}: {t * 1e6:.1f} us per launch, {row['tflops']:.0f} TFLOP/s, "
               f"{row['gbs']:.0f} GB/s, {row['pct_roofline']:.1f}% of roofline",
@@ -272,30 +317,104 @@ def time_rows(tern, tern_inputs, torch, dev, reps, pool_mib):
     return rows
 
 
-def time_graph(torch, fn, launches):
-    """Seconds per call of fn() with `launches` calls captured in one HIP graph
-    and replayed back to back (after one eager warm-up call on a side stream)."""
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        fn()
-    torch.cuda.current_stream().wait_stream(side)
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for _ in range(launches):
-            fn()
-    graph.replay()
-    torch.cuda.synchronize()
-    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    g0.record()
-    graph.replay()
-    g1.record()
-    torch.cuda.synchronize()
-    del graph
-    return g0.elapsed_time(g1) * 1e-3 / launches
+def time_sweep(tern, torch, dev, replays, pool_mib, ms=(1, 8, 16, 32)):
+    """tern_gemm on the FLUX single-stream in-projection weight (N = 21504,
+    K = 3072: 16.5 MB packed) at a few tokens, cycling a pool of at least
+    pool_mib MiB of distinct weights: the weight-streaming (HBM-bound) regime."""
+    n, k = 21504, 3072
+    operands, pool_bytes = weight_pool(tern, torch, dev, n, k, 5000, pool_mib)
+    rows = []
+    for m in ms:
+        gen = torch.Generator(device=dev).manual_seed(5100 + m)
+        xd = torch.randn((m, k), generator=gen, device=dev).to(torch.bfloat16)
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+
+        def launch(p_i, s_i, xd=xd, y=y):
+            tern.tern_gemm(xd, p_i, s_i, y, k)
+
+        t, t_min = time_graph(torch, Cycler(launch, operands), len(operands), replays)
+        flops = 2 * m * n * k
+        byts = gemm_alg_bytes(m, k, n)
+        row = {"layer": f"in_proj_weight.m{m}", "m": m, "k": k, "n": n,
+               "launches": len(operands), "us_per_launch": t * 1e6,
+               "min_us_per_launch": t_min * 1e6, "alg_flops": flops, "alg_bytes": byts,
+               "weight_pool_mib": round(pool_bytes / 2**20, 1), "entry": "tern_gemm"}
+        row.update(roofline_of(flops, byts, t))
+        rows.append(row)
+        print(f"# sweep m={m}: {t * 1e6:.2f} us per launch, {row['gbs']:.0f} GB/s "
+              f"({row['pct_hbm']:.1f}% of HBM peak)", file=sys.stderr, flush=True)
+    del operands
+    torch.cuda.empty_cache()
+    return rows
 
 
-def time_dx_rows(tern, tern_inputs, torch, dev, reps):
+def time_config3(tern, tern_inputs, torch, dev, replays):
+    """The 38 single-stream blocks of a FLUX-style transformer, each an
+    in-projection (4608 x 3072 -> 21504) and an out-projection (4608 x 15360 ->
+    3072) with fresh seeded inputs (seeds 3000 + 2l and 3000 + 2l + 1; X ~ N(0,
+    1) in bf16 and W ~ N(0, 0.02^2) drawn on the GPU, W converted by
+    tern_quantize_pack): the 76 tern_gemm launches back to back on one stream,
+    timed as a whole (median of `replays` sequences between two events) and
+    per launch (events around each launch of one more sequence)."""
+    layers = list(tern_inputs.iter_layers("flux_single_stream"))
+    bufs = []
+    for layer in layers:
+        gen = torch.Generator(device=dev).manual_seed(layer.seed)
+        x = torch.randn((layer.m, layer.k), generator=gen, device=dev).to(torch.bfloat16)
+        w = torch.randn((layer.n, layer.k), generator=gen, device=dev) * W_STD
+        p, s = tern.quantize_pack(w)
+        del w
+        y = torch.empty((layer.m, layer.n), dtype=torch.bfloat16, device=dev)
+        bufs.append((x, p, s, y, layer.k))
+    torch.cuda.synchronize()
+
+    def sequence():
+        for x, p, s, y, k in bufs:
+            tern.tern_gemm(x, p, s, y, k)
+
+    sequence()
+    torch.cuda.synchronize()
+    per_seq = []
+    for _ in range(max(1, replays)):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        sequence()
+        e1.record()
+        torch.cuda.synchronize()
+        per_seq.append(e0.elapsed_time(e1) * 1e-3)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(bufs) + 1)]
+    ev[0].record()
+    for i, (x, p, s, y, k) in enumerate(bufs):
+        tern.tern_gemm(x, p, s, y, k)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    launch_s = [ev[i].elapsed_time(ev[i + 1]) * 1e-3 for i in range(len(bufs))]
+    t = statistics.median(per_seq)
+    flops = sum(2 * l.m * l.n * l.k for l in layers)
+    in_s = launch_s[0::2]
+    out_s = launch_s[1::2]
+    lin, lout = layers[0], layers[1]
+    f_in, f_out = 2 * lin.m * lin.n * lin.k, 2 * lout.m * lout.n * lout.k
+    out = {"layers": len(layers), "launches": len(bufs), "sequence_ms": t * 1e3,
+           "sequence_min_ms": min(per_seq) * 1e3, "tflops": flops / t / 1e12,
+           "pct_mfma": 100 * flops / t / 1e12 / PEAK_BF16_TFLOPS,
+           "in_proj": {"m": lin.m, "k": lin.k, "n": lin.n,
+                       "avg_us": 1e6 * sum(in_s) / len(in_s), "min_us": 1e6 * min(in_s),
+                       "max_us": 1e6 * max(in_s),
+                       "tflops": f_in / (sum(in_s) / len(in_s)) / 1e12},
+           "out_proj": {"m": lout.m, "k": lout.k, "n": lout.n,
+                        "avg_us": 1e6 * sum(out_s) / len(out_s), "min_us": 1e6 * min(out_s),
+                        "max_us": 1e6 * max(out_s),
+                        "tflops": f_out / (sum(out_s) / len(out_s)) / 1e12},
+           "alg_flops": flops}
+    print(f"# config3: 76 launches in {t * 1e3:.2f} ms, {out['tflops']:.0f} TFLOP/s "
+          f"({out['pct_mfma']:.1f}% of the bf16 peak)", file=sys.stderr, flush=True)
+    del bufs
+    torch.cuda.empty_cache()
+    return out
+
+
+def time_dx_rows(tern, tern_inputs, torch, dev, reps, replays):
     """The input gradient of the layer, dX = bf16((dY * s) . T), on the backward
     shapes of the DiT and FLUX layers (dY [m, n] of the forward's output, dX
     [m, k]): tern_gemm_dx (the scaling pass and the ternary GEMM over n), and
@@ -315,8 +434,8 @@ def time_dx_rows(tern, tern_inputs, torch, dev, reps):
         u = torch.empty_like(dy)
         dx = torch.empty((m, k), dtype=torch.bfloat16, device=dev)
         tern.tern_pack_transposed(p, pt, n, k)
-        t_pt = time_graph(torch, lambda: tern.tern_pack_transposed(p, pt, n, k), reps)
-        t_dx = time_graph(torch, lambda: tern.tern_gemm_dx(dy, pt, s, u, dx, k), reps)
+        t_pt, _ = time_graph(torch, lambda: tern.tern_pack_transposed(p, pt, n, k), reps, replays)
+        t_dx, _ = time_graph(torch, lambda: tern.tern_gemm_dx(dy, pt, s, u, dx, k), reps, replays)
         flops = 2 * m * n * k
         # algorithmic bytes: dY, the codes, the scales and dX (the bf16 workspace
         # u, written once and read once, is the implementation's own traffic)
@@ -336,7 +455,7 @@ def time_dx_rows(tern, tern_inputs, torch, dev, reps):
     return rows
 
 
-def time_a8_rows(tern, tern_inputs, torch, dev, reps, pool_mib):
+def time_a8_rows(tern, tern_inputs, torch, dev, reps, replays, pool_mib):
     """The 8-bit-activation layer on the forward shapes: tern_quantize_act
     (bf16 X -> int8 codes and per-token scales) and tern_gemm_a8, each
     graph-replayed, and the two together as the layer.  Rates against the
@@ -370,23 +489,22 @@ def time_a8_rows(tern, tern_inputs, torch, dev, reps, pool_mib):
         if pool:
             count = max(1, -(-(pool_mib << 20) // (p8.numel() + 4 * n)))
             p8s = [p8.clone() for _ in range(count)]
-        it = [0]
 
-        def gemm():
-            tern.tern_gemm_a8(q, xs, p8s[it[0] % len(p8s)], s, y, None, act, af, k)
-            it[0] += 1
+        def gemm(p8_i):
+            tern.tern_gemm_a8(q, xs, p8_i, s, y, None, act, af, k)
 
         def quant():
             tern.tern_quantize_act(xd, q, xs)
 
-        def layer_fn():
+        def layer_fn(p8_i):
             quant()
-            gemm()
+            gemm(p8_i)
 
         launches = len(p8s) if pool else reps
-        t_g = time_graph(torch, gemm, launches)
-        t_q = time_graph(torch, quant, reps)
-        t_l = time_graph(torch, layer_fn, launches)
+        operands = [(t,) for t in p8s]
+        t_g, _ = time_graph(torch, Cycler(gemm, operands), launches, replays)
+        t_q, _ = time_graph(torch, quant, reps, replays)
+        t_l, _ = time_graph(torch, Cycler(layer_fn, operands), launches, replays)
         flops = 2 * m * n * k
         byts = m * k + n * k // 4 + 4 * n + 4 * m + 2 * m * n
         q_bytes = 2 * m * k + m * k + 4 * m
@@ -406,13 +524,116 @@ def time_a8_rows(tern, tern_inputs, torch, dev, reps, pool_mib):
               f"({row['pct_i8_peak']:.1f}% of int8 peak); quantize_act {t_q * 1e6:.1f} us "
               f"{row['quantize_act_gbs']:.0f} GB/s; layer {t_l * 1e6:.1f} us",
               file=sys.stderr, flush=True)
-        del p, p8, p8s, q, xs, y, xd
+        del p, p8, p8s, q, xs, y, xd, operands
         torch.cuda.empty_cache()
     return rows
 
 
+def time_conversion(tern, torch, layer, b, reps=10):
+    """The weight-conversion entry points on the first layer's buffers, each
+    `reps` launches back to back between two events, queued behind one layer
+    so that the host's launch latency stays off the GPU's clock.  Not part of
+    the step."""
+    out = {}
+    w16 = b["w"].to(torch.bfloat16)
+    n, k = layer.n, layer.k
+    kb = (k + 3) // 4
+    calls = [
+        ("tern_quantize_pack", lambda: tern.tern_quantize_pack(b["w"], b["t"], b["p"], b["s"]),
+         4 * n * k + n * k + n * kb + 4 * n),
+        ("tern_quantize_pack.bf16_w", lambda: tern.tern_quantize_pack(w16, b["t"], b["p"], b["s"]),
+         2 * n * k + n * k + n * kb + 4 * n),
+        ("tern_quantize", lambda: tern.tern_quantize(b["w"], b["t"], b["s"]),
+         4 * n * k + n * k + 4 * n),
+        ("tern_pack", lambda: tern.tern_pack(b["t"], b["p"], k), n * k + n * kb),
+        ("tern_unpack", lambda: tern.tern_unpack(b["p"], b["tu"], k), n * kb + n * k),
+    ]
+    for name, fn, byts in calls:
+        tern.tern_gemm(b["x"], b["p"], b["s"], b["y"], k)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[name] = {"avg_ms": ms, "alg_bytes": byts, "gbs": byts / (ms * 1e-3) / 1e9,
+                     "in_step": False}
+    del w16
+    return out
+
+
+def summarize_traffic(fetch_dir, write_dir, bench_json, workload, path=None):
+    """Traffic record from two rocprofv3 --pmc runs of bench.py (FETCH_SIZE,
+    then WRITE_SIZE, each ending with a --copy-calibration-mib copy)."""
+
+    def per_kernel(d, counter):
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        by_dispatch = {}
+        for path in files:
+            with open(path, newline="") as f:
+                for r in csv.DictReader(f):
+                    if r.get("Counter_Name") != counter:
+                        continue
+                    key = (path, r["Dispatch_Id"])
+                    name = r["Kernel_Name"]
+                    v = float(r["Counter_Value"])
+                    if key in by_dispatch:
+                        by_dispatch[key] = (name, by_dispatch[key][1] + v)
+                    else:
+                        by_dispatch[key] = (name, v)
+        out = {}
+        for name, v in by_dispatch.values():
+            out.setdefault(name, []).append(v)
+        return out
+
+    with open(bench_json) as f:
+        rec = [json.loads(line) for line in f if line.startswith("{")][-1]
+    calib_bytes = rec["config"]["copy_calibration_bytes"]
+    digest = rec["config"]["gemm_source_sha256"]
+    fetch = per_kernel(fetch_dir, "FETCH_SIZE")
+    write = per_kernel(write_dir, "WRITE_SIZE")
+
+    def copy_kernel(d):
+        cands = [(max(v), k) for k, v in d.items() if "copy" in k.lower()]
+        return max(cands)[1]
+
+    fk, wk = copy_kernel(fetch), copy_kernel(write)
+    f_scale = calib_bytes / (max(fetch[fk]) * 1024.0)
+    w_scale = calib_bytes / (max(write[wk]) * 1024.0)
+    gemm = [k for k in fetch if "gemm_ternary" in k]
+    if not gemm:
+        raise SystemExit("no tern_gemm kernel in the counter runs")
+    gk = max(gemm, key=lambda k: len(fetch[k]))
+    f_kib = statistics.mean(fetch[gk])
+    w_kib = statistics.mean(write[gk]) if gk in write else 0.0
+    read_b = f_kib * 1024.0 * f_scale
+    written_b = w_kib * 1024.0 * w_scale
+    layer = rec["config"]
+    alg = gemm_alg_bytes(layer["m"], layer["k"], layer["n"])
+    out = {"workload": workload, "kernel": gk, "dispatches": len(fetch[gk]),
+           "fetch_size_kib_per_dispatch": f_kib, "write_size_kib_per_dispatch": w_kib,
+           "calibration": {"copy_bytes": calib_bytes, "fetch_kernel": fk, "write_kernel": wk,
+                           "fetch_scale": f_scale, "write_scale": w_scale},
+           "hbm_read_bytes_per_launch": read_b, "hbm_write_bytes_per_launch": written_b,
+           "hbm_bytes_per_launch": read_b + written_b, "alg_bytes_per_launch": alg,
+           "gemm_source_sha256": digest,
+           "measured_run": {"fetch_dir": fetch_dir, "write_dir": write_dir,
+                            "bench_json": bench_json}}
+    path = path or traffic_path(workload)
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
+
+
 def main():
     args = parse()
+    if args.summarize_traffic:
+        summarize_traffic(*args.summarize_traffic, args.workload, args.traffic_out)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
               "(the ternary linear layer is measured on one MI355X).", file=sys.stderr)
@@ -427,6 +648,10 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    tables = {"config3", "sweep", "fwd", "dx", "a8"} if args.rows == "all" else \
+        set(args.rows.split(","))
+    if args.no_rows:
+        tables = set()
 
     layers = list(tern_inputs.iter_layers(args.workload))
     if args.layers:
@@ -438,90 +663,57 @@ def main():
     bufs = []
     for layer, (x, w) in zip(layers, host_inputs):
         ldp = tern.packed_row_bytes(layer.k)
-        bufs.append(dict(
+        b = dict(
             x=x.to(dev), w=w.to(dev),
             t=torch.empty((layer.n, layer.k), dtype=torch.int8, device=dev),
             s=torch.empty((layer.n,), dtype=torch.float32, device=dev),
             p=torch.zeros((layer.n, ldp), dtype=torch.uint8, device=dev),
             tu=torch.empty((layer.n, layer.k), dtype=torch.int8, device=dev),
             y=torch.empty((layer.m, layer.n), dtype=torch.bfloat16, device=dev),
-        ))
+        )
+        # weight conversion, once, before the timed region
+        tern.tern_quantize_pack(b["w"], b["t"], b["p"], b["s"])
+        bufs.append(b)
     torch.cuda.synchronize()
-
-    # A step runs every row of the path on every layer: quantize and pack
-    # (one fused pass, writing the codes, the scales and the packed bytes),
-    # unpack, and the layer.  --separate-quantize runs quantize and pack as two
-    # calls instead.
-    if args.separate_quantize:
-        names = ("tern_quantize", "tern_pack", "tern_unpack", "tern_gemm")
-    else:
-        names = ("tern_quantize_pack", "tern_unpack", "tern_gemm")
 
     def step(events=None):
         for li, (layer, b) in enumerate(zip(layers, bufs)):
-            ev = events[li] if events is not None else None
-            if ev:
-                ev[0].record()
-            j = 1
-            if args.separate_quantize:
-                tern.tern_quantize(b["w"], b["t"], b["s"])
-                if ev:
-                    ev[j].record()
-                j += 1
-                tern.tern_pack(b["t"], b["p"], layer.k)
-            else:
-                tern.tern_quantize_pack(b["w"], b["t"], b["p"], b["s"])
-            if ev:
-                ev[j].record()
-            j += 1
-            tern.tern_unpack(b["p"], b["tu"], layer.k)
-            if ev:
-                ev[j].record()
-            j += 1
+            if events is not None:
+                events[li][0].record()
             tern.tern_gemm(b["x"], b["p"], b["s"], b["y"], layer.k)
-            if ev:
-                ev[j].record()
+            if events is not None:
+                events[li][1].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    per_step_events = [[[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
-                        for _ in layers] for _ in range(args.steps)]
+    # The timed region: K steps between two events, each launch also
+    # bracketed by events on the launch stream (torch's current stream, the
+    # one the binding passes to the library).
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in layers]
+          for _ in range(args.steps)]
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
     for i in range(args.steps):
-        step(per_step_events[i])
+        step(ev[i])
     end.record()
     torch.cuda.synchronize()
-    ms_total = start.elapsed_time(end)
-    ms_per_step = ms_total / args.steps
-
-    kern_ms = {nm: 0.0 for nm in names}
-    gemm_launch_ms = []
-    for i in range(args.steps):
-        for li in range(len(layers)):
-            ev = per_step_events[i][li]
-            for j, nm in enumerate(names):
-                d = ev[j].elapsed_time(ev[j + 1])
-                kern_ms[nm] += d
-                if nm == "tern_gemm":
-                    gemm_launch_ms.append(d)
-    launches = args.steps * len(layers)
-    for nm in names:
-        kern_ms[nm] /= launches
+    ms_per_step = start.elapsed_time(end) / args.steps
+    launch_ms = [ev[i][li][0].elapsed_time(ev[i][li][1]) for i in range(args.steps)
+                 for li in range(len(layers))]
+    gemm_ms = sum(launch_ms) / len(launch_ms)
 
     flops_step = sum(2 * l.m * l.n * l.k for l in layers)
     value = flops_step / (ms_per_step * 1e-3) / 1e12
 
-    # Dominant kernel: tern_gemm.  Algorithmic work per launch, averaged over layers.
+    # Dominant (and only) kernel of the step: tern_gemm.  Algorithmic work per
+    # launch, averaged over the workload's layers.
     gemm_flops = flops_step / len(layers)
     gemm_bytes = sum(gemm_alg_bytes(l.m, l.k, l.n) for l in layers) / len(layers)
-    gemm_ms = kern_ms["tern_gemm"]
-    ai = gemm_flops / gemm_bytes
-    if ai >= RIDGE:
+    if gemm_flops / gemm_bytes >= RIDGE:
         achieved = gemm_flops / (gemm_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS}
@@ -532,95 +724,49 @@ def main():
     roof["traffic"] = load_traffic(args.workload)
     roof["kernel"] = "tern_gemm"
     roof["avg_launch_ms"] = gemm_ms
+    roof["median_launch_ms"] = statistics.median(launch_ms)
     roof["alg_flops_per_launch"] = gemm_flops
     roof["alg_bytes_per_launch"] = gemm_bytes
     roof["gbs"] = gemm_bytes / (gemm_ms * 1e-3) / 1e9
 
-    # The separate quantize and pack entry points, timed after the step loop
-    # on the same buffers (not part of the step when the fused pass is used):
-    # ten back-to-back launches of each between two events, queued behind one
-    # layer so that the host's launch latency stays off the GPU's clock.
-    if not args.separate_quantize:
-        reps = 10
-        b0, l0 = bufs[0], layers[0]
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-        tern.tern_gemm(b0["x"], b0["p"], b0["s"], b0["y"], l0.k)
-        e[0].record()
-        for _ in range(reps):
-            tern.tern_quantize(b0["w"], b0["t"], b0["s"])
-        e[1].record()
-        for _ in range(reps):
-            tern.tern_pack(b0["t"], b0["p"], l0.k)
-        e[2].record()
-        torch.cuda.synchronize()
-        kern_ms["tern_quantize"] = e[0].elapsed_time(e[1]) / reps
-        kern_ms["tern_pack"] = e[1].elapsed_time(e[2]) / reps
-    # The fused conversion from bf16 weights (the 16-bit checkpoints the pages
-    # start from), on the first layer's weights rounded to bf16, same timing.
-    reps = 10
-    b0, l0 = bufs[0], layers[0]
-    w16 = b0["w"].to(torch.bfloat16)
-    e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    tern.tern_gemm(b0["x"], b0["p"], b0["s"], b0["y"], l0.k)
-    e[0].record()
-    for _ in range(reps):
-        tern.tern_quantize_pack(w16, b0["t"], b0["p"], b0["s"])
-    e[1].record()
-    torch.cuda.synchronize()
-    kern_ms["tern_quantize_pack.bf16_w"] = e[0].elapsed_time(e[1]) / reps
-    del w16
+    kernels = {"tern_gemm": {"avg_ms": gemm_ms, "in_step": True, "alg_bytes": gemm_bytes,
+                             "gbs": roof["gbs"],
+                             "tflops": gemm_flops / (gemm_ms * 1e-3) / 1e12}}
+    kernels.update(time_conversion(tern, torch, layers[0], bufs[0]))
 
-    kernels = {}
-    for nm in kern_ms:
-        d = {"avg_ms": kern_ms[nm]}
-        if nm in ("tern_quantize", "tern_pack"):
-            d["in_step"] = bool(args.separate_quantize)
-        if nm == "tern_quantize_pack.bf16_w":
-            d["in_step"] = False
-            byts = l0.n * l0.k * 2 + l0.n * l0.k + l0.n * ((l0.k + 3) // 4) + 4 * l0.n
-        elif nm == "tern_quantize_pack":
-            byts = sum(l.n * l.k * 4 + l.n * l.k + l.n * ((l.k + 3) // 4) + 4 * l.n
-                       for l in layers) / len(layers)
-        elif nm == "tern_quantize":
-            ls = layers if args.separate_quantize else layers[:1]
-            byts = sum(l.n * l.k * 4 + l.n * l.k + 4 * l.n for l in ls) / len(ls)
-        elif nm == "tern_pack":
-            ls = layers if args.separate_quantize else layers[:1]
-            byts = sum(l.n * l.k + l.n * ((l.k + 3) // 4) for l in ls) / len(ls)
-        elif nm == "tern_unpack":
-            byts = sum(l.n * ((l.k + 3) // 4) + l.n * l.k for l in layers) / len(layers)
-        else:
-            byts = gemm_bytes
-            d["tflops"] = gemm_flops / (kern_ms[nm] * 1e-3) / 1e12
-        d["alg_bytes"] = byts
-        d["gbs"] = byts / (kern_ms[nm] * 1e-3) / 1e9
-        kernels[nm] = d
-
-    if args.gemm_only_reps:
-        b, layer = bufs[0], layers[0]
-        for _ in range(args.gemm_only_reps):
-            tern.tern_gemm(b["x"], b["p"], b["s"], b["y"], layer.k)
-        torch.cuda.synchronize()
+    calib_bytes = 0
     if args.copy_calibration_mib:
-        nbytes = args.copy_calibration_mib << 20
-        src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        calib_bytes = args.copy_calibration_mib << 20
+        src = torch.empty(calib_bytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
         dst.copy_(src)
         torch.cuda.synchronize()
-        print(f"# copy calibration: {nbytes} bytes read and written", file=sys.stderr)
+        del src, dst
+        print(f"# copy calibration: {calib_bytes} bytes read and written", file=sys.stderr)
+    del bufs
+    torch.cuda.empty_cache()
 
-    rows = dx_rows = a8_rows = None
-    if not args.no_rows and args.rows in ("all", "fwd"):
+    out_tables = {}
+    if "config3" in tables:
+        print("# timing the 38 single-stream blocks back to back", file=sys.stderr, flush=True)
+        out_tables["config3"] = time_config3(tern, tern_inputs, torch, dev, args.replays)
+    if "sweep" in tables:
+        print("# timing the few-token sweep on the 16.5 MB weight", file=sys.stderr, flush=True)
+        out_tables["sweep"] = time_sweep(tern, torch, dev, args.replays, args.pool_mib)
+    if "fwd" in tables:
         print("# timing tern_gemm on every layer shape", file=sys.stderr, flush=True)
-        rows = time_rows(tern, tern_inputs, torch, dev, args.row_reps, args.pool_mib)
-    if not args.no_rows and args.rows in ("all", "dx"):
+        out_tables["rows"] = time_rows(tern, tern_inputs, torch, dev, args.row_reps,
+                                       args.replays, args.pool_mib)
+    if "dx" in tables:
         print("# timing the input gradient on the backward shapes", file=sys.stderr, flush=True)
-        dx_rows = time_dx_rows(tern, tern_inputs, torch, dev, args.row_reps)
-    if not args.no_rows and args.rows in ("all", "a8"):
+        out_tables["dx_rows"] = time_dx_rows(tern, tern_inputs, torch, dev, args.row_reps,
+                                             args.replays)
+    if "a8" in tables:
         print("# timing the 8-bit-activation layer on the forward shapes", file=sys.stderr,
               flush=True)
-        a8_rows = time_a8_rows(tern, tern_inputs, torch, dev, args.row_reps, args.pool_mib)
+        out_tables["a8_rows"] = time_a8_rows(tern, tern_inputs, torch, dev, args.row_reps,
+                                             args.replays, args.pool_mib)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -629,8 +775,10 @@ def main():
 
     shape = layers[0]
     config = {"workload": args.workload, "layers": len(layers), "m": shape.m, "k": shape.k,
-              "n": shape.n, "step": "+".join(names),
-              "x": f"bf16 {shape.x_dist}", "w": "fp32 N(0, 0.02^2)", "seed": shape.seed}
+              "n": shape.n, "step": "tern_gemm on every layer of the workload",
+              "x": f"bf16 {shape.x_dist}", "w": "fp32 N(0, 0.02^2), converted before timing",
+              "seed": shape.seed, "gemm_source_sha256": source_digest(),
+              "copy_calibration_bytes": calib_bytes}
     out = {
         "metric": METRIC,
         "value": value,
@@ -648,12 +796,10 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels": kernels,
-        "rows": rows,
-        "dx_rows": dx_rows,
-        "a8_rows": a8_rows,
         "peaks": {"bf16_mfma_tflops": PEAK_BF16_TFLOPS, "hbm_gbs": PEAK_HBM_GBS,
                   "i8_mfma_tops": PEAK_I8_TOPS},
     }
+    out.update(out_tables)
     print(json.dumps(out), flush=True)
 
 
