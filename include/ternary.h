@@ -14,7 +14,9 @@
  *
  * Conventions shared by every call:
  *  - All data pointers are DEVICE pointers owned by the caller.  The library
- *    allocates, frees and keeps no device memory and holds no global state.
+ *    allocates and frees no device memory.  It keeps none either, with one
+ *    exception: the fixed array of tern_gemm_dx_static (below), which each
+ *    GPU that runs the library holds until the process ends.
  *  - Matrices are row-major.  Leading dimensions (ld*) count elements, except
  *    ldp, which counts bytes.
  *  - Every call is asynchronous on `stream` (a hipStream_t passed as void*;
@@ -247,6 +249,39 @@ tern_status tern_pack_transposed(const uint8_t* p, int64_t n, int64_t k, int64_t
 tern_status tern_gemm_dx(const void* dy_bf16, int64_t m, int64_t n, int64_t lddy,
                          const uint8_t* pt, int64_t k, int64_t ldpt, const float* s,
                          void* u_bf16, int64_t ldu, void* dx_bf16, int64_t lddx, void* stream);
+
+/* Largest m * n that tern_gemm_dx_static accepts: its array holds this many
+ * bf16 values (128 MiB) on each GPU. */
+#define TERN_GEMM_DX_STATIC_MAX_ELEMS 67108864
+
+/*
+ * tern_gemm_dx_static: tern_gemm_dx without a caller workspace, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving or training loops, and harnesses that forbid hipMalloc.  The
+ * scaled gradient u is written to a fixed device array of the library
+ * instead (row pitch n); the call itself allocates nothing.
+ *
+ *   u[m][j]  = bf16( fp32(dy[m][j]) * s[j] ),   dx[m][c] = bf16( sum_j u[m][j] * T[j][c] )
+ *
+ * exactly as tern_gemm_dx (same kernels, bit-identical dx).
+ *
+ *   dy, pt, s, dx and their sizes and leading dimensions: as tern_gemm_dx
+ * Sizes as tern_gemm_dx, and m * n <= TERN_GEMM_DX_STATIC_MAX_ELEMS (else
+ * TERN_ERR_SHAPE).  Strides, nulls and alignment as tern_gemm_dx without the
+ * rules on u and ldu (n < 2^23 takes the place of ldu < 2^23).
+ *
+ * The array: 128 MiB per GPU, allocated when the library's device code is
+ * loaded on that GPU and held until the process ends.  Its device address on
+ * the GPU of `stream` is looked up on the first call there (a failure of that
+ * lookup returns TERN_ERR_HIP).  Every call on one GPU uses that GPU's one
+ * array and leaves its contents (the last call's u) behind: calls that
+ * overlap in time on one GPU (on different streams, or from different host
+ * threads without ordering) race on it and give undefined results.  Calls on
+ * one stream, or otherwise ordered, are safe.
+ */
+tern_status tern_gemm_dx_static(const void* dy_bf16, int64_t m, int64_t n, int64_t lddy,
+                                const uint8_t* pt, int64_t k, int64_t ldpt, const float* s,
+                                void* dx_bf16, int64_t lddx, void* stream);
 
 /*
  * 8-bit activations (W1.58-A8).  "1.58-bit FLUX" (section 4, limitation on

@@ -32,9 +32,11 @@ TERN_F32 = 0
 TERN_BF16 = 1
 TERN_QUANTIZE_MAX_K = 32768
 
+TERN_GEMM_DX_STATIC_MAX_ELEMS = 67108864
+
 EXPORTED = ("tern_quantize", "tern_quantize_pack", "tern_pack", "tern_unpack", "tern_gemm",
-            "tern_gemm_ex", "tern_pack_transposed", "tern_gemm_dx", "tern_quantize_act",
-            "tern_pack_a8", "tern_gemm_a8", "tern_status_string")
+            "tern_gemm_ex", "tern_pack_transposed", "tern_gemm_dx", "tern_gemm_dx_static",
+            "tern_quantize_act", "tern_pack_a8", "tern_gemm_a8", "tern_status_string")
 
 
 class TernError(RuntimeError):
@@ -61,13 +63,14 @@ def _load(path: str):
                                  i64, vp]
     lib.tern_pack_transposed.argtypes = [vp, i64, i64, i64, vp, i64, vp]
     lib.tern_gemm_dx.argtypes = [vp, i64, i64, i64, vp, i64, i64, vp, vp, i64, vp, i64, vp]
+    lib.tern_gemm_dx_static.argtypes = [vp, i64, i64, i64, vp, i64, i64, vp, vp, i64, vp]
     lib.tern_quantize_act.argtypes = [vp, i64, i64, i64, vp, i64, vp, vp]
     lib.tern_pack_a8.argtypes = [vp, i64, i64, i64, vp, i64, vp]
     lib.tern_gemm_a8.argtypes = [vp, i64, i64, i64, vp, vp, i64, i64, vp, vp, ctypes.c_int, i64,
                                  vp, i64, vp]
     for name in ("tern_quantize", "tern_quantize_pack", "tern_pack", "tern_unpack", "tern_gemm",
-                 "tern_gemm_ex", "tern_pack_transposed", "tern_gemm_dx", "tern_quantize_act",
-                 "tern_pack_a8", "tern_gemm_a8"):
+                 "tern_gemm_ex", "tern_pack_transposed", "tern_gemm_dx", "tern_gemm_dx_static",
+                 "tern_quantize_act", "tern_pack_a8", "tern_gemm_a8"):
         getattr(lib, name).restype = ctypes.c_int
     lib.tern_status_string.argtypes = [ctypes.c_int]
     lib.tern_status_string.restype = ctypes.c_char_p
@@ -259,6 +262,25 @@ def tern_gemm_dx(dy: torch.Tensor, pt: torch.Tensor, s: torch.Tensor, u: torch.T
     _check("tern_gemm_dx", _lib.tern_gemm_dx(dy.data_ptr(), m, n, lddy, pt.data_ptr(), k, ldpt,
                                              s.data_ptr(), u.data_ptr(), ldu, dx.data_ptr(), lddx,
                                              _stream(stream)))
+
+
+def tern_gemm_dx_static(dy: torch.Tensor, pt: torch.Tensor, s: torch.Tensor, dx: torch.Tensor,
+                        k: int | None = None, stream=None) -> None:
+    """``tern_gemm_dx`` with the scaled gradient in the library's fixed device
+    array instead of a caller workspace (m * n <= TERN_GEMM_DX_STATIC_MAX_ELEMS);
+    calls that overlap in time on one GPU race on that array."""
+    lddy = _mat(dy, "dy", (torch.bfloat16,))
+    ldpt = _mat(pt, "pt", (torch.uint8,))
+    lddx = _mat(dx, "dx", (torch.bfloat16,))
+    _vec(s, "s", torch.float32)
+    m, n = dy.shape
+    k = pt.shape[0] if k is None else int(k)
+    if (s.shape[0] != n or k > pt.shape[0] or pt.shape[1] < n // 4 or tuple(dx.shape[:1]) != (m,)
+            or dx.shape[1] < k):
+        raise ValueError("shapes must be dy [m, n], pt [>=k, >=n/4], s [n], dx [m, >=k]")
+    _check("tern_gemm_dx_static",
+           _lib.tern_gemm_dx_static(dy.data_ptr(), m, n, lddy, pt.data_ptr(), k, ldpt,
+                                    s.data_ptr(), dx.data_ptr(), lddx, _stream(stream)))
 
 
 def tern_quantize_act(x: torch.Tensor, q: torch.Tensor, xs: torch.Tensor, k: int | None = None,

@@ -147,6 +147,37 @@ tern_status tern_gemm_dx(const void* dy_bf16, int64_t m, int64_t n, int64_t lddy
                                     static_cast<uint16_t*>(dx_bf16), lddx, st));
 }
 
+tern_status tern_gemm_dx_static(const void* dy_bf16, int64_t m, int64_t n, int64_t lddy,
+                                const uint8_t* pt, int64_t k, int64_t ldpt, const float* s,
+                                void* dx_bf16, int64_t lddx, void* stream) {
+  // tern_gemm_dx with the scaled gradient in the library's device array
+  // (row pitch n): the rules of tern_gemm_dx without u and ldu, and a bound
+  // on m * n.
+  static_assert(TERN_GEMM_DX_STATIC_MAX_ELEMS == tern::kStaticScratchElems, "header limit");
+  if (m < 0 || n < 0 || k < 0 || m > kMaxInt || k > kMaxInt || n > kMaxInt - 63 || n % 64 != 0)
+    return TERN_ERR_SHAPE;
+  if (((m + 63) / 64) * ((k + 127) / 128) > kMaxInt) return TERN_ERR_SHAPE;
+  if (n > 0 && m > TERN_GEMM_DX_STATIC_MAX_ELEMS / n) return TERN_ERR_SHAPE;
+  if (m == 0 || k == 0) return TERN_OK;
+  if (pt == nullptr || dx_bf16 == nullptr || (n > 0 && (dy_bf16 == nullptr || s == nullptr)))
+    return TERN_ERR_NULL;
+  if (lddy < n || ldpt < n / 4 || lddx < k) return TERN_ERR_STRIDE;
+  if ((n > 0 && n > kGemmMaxLdx) || ldpt > kGemmMaxLdp || lddx > kMaxInt) return TERN_ERR_STRIDE;
+  if (!aligned(pt, 16) || ldpt % 16 != 0 || !aligned(dx_bf16, 2)) return TERN_ERR_ALIGN;
+  if (n > 0 && (!aligned(dy_bf16, 2) || !aligned(s, 4))) return TERN_ERR_ALIGN;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  uint16_t* u = nullptr;
+  if (n > 0) {
+    if (tern::static_scratch(st, &u) != hipSuccess) return TERN_ERR_HIP;
+    // Every element of u [m, n] is written before the product reads it.
+    const hipError_t e =
+        tern::launch_scale_grad(static_cast<const uint16_t*>(dy_bf16), m, n, lddy, s, u, n, st);
+    if (e != hipSuccess) return TERN_ERR_HIP;
+  }
+  return from_hip(tern::launch_gemm(u, m, n, n, pt, k, ldpt, nullptr, nullptr, k,
+                                    static_cast<uint16_t*>(dx_bf16), lddx, st));
+}
+
 tern_status tern_quantize_act(const void* x_bf16, int64_t m, int64_t k, int64_t ldx, int8_t* q,
                               int64_t ldq, float* xs, void* stream) {
   if (m < 0 || k < 0 || m > kMaxInt || k > kMaxInt) return TERN_ERR_SHAPE;

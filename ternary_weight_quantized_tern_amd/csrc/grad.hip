@@ -13,6 +13,8 @@
 // in cache).  One thread converts 8 consecutive elements of a row with 16-byte
 // loads and stores where the pointers and pitches allow it, else one at a
 // time; a grid-stride loop covers any m x n.
+#include <mutex>
+
 #include "internal.h"
 
 namespace tern {
@@ -60,7 +62,45 @@ __global__ __launch_bounds__(kThreads) void scale_grad_kernel(const uint16_t* __
   }
 }
 
+// The device array behind tern_gemm_dx_static: the scaled gradient u of one
+// call, for callers that cannot allocate.  Every GPU that runs the library
+// holds its own copy (kStaticScratchElems bf16 values) from the module's load
+// until the process ends.  In host code `scratch` names a host-side stand-in:
+// its device address on a GPU comes from hipGetSymbolAddress, taken once per
+// device and kept in g_scratch_ptr.
+__device__ __align__(256) uint16_t scratch[kStaticScratchElems];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
 }  // namespace
+
+hipError_t static_scratch(hipStream_t stream, uint16_t** ptr) {
+  int dev = 0;
+  hipError_t e = stream != nullptr ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    // The symbol's address is per device: look it up with that device current.
+    int cur = 0;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = static_cast<uint16_t*>(g_scratch_ptr[dev]);
+  return hipSuccess;
+}
 
 hipError_t launch_scale_grad(const uint16_t* dy, int64_t m, int64_t n, int64_t lddy,
                              const float* s, uint16_t* u, int64_t ldu, hipStream_t stream) {

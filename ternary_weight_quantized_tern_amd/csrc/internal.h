@@ -44,6 +44,14 @@ hipError_t launch_pack_transposed(const uint8_t* p, int64_t n, int64_t k, int64_
 hipError_t launch_scale_grad(const uint16_t* dy, int64_t m, int64_t n, int64_t lddy,
                              const float* s, uint16_t* u, int64_t ldu, hipStream_t stream);
 
+// Size of the per-device array that tern_gemm_dx_static uses for the scaled
+// gradient (bf16 elements; 128 MiB).
+inline constexpr int64_t kStaticScratchElems = int64_t(1) << 26;
+
+// The device address of that array on the device of `stream` (the current
+// device for the null stream), looked up once per device.
+hipError_t static_scratch(hipStream_t stream, uint16_t** ptr);
+
 // m <= 32 with int8 activations (called by launch_gemm_a8).
 hipError_t launch_gemm_small_a8(const int8_t* q, int64_t m, int64_t k, int64_t ldq,
                                 const float* xs, const uint8_t* p8, int64_t n, int64_t ldp8,

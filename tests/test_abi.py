@@ -226,6 +226,44 @@ def test_gemm_dx_validation():
     assert call(s=A + 2) == tern.TERN_ERR_ALIGN
 
 
+def test_gemm_dx_static_validation():
+    # Every rejection below happens before any HIP call (in particular before
+    # the array's address is looked up), so it runs without a GPU.
+    g = lib.tern_gemm_dx_static
+    ok = dict(dy=A, m=8, n=128, lddy=128, pt=A, k=16, ldpt=32, s=A, dx=A, lddx=16)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return g(a["dy"], a["m"], a["n"], a["lddy"], a["pt"], a["k"], a["ldpt"], a["s"], a["dx"],
+                 a["lddx"], NULL)
+
+    cap = tern.TERN_GEMM_DX_STATIC_MAX_ELEMS
+    assert cap == 1 << 26
+    assert call(m=-1) == tern.TERN_ERR_SHAPE
+    assert call(n=100, lddy=128) == tern.TERN_ERR_SHAPE   # n % 64 != 0
+    assert call(k=2 ** 31) == tern.TERN_ERR_SHAPE
+    # the array's capacity: m * n above it is refused, exactly at it passes
+    # validation (shown by a later check failing instead)
+    assert call(m=cap // 128 + 1) == tern.TERN_ERR_SHAPE
+    assert call(m=4608, n=21504, lddy=21504, ldpt=5376) == tern.TERN_ERR_SHAPE
+    assert call(m=cap // 128, lddx=15) == tern.TERN_ERR_STRIDE
+    assert call(m=0, dy=NULL, pt=NULL, s=NULL, dx=NULL) == tern.TERN_OK
+    assert call(k=0, dy=NULL, pt=NULL, s=NULL, dx=NULL) == tern.TERN_OK
+    for name in ("dy", "pt", "s", "dx"):
+        assert call(**{name: NULL}) == tern.TERN_ERR_NULL
+    assert call(n=0, pt=NULL) == tern.TERN_ERR_NULL
+    assert call(n=0, dy=NULL, s=NULL, lddx=15) == tern.TERN_ERR_STRIDE  # not read at n = 0
+    assert call(lddy=120) == tern.TERN_ERR_STRIDE
+    assert call(ldpt=16) == tern.TERN_ERR_STRIDE                  # < n/4
+    assert call(lddx=15) == tern.TERN_ERR_STRIDE
+    assert call(ldpt=1 << 24) == tern.TERN_ERR_STRIDE
+    assert call(pt=A + 4) == tern.TERN_ERR_ALIGN
+    assert call(ldpt=40) == tern.TERN_ERR_ALIGN
+    assert call(dy=A + 1) == tern.TERN_ERR_ALIGN
+    assert call(dx=A + 1) == tern.TERN_ERR_ALIGN
+    assert call(s=A + 2) == tern.TERN_ERR_ALIGN
+
+
 def test_quantize_act_validation():
     f = lib.tern_quantize_act
     ok = dict(x=A, m=8, k=64, ldx=64, q=A, ldq=64, xs=A)
