@@ -250,6 +250,42 @@ tern_status tern_gemm_dx(const void* dy_bf16, int64_t m, int64_t n, int64_t lddy
                          const uint8_t* pt, int64_t k, int64_t ldpt, const float* s,
                          void* u_bf16, int64_t ldu, void* dx_bf16, int64_t lddx, void* stream);
 
+/*
+ * tern_gemm_dw: the gradient of the layer's latent full-precision weights, for
+ * training the ternary weights in the loop ("TerDiT: Ternary Diffusion Models
+ * with Transformers", abstract: quantization-aware training of ternary DiTs;
+ * the pages give no formula).  The forward layer is Y = X . (s (.) T)^T, the
+ * quantized weight s_n T_nk standing in for the latent weight w_nk; the
+ * straight-through estimator passes the gradient of the quantized weight to
+ * the latent one unchanged, so
+ *
+ *   dw[j][c] = (accumulate ? dw[j][c] : 0) + sum_i dy[i][j] * x[i][c]
+ *
+ * with the products exact and the sum in fp32, in an order that is fixed for
+ * given sizes (repeated calls give identical bits).  The ternary codes and the
+ * scales do not enter.
+ *
+ *   dy  [m, lddy] bf16 gradient of the layer output Y (m tokens, n channels)
+ *   x   [m, ldx] bf16 layer input X (k input features)
+ *   dw  [n, lddw] fp32 output (the latent weights' gradient, row n = output
+ *       channel); with accumulate != 0 it is added into (gradient
+ *       accumulation over micro-batches); columns >= k untouched
+ * Sizes: 0 <= m, n, k <= 2^31 - 1 and ceil(n/128) * ceil(k/128) <= 2^31 - 1,
+ * (m - 1) * lddy + n and (m - 1) * ldx + k, each with the width rounded up to
+ * a multiple of 8, below 2^31 (else TERN_ERR_SHAPE);
+ * n == 0 or k == 0 is a no-op; m == 0 writes zeros (nothing with accumulate).
+ * lddw >= k (and lddw < 2^31), and with m > 0: lddy >= n, ldx >= k (else
+ * TERN_ERR_STRIDE).  dw must not be NULL, nor dy and x when m > 0
+ * (TERN_ERR_NULL).  Alignment (else TERN_ERR_ALIGN): dw 4-byte aligned; with
+ * m > 0, dy and x 16-byte aligned and lddy % 8 == 0, ldx % 8 == 0.  Rows of
+ * dy and x are read in whole 16-byte pieces: the last row must be readable up
+ * to its width rounded up to a multiple of 8 elements (true of every pitched
+ * matrix, whose rows span lddy or ldx elements).  dw must not overlap dy or x.
+ */
+tern_status tern_gemm_dw(const void* dy_bf16, int64_t m, int64_t n, int64_t lddy,
+                         const void* x_bf16, int64_t k, int64_t ldx, float* dw, int64_t lddw,
+                         int accumulate, void* stream);
+
 /* Largest m * n that tern_gemm_dx_static accepts: its array holds this many
  * bf16 values (128 MiB) on each GPU. */
 #define TERN_GEMM_DX_STATIC_MAX_ELEMS 67108864

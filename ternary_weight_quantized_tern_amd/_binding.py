@@ -36,7 +36,8 @@ TERN_GEMM_DX_STATIC_MAX_ELEMS = 67108864
 
 EXPORTED = ("tern_quantize", "tern_quantize_pack", "tern_pack", "tern_unpack", "tern_gemm",
             "tern_gemm_ex", "tern_pack_transposed", "tern_gemm_dx", "tern_gemm_dx_static",
-            "tern_quantize_act", "tern_pack_a8", "tern_gemm_a8", "tern_status_string")
+            "tern_gemm_dw", "tern_quantize_act", "tern_pack_a8", "tern_gemm_a8",
+            "tern_status_string")
 
 
 class TernError(RuntimeError):
@@ -64,13 +65,14 @@ def _load(path: str):
     lib.tern_pack_transposed.argtypes = [vp, i64, i64, i64, vp, i64, vp]
     lib.tern_gemm_dx.argtypes = [vp, i64, i64, i64, vp, i64, i64, vp, vp, i64, vp, i64, vp]
     lib.tern_gemm_dx_static.argtypes = [vp, i64, i64, i64, vp, i64, i64, vp, vp, i64, vp]
+    lib.tern_gemm_dw.argtypes = [vp, i64, i64, i64, vp, i64, i64, vp, i64, ctypes.c_int, vp]
     lib.tern_quantize_act.argtypes = [vp, i64, i64, i64, vp, i64, vp, vp]
     lib.tern_pack_a8.argtypes = [vp, i64, i64, i64, vp, i64, vp]
     lib.tern_gemm_a8.argtypes = [vp, i64, i64, i64, vp, vp, i64, i64, vp, vp, ctypes.c_int, i64,
                                  vp, i64, vp]
     for name in ("tern_quantize", "tern_quantize_pack", "tern_pack", "tern_unpack", "tern_gemm",
                  "tern_gemm_ex", "tern_pack_transposed", "tern_gemm_dx", "tern_gemm_dx_static",
-                 "tern_quantize_act", "tern_pack_a8", "tern_gemm_a8"):
+                 "tern_gemm_dw", "tern_quantize_act", "tern_pack_a8", "tern_gemm_a8"):
         getattr(lib, name).restype = ctypes.c_int
     lib.tern_status_string.argtypes = [ctypes.c_int]
     lib.tern_status_string.restype = ctypes.c_char_p
@@ -283,6 +285,23 @@ def tern_gemm_dx_static(dy: torch.Tensor, pt: torch.Tensor, s: torch.Tensor, dx:
                                     s.data_ptr(), dx.data_ptr(), lddx, _stream(stream)))
 
 
+def tern_gemm_dw(dy: torch.Tensor, x: torch.Tensor, dw: torch.Tensor, accumulate: bool = False,
+                 stream=None) -> None:
+    """Latent-weight gradient of the layer (straight-through reading):
+    ``dw [n, >=k] fp32 (+)= dy^T . x`` with ``dy`` bf16 [m, n] and ``x`` bf16
+    [m, k]; with ``accumulate`` the product is added into ``dw``."""
+    lddy = _mat(dy, "dy", (torch.bfloat16,))
+    ldx = _mat(x, "x", (torch.bfloat16,))
+    lddw = _mat(dw, "dw", (torch.float32,))
+    m, n = dy.shape
+    mx, k = x.shape
+    if mx != m or dw.shape[0] != n or dw.shape[1] < k:
+        raise ValueError("shapes must be dy [m, n], x [m, k], dw [n, >=k]")
+    _check("tern_gemm_dw", _lib.tern_gemm_dw(dy.data_ptr(), m, n, lddy, x.data_ptr(), k, ldx,
+                                             dw.data_ptr(), lddw, 1 if accumulate else 0,
+                                             _stream(stream)))
+
+
 def tern_quantize_act(x: torch.Tensor, q: torch.Tensor, xs: torch.Tensor, k: int | None = None,
                       stream=None) -> None:
     """Per-token int8 activations of bf16 ``x`` [m, k]: codes into ``q`` int8
@@ -414,6 +433,14 @@ def linear_dx(dy: torch.Tensor, pt: torch.Tensor, s: torch.Tensor, k: int, strea
     dx = torch.empty((dy.shape[0], k), dtype=torch.bfloat16, device=dy.device)
     tern_gemm_dx(dy, pt, s, u, dx, k, stream)
     return dx
+
+
+def linear_dw(dy: torch.Tensor, x: torch.Tensor, stream=None) -> torch.Tensor:
+    """Latent-weight gradient ``dy^T . x`` (fp32 [n, k]) of the layer for bf16
+    ``dy`` [m, n] and ``x`` [m, k] (straight-through reading)."""
+    dw = torch.empty((dy.shape[1], x.shape[1]), dtype=torch.float32, device=dy.device)
+    tern_gemm_dw(dy, x, dw, False, stream)
+    return dw
 
 
 def quantize_act(x: torch.Tensor, stream=None):

@@ -178,6 +178,28 @@ tern_status tern_gemm_dx_static(const void* dy_bf16, int64_t m, int64_t n, int64
                                     static_cast<uint16_t*>(dx_bf16), lddx, st));
 }
 
+tern_status tern_gemm_dw(const void* dy_bf16, int64_t m, int64_t n, int64_t lddy,
+                         const void* x_bf16, int64_t k, int64_t ldx, float* dw, int64_t lddw,
+                         int accumulate, void* stream) {
+  if (m < 0 || n < 0 || k < 0 || m > kMaxInt || n > kMaxInt || k > kMaxInt) return TERN_ERR_SHAPE;
+  // The smallest tile is 128 x 128: the tile count must fit the grid.
+  if (((n + 127) / 128) * ((k + 127) / 128) > kMaxInt) return TERN_ERR_SHAPE;
+  if (n == 0 || k == 0) return TERN_OK;
+  if (dw == nullptr || (m > 0 && (dy_bf16 == nullptr || x_bf16 == nullptr))) return TERN_ERR_NULL;
+  if (lddw < k || (m > 0 && (lddy < n || ldx < k))) return TERN_ERR_STRIDE;
+  if (lddw > kMaxInt) return TERN_ERR_STRIDE;
+  // A stage's buffer resource spans the rest of the matrix from its first
+  // token: its byte count must fit 32 bits.
+  if (m > 0 && ((m - 1) * lddy + (n + 7) / 8 * 8 > kMaxInt || (m - 1) * ldx + (k + 7) / 8 * 8 > kMaxInt))
+    return TERN_ERR_SHAPE;
+  if (!aligned(dw, 4)) return TERN_ERR_ALIGN;
+  if (m > 0 && (!aligned(dy_bf16, 16) || lddy % 8 != 0 || !aligned(x_bf16, 16) || ldx % 8 != 0))
+    return TERN_ERR_ALIGN;
+  return from_hip(tern::launch_gemm_dw(static_cast<const uint16_t*>(dy_bf16), m, n, lddy,
+                                       static_cast<const uint16_t*>(x_bf16), k, ldx, dw, lddw,
+                                       accumulate != 0, static_cast<hipStream_t>(stream)));
+}
+
 tern_status tern_quantize_act(const void* x_bf16, int64_t m, int64_t k, int64_t ldx, int8_t* q,
                               int64_t ldq, float* xs, void* stream) {
   if (m < 0 || k < 0 || m > kMaxInt || k > kMaxInt) return TERN_ERR_SHAPE;

@@ -44,6 +44,12 @@ hipError_t launch_pack_transposed(const uint8_t* p, int64_t n, int64_t k, int64_
 hipError_t launch_scale_grad(const uint16_t* dy, int64_t m, int64_t n, int64_t lddy,
                              const float* s, uint16_t* u, int64_t ldu, hipStream_t stream);
 
+// dw[n][k] = (accumulate ? dw : 0) + sum_m dy[m][n] * x[m][k], fp32 dw; dy
+// and x 16-byte aligned with ld % 8 == 0, (m - 1) * ld + width < 2^31.
+hipError_t launch_gemm_dw(const uint16_t* dy, int64_t m, int64_t n, int64_t lddy,
+                          const uint16_t* x, int64_t k, int64_t ldx, float* dw, int64_t lddw,
+                          bool accumulate, hipStream_t stream);
+
 // Size of the per-device array that tern_gemm_dx_static uses for the scaled
 // gradient (bf16 elements; 128 MiB).
 inline constexpr int64_t kStaticScratchElems = int64_t(1) << 26;

@@ -264,6 +264,35 @@ def test_gemm_dx_static_validation():
     assert call(s=A + 2) == tern.TERN_ERR_ALIGN
 
 
+def test_gemm_dw_validation():
+    g = lib.tern_gemm_dw
+    ok = dict(dy=A, m=64, n=256, lddy=256, x=A, k=128, ldx=128, dw=A, lddw=128, acc=0)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return g(a["dy"], a["m"], a["n"], a["lddy"], a["x"], a["k"], a["ldx"], a["dw"], a["lddw"],
+                 a["acc"], NULL)
+
+    assert call(m=-1) == tern.TERN_ERR_SHAPE
+    assert call(n=-1) == tern.TERN_ERR_SHAPE
+    assert call(k=2 ** 31) == tern.TERN_ERR_SHAPE
+    assert call(n=0, dy=NULL, x=NULL, dw=NULL) == tern.TERN_OK       # no-op
+    assert call(k=0, dy=NULL, x=NULL, dw=NULL) == tern.TERN_OK
+    assert call(dw=NULL) == tern.TERN_ERR_NULL
+    assert call(dy=NULL) == tern.TERN_ERR_NULL
+    assert call(x=NULL) == tern.TERN_ERR_NULL
+    assert call(m=0, dy=NULL, x=NULL, lddy=0, ldx=0, dw=A + 1) == tern.TERN_ERR_ALIGN  # m = 0: not read
+    assert call(lddy=255) == tern.TERN_ERR_STRIDE
+    assert call(ldx=127) == tern.TERN_ERR_STRIDE
+    assert call(lddw=127) == tern.TERN_ERR_STRIDE
+    assert call(m=1 << 20, lddy=4096) == tern.TERN_ERR_SHAPE        # a stage's span past 2^31
+    assert call(dy=A + 2) == tern.TERN_ERR_ALIGN
+    assert call(x=A + 8) == tern.TERN_ERR_ALIGN
+    assert call(lddy=260) == tern.TERN_ERR_ALIGN
+    assert call(ldx=132) == tern.TERN_ERR_ALIGN
+    assert call(dw=A + 2) == tern.TERN_ERR_ALIGN
+
+
 def test_quantize_act_validation():
     f = lib.tern_quantize_act
     ok = dict(x=A, m=8, k=64, ldx=64, q=A, ldq=64, xs=A)
