@@ -252,6 +252,189 @@ __global__ __launch_bounds__(kSmallThreads) void gemm_ternary_small(
   }
 }
 
+// bf16 activations, a handful of tokens: the weight stream with every load of
+// a wave in flight at once.  A workgroup owns RB blocks of 16 output channels
+// and all of K; its W waves (W = blockDim.x / 64, at most MAXW) split K in
+// 256-wide chunks, wave w taking chunks w, w + W, w + 2 W, ...  In each round
+// a wave issues the loads of its next CPW chunks together (the chunk loop is
+// unrolled), then decodes the codes in registers and accumulates R blocks of
+// 16 tokens; one round covers W * CPW chunks, which is all of K for the
+// launch shapes chosen below up to K = 16384.  Lane (r, g) fetches 16 bytes of weight row r of every channel
+// block per chunk (codes 64 g .. 64 g + 63 of the chunk) and the matching
+// eight 16-byte pieces of X per token block; MFMA j of a chunk uses codes
+// 8 j .. 8 j + 7 of those 64 (the same permutation of k on both operands).
+// Chunk slots past the last chunk are skipped (a wave-uniform branch); the
+// 64-code pieces past k, weight rows past n and tokens past m read as zero
+// through the buffer range check.  The partial sums of the W waves meet in
+// LDS; wave 0 applies the fp32 channel scale (and the optional bias and
+// tanh-form GELU) and rounds once to bf16.  The MFMAs are the compiler's
+// builtin, so that the compiler sees their latencies: with a chunk slot that
+// may be skipped, it moves accumulators between registers at the join, and
+// only a visible MFMA makes it wait for the result before such a move.
+template <int RB, int R, int CPW, int MAXW, bool EPI, bool LOOP>
+__global__ __launch_bounds__(64 * MAXW) void gemm_ternary_few(
+    const uint8_t* __restrict__ x, int m, int k, int ldx, const uint8_t* __restrict__ p, int n,
+    int ldp, const float* __restrict__ s, const float* __restrict__ bias, int act_from,
+    uint16_t* __restrict__ y, int ldy, int y_vec_ok) {
+  extern __shared__ f32x4_t red_few[];  // [waves - 1][RB][R][64]
+
+  const int waves = blockDim.x >> 6;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r16 = lane & 15;
+  const int g = lane >> 4;
+  const int n0 = blockIdx.x * (16 * RB);
+  const int rows = (n - n0) < 16 * RB ? (n - n0) : 16 * RB;
+
+  const __amdgpu_buffer_rsrc_t prs = make_rsrc(
+      p + static_cast<int64_t>(n0) * ldp, static_cast<uint32_t>((rows - 1) * ldp + k / 4));
+  const __amdgpu_buffer_rsrc_t xrs =
+      make_rsrc(x, static_cast<uint32_t>((static_cast<int64_t>(m) - 1) * ldx * 2 + k * 2));
+  const int chunks = (k + kChunk - 1) / kChunk;
+
+  const uint32_t p_off = static_cast<uint32_t>(r16 * ldp + 16 * g);
+  uint32_t x_off[R];
+#pragma unroll
+  for (int b = 0; b < R; ++b) x_off[b] = static_cast<uint32_t>(((16 * b + r16) * ldx + 64 * g) * 2);
+
+  // The channel scales (and biases) of this lane's outputs, requested before
+  // the weight stream so that they have arrived by the epilogue: buffer loads
+  // without any branch (channels past n, and a null vector, read as zero;
+  // the values are only used in the epilogue, so no wait is placed here).
+  // A null scale vector means unit scales (the input-gradient product).
+  const bool unit = s == nullptr;
+  const __amdgpu_buffer_rsrc_t srs =
+      make_rsrc(unit ? p : reinterpret_cast<const uint8_t*>(s + n0),
+                unit ? 0u : static_cast<uint32_t>(rows * 4));
+  const __amdgpu_buffer_rsrc_t brs =
+      make_rsrc(bias == nullptr ? p : reinterpret_cast<const uint8_t*>(bias + n0),
+                (!EPI || bias == nullptr) ? 0u : static_cast<uint32_t>(rows * 4));
+  float sraw[RB][4];
+  float braw[EPI ? RB : 1][4];
+#pragma unroll
+  for (int bl = 0; bl < RB; ++bl)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t off = static_cast<uint32_t>((16 * bl + 4 * g + e) * 4);
+      sraw[bl][e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, off, 0, 0));
+      if constexpr (EPI)
+        braw[bl][e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(brs, off, 0, 0));
+    }
+
+  f32x4_t acc[RB][R];
+#pragma unroll
+  for (int bl = 0; bl < RB; ++bl)
+#pragma unroll
+    for (int b = 0; b < R; ++b) acc[bl][b] = f32x4_t{};
+
+  // Without LOOP the launch covers K in one round (chunks <= waves * CPW) and
+  // the body is straight-line code: a loop would make the compiler wait for
+  // the scale loads at its head, before the first weight load.
+  for (int base = 0; base < chunks; base += waves * CPW) {
+    u32x4_t wq[CPW][RB];
+    u32x4_t xq[CPW][R][8];
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+      const int c = base + wave + waves * i;
+      if (c < chunks) {
+        // Codes kc .. kc + 63 of this lane lie past k exactly when kc >= k
+        // (k is a multiple of 64); their offsets get the out-of-range bit.
+        const int kc = c * kChunk + 64 * g;
+        const uint32_t oob = static_cast<uint32_t>(k - 1 - kc) & kOutOfRange;
+#pragma unroll
+        for (int bl = 0; bl < RB; ++bl)
+          wq[i][bl] = __builtin_bit_cast(
+              u32x4_t,
+              __builtin_amdgcn_raw_buffer_load_b128(
+                  prs, (p_off + static_cast<uint32_t>(bl * 16 * ldp + c * (kChunk / 4))) | oob, 0,
+                  0));
+#pragma unroll
+        for (int b = 0; b < R; ++b)
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            xq[i][b][j] = __builtin_bit_cast(
+                u32x4_t,
+                __builtin_amdgcn_raw_buffer_load_b128(
+                    xrs, (x_off[b] + static_cast<uint32_t>(c * kChunk * 2 + 16 * j)) | oob, 0, 0));
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+      if (base + wave + waves * i < chunks) {
+#pragma unroll
+        for (int bl = 0; bl < RB; ++bl)
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            bf16x8_t lo, hi;
+            decode16(wq[i][bl][d], lo, hi);
+#pragma unroll
+            for (int b = 0; b < R; ++b) {
+              acc[bl][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  lo, __builtin_bit_cast(bf16x8_t, xq[i][b][2 * d]), acc[bl][b], 0, 0, 0);
+              acc[bl][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  hi, __builtin_bit_cast(bf16x8_t, xq[i][b][2 * d + 1]), acc[bl][b], 0, 0, 0);
+            }
+          }
+      }
+    }
+    if constexpr (!LOOP) break;
+  }
+
+  if (waves > 1) {
+    if (wave > 0) {
+#pragma unroll
+      for (int bl = 0; bl < RB; ++bl)
+#pragma unroll
+        for (int b = 0; b < R; ++b)
+          red_few[(((wave - 1) * RB + bl) * R + b) * 64 + lane] = acc[bl][b];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    for (int w = 0; w < waves - 1; ++w) {
+#pragma unroll
+      for (int bl = 0; bl < RB; ++bl)
+#pragma unroll
+        for (int b = 0; b < R; ++b) acc[bl][b] += red_few[((w * RB + bl) * R + b) * 64 + lane];
+    }
+  }
+
+#pragma unroll
+  for (int bl = 0; bl < RB; ++bl) {
+    const int nb = n0 + 16 * bl + 4 * g;  // output channels nb .. nb + 3 of this lane
+#pragma unroll
+    for (int b = 0; b < R; ++b) {
+      const int token = 16 * b + r16;
+      if (token >= m) continue;
+      __bf16 o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        // The decode produced 2 T: y = bf16(acc * (s / 2)), which rounds like
+        // bf16(fp32(acc / 2 * s)) (the halving is exact).
+        float z = acc[bl][b][e] * ((unit ? 1.0f : sraw[bl][e]) * 0.5f);
+        if constexpr (EPI) {
+          z += braw[bl][e];
+          if (nb + e >= act_from) z = gelu_tanh_f32(z);
+        }
+        o[e] = static_cast<__bf16>(z);
+      }
+      uint16_t* yr = y + static_cast<int64_t>(token) * ldy + nb;
+      if (y_vec_ok && nb + 4 <= n) {
+        u32x2_t q;
+        q[0] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, o[0])) |
+               (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, o[1])) << 16);
+        q[1] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, o[2])) |
+               (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, o[3])) << 16);
+        *reinterpret_cast<u32x2_t*>(yr) = q;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (nb + e < n) yr[e] = __builtin_bit_cast(uint16_t, o[e]);
+      }
+    }
+  }
+}
+
 template <int R, int B, int DEPTH, bool EPI, bool A8>
 hipError_t launch_small(const void* x, int64_t m, int64_t k, int64_t ldx, const float* xs,
                         const uint8_t* p, int64_t n, int64_t ldp, const float* s,
@@ -311,6 +494,62 @@ hipError_t launch_small_any(const void* x, int64_t m, int64_t k, int64_t ldx, co
 #undef TERN_SMALL
 }
 
+template <int RB, int R, int CPW, int MAXW, bool EPI>
+hipError_t launch_few(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const uint8_t* p,
+                      int64_t n, int64_t ldp, const float* s, const float* bias, int act_from,
+                      uint16_t* y, int64_t ldy, hipStream_t stream) {
+  const int64_t blocks = (n + 16 * RB - 1) / (16 * RB);
+  const int64_t chunks = (k + kChunk - 1) / kChunk;
+  int64_t waves = (chunks + CPW - 1) / CPW;
+  if (waves > MAXW) waves = MAXW;
+  if (waves < 1) waves = 1;
+  const int y_vec_ok = ((reinterpret_cast<uintptr_t>(y) & 7) == 0) && (ldy % 4 == 0);
+  const size_t lds = static_cast<size_t>(waves - 1) * RB * R * 64 * sizeof(f32x4_t);
+  const dim3 grid(static_cast<unsigned>(blocks)), block(static_cast<unsigned>(64 * waves));
+  const uint8_t* xb = reinterpret_cast<const uint8_t*>(x);
+  if (chunks <= waves * CPW)
+    hipLaunchKernelGGL((gemm_ternary_few<RB, R, CPW, MAXW, EPI, false>), grid, block, lds, stream,
+                       xb, static_cast<int>(m), static_cast<int>(k), static_cast<int>(ldx), p,
+                       static_cast<int>(n), static_cast<int>(ldp), s, bias, act_from, y,
+                       static_cast<int>(ldy), y_vec_ok);
+  else
+    hipLaunchKernelGGL((gemm_ternary_few<RB, R, CPW, MAXW, EPI, true>), grid, block, lds, stream,
+                       xb, static_cast<int>(m), static_cast<int>(k), static_cast<int>(ldx), p,
+                       static_cast<int>(n), static_cast<int>(ldp), s, bias, act_from, y,
+                       static_cast<int>(ldy), y_vec_ok);
+  return hipGetLastError();
+}
+
+// Shape of the few-token launch.  Channel blocks per workgroup: two (each X
+// operand then feeds two blocks of MFMAs, halving the X loads per weight
+// byte) for layers of at least 512 blocks of 16 channels, unless one block per
+// workgroup spreads the blocks more evenly over the CUs (the busiest CU's
+// blocks, RB * ceil(ceil(nb / RB) / 256), are fewer); one block otherwise, so
+// that small layers spread their weight requests over as many CUs as
+// possible.  Waves per workgroup: enough that every chunk of K is in flight
+// in one round, with at most CPW chunks per wave (two when two blocks share
+// the X operands, else one, or two past 16 chunks) and at most 8 or 16 waves.
+template <bool EPI>
+hipError_t launch_few_any(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const uint8_t* p,
+                          int64_t n, int64_t ldp, const float* s, const float* bias, int act_from,
+                          uint16_t* y, int64_t ldy, hipStream_t stream) {
+  const int64_t nb = (n + 15) / 16;
+  const int64_t chunks = (k + kChunk - 1) / kChunk;
+  const bool r2 = m > 16;
+  const bool rb2 = nb >= 512 && 2 * (((nb + 1) / 2 + 255) / 256) <= (nb + 255) / 256;
+  if (rb2) {
+    if (r2)
+      return launch_few<2, 2, 2, 8, EPI>(x, m, k, ldx, p, n, ldp, s, bias, act_from, y, ldy,
+                                         stream);
+    return launch_few<2, 1, 2, 8, EPI>(x, m, k, ldx, p, n, ldp, s, bias, act_from, y, ldy, stream);
+  }
+  if (r2)
+    return launch_few<1, 2, 1, 16, EPI>(x, m, k, ldx, p, n, ldp, s, bias, act_from, y, ldy, stream);
+  if (chunks > 16)
+    return launch_few<1, 1, 2, 16, EPI>(x, m, k, ldx, p, n, ldp, s, bias, act_from, y, ldy, stream);
+  return launch_few<1, 1, 1, 16, EPI>(x, m, k, ldx, p, n, ldp, s, bias, act_from, y, ldy, stream);
+}
+
 }  // namespace
 
 hipError_t launch_gemm_small(const uint16_t* x, int64_t m, int64_t k, int64_t ldx,
@@ -318,10 +557,10 @@ hipError_t launch_gemm_small(const uint16_t* x, int64_t m, int64_t k, int64_t ld
                              const float* bias, int64_t act_from, uint16_t* y, int64_t ldy,
                              hipStream_t stream) {
   if (bias != nullptr || act_from < n)
-    return launch_small_any<true>(x, m, k, ldx, nullptr, p, n, ldp, s, bias,
-                                  static_cast<int>(act_from), y, ldy, stream);
-  return launch_small_any<false>(x, m, k, ldx, nullptr, p, n, ldp, s, nullptr,
-                                 static_cast<int>(act_from), y, ldy, stream);
+    return launch_few_any<true>(x, m, k, ldx, p, n, ldp, s, bias, static_cast<int>(act_from), y,
+                                ldy, stream);
+  return launch_few_any<false>(x, m, k, ldx, p, n, ldp, s, nullptr, static_cast<int>(act_from), y,
+                               ldy, stream);
 }
 
 hipError_t launch_gemm_small_a8(const int8_t* q, int64_t m, int64_t k, int64_t ldq,

@@ -192,6 +192,9 @@ GEMM_SHAPES = [
     (5, 320, 16400), (20, 256, 16448),
     # 64 x 576 tiles, one per CU; k of 3 pipeline stages (fewer than the ring)
     (1024, 192, 9216),
+    # few-token kernel, K past one round of its waves (the looping form): one
+    # block per workgroup with 16 and 32 tokens, two blocks with 16 and 32
+    (5, 8448, 100), (31, 4352, 70), (2, 4352, 21496), (17, 4160, 21480),
 ]
 
 

@@ -1,11 +1,17 @@
-"""The MFMAs of the GEMM kernels are inline asm, so the compiler does not pad
-them for hazards.  gfx950 requires two wait states between a VALU instruction
-that writes a VGPR and an MFMA that reads it as its A or B operand.  The wide
-schedules keep every decoded operand far from its MFMA and emit no padding;
-this test compiles the GEMM sources for gfx950 and checks every MFMA of every
-kernel against the instructions that can precede it (fall-through and
-branches), so that a schedule or compiler change that breaks the rule fails
-here instead of producing wrong numbers on the GPU.
+"""The MFMAs of the tiled GEMM kernels are inline asm, so the compiler does not
+pad them for hazards.  gfx950 requires two wait states between a VALU
+instruction that writes a VGPR and an MFMA that reads it as its A or B
+operand, and up to 19 between an MFMA and an instruction that reads its result
+other than as the accumulator of the next MFMA.  The wide schedules keep
+every decoded operand far from its MFMA and emit no padding, and the kernels
+read their accumulators only after an explicit padding block; but the
+compiler, which does not see the MFMA inside the asm, may move an
+accumulator between registers right after one (it did so at the join of a
+conditional block).  This test compiles the GEMM sources for gfx950 and checks
+every MFMA of every kernel against the instructions that can precede it, and
+every read of an accumulator register against the MFMAs before it
+(fall-through and branches), so that a schedule or compiler change that breaks
+either rule fails here instead of producing wrong numbers on the GPU.
 
 CPU only: it needs hipcc, not a GPU.
 """
@@ -19,7 +25,8 @@ import pytest
 from ternary_weight_quantized_tern_amd import build as B
 
 WAIT_STATES = 2
-SOURCES = ["gemm.hip", "gemm_small.hip"]
+RESULT_WAIT_STATES = 19
+SOURCES = ["gemm.hip", "gemm_small.hip", "dw.hip"]
 
 
 def _asm(src: str, tmp_path) -> str:
@@ -119,11 +126,97 @@ def _hazards(items):
     return count, found
 
 
+def _agprs(tok: str):
+    tok = tok.strip()
+    m = re.match(r"a\[(\d+):(\d+)\]$", tok)
+    if m:
+        return set(range(int(m.group(1)), int(m.group(2)) + 1))
+    m = re.match(r"a(\d+)$", tok)
+    return {int(m.group(1))} if m else set()
+
+
+def _result_hazards(items):
+    """Instructions other than MFMAs that read an accumulator register (AGPR)
+    written by an MFMA fewer than RESULT_WAIT_STATES wait states before."""
+    branches = {}
+    for i, (kind, t) in enumerate(items):
+        if kind == "inst" and (t.startswith("s_cbranch") or t.startswith("s_branch")):
+            branches.setdefault(t.split()[-1], []).append(i)
+    found = []
+
+    def walk(idx, ws, srcs, seen, reader):
+        j = idx - 1
+        while j >= 0 and ws < RESULT_WAIT_STATES:
+            kind, t = items[j]
+            if kind == "label":
+                for b in branches.get(t, []):
+                    if (b, ws) not in seen:
+                        seen.add((b, ws))
+                        walk(b, ws + 1, srcs, seen, reader)
+                j -= 1
+                continue
+            op = t.split()[0]
+            if op == "s_nop":
+                ws += int(t.split()[1], 0) + 1
+                j -= 1
+                continue
+            if op in ("s_branch",) or op.startswith("s_endpgm"):
+                return
+            if op.startswith("v_mfma"):
+                dst = t.split(None, 1)[1].split(",")[0]
+                if _agprs(dst) & srcs:
+                    found.append(reader)
+                    return
+            ws += 1
+            j -= 1
+
+    for i, (kind, t) in enumerate(items):
+        if kind != "inst" or t.startswith("v_mfma") or not t.startswith("v_"):
+            continue
+        parts = t.split(None, 1)
+        if len(parts) < 2:
+            continue
+        srcs = set()
+        for tok in parts[1].split(",")[1:]:
+            srcs |= _agprs(tok)
+        if srcs:
+            walk(i, 0, srcs, set(), t)
+    return found
+
+
+def _gemm_kernels(src, tmp_path):
+    return [(n, b) for n, b in _kernels(_asm(src, tmp_path))
+            if "gemm_ternary" in n or "gemm_dw" in n]
+
+
+@pytest.mark.skipif(shutil.which(B.hipcc()) is None and not os.path.exists(B.hipcc()),
+                    reason="hipcc not available")
+@pytest.mark.parametrize("src", SOURCES)
+def test_no_mfma_result_read_too_early(src, tmp_path):
+    kernels = _gemm_kernels(src, tmp_path)
+    assert kernels, "no GEMM kernels found in the assembly"
+    for name, body in kernels:
+        found = _result_hazards(_parse(body))
+        assert not found, f"{name}: an MFMA result is read too early: {found[:3]}"
+
+
+def test_result_checker_sees_a_planted_hazard():
+    body = [
+        "v_mfma_f32_16x16x32_bf16 a[4:7], v[0:3], v[8:11], a[4:7]",
+        "v_accvgpr_mov_b32 a12, a4",
+    ]
+    assert _result_hazards(_parse(body))
+    padded = [body[0], "s_nop 7", "s_nop 7", "s_nop 7", body[1]]
+    assert not _result_hazards(_parse(padded))
+    chained = [body[0], "v_mfma_f32_16x16x32_bf16 a[4:7], v[0:3], v[8:11], a[4:7]"]
+    assert not _result_hazards(_parse(chained))
+
+
 @pytest.mark.skipif(shutil.which(B.hipcc()) is None and not os.path.exists(B.hipcc()),
                     reason="hipcc not available")
 @pytest.mark.parametrize("src", SOURCES)
 def test_no_valu_to_mfma_hazard(src, tmp_path):
-    kernels = [(n, b) for n, b in _kernels(_asm(src, tmp_path)) if "gemm_ternary" in n]
+    kernels = _gemm_kernels(src, tmp_path)
     assert kernels, "no GEMM kernels found in the assembly"
     total = 0
     for name, body in kernels:
