@@ -254,29 +254,45 @@ __global__ __launch_bounds__(kSmallThreads) void gemm_ternary_small(
 
 // bf16 activations, a handful of tokens: the weight stream with every load of
 // a wave in flight at once.  A workgroup owns RB blocks of 16 output channels
-// and all of K; its W waves (W = blockDim.x / 64, at most MAXW) split K in
+// and all of K; its W waves (W = blockDim.x / 64, at most 16) split K in
 // 256-wide chunks, wave w taking chunks w, w + W, w + 2 W, ...  In each round
 // a wave issues the loads of its next CPW chunks together (the chunk loop is
 // unrolled), then decodes the codes in registers and accumulates R blocks of
-// 16 tokens; one round covers W * CPW chunks, which is all of K for the
-// launch shapes chosen below up to K = 16384.  Lane (r, g) fetches 16 bytes of weight row r of every channel
-// block per chunk (codes 64 g .. 64 g + 63 of the chunk) and the matching
-// eight 16-byte pieces of X per token block; MFMA j of a chunk uses codes
-// 8 j .. 8 j + 7 of those 64 (the same permutation of k on both operands).
+// 16 tokens.  Without LOOP one round covers all of K.  MAXW bounds the waves
+// per workgroup (and so sets the register budget: 128 per lane at 16 waves,
+// 256 at 8).
+//
+// Lane (r, g) fetches 16 bytes of weight row r of every channel block per
+// chunk (codes 64 g .. 64 g + 63 of the chunk); MFMA (d, h) of a chunk uses
+// codes 16 d + 8 h .. 16 d + 8 h + 7 of those 64, i.e. the 16-byte piece
+// 8 g + 2 d + h of the chunk's 256 X values of token r (the same permutation
+// of k on both operands).  Loaded straight into registers, those X pieces
+// would be 64 lanes touching 64 different cache lines per load instruction,
+// which keeps the texture addresser busy for most of the kernel; instead each
+// wave copies the X rows of its chunk (only the real tokens, rounded up to
+// two) into its own LDS region with buffer loads in the LDS-DMA form, 512
+// contiguous bytes per row, and reads the MFMA operands from there.  The
+// 16-byte pieces of LDS row r are XOR-swizzled by r % 16 (applied on the
+// global side of the copy), so that an operand read of 16 token rows hits 16
+// distinct bank groups; operand lanes of tokens past the copied rows read
+// row 0 (their outputs are not stored).
+//
 // Chunk slots past the last chunk are skipped (a wave-uniform branch); the
 // 64-code pieces past k, weight rows past n and tokens past m read as zero
 // through the buffer range check.  The partial sums of the W waves meet in
-// LDS; wave 0 applies the fp32 channel scale (and the optional bias and
-// tanh-form GELU) and rounds once to bf16.  The MFMAs are the compiler's
-// builtin, so that the compiler sees their latencies: with a chunk slot that
-// may be skipped, it moves accumulators between registers at the join, and
-// only a visible MFMA makes it wait for the result before such a move.
+// LDS (in the X regions, after a barrier); wave 0 applies the fp32 channel
+// scale (and the optional bias and tanh-form GELU) and rounds once to bf16.
+// The MFMAs are the compiler's builtin, so that the compiler sees their
+// latencies (with a chunk slot that may be skipped, it moves accumulators
+// between registers at the join, and only a visible MFMA makes it wait for
+// the result before such a move).
 template <int RB, int R, int CPW, int MAXW, bool EPI, bool LOOP>
 __global__ __launch_bounds__(64 * MAXW) void gemm_ternary_few(
     const uint8_t* __restrict__ x, int m, int k, int ldx, const uint8_t* __restrict__ p, int n,
     int ldp, const float* __restrict__ s, const float* __restrict__ bias, int act_from,
     uint16_t* __restrict__ y, int ldy, int y_vec_ok) {
-  extern __shared__ f32x4_t red_few[];  // [waves - 1][RB][R][64]
+#if defined(__HIP_DEVICE_COMPILE__)
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem_few[];
 
   const int waves = blockDim.x >> 6;
   const int tid = threadIdx.x;
@@ -286,6 +302,10 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_ternary_few(
   const int g = lane >> 4;
   const int n0 = blockIdx.x * (16 * RB);
   const int rows = (n - n0) < 16 * RB ? (n - n0) : 16 * RB;
+  // X rows copied per chunk (the real tokens, rounded up to two) and their
+  // LDS bytes; the LDS region of slot i of this wave.
+  const int mrows = (m < 16 * R ? m : 16 * R) + 1 & ~1;
+  const uint32_t region = static_cast<uint32_t>(mrows) * 512u;
 
   const __amdgpu_buffer_rsrc_t prs = make_rsrc(
       p + static_cast<int64_t>(n0) * ldp, static_cast<uint32_t>((rows - 1) * ldp + k / 4));
@@ -294,14 +314,25 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_ternary_few(
   const int chunks = (k + kChunk - 1) / kChunk;
 
   const uint32_t p_off = static_cast<uint32_t>(r16 * ldp + 16 * g);
-  uint32_t x_off[R];
+  // Copy plan: copy d of a chunk moves rows 2 d and 2 d + 1; lane l fills the
+  // 16-byte slot l % 32 of row 2 d + l / 32, which holds piece slot ^ (row %
+  // 16) of the row's chunk.
+  const uint32_t crow = static_cast<uint32_t>(lane >> 5);
+  const uint32_t cslot = static_cast<uint32_t>(lane & 31);
+  // Operand reads: token row r (tokens past the copied rows read row 0),
+  // piece (8 g + j) ^ (r % 16) for j = 2 d + h.
+  uint32_t rd_row[R], rd_x[R];
 #pragma unroll
-  for (int b = 0; b < R; ++b) x_off[b] = static_cast<uint32_t>(((16 * b + r16) * ldx + 64 * g) * 2);
+  for (int b = 0; b < R; ++b) {
+    const int r = 16 * b + r16;
+    const int rc = r < mrows ? r : 0;
+    rd_row[b] = static_cast<uint32_t>(rc) * 512u;
+    rd_x[b] = static_cast<uint32_t>(8 * g) ^ static_cast<uint32_t>(rc & 15);
+  }
 
   // The channel scales (and biases) of this lane's outputs, requested before
   // the weight stream so that they have arrived by the epilogue: buffer loads
-  // without any branch (channels past n, and a null vector, read as zero;
-  // the values are only used in the epilogue, so no wait is placed here).
+  // without any branch (channels past n, and a null vector, read as zero).
   // A null scale vector means unit scales (the input-gradient product).
   const bool unit = s == nullptr;
   const __amdgpu_buffer_rsrc_t srs =
@@ -328,12 +359,8 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_ternary_few(
 #pragma unroll
     for (int b = 0; b < R; ++b) acc[bl][b] = f32x4_t{};
 
-  // Without LOOP the launch covers K in one round (chunks <= waves * CPW) and
-  // the body is straight-line code: a loop would make the compiler wait for
-  // the scale loads at its head, before the first weight load.
   for (int base = 0; base < chunks; base += waves * CPW) {
     u32x4_t wq[CPW][RB];
-    u32x4_t xq[CPW][R][8];
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
       const int c = base + wave + waves * i;
@@ -349,45 +376,67 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_ternary_few(
               __builtin_amdgcn_raw_buffer_load_b128(
                   prs, (p_off + static_cast<uint32_t>(bl * 16 * ldp + c * (kChunk / 4))) | oob, 0,
                   0));
+        // The chunk's X rows into this wave's region (LDS address uniform).
+        const uint32_t dst = static_cast<uint32_t>((wave * CPW + i)) * region;
 #pragma unroll
-        for (int b = 0; b < R; ++b)
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-            xq[i][b][j] = __builtin_bit_cast(
-                u32x4_t,
-                __builtin_amdgcn_raw_buffer_load_b128(
-                    xrs, (x_off[b] + static_cast<uint32_t>(c * kChunk * 2 + 16 * j)) | oob, 0, 0));
+        for (int d = 0; d < 8 * R; ++d) {
+          if (2 * d >= mrows) break;
+          const uint32_t row = 2u * d + crow;
+          const uint32_t piece = cslot ^ (row & 15u);
+          const uint32_t kp = static_cast<uint32_t>(c * kChunk) + 8u * piece;
+          const uint32_t poob = (static_cast<uint32_t>(k - 1) - kp) & kOutOfRange;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              xrs, (lds_void_t*)(smem_few + dst + 1024u * d), 16,
+              (row * static_cast<uint32_t>(ldx) * 2u + 2u * kp) | poob, 0, 0, 0);
+        }
       }
     }
+    // Every copy and weight load of the round has landed (the copies are
+    // tracked by the same counter as the loads).
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt, lgkmcnt not waited for
+    asm volatile("" ::: "memory");
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
       if (base + wave + waves * i < chunks) {
+        const uint8_t* xl = smem_few + static_cast<uint32_t>((wave * CPW + i)) * region;
 #pragma unroll
-        for (int bl = 0; bl < RB; ++bl)
+        for (int d = 0; d < 4; ++d) {
+          // The two X operands of code word d (pieces 2 d and 2 d + 1), each
+          // feeding RB blocks of MFMAs.
+          bf16x8_t xo[2][R];
 #pragma unroll
-          for (int d = 0; d < 4; ++d) {
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int b = 0; b < R; ++b)
+              xo[h][b] = *reinterpret_cast<const bf16x8_t*>(
+                  xl + rd_row[b] + 16u * (rd_x[b] ^ static_cast<uint32_t>(2 * d + h)));
+#pragma unroll
+          for (int bl = 0; bl < RB; ++bl) {
             bf16x8_t lo, hi;
             decode16(wq[i][bl][d], lo, hi);
 #pragma unroll
             for (int b = 0; b < R; ++b) {
-              acc[bl][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                  lo, __builtin_bit_cast(bf16x8_t, xq[i][b][2 * d]), acc[bl][b], 0, 0, 0);
-              acc[bl][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                  hi, __builtin_bit_cast(bf16x8_t, xq[i][b][2 * d + 1]), acc[bl][b], 0, 0, 0);
+              acc[bl][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, xo[0][b], acc[bl][b], 0, 0, 0);
+              acc[bl][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, xo[1][b], acc[bl][b], 0, 0, 0);
             }
           }
+        }
       }
     }
     if constexpr (!LOOP) break;
+    // The next round refills the regions: every wave must be done reading.
+    __syncthreads();
   }
 
   if (waves > 1) {
+    // The X regions are free once every wave is past its last read.
+    __syncthreads();
+    f32x4_t* red = reinterpret_cast<f32x4_t*>(smem_few);  // [waves - 1][RB][R][64]
     if (wave > 0) {
 #pragma unroll
       for (int bl = 0; bl < RB; ++bl)
 #pragma unroll
-        for (int b = 0; b < R; ++b)
-          red_few[(((wave - 1) * RB + bl) * R + b) * 64 + lane] = acc[bl][b];
+        for (int b = 0; b < R; ++b) red[(((wave - 1) * RB + bl) * R + b) * 64 + lane] = acc[bl][b];
     }
     __syncthreads();
     if (wave != 0) return;
@@ -395,7 +444,7 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_ternary_few(
 #pragma unroll
       for (int bl = 0; bl < RB; ++bl)
 #pragma unroll
-        for (int b = 0; b < R; ++b) acc[bl][b] += red_few[((w * RB + bl) * R + b) * 64 + lane];
+        for (int b = 0; b < R; ++b) acc[bl][b] += red[((w * RB + bl) * R + b) * 64 + lane];
     }
   }
 
@@ -433,6 +482,7 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_ternary_few(
       }
     }
   }
+#endif  // __HIP_DEVICE_COMPILE__
 }
 
 template <int R, int B, int DEPTH, bool EPI, bool A8>
@@ -494,41 +544,51 @@ hipError_t launch_small_any(const void* x, int64_t m, int64_t k, int64_t ldx, co
 #undef TERN_SMALL
 }
 
+// LDS of a few-token launch: the X regions (waves * CPW chunks of the copied
+// token rows, 512 bytes each), reused for the partial sums of waves 1.. .
+constexpr int64_t kFewLdsMax = 96 * 1024;
+
 template <int RB, int R, int CPW, int MAXW, bool EPI>
 hipError_t launch_few(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const uint8_t* p,
                       int64_t n, int64_t ldp, const float* s, const float* bias, int act_from,
                       uint16_t* y, int64_t ldy, hipStream_t stream) {
   const int64_t blocks = (n + 16 * RB - 1) / (16 * RB);
   const int64_t chunks = (k + kChunk - 1) / kChunk;
+  const int64_t mrows = ((m < 16 * R ? m : 16 * R) + 1) & ~int64_t{1};
+  // Waves: enough for one round over K with CPW chunks each, at most MAXW
+  // and at most what the LDS budget holds.
   int64_t waves = (chunks + CPW - 1) / CPW;
   if (waves > MAXW) waves = MAXW;
+  const int64_t by_lds = kFewLdsMax / (CPW * mrows * 512);
+  if (waves > by_lds) waves = by_lds;
   if (waves < 1) waves = 1;
+  const int64_t x_lds = waves * CPW * mrows * 512;
+  const int64_t red_lds = (waves - 1) * RB * R * 64 * static_cast<int64_t>(sizeof(f32x4_t));
+  const size_t lds = static_cast<size_t>(x_lds > red_lds ? x_lds : red_lds);
   const int y_vec_ok = ((reinterpret_cast<uintptr_t>(y) & 7) == 0) && (ldy % 4 == 0);
-  const size_t lds = static_cast<size_t>(waves - 1) * RB * R * 64 * sizeof(f32x4_t);
   const dim3 grid(static_cast<unsigned>(blocks)), block(static_cast<unsigned>(64 * waves));
   const uint8_t* xb = reinterpret_cast<const uint8_t*>(x);
   if (chunks <= waves * CPW)
-    hipLaunchKernelGGL((gemm_ternary_few<RB, R, CPW, MAXW, EPI, false>), grid, block, lds, stream,
-                       xb, static_cast<int>(m), static_cast<int>(k), static_cast<int>(ldx), p,
+    hipLaunchKernelGGL((gemm_ternary_few<RB, R, CPW, MAXW, EPI, false>), grid, block, lds, stream, xb,
+                       static_cast<int>(m), static_cast<int>(k), static_cast<int>(ldx), p,
                        static_cast<int>(n), static_cast<int>(ldp), s, bias, act_from, y,
                        static_cast<int>(ldy), y_vec_ok);
   else
-    hipLaunchKernelGGL((gemm_ternary_few<RB, R, CPW, MAXW, EPI, true>), grid, block, lds, stream,
-                       xb, static_cast<int>(m), static_cast<int>(k), static_cast<int>(ldx), p,
+    hipLaunchKernelGGL((gemm_ternary_few<RB, R, CPW, MAXW, EPI, true>), grid, block, lds, stream, xb,
+                       static_cast<int>(m), static_cast<int>(k), static_cast<int>(ldx), p,
                        static_cast<int>(n), static_cast<int>(ldp), s, bias, act_from, y,
                        static_cast<int>(ldy), y_vec_ok);
   return hipGetLastError();
 }
 
-// Shape of the few-token launch.  Channel blocks per workgroup: two (each X
-// operand then feeds two blocks of MFMAs, halving the X loads per weight
-// byte) for layers of at least 512 blocks of 16 channels, unless one block per
-// workgroup spreads the blocks more evenly over the CUs (the busiest CU's
-// blocks, RB * ceil(ceil(nb / RB) / 256), are fewer); one block otherwise, so
-// that small layers spread their weight requests over as many CUs as
-// possible.  Waves per workgroup: enough that every chunk of K is in flight
-// in one round, with at most CPW chunks per wave (two when two blocks share
-// the X operands, else one, or two past 16 chunks) and at most 8 or 16 waves.
+// Shape of the few-token launch.  Channel blocks per workgroup (RB): each X
+// operand read from LDS feeds RB blocks of MFMAs, so large layers take six
+// (three with at most four tokens, where the X operands are cheap), keeping
+// at least 128 workgroups; layers of 256 to 1023 blocks take two; smaller
+// ones one, so that their weight requests spread over as many CUs as
+// possible.  One chunk per wave and up to 16 waves, or two chunks per wave
+// where a workgroup would otherwise need more than 16 waves, and with six
+// blocks (up to 8 waves, for the registers of six blocks).
 template <bool EPI>
 hipError_t launch_few_any(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const uint8_t* p,
                           int64_t n, int64_t ldp, const float* s, const float* bias, int act_from,
@@ -536,18 +596,19 @@ hipError_t launch_few_any(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, 
   const int64_t nb = (n + 15) / 16;
   const int64_t chunks = (k + kChunk - 1) / kChunk;
   const bool r2 = m > 16;
-  const bool rb2 = nb >= 512 && 2 * (((nb + 1) / 2 + 255) / 256) <= (nb + 255) / 256;
-  if (rb2) {
-    if (r2)
-      return launch_few<2, 2, 2, 8, EPI>(x, m, k, ldx, p, n, ldp, s, bias, act_from, y, ldy,
-                                         stream);
-    return launch_few<2, 1, 2, 8, EPI>(x, m, k, ldx, p, n, ldp, s, bias, act_from, y, ldy, stream);
-  }
-  if (r2)
-    return launch_few<1, 2, 1, 16, EPI>(x, m, k, ldx, p, n, ldp, s, bias, act_from, y, ldy, stream);
-  if (chunks > 16)
-    return launch_few<1, 1, 2, 16, EPI>(x, m, k, ldx, p, n, ldp, s, bias, act_from, y, ldy, stream);
-  return launch_few<1, 1, 1, 16, EPI>(x, m, k, ldx, p, n, ldp, s, bias, act_from, y, ldy, stream);
+  // (With 32 tokens the LDS budget allows at most six waves of one chunk,
+  // so those launches take the register budget of 8 waves.)
+#define TERN_FEW(RB, CPW, MAXW)                                                                 \
+  return r2 ? launch_few<RB, 2, CPW, 8, EPI>(x, m, k, ldx, p, n, ldp, s, bias, act_from, y,     \
+                                             ldy, stream)                                       \
+            : launch_few<RB, 1, CPW, MAXW, EPI>(x, m, k, ldx, p, n, ldp, s, bias, act_from, y,  \
+                                                ldy, stream);
+  if (nb >= 6 * 128 && m > 4) TERN_FEW(6, 2, 8)
+  if (nb >= 3 * 128) TERN_FEW(3, 1, 16)
+  if (nb >= 256) TERN_FEW(2, 1, 16)
+  if (chunks > 16) TERN_FEW(1, 2, 16)
+  TERN_FEW(1, 1, 16)
+#undef TERN_FEW
 }
 
 }  // namespace
