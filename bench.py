@@ -23,7 +23,8 @@ After the timed steps:
   * "rows": tern_gemm on every layer shape of the five workloads, and
     tern_gemm_ex with the bias and GELU of the layers that have them;
   * "dx_rows": the input gradient (tern_gemm_dx, tern_pack_transposed) on the
-    backward shapes; "a8_rows": the 8-bit-activation layer (tern_quantize_act,
+    backward shapes; "dw_rows": the latent-weight gradient (tern_gemm_dw) on
+    the same shapes; "a8_rows": the 8-bit-activation layer (tern_quantize_act,
     tern_gemm_a8) on the forward shapes against the int8 matrix peak.
 Few-token rows cycle through a pool of distinct packed weights of at least
 --pool-mib MiB, so that each launch streams its weights from HBM.  Table rows
@@ -81,7 +82,7 @@ def parse():
                     help="skip every table after the timed steps")
     ap.add_argument("--rows", default="all",
                     help="comma-separated tables to time after the steps: config3, sweep, fwd, "
-                         "dx, a8, or all")
+                         "dx, dw, a8, or all")
     ap.add_argument("--row-reps", type=int, default=30, help="launches per graph of a table row")
     ap.add_argument("--replays", type=int, default=5, help="timed graph replays per table row")
     ap.add_argument("--pool-mib", type=int, default=1024,
@@ -455,6 +456,37 @@ def time_dx_rows(tern, tern_inputs, torch, dev, reps, replays):
     return rows
 
 
+def time_dw_rows(tern, tern_inputs, torch, dev, reps, replays):
+    """The latent-weight gradient dW = dY^T . X (fp32 [n, k], straight-through
+    reading) on the backward shapes of the DiT and FLUX layers: X [m, k] the
+    forward layer's input (seeded as the forward), dY ~ N(0, 1) [m, n] in
+    bf16; graph-replayed tern_gemm_dw launches."""
+    names = ["dit.up.m2048", "dit.down.m2048", "flux_qkv", "flux_mlp.up", "flux_mlp.down",
+             "single_stream0.in_proj", "single_stream0.out_proj"]
+    layers = {l.name: l for wl in tern_inputs.WORKLOADS.values() for l in wl}
+    rows = []
+    for name in names:
+        layer = layers[name]
+        m, k, n = layer.m, layer.k, layer.n
+        g = torch.Generator(device=dev).manual_seed(layer.seed + 900)
+        x = torch.randn((m, k), generator=g, device=dev).to(torch.bfloat16)
+        dy = torch.randn((m, n), generator=g, device=dev).to(torch.bfloat16)
+        dw = torch.empty((n, k), dtype=torch.float32, device=dev)
+        t, t_min = time_graph(torch, lambda: tern.tern_gemm_dw(dy, x, dw), reps, replays)
+        flops = 2 * m * n * k
+        byts = 2 * m * n + 2 * m * k + 4 * n * k
+        row = {"layer": name + ".dw", "m": m, "n": n, "k": k, "us_per_launch": t * 1e6,
+               "min_us_per_launch": t_min * 1e6, "alg_flops": flops, "alg_bytes": byts,
+               "entry": "tern_gemm_dw"}
+        row.update(roofline_of(flops, byts, t))
+        rows.append(row)
+        print(f"# dw row {name}: {t * 1e6:.1f} us per launch, {row['tflops']:.0f} TFLOP/s, "
+              f"{row['pct_roofline']:.1f}% of roofline", file=sys.stderr, flush=True)
+        del x, dy, dw
+        torch.cuda.empty_cache()
+    return rows
+
+
 def time_a8_rows(tern, tern_inputs, torch, dev, reps, replays, pool_mib):
     """The 8-bit-activation layer on the forward shapes: tern_quantize_act
     (bf16 X -> int8 codes and per-token scales) and tern_gemm_a8, each
@@ -648,7 +680,7 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    tables = {"config3", "sweep", "fwd", "dx", "a8"} if args.rows == "all" else \
+    tables = {"config3", "sweep", "fwd", "dx", "dw", "a8"} if args.rows == "all" else \
         set(args.rows.split(","))
     if args.no_rows:
         tables = set()
@@ -676,35 +708,28 @@ def main():
         bufs.append(b)
     torch.cuda.synchronize()
 
-    def step(events=None):
-        for li, (layer, b) in enumerate(zip(layers, bufs)):
-            if events is not None:
-                events[li][0].record()
+    def step():
+        for layer, b in zip(layers, bufs):
             tern.tern_gemm(b["x"], b["p"], b["s"], b["y"], layer.k)
-            if events is not None:
-                events[li][1].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    # The timed region: K steps between two events, each launch also
-    # bracketed by events on the launch stream (torch's current stream, the
-    # one the binding passes to the library).
-    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in layers]
-          for _ in range(args.steps)]
+    # The timed region: K steps back to back between two events recorded on
+    # the launch stream (torch's current stream, the one the binding passes to
+    # the library); nothing else is queued in between, so the average launch
+    # duration is the region's time over the launches.
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
-    for i in range(args.steps):
-        step(ev[i])
+    for _ in range(args.steps):
+        step()
     end.record()
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(end) / args.steps
-    launch_ms = [ev[i][li][0].elapsed_time(ev[i][li][1]) for i in range(args.steps)
-                 for li in range(len(layers))]
-    gemm_ms = sum(launch_ms) / len(launch_ms)
+    gemm_ms = ms_per_step / len(layers)
 
     flops_step = sum(2 * l.m * l.n * l.k for l in layers)
     value = flops_step / (ms_per_step * 1e-3) / 1e12
@@ -724,7 +749,6 @@ def main():
     roof["traffic"] = load_traffic(args.workload)
     roof["kernel"] = "tern_gemm"
     roof["avg_launch_ms"] = gemm_ms
-    roof["median_launch_ms"] = statistics.median(launch_ms)
     roof["alg_flops_per_launch"] = gemm_flops
     roof["alg_bytes_per_launch"] = gemm_bytes
     roof["gbs"] = gemm_bytes / (gemm_ms * 1e-3) / 1e9
@@ -761,6 +785,11 @@ def main():
     if "dx" in tables:
         print("# timing the input gradient on the backward shapes", file=sys.stderr, flush=True)
         out_tables["dx_rows"] = time_dx_rows(tern, tern_inputs, torch, dev, args.row_reps,
+                                             args.replays)
+    if "dw" in tables:
+        print("# timing the latent-weight gradient on the backward shapes", file=sys.stderr,
+              flush=True)
+        out_tables["dw_rows"] = time_dw_rows(tern, tern_inputs, torch, dev, args.row_reps,
                                              args.replays)
     if "a8" in tables:
         print("# timing the 8-bit-activation layer on the forward shapes", file=sys.stderr,
