@@ -11,7 +11,10 @@ TFLOP/s.  The weights are converted once before the timed region
 conversion entry points are timed on their own afterwards and reported in
 "kernels" with in_step false.  The roofline object describes tern_gemm,
 timed with HIP events on the stream it is launched on; the CPU baseline is the
-oracle timed on this host's cores on a bounded sample of the same step.
+oracle timed on this host's cores on a bounded sample of the same step.  The
+timed steps follow the W warm-up steps and further untimed steps up to
+--warmup-ms of warm-up (default 100 ms): the power management lowers the
+clock for a few milliseconds after matrix work starts, then settles.
 
 After the timed steps:
   * "config3": the FLUX single-stream block set, 38 seeded (in-projection,
@@ -61,7 +64,7 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak
 PEAK_I8_TOPS = 5000.0       # MI355X dense int8 matrix peak
 RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
 CSRC = os.path.join(ROOT, "ternary_weight_quantized_tern_amd", "csrc")
-GEMM_SRCS = [os.path.join(CSRC, f) for f in ("gemm.hip", "gemm_small.hip", "gemm_common.h")]
+GEMM_SRCS = [os.path.join(CSRC, f) for f in ("gemm.hip", "gemm_small.hip", "gemm_ksplit.hip", "gemm_common.h")]
 W_STD = 0.02
 
 
@@ -70,6 +73,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup-ms", type=float, default=100.0,
+                    help="after the warm-up steps, keep running untimed steps until the "
+                         "warm-up has lasted this long (the clock settles under sustained load)")
     ap.add_argument("--workload", default="flux_qkv")
     ap.add_argument("--layers", type=int, default=0,
                     help="use only the first L layers of a multi-layer workload (0 = all)")
@@ -84,6 +90,8 @@ def parse():
                     help="comma-separated tables to time after the steps: config3, sweep, fwd, "
                          "dx, dw, a8, or all")
     ap.add_argument("--row-reps", type=int, default=30, help="launches per graph of a table row")
+    ap.add_argument("--row-filter", default=None,
+                    help="time only the forward rows whose name contains this text")
     ap.add_argument("--replays", type=int, default=5, help="timed graph replays per table row")
     ap.add_argument("--pool-mib", type=int, default=1024,
                     help="packed-weight pool cycled by the few-token rows")
@@ -251,7 +259,7 @@ def weight_pool(tern, torch, dev, n, k, seed, pool_mib):
     return [(ps[i], ss[i]) for i in range(count)], count * per
 
 
-def time_rows(tern, tern_inputs, torch, dev, reps, replays, pool_mib):
+def time_rows(tern, tern_inputs, torch, dev, reps, replays, pool_mib, only=None):
     """The layer on every layer shape of the workloads (layer 0 inputs of each
     shape): tern_gemm, and tern_gemm_ex where the layer's consumer applies a
     bias and the tanh-form GELU (the MLP up-projections; the single-stream
@@ -270,6 +278,8 @@ def time_rows(tern, tern_inputs, torch, dev, reps, replays, pool_mib):
         shapes.append((l.name, l, None))
         if ".up." in l.name:
             shapes.append((l.name + "+bias+gelu", l, (True, 0)))
+    if only:
+        shapes = [sh for sh in shapes if only in sh[0]]
     rows = []
     for name, layer, epi in shapes:
         x, w = tern_inputs.draw_layer(layer)
@@ -715,6 +725,17 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # Sustained-load warm-up: the chip's power management lowers the clock for
+    # a few milliseconds after a burst of matrix work begins, then settles;
+    # untimed steps continue until the warm-up has run --warmup-ms, so that the
+    # timed steps see the settled clock of continuous operation.
+    warm_steps = args.warmup
+    t_warm = time.perf_counter()
+    while (time.perf_counter() - t_warm) * 1e3 < args.warmup_ms:
+        for _ in range(max(1, args.warmup)):
+            step()
+            warm_steps += 1
+        torch.cuda.synchronize()
 
     # The timed region: K steps back to back between two events recorded on
     # the launch stream (torch's current stream, the one the binding passes to
@@ -781,7 +802,7 @@ def main():
     if "fwd" in tables:
         print("# timing tern_gemm on every layer shape", file=sys.stderr, flush=True)
         out_tables["rows"] = time_rows(tern, tern_inputs, torch, dev, args.row_reps,
-                                       args.replays, args.pool_mib)
+                                       args.replays, args.pool_mib, args.row_filter)
     if "dx" in tables:
         print("# timing the input gradient on the backward shapes", file=sys.stderr, flush=True)
         out_tables["dx_rows"] = time_dx_rows(tern, tern_inputs, torch, dev, args.row_reps,
@@ -806,7 +827,8 @@ def main():
     config = {"workload": args.workload, "layers": len(layers), "m": shape.m, "k": shape.k,
               "n": shape.n, "step": "tern_gemm on every layer of the workload",
               "x": f"bf16 {shape.x_dist}", "w": "fp32 N(0, 0.02^2), converted before timing",
-              "seed": shape.seed, "gemm_source_sha256": source_digest(),
+              "seed": shape.seed, "warmup_steps_run": warm_steps,
+              "warmup_ms_min": args.warmup_ms, "gemm_source_sha256": source_digest(),
               "copy_calibration_bytes": calib_bytes}
     out = {
         "metric": METRIC,

@@ -1,0 +1,439 @@
+// Ternary linear layer for layers with few output tiles and a long K:
+//   Y = bf16(f((X . T^T) (.) s + b)), bf16 X, 2-bit packed T.
+//
+// "1.58-bit FLUX" (arXiv 2412.18653) builds a linear kernel for 1.58-bit
+// weights with unquantized activations (section 1 contributions, section
+// 3.2, section 4 limitations), and "TerDiT: Ternary Diffusion Models with
+// Transformers" (abstract) applies the same weights to DiT-style models.  A
+// DiT MLP down-projection at 2048 tokens (X [2048, 4608], output 1152
+// channels) has only 256 output tiles of 64 x 144 but 4608 terms per sum: one
+// workgroup per tile with the whole K in sequence leaves the matrix cores
+// waiting on a long dependent stream, and smaller tiles re-read X many times.
+//
+// Design:
+//  * One workgroup per 64 (tokens) x 144 (channels) tile, four waves that
+//    split K: wave w takes the K steps w, w + 4, w + 8, ... (64 values of K
+//    per step).  Each wave owns the whole tile as 9 x 4 tiles of
+//    v_mfma_f32_16x16x32_bf16 (144 accumulator registers): a decoded weight
+//    operand feeds 4 MFMAs, an X operand 9.
+//  * Every wave streams its own steps through its own three-stage ring in
+//    LDS by LDS-DMA buffer loads (16 bytes per lane; per step X 64 rows x 128
+//    bytes and the packed weights 144 rows x 16 bytes, padded to 192 rows
+//    that read as zero): there is no workgroup barrier in the loop, and a
+//    wave waits only for its own loads.  Each ring stage index is its own
+//    LDS object (holding that stage for all four waves), so the compiler
+//    tracks the DMA writes of the stages apart.
+//  * The data layout in a stage, the operand reads and the decode are those
+//    of gemm.hip: 16-byte X chunks XOR-swizzled by ((row >> 1) & 7), the
+//    weights kept packed and decoded between the MFMAs (15 VALU instructions
+//    per 16 codes, bf16 values 0 / +2 / -2, the factor 2 removed in the
+//    epilogue).  The weights are the MFMA's A operand, X the B operand, so a
+//    lane ends with four consecutive channels of one token.
+//  * After the last step the four partial tiles meet in LDS (the rings are
+//    free by then): wave v writes its sums for the token blocks other than
+//    v, and wave w adds, for token block w, the partials in wave order 0, 1,
+//    2, 3, a fixed order (repeated calls give identical bits).  It then
+//    applies the scale (and the bias and GELU), rounds once to bf16 and
+//    stores its 16 token rows.
+//  * Workgroups are renumbered so that each XCD (one L2 each) takes a
+//    contiguous range of tiles in row-major order: the channel tiles of a
+//    64-token block run on one XCD and share its X rows in that L2.
+#include <type_traits>
+
+#include "gemm_common.h"
+#include "internal.h"
+
+namespace tern {
+namespace {
+
+constexpr int kKsThreads = 256;  // four waves
+constexpr int kKsTM = 4;         // 16-token blocks per tile: one per wave in the reduction
+constexpr int kKsRing = 3;       // stages per wave ring
+
+// s_waitcnt: this wave's vector-memory counter <= N (LDS counter untouched).
+template <int N>
+__device__ inline void ks_wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Slot of the logical 16-byte X chunk c of LDS row r: c ^ ks_xswz(r).  The 16
+// rows that one 16-lane group of an operand read touches (one logical chunk)
+// land in 16 distinct 16-byte bank groups.
+__device__ inline uint32_t ks_xswz(uint32_t r) { return (r >> 1) & 7u; }
+
+template <int TN>
+struct KsCfg {
+  static constexpr int kBM = 16 * kKsTM;            // tokens per tile
+  static constexpr int kBN = 16 * TN;               // channels per tile
+  static constexpr int kXBytes = kBM * 128;         // X of one step: 64 bf16 per row
+  static constexpr int kXInstr = kXBytes / 1024;    // DMA instructions of 8 rows
+  static constexpr int kPInstr = (kBN + 63) / 64;   // DMA instructions of 64 weight rows
+  static constexpr int kPBytes = kPInstr * 1024;
+  static constexpr int kStage = kXBytes + kPBytes;  // one wave's stage
+  static constexpr int kLoads = kXInstr + kPInstr;  // DMA instructions per step
+  static constexpr int kSlots = TN * kKsTM;         // MFMAs per half step
+  static constexpr int kPerArr = kStage / 1024;     // 1 KiB partial tiles per stage object
+  static_assert(3 * TN <= kKsRing * kPerArr, "a wave's partial tiles fit in its ring");
+  static_assert(kLoads + TN + kKsTM <= kSlots, "half B has a slot for every memory operation");
+  static_assert(4 * kKsRing * kStage <= 160 * 1024, "LDS");
+};
+
+// Maps the hardware workgroup id to a logical tile: workgroups are dealt to
+// the 8 XCDs round-robin, and renumbering gives each XCD a contiguous range.
+__device__ inline int ks_logical_tile(int bid, int grid) {
+  const int xcd = bid & 7;
+  const int local = bid >> 3;
+  const int per = grid >> 3;
+  const int rem = grid & 7;
+  return xcd * per + (xcd < rem ? xcd : rem) + local;
+}
+
+__device__ inline uint32_t ks_pack_bf16x2(float a, float b) {
+  typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+
+// y_flags bit 0: Y rows allow 8-byte stores (y 8-byte aligned, ldy % 4 == 0);
+// bit 1: the scale vector (and the bias, if any) are 16-byte aligned.
+template <int TN, bool EPI>
+__global__ __launch_bounds__(kKsThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_ternary_ksplit(const uint8_t* __restrict__ x, int m, int k, int ldx,
+                         const uint8_t* __restrict__ p, int n, int ldp,
+                         const float* __restrict__ s, const float* __restrict__ bias,
+                         int act_from, uint16_t* __restrict__ y, int ldy, int tiles_n,
+                         int y_flags) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  // (The body uses LDS address-space casts that only the device pass accepts.)
+  using C = KsCfg<TN>;
+  constexpr int TM = kKsTM;
+  __shared__ __attribute__((aligned(1024))) uint8_t ks0[4 * C::kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t ks1[4 * C::kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t ks2[4 * C::kStage];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  __builtin_assume(wave >= 0 && wave < 4);
+  const int l16 = lane & 15;
+  const int g = lane >> 4;
+  const uint32_t wbase = static_cast<uint32_t>(wave) * C::kStage;
+
+  const int logical = ks_logical_tile(blockIdx.x, gridDim.x);
+  const int tm = logical / tiles_n;
+  const int m0 = tm * C::kBM;
+  const int n0 = (logical - tm * tiles_n) * C::kBN;
+  const int rows_m = (m - m0) < C::kBM ? (m - m0) : C::kBM;
+  const int rows_n = (n - n0) < C::kBN ? (n - n0) : C::kBN;
+  const int ldxb = ldx * 2;  // X pitch in bytes (< 2^24, checked by the host)
+
+  // Buffer resources rebased at the tile's first row: rows past the last
+  // valid one read as zero; a step past this wave's last is requested
+  // through an empty resource and arrives as zeros.
+  const __amdgpu_buffer_rsrc_t xr =
+      make_rsrc(x + static_cast<int64_t>(m0) * ldxb,
+                static_cast<uint32_t>(static_cast<int64_t>(rows_m - 1) * ldxb + 2 * static_cast<int64_t>(k)));
+  const __amdgpu_buffer_rsrc_t pr =
+      make_rsrc(p + static_cast<int64_t>(n0) * ldp,
+                static_cast<uint32_t>(static_cast<int64_t>(rows_n - 1) * ldp + k / 4));
+  const __amdgpu_buffer_rsrc_t null_rsrc = make_rsrc(x, 0);
+
+  const int stages = k >> 6;
+  const int my_steps = wave < stages ? (stages - 1 - wave) / 4 + 1 : 0;
+
+  // DMA plan of a step.  X load q (q < kXInstr) fills stage bytes [1024 q,
+  // +1024): rows 8 q + lane / 8, slot lane % 8, which holds logical chunk
+  // (lane % 8) ^ ks_xswz(row).  Weight load q fills [kXBytes + 1024 q, +1024):
+  // row 64 q + lane, 16 bytes.
+  uint32_t voff[C::kLoads];
+#pragma unroll
+  for (int q = 0; q < C::kLoads; ++q) {
+    if (q < C::kXInstr) {
+      const uint32_t r = 8u * q + (lane >> 3);
+      voff[q] = r * static_cast<uint32_t>(ldxb) + 16u * ((lane & 7) ^ ks_xswz(r));
+    } else {
+      voff[q] = (64u * (q - C::kXInstr) + lane) * static_cast<uint32_t>(ldp);
+    }
+  }
+#define KS_LOFF(Q) ((Q) < C::kXInstr ? 1024 * (Q) : C::kXBytes + 1024 * ((Q) - C::kXInstr))
+#define KS_DMA(BUF, ST, Q)                                                                 \
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                \
+      (ST) < my_steps ? ((Q) < C::kXInstr ? xr : pr) : null_rsrc,                          \
+      (lds_void_t*)(&BUF[wbase + KS_LOFF(Q)]), 16, voff[Q],                                \
+      ((ST) < my_steps ? wave + 4 * (ST) : 0) * ((Q) < C::kXInstr ? 128 : 16), 0, 0);
+#define KS_ISSUE(BUF, ST) \
+  _Pragma("unroll") for (int q = 0; q < C::kLoads; ++q) KS_DMA(BUF, ST, q)
+
+  // Operand reads.  For the lanes of k-group g, k-block b of a step covers
+  // k = 16 g + 8 b .. 16 g + 8 b + 7: X chunk 2 g + b of token row 16 i +
+  // l16, and codes 8 b .. 8 b + 7 of 32-bit word g of weight row 16 j + l16.
+  const uint32_t xo0 = wbase + static_cast<uint32_t>(l16) * 128u +
+                       ((static_cast<uint32_t>(2 * g) ^ ks_xswz(l16)) << 4);
+  const uint32_t xo1 = wbase + static_cast<uint32_t>(l16) * 128u +
+                       ((static_cast<uint32_t>(2 * g + 1) ^ ks_xswz(l16)) << 4);
+  const uint32_t po = wbase + C::kXBytes + static_cast<uint32_t>(l16) * 16u + 4u * g;
+#define KS_READ_PW(BUF, J) pw[J] = *reinterpret_cast<const uint32_t*>(&BUF[po + (J) * 256]);
+#define KS_READ_XA(BUF, I) xa[I] = *reinterpret_cast<const u32x4_t*>(&BUF[xo0 + (I) * 2048]);
+#define KS_READ_XB(BUF, I) xb[I] = *reinterpret_cast<const u32x4_t*>(&BUF[xo1 + (I) * 2048]);
+
+  f32x4_t acc[TN][TM];
+  uint32_t pw[TN];
+  uint32_t tq[TN][4];
+  u32x4_t wa[TN], wb[TN];
+  u32x4_t xa[TM], xb[TM];
+
+  // Decode of weight word j in units of two VALU instructions.  Lo units 0..3
+  // build tq[j][r] = (pw << (6 - 2r)) & 0xC0C0C0C0 (code 4 b + r in the top
+  // bits of byte b: the high byte of its bf16 value 0 / +2 / -2), lo units 4
+  // and 5 the k-block 0 operand wa[j] (codes 0..7) with byte permutes; the
+  // two hi units build wb[j] (codes 8..15) out of the same tq[j].
+  auto lo_unit = [&](int j, int u) {
+    if (u < 4) {
+      tq[j][u] = (pw[j] << (6 - 2 * u)) & 0xC0C0C0C0u;
+    } else {
+      const uint32_t sel = u == 4 ? 0x040C000Cu : 0x050C010Cu;
+      wa[j][2 * (u - 4)] = __builtin_amdgcn_perm(tq[j][1], tq[j][0], sel);
+      wa[j][2 * (u - 4) + 1] = __builtin_amdgcn_perm(tq[j][3], tq[j][2], sel);
+    }
+  };
+  auto hi_unit = [&](int j, int u) {
+    const uint32_t sel = u == 0 ? 0x060C020Cu : 0x070C030Cu;
+    wb[j][2 * u] = __builtin_amdgcn_perm(tq[j][1], tq[j][0], sel);
+    wb[j][2 * u + 1] = __builtin_amdgcn_perm(tq[j][3], tq[j][2], sel);
+  };
+  auto mfma = [&](f32x4_t& a, const u32x4_t& w, const u32x4_t& xv) {
+    mfma16<false, false>(a, __builtin_bit_cast(bf16x8_t, w), __builtin_bit_cast(bf16x8_t, xv));
+  };
+
+  // The sums start at zero (a wave may have no step at all when K < 256).
+  // The asm statements keep the writes here; the s_nop below keeps two wait
+  // states between them and the first MFMA.
+#pragma unroll
+  for (int j = 0; j < TN; ++j)
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      acc[j][i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      asm volatile("" : "+a"(acc[j][i]));
+    }
+
+  // Half A of a step: k-block 0 (wa x xa); between its MFMAs the X chunks of
+  // k-block 1 are read and the k-block 1 weight operands decoded.  Half B:
+  // k-block 1 (wb x xb); between its MFMAs the next step's weight words and
+  // k-block 0 X chunks are read out of NXT, the step three ahead is requested
+  // into CUR (every read of CUR is complete: its last ones, the xb chunks, feed
+  // the first MFMAs of half B), and the next step's wa is decoded.  Each slot
+  // ends in a scheduling barrier, so this interleave is the issue order; every
+  // VALU-written operand is written several slots before the MFMA that reads it.
+  constexpr int kHiUnits = 2 * TN;
+  constexpr int kLoUnits = 6 * TN;
+  constexpr int kDecodeFrom = 6;  // the first weight words have had a few MFMAs to arrive
+  constexpr int kUps = (kLoUnits + (C::kSlots - kDecodeFrom) - 1) / (C::kSlots - kDecodeFrom);
+  static_assert(kHiUnits + TM <= C::kSlots, "half A has a slot for every hi unit");
+#define KS_STEP(CUR, NXT, ST)                                                              \
+  {                                                                                       \
+    _Pragma("unroll") for (int t = 0; t < C::kSlots; ++t) {                               \
+      mfma(acc[t / TM][t % TM], wa[t / TM], xa[t % TM]);                                  \
+      if (t < TM) {                                                                       \
+        KS_READ_XB(CUR, t)                                                                \
+      } else if (t < TM + kHiUnits) {                                                     \
+        hi_unit((t - TM) / 2, (t - TM) % 2);                                              \
+      }                                                                                   \
+      __builtin_amdgcn_sched_barrier(0);                                                  \
+    }                                                                                     \
+    ks_wait_vmcnt<C::kLoads>();                                                           \
+    _Pragma("unroll") for (int t = 0; t < C::kSlots; ++t) {                               \
+      mfma(acc[t / TM][t % TM], wb[t / TM], xb[t % TM]);                                  \
+      if (t < TN) {                                                                       \
+        KS_READ_PW(NXT, t)                                                                \
+      } else if (t < TN + C::kLoads) {                                                    \
+        KS_DMA(CUR, (ST) + 3, t - TN)                                                     \
+      } else if (t < TN + C::kLoads + TM) {                                               \
+        KS_READ_XA(NXT, t - TN - C::kLoads)                                               \
+      }                                                                                   \
+      if (t >= kDecodeFrom) {                                                             \
+        _Pragma("unroll") for (int u = (t - kDecodeFrom) * kUps;                          \
+                               u < (t - kDecodeFrom + 1) * kUps && u < kLoUnits; ++u)     \
+          lo_unit(u / 6, u % 6);                                                          \
+      }                                                                                   \
+      __builtin_amdgcn_sched_barrier(0);                                                  \
+    }                                                                                     \
+  }
+
+  // Prologue: steps 0, 1, 2 requested, step 0's operands read and decoded.
+  KS_ISSUE(ks0, 0)
+  KS_ISSUE(ks1, 1)
+  KS_ISSUE(ks2, 2)
+  ks_wait_vmcnt<2 * C::kLoads>();
+#pragma unroll
+  for (int j = 0; j < TN; ++j) KS_READ_PW(ks0, j)
+#pragma unroll
+  for (int i = 0; i < TM; ++i) KS_READ_XA(ks0, i)
+#pragma unroll
+  for (int j = 0; j < TN; ++j)
+#pragma unroll
+    for (int u = 0; u < 6; ++u) lo_unit(j, u);
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 1");
+  __builtin_amdgcn_sched_barrier(0);
+
+  // Three steps per iteration, one per ring stage; steps past my_steps run on
+  // zeros (the last iteration may have one or two of them).
+  for (int st = 0; st < my_steps; st += 3) {
+    KS_STEP(ks0, ks1, st)
+    KS_STEP(ks1, ks2, st + 1)
+    KS_STEP(ks2, ks0, st + 2)
+  }
+  ks_wait_vmcnt<0>();  // the requests past the end are in flight too
+#undef KS_STEP
+#undef KS_ISSUE
+#undef KS_DMA
+#undef KS_LOFF
+#undef KS_READ_PW
+#undef KS_READ_XA
+#undef KS_READ_XB
+
+  // Every MFMA result is ready 19 wait states after its MFMA; the asm
+  // statements order every accumulator read after the s_nop block.
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+  for (int j = 0; j < TN; ++j)
+#pragma unroll
+    for (int i = 0; i < TM; ++i) asm volatile("" : "+a"(acc[j][i]));
+  __syncthreads();  // every wave is done with the rings
+
+  // Partial tile (token block i, channel block j) of wave v goes to slot q =
+  // i' TN + j of wave v's part of the rings (i' = the rank of i among the
+  // token blocks other than v), 1 KiB per slot, kPerArr slots per stage
+  // object.
+  auto slot_ptr = [&](int v, int q) -> uint8_t* {
+    const int arr = q / C::kPerArr;
+    uint8_t* base = arr == 0 ? ks0 : (arr == 1 ? ks1 : ks2);
+    return base + v * C::kStage + (q % C::kPerArr) * 1024 + lane * 16;
+  };
+  auto hand_over = [&](auto vc) {
+    constexpr int V = decltype(vc)::value;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      if (i == V) continue;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        *reinterpret_cast<f32x4_t*>(slot_ptr(V, (i - (i > V ? 1 : 0)) * TN + j)) = acc[j][i];
+    }
+  };
+  switch (wave) {
+    case 0: hand_over(std::integral_constant<int, 0>{}); break;
+    case 1: hand_over(std::integral_constant<int, 1>{}); break;
+    case 2: hand_over(std::integral_constant<int, 2>{}); break;
+    default: hand_over(std::integral_constant<int, 3>{}); break;
+  }
+  __syncthreads();
+
+  // Wave w: token block w.  Lane (g, l16) of MFMA tile j holds channels
+  // n0 + 16 j + 4 g + e (e = 0..3) of token m0 + 16 w + l16.  The decode
+  // produced 2 T, so y = bf16(f(acc * (s / 2) + b)); (acc * (s / 2)) rounds
+  // like (acc * s) / 2 except where a result is subnormal.
+  auto finish = [&](auto wc) {
+    constexpr int W = decltype(wc)::value;
+    const int row = m0 + 16 * W + l16;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      f32x4_t v = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int src = 0; src < 4; ++src) {
+        if (src == W)
+          v += acc[j][W];
+        else
+          v += *reinterpret_cast<const f32x4_t*>(slot_ptr(src, (W - (W > src ? 1 : 0)) * TN + j));
+      }
+      const int nb = n0 + 16 * j + 4 * g;
+      const bool whole = nb + 3 < n;
+      f32x4_t sc, bv = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      if (s == nullptr) {
+        sc = f32x4_t{0.5f, 0.5f, 0.5f, 0.5f};
+      } else if (whole && (y_flags & 2)) {
+        sc = *reinterpret_cast<const f32x4_t*>(s + nb) * 0.5f;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sc[e] = nb + e < n ? s[nb + e] * 0.5f : 0.0f;
+      }
+      if constexpr (EPI) {
+        if (bias != nullptr) {
+          if (whole && (y_flags & 2)) {
+            bv = *reinterpret_cast<const f32x4_t*>(bias + nb);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) bv[e] = nb + e < n ? bias[nb + e] : 0.0f;
+          }
+        }
+      }
+      v *= sc;
+      if constexpr (EPI) {
+        v += bv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (nb + e >= act_from) v[e] = gelu_tanh_f32(v[e]);
+      }
+      if (row < m) {
+        uint16_t* yr = y + static_cast<int64_t>(row) * ldy + nb;
+        if (whole && (y_flags & 1)) {
+          u32x2_t o;
+          o[0] = ks_pack_bf16x2(v[0], v[1]);
+          o[1] = ks_pack_bf16x2(v[2], v[3]);
+          *reinterpret_cast<u32x2_t*>(yr) = o;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (nb + e < n) yr[e] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v[e]));
+        }
+      }
+    }
+  };
+  switch (wave) {
+    case 0: finish(std::integral_constant<int, 0>{}); break;
+    case 1: finish(std::integral_constant<int, 1>{}); break;
+    case 2: finish(std::integral_constant<int, 2>{}); break;
+    default: finish(std::integral_constant<int, 3>{}); break;
+  }
+#endif  // __HIP_DEVICE_COMPILE__
+}
+
+template <int TN, bool EPI>
+hipError_t launch_ks(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const uint8_t* p,
+                     int64_t n, int64_t ldp, const float* s, const float* bias, int act_from,
+                     uint16_t* y, int64_t ldy, hipStream_t stream) {
+  using C = KsCfg<TN>;
+  const int tiles_m = static_cast<int>((m + C::kBM - 1) / C::kBM);
+  const int tiles_n = static_cast<int>((n + C::kBN - 1) / C::kBN);
+  const int y_flags =
+      (((reinterpret_cast<uintptr_t>(y) & 7) == 0 && ldy % 4 == 0) ? 1 : 0) |
+      (((reinterpret_cast<uintptr_t>(s) & 15) == 0 &&
+        (reinterpret_cast<uintptr_t>(bias) & 15) == 0) ? 2 : 0);
+  hipLaunchKernelGGL((gemm_ternary_ksplit<TN, EPI>), dim3(static_cast<unsigned>(tiles_m) * tiles_n),
+                     dim3(kKsThreads), 0, stream, reinterpret_cast<const uint8_t*>(x),
+                     static_cast<int>(m), static_cast<int>(k), static_cast<int>(ldx), p,
+                     static_cast<int>(n), static_cast<int>(ldp), s, bias, act_from, y,
+                     static_cast<int>(ldy), tiles_n, y_flags);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool gemm_ksplit_fits(int64_t m, int64_t k, int64_t n) {
+  // Worth it when the 64 x 144 tiles about fill the chip once and every wave
+  // has a few steps: the layers whose larger tiles would leave CUs idle or
+  // whose smaller tiles would re-read X many times.
+  const int64_t tiles = ((m + 63) / 64) * ((n + 143) / 144);
+  return k >= 1024 && tiles >= 192 && tiles <= 320;
+}
+
+hipError_t launch_gemm_ksplit(const uint16_t* x, int64_t m, int64_t k, int64_t ldx,
+                              const uint8_t* p, int64_t n, int64_t ldp, const float* s,
+                              const float* bias, int64_t act_from, uint16_t* y, int64_t ldy,
+                              hipStream_t stream) {
+  const int af = static_cast<int>(act_from);
+  if (bias != nullptr || act_from < n)
+    return launch_ks<9, true>(x, m, k, ldx, p, n, ldp, s, bias, af, y, ldy, stream);
+  return launch_ks<9, false>(x, m, k, ldx, p, n, ldp, s, nullptr, af, y, ldy, stream);
+}
+
+}  // namespace tern

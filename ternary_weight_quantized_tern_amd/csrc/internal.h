@@ -30,6 +30,14 @@ hipError_t launch_gemm(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, con
                        int64_t n, int64_t ldp, const float* s, const float* bias,
                        int64_t act_from, uint16_t* y, int64_t ldy, hipStream_t stream);
 
+// Layers with about one 64 x 144 output tile per CU and k >= 1024: the
+// K-split kernel (called by launch_gemm for m > 32).
+bool gemm_ksplit_fits(int64_t m, int64_t k, int64_t n);
+hipError_t launch_gemm_ksplit(const uint16_t* x, int64_t m, int64_t k, int64_t ldx,
+                              const uint8_t* p, int64_t n, int64_t ldp, const float* s,
+                              const float* bias, int64_t act_from, uint16_t* y, int64_t ldy,
+                              hipStream_t stream);
+
 // m <= 32 (called by launch_gemm).
 hipError_t launch_gemm_small(const uint16_t* x, int64_t m, int64_t k, int64_t ldx,
                              const uint8_t* p, int64_t n, int64_t ldp, const float* s,

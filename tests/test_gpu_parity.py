@@ -195,6 +195,11 @@ GEMM_SHAPES = [
     # few-token kernel, K past one round of its waves (the looping form): one
     # block per workgroup with 16 and 32 tokens, two blocks with 16 and 32
     (5, 8448, 100), (31, 4352, 70), (2, 4352, 21496), (17, 4160, 21480),
+    # K-split kernel (192-320 tiles of 64 x 144, k >= 1024): ragged m and n (n
+    # ending inside a 4-channel group), 17 and 25 K steps over four waves (a
+    # wave with one step more than the others, and steps on zeros after the
+    # last), and a DiT down-projection-like layer with 256 whole tiles
+    (1000, 1088, 1700), (1300, 1600, 2002), (2048, 1024, 1152),
 ]
 
 
@@ -227,6 +232,33 @@ def test_gemm_strided_operands(m):
     xb = tern_inputs.bf16_bits(x)
     y_ref = oracle.oracle_gemm(xb, p_ref, s_ref, k=k)
     assert_within_tolerance(yh[:, :n], y_ref, s_ref, row_norms(xb), "strided")
+
+
+def test_gemm_ksplit_strided_unaligned():
+    # The K-split kernel with padded rows of X (NaN past k) and of the packed
+    # weights (codes that would decode as -2 past k), a scale vector that is
+    # not 16-byte aligned and an output whose rows do not allow 8-byte stores.
+    m, k, n = 1000, 1152, 1700
+    log(f"gemm ksplit strided m={m} k={k} n={n}")
+    x, w = tern_inputs.draw(m, k, n, seed=4242)
+    t_ref, s_ref, p_ref = oracle_weights(w)
+    xg = torch.zeros((m, k + 64), dtype=torch.bfloat16, device=DEV)
+    xg[:, :k] = x.to(DEV)
+    xg[:, k:] = float("nan")
+    pg = torch.zeros((n, k // 4 + 48), dtype=torch.uint8, device=DEV)
+    pg[:, : k // 4] = torch.from_numpy(p_ref).to(DEV)
+    pg[:, k // 4:] = 0xAA
+    sbuf = torch.zeros(n + 1, dtype=torch.float32, device=DEV)
+    sbuf[1:] = torch.from_numpy(s_ref).to(DEV)
+    ybuf = torch.full((m, n + 7), 1.0, dtype=torch.bfloat16, device=DEV)
+    y = ybuf[:, 1:n + 1]
+    tern.tern_gemm(xg[:, :k], pg, sbuf[1:], y, k)
+    torch.cuda.synchronize()
+    yh = bf16_to_f64(ybuf)
+    assert np.all(yh[:, 0] == 1.0) and np.all(yh[:, n + 1:] == 1.0)
+    xb = tern_inputs.bf16_bits(x)
+    y_ref = oracle.oracle_gemm(xb, p_ref, s_ref, k=k)
+    assert_within_tolerance(yh[:, 1:n + 1], y_ref, s_ref, row_norms(xb), "ksplit strided")
 
 
 def test_gemm_k_zero_writes_zeros():
@@ -278,6 +310,7 @@ EPI_SHAPES = [
     (300, 320, 520), (513, 192, 700),                  # 64 x 128 tiles
     (1100, 128, 7500),                                 # 64 x 256 tiles
     (1024, 192, 9216),                                 # 64 x 576 tiles
+    (1000, 1088, 1700),                                # K-split (act_from inside a 4-channel group)
 ]
 
 
@@ -436,7 +469,9 @@ def test_kernel_configurations_agree_bitwise():
     # kernel (whose LDS ring streams across tiles), the one-tile-per-workgroup
     # 144 x 384 kernel, the 64 x 576 kernel and the 64 x 128 kernel (two
     # workgroups per CU) must give bit-identical outputs on the same operands.
-    # A race in any of the LDS pipelines shows up as a mismatch here.
+    # A race in any of the LDS pipelines shows up as a mismatch here.  (The
+    # K-split kernel sums four partial sums and is checked for repeatability
+    # on its own shapes instead.)
     m, k, n = 4608, 3072, 9216
     x, w = tern_inputs.draw(m, k, n, seed=77)
     t, s, p = gpu_quantize_pack(w)

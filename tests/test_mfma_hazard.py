@@ -26,7 +26,7 @@ from ternary_weight_quantized_tern_amd import build as B
 
 WAIT_STATES = 2
 RESULT_WAIT_STATES = 19
-SOURCES = ["gemm.hip", "gemm_small.hip", "dw.hip"]
+SOURCES = ["gemm.hip", "gemm_small.hip", "gemm_ksplit.hip", "dw.hip"]
 
 
 def _asm(src: str, tmp_path) -> str:
