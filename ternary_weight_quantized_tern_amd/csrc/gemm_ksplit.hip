@@ -95,8 +95,7 @@ __device__ inline uint32_t ks_pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
-// y_flags bit 0: Y rows allow 8-byte stores (y 8-byte aligned, ldy % 4 == 0);
-// bit 1: the scale vector (and the bias, if any) are 16-byte aligned.
+// y_flags bit 0: Y rows allow 8-byte stores (y 8-byte aligned, ldy % 4 == 0).
 template <int TN, bool EPI>
 __global__ __launch_bounds__(kKsThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_ternary_ksplit(const uint8_t* __restrict__ x, int m, int k, int ldx,
@@ -216,45 +215,46 @@ void gemm_ternary_ksplit(const uint8_t* __restrict__ x, int m, int k, int ldx,
       asm volatile("" : "+a"(acc[j][i]));
     }
 
-  // Half A of a step: k-block 0 (wa x xa); between its MFMAs the X chunks of
-  // k-block 1 are read and the k-block 1 weight operands decoded.  Half B:
-  // k-block 1 (wb x xb); between its MFMAs the next step's weight words and
-  // k-block 0 X chunks are read out of NXT, the step three ahead is requested
-  // into CUR (every read of CUR is complete: its last ones, the xb chunks, feed
-  // the first MFMAs of half B), and the next step's wa is decoded.  Each slot
-  // ends in a scheduling barrier, so this interleave is the issue order; every
-  // VALU-written operand is written several slots before the MFMA that reads it.
-  constexpr int kHiUnits = 2 * TN;
-  constexpr int kLoUnits = 6 * TN;
-  constexpr int kDecodeFrom = 6;  // the first weight words have had a few MFMAs to arrive
-  constexpr int kUps = (kLoUnits + (C::kSlots - kDecodeFrom) - 1) / (C::kSlots - kDecodeFrom);
-  static_assert(kHiUnits + TM <= C::kSlots, "half A has a slot for every hi unit");
+  // Half A of a step: k-block 0 (wa x xa).  Between its MFMAs: the X chunks
+  // of k-block 1 (xb) are read out of CUR; after the wait for the next step's
+  // loads, its weight words are read out of NXT; the k-block 1 operands wb of
+  // this step are decoded (the two hi units of each word), and the first part
+  // of the next step's decode (the tq vectors of words 0..4) follows each word's
+  // hi units.  Half B: k-block 1 (wb x xb).  Between its MFMAs: the step three
+  // ahead is requested into CUR (every read of CUR is complete: its last ones,
+  // the xb chunks, feed the first MFMAs of this half), the next step's
+  // k-block 0 X chunks are read out of NXT, and the rest of the next step's
+  // decode runs (tq of words 5..8, then every wa).  Each slot ends in a
+  // scheduling barrier, so this interleave is the issue order, with at most
+  // two decode units (four VALU instructions) per MFMA; every VALU-written
+  // operand is written several slots before the MFMA that reads it.
+  static_assert(TM + 2 * TN <= C::kSlots && 16 + 20 <= C::kSlots, "half A slots");
+  static_assert(C::kLoads + TM <= C::kSlots && 16 + 2 * TN <= C::kSlots, "half B slots");
+  static_assert(TN == 9, "the split of the next step's decode assumes nine words");
 #define KS_STEP(CUR, NXT, ST)                                                              \
   {                                                                                       \
     _Pragma("unroll") for (int t = 0; t < C::kSlots; ++t) {                               \
       mfma(acc[t / TM][t % TM], wa[t / TM], xa[t % TM]);                                  \
       if (t < TM) {                                                                       \
         KS_READ_XB(CUR, t)                                                                \
-      } else if (t < TM + kHiUnits) {                                                     \
-        hi_unit((t - TM) / 2, (t - TM) % 2);                                              \
       }                                                                                   \
+      if (t == TM) ks_wait_vmcnt<C::kLoads>();                                            \
+      if (t >= TM && t < TM + TN) {                                                       \
+        KS_READ_PW(NXT, t - TM)                                                           \
+      }                                                                                   \
+      if (t >= TM && t < TM + 2 * TN) hi_unit((t - TM) / 2, (t - TM) % 2);                \
+      if (t >= 16 && t < 16 + 20) lo_unit((t - 16) / 4, (t - 16) % 4);                   \
       __builtin_amdgcn_sched_barrier(0);                                                  \
     }                                                                                     \
-    ks_wait_vmcnt<C::kLoads>();                                                           \
     _Pragma("unroll") for (int t = 0; t < C::kSlots; ++t) {                               \
       mfma(acc[t / TM][t % TM], wb[t / TM], xb[t % TM]);                                  \
-      if (t < TN) {                                                                       \
-        KS_READ_PW(NXT, t)                                                                \
-      } else if (t < TN + C::kLoads) {                                                    \
-        KS_DMA(CUR, (ST) + 3, t - TN)                                                     \
-      } else if (t < TN + C::kLoads + TM) {                                               \
-        KS_READ_XA(NXT, t - TN - C::kLoads)                                               \
+      if (t < C::kLoads) {                                                                \
+        KS_DMA(CUR, (ST) + 3, t)                                                          \
+      } else if (t < C::kLoads + TM) {                                                    \
+        KS_READ_XA(NXT, t - C::kLoads)                                                    \
       }                                                                                   \
-      if (t >= kDecodeFrom) {                                                             \
-        _Pragma("unroll") for (int u = (t - kDecodeFrom) * kUps;                          \
-                               u < (t - kDecodeFrom + 1) * kUps && u < kLoUnits; ++u)     \
-          lo_unit(u / 6, u % 6);                                                          \
-      }                                                                                   \
+      if (t < 16) lo_unit(5 + t / 4, t % 4);                                              \
+      if (t >= 16 && t < 16 + 2 * TN) lo_unit((t - 16) / 2, 4 + (t - 16) % 2);            \
       __builtin_amdgcn_sched_barrier(0);                                                  \
     }                                                                                     \
   }
@@ -284,6 +284,28 @@ void gemm_ternary_ksplit(const uint8_t* __restrict__ x, int m, int k, int ldx,
     KS_STEP(ks2, ks0, st + 2)
   }
   ks_wait_vmcnt<0>();  // the requests past the end are in flight too
+
+  // The channel scales (and biases) of this lane's outputs, requested now so
+  // that they arrive during the hand-over below: buffer loads without a
+  // branch (the range check is per 4-byte word, so channels past n read as
+  // zero).  A null scale vector means unit scales (the input-gradient
+  // product).
+  const bool unit = s == nullptr;
+  const __amdgpu_buffer_rsrc_t srs =
+      make_rsrc(unit ? p : reinterpret_cast<const uint8_t*>(s + n0),
+                unit ? 0u : static_cast<uint32_t>(rows_n * 4));
+  const __amdgpu_buffer_rsrc_t brs =
+      make_rsrc(bias == nullptr ? p : reinterpret_cast<const uint8_t*>(bias + n0),
+                (!EPI || bias == nullptr) ? 0u : static_cast<uint32_t>(rows_n * 4));
+  f32x4_t sc[TN];
+  f32x4_t bv[EPI ? TN : 1];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const uint32_t off = static_cast<uint32_t>((16 * j + 4 * g) * 4);
+    sc[j] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(srs, off, 0, 0));
+    if constexpr (EPI)
+      bv[j] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(brs, off, 0, 0));
+  }
 #undef KS_STEP
 #undef KS_ISSUE
 #undef KS_DMA
@@ -347,28 +369,9 @@ void gemm_ternary_ksplit(const uint8_t* __restrict__ x, int m, int k, int ldx,
       }
       const int nb = n0 + 16 * j + 4 * g;
       const bool whole = nb + 3 < n;
-      f32x4_t sc, bv = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-      if (s == nullptr) {
-        sc = f32x4_t{0.5f, 0.5f, 0.5f, 0.5f};
-      } else if (whole && (y_flags & 2)) {
-        sc = *reinterpret_cast<const f32x4_t*>(s + nb) * 0.5f;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sc[e] = nb + e < n ? s[nb + e] * 0.5f : 0.0f;
-      }
+      v *= unit ? f32x4_t{0.5f, 0.5f, 0.5f, 0.5f} : sc[j] * 0.5f;
       if constexpr (EPI) {
-        if (bias != nullptr) {
-          if (whole && (y_flags & 2)) {
-            bv = *reinterpret_cast<const f32x4_t*>(bias + nb);
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) bv[e] = nb + e < n ? bias[nb + e] : 0.0f;
-          }
-        }
-      }
-      v *= sc;
-      if constexpr (EPI) {
-        v += bv;
+        v += bv[j];
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           if (nb + e >= act_from) v[e] = gelu_tanh_f32(v[e]);
@@ -404,10 +407,7 @@ hipError_t launch_ks(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const
   using C = KsCfg<TN>;
   const int tiles_m = static_cast<int>((m + C::kBM - 1) / C::kBM);
   const int tiles_n = static_cast<int>((n + C::kBN - 1) / C::kBN);
-  const int y_flags =
-      (((reinterpret_cast<uintptr_t>(y) & 7) == 0 && ldy % 4 == 0) ? 1 : 0) |
-      (((reinterpret_cast<uintptr_t>(s) & 15) == 0 &&
-        (reinterpret_cast<uintptr_t>(bias) & 15) == 0) ? 2 : 0);
+  const int y_flags = ((reinterpret_cast<uintptr_t>(y) & 7) == 0 && ldy % 4 == 0) ? 1 : 0;
   hipLaunchKernelGGL((gemm_ternary_ksplit<TN, EPI>), dim3(static_cast<unsigned>(tiles_m) * tiles_n),
                      dim3(kKsThreads), 0, stream, reinterpret_cast<const uint8_t*>(x),
                      static_cast<int>(m), static_cast<int>(k), static_cast<int>(ldx), p,
