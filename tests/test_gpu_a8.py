@@ -186,6 +186,44 @@ def test_gemm_a8_epilogue_big_tiles_sampled():
                    act=tern.TERN_ACT_GELU_TANH, act_from=9000)
 
 
+def test_gemm_a8_persistent_epilogue_sampled():
+    # The FLUX MLP up-projection shape: 1024 tiles of 144 x 384 with K / 128 = 24
+    # steps, a multiple of the four-stage ring, a 16-byte aligned output, scale
+    # and bias: the persistent kernel with the fused epilogue (its staging
+    # through the ring's last stage while the next tile's stages are in flight).
+    # act_from inside a tile and inside a 16-channel block.
+    m, k, n = 4608, 3072, 12288
+    x, w = tern_inputs.draw(m, k, n, seed=81)
+    bias = np.random.default_rng(7).normal(0, 0.5, n).astype(np.float32)
+    act_from = 6002
+    rows = edge_indices(m, tile=144, extra=24, seed=8)
+    cols = np.unique(np.concatenate([edge_indices(n, tile=384, extra=48, seed=9),
+                                     np.arange(act_from - 10, act_from + 10)]))
+    check_layer_a8(x, w, "a8 epi persistent 4608x12288", rows=rows, cols=cols, bias=bias,
+                   act=tern.TERN_ACT_GELU_TANH, act_from=act_from, repeat_check=True)
+
+
+def test_gemm_a8_persistent_and_direct_epilogues_agree_bitwise():
+    # The same fused layer through the persistent kernel (its epilogue staged in
+    # LDS) and, with the output misaligned, through the one-tile-per-workgroup
+    # kernel with the direct epilogue: the same formula on the same int32 sums.
+    m, k, n = 4608, 3072, 12288
+    g = torch.Generator().manual_seed(13)
+    q = torch.randint(-127, 128, (m, k), generator=g, dtype=torch.int8).to(DEV)
+    xs = (torch.rand(m, generator=g) * 0.05).to(DEV)
+    s = (torch.rand(n, generator=g) * 0.05).to(DEV)
+    bias = (torch.randn(n, generator=g) * 0.5).to(DEV)
+    t = tern_inputs.random_ternary(n, k, seed=14).numpy()
+    p8 = torch.from_numpy(oracle.oracle_pack_a8(oracle.oracle_pack(t), k)).to(DEV)
+    y1 = torch.empty((m, n), dtype=torch.bfloat16, device=DEV)
+    tern.tern_gemm_a8(q, xs, p8, s, y1, bias, tern.TERN_ACT_GELU_TANH, 6002)
+    buf = torch.empty(m * n + 1, dtype=torch.bfloat16, device=DEV)
+    y2 = buf[1:].view(m, n)
+    tern.tern_gemm_a8(q, xs, p8, s, y2, bias, tern.TERN_ACT_GELU_TANH, 6002)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
 def test_gemm_a8_one_tile_per_cu_epilogue_sampled():
     # M = 2048, N = 4608: the 64 x 576 tiles, one per CU
     m, k, n = 2048, 1152, 4608
