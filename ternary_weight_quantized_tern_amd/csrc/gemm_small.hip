@@ -280,8 +280,10 @@ __global__ __launch_bounds__(kSmallThreads) void gemm_ternary_small(
 // Chunk slots past the last chunk are skipped (a wave-uniform branch); the
 // 64-code pieces past k, weight rows past n and tokens past m read as zero
 // through the buffer range check.  The partial sums of the W waves meet in
-// LDS (in the X regions, after a barrier); wave 0 applies the fp32 channel
-// scale (and the optional bias and tanh-form GELU) and rounds once to bf16.
+// LDS (in the X regions, after a barrier); channel block bl is finished by
+// wave bl % W, which adds the partials in wave order, applies the fp32
+// channel scale (and the optional bias and tanh-form GELU) and rounds once to
+// bf16, so the blocks' epilogues run in parallel.
 // The MFMAs are the compiler's builtin, so that the compiler sees their
 // latencies (with a chunk slot that may be skipped, it moves accumulators
 // between registers at the join, and only a visible MFMA makes it wait for
@@ -330,10 +332,13 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_ternary_few(
     rd_x[b] = static_cast<uint32_t>(8 * g) ^ static_cast<uint32_t>(rc & 15);
   }
 
-  // The channel scales (and biases) of this lane's outputs, requested before
-  // the weight stream so that they have arrived by the epilogue: buffer loads
-  // without any branch (channels past n, and a null vector, read as zero).
-  // A null scale vector means unit scales (the input-gradient product).
+  // Channel block bl of the output is finished by wave bl % waves.  That wave
+  // requests the block's channel scales (and biases) before the weight
+  // stream, so that they have arrived by the epilogue: one 16-byte buffer load
+  // per block and lane (four consecutive channels), without a per-lane branch
+  // (the range check is per 4-byte word: channels past n, and a null vector,
+  // read as zero).  A null scale vector means unit scales (the input-gradient
+  // product).
   const bool unit = s == nullptr;
   const __amdgpu_buffer_rsrc_t srs =
       make_rsrc(unit ? p : reinterpret_cast<const uint8_t*>(s + n0),
@@ -341,17 +346,19 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_ternary_few(
   const __amdgpu_buffer_rsrc_t brs =
       make_rsrc(bias == nullptr ? p : reinterpret_cast<const uint8_t*>(bias + n0),
                 (!EPI || bias == nullptr) ? 0u : static_cast<uint32_t>(rows * 4));
-  float sraw[RB][4];
-  float braw[EPI ? RB : 1][4];
+  f32x4_t sraw[RB];
+  f32x4_t braw[EPI ? RB : 1];
 #pragma unroll
-  for (int bl = 0; bl < RB; ++bl)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t off = static_cast<uint32_t>((16 * bl + 4 * g + e) * 4);
-      sraw[bl][e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, off, 0, 0));
+  for (int bl = 0; bl < RB; ++bl) {
+    sraw[bl] = f32x4_t{};
+    if constexpr (EPI) braw[bl] = f32x4_t{};
+    if (bl % waves == wave) {
+      const uint32_t off = static_cast<uint32_t>((16 * bl + 4 * g) * 4);
+      sraw[bl] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(srs, off, 0, 0));
       if constexpr (EPI)
-        braw[bl][e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(brs, off, 0, 0));
+        braw[bl] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(brs, off, 0, 0));
     }
+  }
 
   f32x4_t acc[RB][R];
 #pragma unroll
@@ -428,31 +435,43 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_ternary_few(
     __syncthreads();
   }
 
+  // The partial sums of the waves meet in LDS (in the X regions, free once
+  // every wave is past its last read): [waves][RB][R][64] sums of 4 channels.
+  // Wave bl % waves then adds, for channel block bl, the partials in wave
+  // order 0, 1, 2, ... (a fixed order: repeated calls give identical bits),
+  // applies the scale (and bias and GELU) and stores the block's outputs.
+  f32x4_t* red = reinterpret_cast<f32x4_t*>(smem_few);
   if (waves > 1) {
-    // The X regions are free once every wave is past its last read.
     __syncthreads();
-    f32x4_t* red = reinterpret_cast<f32x4_t*>(smem_few);  // [waves - 1][RB][R][64]
-    if (wave > 0) {
 #pragma unroll
-      for (int bl = 0; bl < RB; ++bl)
+    for (int bl = 0; bl < RB; ++bl)
 #pragma unroll
-        for (int b = 0; b < R; ++b) red[(((wave - 1) * RB + bl) * R + b) * 64 + lane] = acc[bl][b];
-    }
+      for (int b = 0; b < R; ++b) red[((wave * RB + bl) * R + b) * 64 + lane] = acc[bl][b];
     __syncthreads();
-    if (wave != 0) return;
-    for (int w = 0; w < waves - 1; ++w) {
-#pragma unroll
-      for (int bl = 0; bl < RB; ++bl)
-#pragma unroll
-        for (int b = 0; b < R; ++b) acc[bl][b] += red[((w * RB + bl) * R + b) * 64 + lane];
-    }
   }
 
 #pragma unroll
   for (int bl = 0; bl < RB; ++bl) {
+    if (bl % waves != wave) continue;
     const int nb = n0 + 16 * bl + 4 * g;  // output channels nb .. nb + 3 of this lane
 #pragma unroll
     for (int b = 0; b < R; ++b) {
+      f32x4_t v = acc[bl][b];
+      if (waves > 1) {
+        // Partials read four at a time ahead of their (ordered) additions.
+        v = red[(bl * R + b) * 64 + lane];
+        for (int w0 = 1; w0 < waves; w0 += 4) {
+          f32x4_t t[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int w = (w0 + i < waves) ? w0 + i : waves - 1;
+            t[i] = red[((w * RB + bl) * R + b) * 64 + lane];
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (w0 + i < waves) v += t[i];
+        }
+      }
       const int token = 16 * b + r16;
       if (token >= m) continue;
       __bf16 o[4];
@@ -460,7 +479,7 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_ternary_few(
       for (int e = 0; e < 4; ++e) {
         // The decode produced 2 T: y = bf16(acc * (s / 2)), which rounds like
         // bf16(fp32(acc / 2 * s)) (the halving is exact).
-        float z = acc[bl][b][e] * ((unit ? 1.0f : sraw[bl][e]) * 0.5f);
+        float z = v[e] * ((unit ? 1.0f : sraw[bl][e]) * 0.5f);
         if constexpr (EPI) {
           z += braw[bl][e];
           if (nb + e >= act_from) z = gelu_tanh_f32(z);
@@ -545,7 +564,7 @@ hipError_t launch_small_any(const void* x, int64_t m, int64_t k, int64_t ldx, co
 }
 
 // LDS of a few-token launch: the X regions (waves * CPW chunks of the copied
-// token rows, 512 bytes each), reused for the partial sums of waves 1.. .
+// token rows, 512 bytes each), reused for the partial sums of every wave.
 constexpr int64_t kFewLdsMax = 96 * 1024;
 
 template <int RB, int R, int CPW, int MAXW, bool EPI>
@@ -563,7 +582,7 @@ hipError_t launch_few(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, cons
   if (waves > by_lds) waves = by_lds;
   if (waves < 1) waves = 1;
   const int64_t x_lds = waves * CPW * mrows * 512;
-  const int64_t red_lds = (waves - 1) * RB * R * 64 * static_cast<int64_t>(sizeof(f32x4_t));
+  const int64_t red_lds = waves * RB * R * 64 * static_cast<int64_t>(sizeof(f32x4_t));
   const size_t lds = static_cast<size_t>(x_lds > red_lds ? x_lds : red_lds);
   const int y_vec_ok = ((reinterpret_cast<uintptr_t>(y) & 7) == 0) && (ldy % 4 == 0);
   const dim3 grid(static_cast<unsigned>(blocks)), block(static_cast<unsigned>(64 * waves));
