@@ -226,7 +226,7 @@ __global__ __launch_bounds__(kDwThreads) void gemm_dw_mfma(
       if (ti + 1 < C::kTI)                                                                       \
         aq[(ti + 1) & 1] = operand(tr(&BUF[offa[ti + 1]]), tr(&BUF[offa[ti + 1] + kXRow4]));     \
       _Pragma("unroll") for (int tj = 0; tj < C::kTJ; ++tj)                                      \
-          mfma16<false, true>(acc[ti][tj], __builtin_bit_cast(bf16x8_t, aq[ti & 1]),             \
+          mfma16<false, false>(acc[ti][tj], __builtin_bit_cast(bf16x8_t, aq[ti & 1]),             \
                               __builtin_bit_cast(bf16x8_t, bq[tj]));                             \
     }                                                                                            \
   }
@@ -249,6 +249,10 @@ __global__ __launch_bounds__(kDwThreads) void gemm_dw_mfma(
     TERN_DW_STEP(lds1, lds0, st + 1)
     TERN_DW_STEP(lds2, lds1, st + 2)
     TERN_DW_STEP(lds3, lds2, st + 3)
+    // The loop's exit and back edge are joins where the compiler may move
+    // accumulators between registers; 24 wait states after the last MFMA
+    // make every result readable there.
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
   }
   dw_wait_vmcnt<0>();  // no DMA may outlive the workgroup's LDS
 #undef TERN_DW_STEP
