@@ -571,11 +571,11 @@ def time_a8_rows(tern, tern_inputs, torch, dev, reps, replays, pool_mib):
     return rows
 
 
-def time_conversion(tern, torch, layer, b, reps=10):
+def time_conversion(tern, torch, layer, b, reps=10, replays=5):
     """The weight-conversion entry points on the first layer's buffers, each
-    `reps` launches back to back between two events, queued behind one layer
-    so that the host's launch latency stays off the GPU's clock.  Not part of
-    the step."""
+    `reps` launches captured in a HIP graph and replayed (the median over
+    `replays`), so that neither the host's launch latency nor a kernel's first
+    launch in the process is on the GPU's clock.  Not part of the step."""
     out = {}
     w16 = b["w"].to(torch.bfloat16)
     n, k = layer.n, layer.k
@@ -591,14 +591,8 @@ def time_conversion(tern, torch, layer, b, reps=10):
         ("tern_unpack", lambda: tern.tern_unpack(b["p"], b["tu"], k), n * kb + n * k),
     ]
     for name, fn, byts in calls:
-        tern.tern_gemm(b["x"], b["p"], b["s"], b["y"], k)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / reps
+        t, _ = time_graph(torch, fn, reps, replays)
+        ms = t * 1e3
         out[name] = {"avg_ms": ms, "alg_bytes": byts, "gbs": byts / (ms * 1e-3) / 1e9,
                      "in_step": False}
     del w16
