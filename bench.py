@@ -20,9 +20,10 @@ After the timed steps:
   * "config3": the FLUX single-stream block set, 38 seeded (in-projection,
     out-projection) pairs, 76 tern_gemm launches back to back, timed as a
     whole sequence and per launch;
-  * "sweep": tern_gemm at M = 1, 8, 16, 32 tokens on the 16.5 MB packed
-    in-projection weight [21504, 3072], cycling a pool of distinct weights
-    larger than every cache, against the HBM peak;
+  * "sweep": tern_gemm at M = 1, 8, 16, 32, 64, 128, 256 tokens on the
+    16.5 MB packed in-projection weight [21504, 3072], cycling a pool of
+    distinct weights larger than every cache (the crossover from the HBM to
+    the matrix-core bound);
   * "rows": tern_gemm on every layer shape of the five workloads, and
     tern_gemm_ex with the bias and GELU of the layers that have them;
   * "dx_rows": the input gradient (tern_gemm_dx, tern_pack_transposed) on the
@@ -328,10 +329,12 @@ def time_rows(tern, tern_inputs, torch, dev, reps, replays, pool_mib, only=None)
     return rows
 
 
-def time_sweep(tern, torch, dev, replays, pool_mib, ms=(1, 8, 16, 32)):
+def time_sweep(tern, torch, dev, replays, pool_mib, ms=(1, 8, 16, 32, 64, 128, 256)):
     """tern_gemm on the FLUX single-stream in-projection weight (N = 21504,
-    K = 3072: 16.5 MB packed) at a few tokens, cycling a pool of at least
-    pool_mib MiB of distinct weights: the weight-streaming (HBM-bound) regime."""
+    K = 3072: 16.5 MB packed) from a few tokens to 256, cycling a pool of at
+    least pool_mib MiB of distinct weights: the weight-streaming (HBM-bound)
+    regime and the crossover to the matrix cores (the arithmetic intensity
+    reaches the ridge near M = 45)."""
     n, k = 21504, 3072
     operands, pool_bytes = weight_pool(tern, torch, dev, n, k, 5000, pool_mib)
     rows = []
@@ -353,7 +356,9 @@ def time_sweep(tern, torch, dev, replays, pool_mib, ms=(1, 8, 16, 32)):
         row.update(roofline_of(flops, byts, t))
         rows.append(row)
         print(f"# sweep m={m}: {t * 1e6:.2f} us per launch, {row['gbs']:.0f} GB/s "
-              f"({row['pct_hbm']:.1f}% of HBM peak)", file=sys.stderr, flush=True)
+              f"({row['pct_hbm']:.1f}% of HBM peak), {row['tflops']:.0f} TFLOP/s, "
+              f"{row['pct_roofline']:.1f}% of roofline ({row['bound']})", file=sys.stderr,
+              flush=True)
     del operands
     torch.cuda.empty_cache()
     return rows

@@ -419,11 +419,12 @@ hipError_t launch_ks(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const
 }  // namespace
 
 bool gemm_ksplit_fits(int64_t m, int64_t k, int64_t n) {
-  // Worth it when the 64 x 144 tiles about fill the chip once and every wave
-  // has a few steps: the layers whose larger tiles would leave CUs idle or
-  // whose smaller tiles would re-read X many times.
+  // Worth it when the 64 x 144 tiles fill the chip at most once (a workgroup
+  // holds 132 KiB of LDS, one per CU, so a 257th tile would start a second
+  // round) and every wave has a few steps: the layers whose larger tiles would
+  // leave CUs idle or whose smaller tiles would re-read X many times.
   const int64_t tiles = ((m + 63) / 64) * ((n + 143) / 144);
-  return k >= 1024 && tiles >= 192 && tiles <= 320;
+  return k >= 1024 && tiles >= 128 && tiles <= 256;
 }
 
 hipError_t launch_gemm_ksplit(const uint16_t* x, int64_t m, int64_t k, int64_t ldx,

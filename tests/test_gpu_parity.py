@@ -195,11 +195,12 @@ GEMM_SHAPES = [
     # few-token kernel, K past one round of its waves (the looping form): one
     # block per workgroup with 16 and 32 tokens, two blocks with 16 and 32
     (5, 8448, 100), (31, 4352, 70), (2, 4352, 21496), (17, 4160, 21480),
-    # K-split kernel (192-320 tiles of 64 x 144, k >= 1024): ragged m and n (n
+    # K-split kernel (128-256 tiles of 64 x 144, k >= 1024): ragged m and n (n
     # ending inside a 4-channel group), 17 and 25 K steps over four waves (a
     # wave with one step more than the others, and steps on zeros after the
-    # last), and a DiT down-projection-like layer with 256 whole tiles
-    (1000, 1088, 1700), (1300, 1600, 2002), (2048, 1024, 1152),
+    # last), a DiT down-projection-like layer with 256 whole tiles, and the
+    # fewest tiles that take it
+    (1000, 1088, 1700), (1300, 1600, 1702), (2048, 1024, 1152), (640, 1216, 1880),
 ]
 
 
