@@ -44,6 +44,9 @@ namespace {
 constexpr int kSmallThreads = 256;
 constexpr int kChunk = 256;           // K per chunk and wave
 constexpr uint32_t kOutOfRange = 0x80000000u;
+// s_waitcnt immediate that waits until at most n vector memory operations
+// are outstanding (expcnt and lgkmcnt not waited for).
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) & 3) << 14; }
 
 // R MFMA row blocks (m <= 16 R), B blocks of 16 output channels per
 // workgroup (every wave covers all of them for its K chunks, so one X operand
@@ -257,8 +260,11 @@ __global__ __launch_bounds__(kSmallThreads) void gemm_ternary_small(
 // and all of K; its W waves (W = blockDim.x / 64, at most 16) split K in
 // 256-wide chunks, wave w taking chunks w, w + W, w + 2 W, ...  In each round
 // a wave issues the loads of its next CPW chunks together (the chunk loop is
-// unrolled), then decodes the codes in registers and accumulates R blocks of
-// 16 tokens.  Without LOOP one round covers all of K.  MAXW bounds the waves
+// unrolled): first the X copies of every chunk, then the weight words chunk
+// by chunk, so that it can decode each chunk's codes as soon as that chunk's
+// words have landed (the loads complete in issue order) while the later
+// ones are still in flight, accumulating R blocks of 16 tokens.  Without
+// LOOP one round covers all of K.  MAXW bounds the waves
 // per workgroup (and so sets the register budget: 128 per lane at 16 waves,
 // 256 at 8).
 //
@@ -277,9 +283,11 @@ __global__ __launch_bounds__(kSmallThreads) void gemm_ternary_small(
 // distinct bank groups; operand lanes of tokens past the copied rows read
 // row 0 (their outputs are not stored).
 //
-// Chunk slots past the last chunk are skipped (a wave-uniform branch); the
-// 64-code pieces past k, weight rows past n and tokens past m read as zero
-// through the buffer range check.  The partial sums of the W waves meet in
+// Chunk slots past the last chunk copy no X and skip their decode (a
+// wave-uniform branch) but still load their weight words, which lie past k
+// and read as zero, so that exactly CPW * RB weight loads follow the copies;
+// the 64-code pieces past k, weight rows past n and tokens past m read as
+// zero through the buffer range check.  The partial sums of the W waves meet in
 // LDS (in the X regions, after a barrier); channel block bl is finished by
 // wave bl % W, which adds the partials in wave order, applies the fp32
 // channel scale (and the optional bias and tanh-form GELU) and rounds once to
@@ -287,10 +295,13 @@ __global__ __launch_bounds__(kSmallThreads) void gemm_ternary_small(
 // The MFMAs are the compiler's builtin, so that the compiler sees their
 // latencies (with a chunk slot that may be skipped, it moves accumulators
 // between registers at the join, and only a visible MFMA makes it wait for
-// the result before such a move).
+// the result before such a move).  p is not declared __restrict__: with it
+// the compiler takes the weight loads for invariant and may move them past
+// the wait for the X copies (or into the conditional decode), where that
+// wait would no longer cover the copies.
 template <int RB, int R, int CPW, int MAXW, bool EPI, bool LOOP>
 __global__ __launch_bounds__(64 * MAXW) void gemm_ternary_few(
-    const uint8_t* __restrict__ x, int m, int k, int ldx, const uint8_t* __restrict__ p, int n,
+    const uint8_t* __restrict__ x, int m, int k, int ldx, const uint8_t* p, int n,
     int ldp, const float* __restrict__ s, const float* __restrict__ bias, int act_from,
     uint16_t* __restrict__ y, int ldy, int y_vec_ok) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -367,23 +378,11 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_ternary_few(
     for (int b = 0; b < R; ++b) acc[bl][b] = f32x4_t{};
 
   for (int base = 0; base < chunks; base += waves * CPW) {
-    u32x4_t wq[CPW][RB];
+    // The X rows of every live slot first ...
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
       const int c = base + wave + waves * i;
       if (c < chunks) {
-        // Codes kc .. kc + 63 of this lane lie past k exactly when kc >= k
-        // (k is a multiple of 64); their offsets get the out-of-range bit.
-        const int kc = c * kChunk + 64 * g;
-        const uint32_t oob = static_cast<uint32_t>(k - 1 - kc) & kOutOfRange;
-#pragma unroll
-        for (int bl = 0; bl < RB; ++bl)
-          wq[i][bl] = __builtin_bit_cast(
-              u32x4_t,
-              __builtin_amdgcn_raw_buffer_load_b128(
-                  prs, (p_off + static_cast<uint32_t>(bl * 16 * ldp + c * (kChunk / 4))) | oob, 0,
-                  0));
-        // The chunk's X rows into this wave's region (LDS address uniform).
         const uint32_t dst = static_cast<uint32_t>((wave * CPW + i)) * region;
 #pragma unroll
         for (int d = 0; d < 8 * R; ++d) {
@@ -398,9 +397,30 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_ternary_few(
         }
       }
     }
-    // Every copy and weight load of the round has landed (the copies are
-    // tracked by the same counter as the loads).
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt, lgkmcnt not waited for
+    asm volatile("" ::: "memory");
+    // ... then the weight words of every slot in slot order (a slot past the
+    // last chunk reads zeros: its codes lie past k), so that CPW * RB loads
+    // always follow the copies.
+    u32x4_t wq[CPW][RB];
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+      const int c = base + wave + waves * i;
+      const int kc = c * kChunk + 64 * g;
+      const uint32_t oob = static_cast<uint32_t>(k - 1 - kc) & kOutOfRange;
+#pragma unroll
+      for (int bl = 0; bl < RB; ++bl)
+        wq[i][bl] = __builtin_bit_cast(
+            u32x4_t,
+            __builtin_amdgcn_raw_buffer_load_b128(
+                prs, (p_off + static_cast<uint32_t>(bl * 16 * ldp + c * (kChunk / 4))) | oob, 0,
+                0));
+    }
+    // The copies have landed once at most CPW * RB loads are outstanding; the
+    // weight words are waited for one by one where they are decoded.  (The
+    // empty asm statements keep the loads before the wait and the LDS reads
+    // after it.)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(CPW * RB));
     asm volatile("" ::: "memory");
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
@@ -431,7 +451,11 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_ternary_few(
       }
     }
     if constexpr (!LOOP) break;
-    // The next round refills the regions: every wave must be done reading.
+    // Only the loads of slots past the last chunk (zeros) can still be in
+    // flight; with none left, the next round's copies and loads need not
+    // wait for them before reusing their registers.  The next round refills
+    // the regions: every wave must be done reading.
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
   }
 
@@ -600,33 +624,45 @@ hipError_t launch_few(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, cons
   return hipGetLastError();
 }
 
-// Shape of the few-token launch.  Channel blocks per workgroup (RB): each X
-// operand read from LDS feeds RB blocks of MFMAs, so large layers take six
-// (three with at most four tokens, where the X operands are cheap), keeping
-// at least 128 workgroups; layers of 256 to 1023 blocks take two; smaller
-// ones one, so that their weight requests spread over as many CUs as
-// possible.  One chunk per wave and up to 16 waves, or two chunks per wave
-// where a workgroup would otherwise need more than 16 waves, and with six
-// blocks (up to 8 waves, for the registers of six blocks).
+// Shape of the few-token launch, from a sweep of the FLUX and DiT layer
+// shapes at 1 to 32 tokens (graph replays over a 1 GiB pool of distinct
+// weights).  Each X operand read from LDS feeds RB channel blocks of MFMAs
+// and every workgroup copies the X rows of all of K, so RB grows with the
+// tokens as long as the layer still gives enough workgroups:
+//  * at most 4 tokens (X is cheap): two blocks and three chunks per wave on
+//    the largest layers (at least 1024 blocks), else one block and two
+//    chunks per wave, up to 16 waves;
+//  * 5 to 16 tokens: six blocks (one chunk per wave, up to 16 waves) with
+//    more than 8 tokens where that still gives 224 workgroups; else three
+//    blocks and three chunks per wave from 384 blocks (up to 8 waves); two
+//    blocks from 256; one block (two chunks per wave past 16 chunks);
+//  * 17 to 32 tokens (two MFMA row blocks, up to 8 waves for the
+//    registers): six blocks from 1344, three from 384, two from 256, else
+//    one, one chunk per wave (two past 16 chunks on one block).
 template <bool EPI>
 hipError_t launch_few_any(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const uint8_t* p,
                           int64_t n, int64_t ldp, const float* s, const float* bias, int act_from,
                           uint16_t* y, int64_t ldy, hipStream_t stream) {
   const int64_t nb = (n + 15) / 16;
   const int64_t chunks = (k + kChunk - 1) / kChunk;
-  const bool r2 = m > 16;
-  // (With 32 tokens the LDS budget allows at most six waves of one chunk,
-  // so those launches take the register budget of 8 waves.)
-#define TERN_FEW(RB, CPW, MAXW)                                                                 \
-  return r2 ? launch_few<RB, 2, CPW, 8, EPI>(x, m, k, ldx, p, n, ldp, s, bias, act_from, y,     \
-                                             ldy, stream)                                       \
-            : launch_few<RB, 1, CPW, MAXW, EPI>(x, m, k, ldx, p, n, ldp, s, bias, act_from, y,  \
-                                                ldy, stream);
-  if (nb >= 6 * 128 && m > 4) TERN_FEW(6, 2, 8)
-  if (nb >= 3 * 128) TERN_FEW(3, 1, 16)
-  if (nb >= 256) TERN_FEW(2, 1, 16)
-  if (chunks > 16) TERN_FEW(1, 2, 16)
-  TERN_FEW(1, 1, 16)
+#define TERN_FEW(RB, R, CPW, MAXW) \
+  return launch_few<RB, R, CPW, MAXW, EPI>(x, m, k, ldx, p, n, ldp, s, bias, act_from, y, ldy, stream);
+  if (m <= 4) {
+    if (nb >= 1024) TERN_FEW(2, 1, 3, 8)
+    TERN_FEW(1, 1, 2, 16)
+  }
+  if (m <= 16) {
+    if (m > 8 && nb >= 6 * 224) TERN_FEW(6, 1, 1, 16)
+    if (nb >= 384) TERN_FEW(3, 1, 3, 8)
+    if (nb >= 256) TERN_FEW(2, 1, 1, 16)
+    if (chunks > 16) TERN_FEW(1, 1, 2, 16)
+    TERN_FEW(1, 1, 1, 16)
+  }
+  if (nb >= 6 * 224) TERN_FEW(6, 2, 1, 8)
+  if (nb >= 384) TERN_FEW(3, 2, 1, 8)
+  if (nb >= 256) TERN_FEW(2, 2, 1, 8)
+  if (chunks > 16) TERN_FEW(1, 2, 2, 8)
+  TERN_FEW(1, 2, 1, 8)
 #undef TERN_FEW
 }
 

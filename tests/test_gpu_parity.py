@@ -186,15 +186,20 @@ GEMM_SHAPES = [
     (32, 256, 16), (33, 576, 40), (8, 64, 4608),
     # 64 x 256 tiles (fewer than 256 big tiles, at least 512 of these): ragged m and n
     (1100, 128, 7500),
-    # few-token path, every channel-block count per workgroup (6, 3, 2) with
-    # one and two MFMA row blocks, each with a ragged last block
+    # few-token path, every launch shape (channel blocks per workgroup 6, 3, 2
+    # and 1; one, two and three chunks per wave) with one and two MFMA row
+    # blocks, each with a ragged last block, and chunk slots past the last
+    # chunk (3 x 1088, 4 x 704, 5 x 320)
     (3, 1088, 24536), (24, 320, 21496), (4, 704, 12280), (20, 576, 9208), (30, 448, 4600),
-    (5, 320, 16400), (20, 256, 16448),
+    (5, 320, 16400), (20, 256, 16448), (12, 576, 21520),
     # 64 x 576 tiles, one per CU; k of 3 pipeline stages (fewer than the ring)
     (1024, 192, 9216),
     # few-token kernel, K past one round of its waves (the looping form): one
-    # block per workgroup with 16 and 32 tokens, two blocks with 16 and 32
-    (5, 8448, 100), (31, 4352, 70), (2, 4352, 21496), (17, 4160, 21480),
+    # block per workgroup with 16 and 32 tokens, six blocks with 16 and 32,
+    # two and three blocks of three chunks per wave (a last round with one
+    # live slot)
+    (5, 8448, 100), (31, 4352, 70), (10, 4352, 21504), (17, 4160, 21512),
+    (3, 6400, 16400), (7, 6400, 6150),
     # K-split kernel (128-256 tiles of 64 x 144, k >= 1024): ragged m and n (n
     # ending inside a 4-channel group), 17 and 25 K steps over four waves (a
     # wave with one step more than the others, and steps on zeros after the
@@ -307,7 +312,8 @@ EPI_VARIANTS = {            # (bias?, act, act_from as a function of n)
 }
 
 EPI_SHAPES = [
-    (8, 256, 100), (24, 320, 210), (3, 1088, 24536),   # few-token kernel (R = 1, 2; B = 6)
+    (8, 256, 100), (24, 320, 210), (3, 1088, 24536),   # few-token kernel: one block, two
+    (5, 320, 16400), (12, 576, 21520),                 # with three chunks a wave, three, six
     (300, 320, 520), (513, 192, 700),                  # 64 x 128 tiles
     (1100, 128, 7500),                                 # 64 x 256 tiles
     (1024, 192, 9216),                                 # 64 x 576 tiles
