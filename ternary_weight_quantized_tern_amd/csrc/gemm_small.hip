@@ -305,6 +305,7 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_ternary_few(
     int ldp, const float* __restrict__ s, const float* __restrict__ bias, int act_from,
     uint16_t* __restrict__ y, int ldy, int y_vec_ok) {
 #if defined(__HIP_DEVICE_COMPILE__)
+  static_assert(CPW * RB < 64, "the wait for the X copies counts CPW * RB loads");
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem_few[];
 
   const int waves = blockDim.x >> 6;

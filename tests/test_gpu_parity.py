@@ -553,6 +553,59 @@ def test_hip_graph_replays_match_eager():
     del graph
 
 
+def test_concurrent_streams_match_serial():
+    # The entry points keep no state between calls (apart from
+    # tern_gemm_dx_static's array), so calls on two streams that overlap on
+    # the GPU must give the bits of the same calls made one after another:
+    # the few-token kernel, the tiled kernels with and without the fused
+    # epilogue, the input and the latent-weight gradients.
+    gen = torch.Generator().manual_seed(91)
+    xs, ws = tern_inputs.draw(8, 3072, 4608, seed=92)
+    xb, wb = tern_inputs.draw(600, 1024, 2048, seed=93)
+    dyb = draw_grad(600, 2048, seed=94)
+    bias = (torch.randn(2048, generator=gen) * 0.1).to(DEV)
+    ps, ss = tern.quantize_pack(ws.to(DEV))
+    pb, sb = tern.quantize_pack(wb.to(DEV))
+    ptb = tern.pack_transposed(pb, 2048, 1024)
+    xsd, xbd, dybd = xs.to(DEV), xb.to(DEV), dyb.to(DEV)
+
+    def outs():
+        return dict(ys=torch.zeros((8, 4608), dtype=torch.bfloat16, device=DEV),
+                    yb=torch.zeros((600, 2048), dtype=torch.bfloat16, device=DEV),
+                    ye=torch.zeros((600, 2048), dtype=torch.bfloat16, device=DEV),
+                    u=torch.zeros((600, 2048), dtype=torch.bfloat16, device=DEV),
+                    dx=torch.zeros((600, 1024), dtype=torch.bfloat16, device=DEV),
+                    dw=torch.zeros((2048, 1024), dtype=torch.float32, device=DEV))
+
+    def work_a(o):
+        tern.tern_gemm(xsd, ps, ss, o["ys"], 3072)
+        tern.tern_gemm_dw(dybd, xbd, o["dw"])
+        tern.tern_gemm_dx(dybd, ptb, sb, o["u"], o["dx"], 1024)
+
+    def work_b(o):
+        tern.tern_gemm(xbd, pb, sb, o["yb"], 1024)
+        tern.tern_gemm_ex(xbd, pb, sb, o["ye"], bias, tern.TERN_ACT_GELU_TANH, 700, 1024)
+
+    serial = outs()
+    work_a(serial)
+    work_b(serial)
+    torch.cuda.synchronize()
+    runs = [outs() for _ in range(4)]
+    sa, sb_ = torch.cuda.Stream(), torch.cuda.Stream()
+    sa.wait_stream(torch.cuda.current_stream())
+    sb_.wait_stream(torch.cuda.current_stream())
+    for o in runs:                                 # launches of the two streams interleave
+        with torch.cuda.stream(sa):
+            work_a(o)
+        with torch.cuda.stream(sb_):
+            work_b(o)
+    torch.cuda.synchronize()
+    for r, o in enumerate(runs):
+        for name in serial:
+            assert torch.equal(o[name].view(torch.uint8), serial[name].view(torch.uint8)), \
+                f"run {r}: {name} differs from the serial result"
+
+
 # ---------------------------------------------------------------------------
 # input gradient: tern_pack_transposed and tern_gemm_dx
 # ---------------------------------------------------------------------------
