@@ -314,6 +314,7 @@ EPI_VARIANTS = {            # (bias?, act, act_from as a function of n)
 EPI_SHAPES = [
     (8, 256, 100), (24, 320, 210), (3, 1088, 24536),   # few-token kernel: one block, two
     (5, 320, 16400), (12, 576, 21520),                 # with three chunks a wave, three, six
+    (5, 8448, 100), (7, 6400, 6150),                   # the looping form: one block, three
     (300, 320, 520), (513, 192, 700),                  # 64 x 128 tiles
     (1100, 128, 7500),                                 # 64 x 256 tiles
     (1024, 192, 9216),                                 # 64 x 576 tiles
