@@ -10,9 +10,9 @@
 // along n.
 //
 // HBM-bound stream: 2 bytes read and 2 written per element (the scales stay
-// in cache).  One thread converts 8 consecutive elements of a row with 16-byte
-// loads and stores where the pointers and pitches allow it, else one at a
-// time; a grid-stride loop covers any m x n.
+// in cache).  A thread converts groups of 8 consecutive elements of a row
+// with 16-byte loads and stores where the pointers and pitches allow it, else
+// one at a time; a grid-stride loop covers any m x n.
 #include <mutex>
 
 #include "internal.h"
@@ -32,6 +32,9 @@ __device__ inline uint32_t to_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
+// Each thread converts G groups of 8 elements, grid-stride apart, with all G
+// loads issued before the first conversion (more bytes in flight per thread).
+template <int G>
 __global__ __launch_bounds__(kThreads) void scale_grad_kernel(const uint16_t* __restrict__ dy,
                                                               int64_t m, int64_t n, int64_t lddy,
                                                               const float* __restrict__ s,
@@ -39,25 +42,38 @@ __global__ __launch_bounds__(kThreads) void scale_grad_kernel(const uint16_t* __
                                                               int64_t ldu, bool vec) {
   const int64_t groups = (n + 7) / 8;  // 8 elements per group
   const int64_t total = m * groups;
-  for (int64_t idx = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; idx < total;
-       idx += static_cast<int64_t>(gridDim.x) * kThreads) {
-    const int64_t row = idx / groups;
-    const int64_t c0 = (idx - row * groups) * 8;
-    const uint16_t* src = dy + row * lddy + c0;
-    uint16_t* dst = u + row * ldu + c0;
-    if (vec && c0 + 8 <= n) {
-      const uint4 v = *reinterpret_cast<const uint4*>(src);
-      const float4 s0 = *reinterpret_cast<const float4*>(s + c0);
-      const float4 s1 = *reinterpret_cast<const float4*>(s + c0 + 4);
-      uint4 o;
-      o.x = to_bf16x2(bf16_to_f32(v.x & 0xFFFFu) * s0.x, bf16_to_f32(v.x >> 16) * s0.y);
-      o.y = to_bf16x2(bf16_to_f32(v.y & 0xFFFFu) * s0.z, bf16_to_f32(v.y >> 16) * s0.w);
-      o.z = to_bf16x2(bf16_to_f32(v.z & 0xFFFFu) * s1.x, bf16_to_f32(v.z >> 16) * s1.y);
-      o.w = to_bf16x2(bf16_to_f32(v.w & 0xFFFFu) * s1.z, bf16_to_f32(v.w >> 16) * s1.w);
-      *reinterpret_cast<uint4*>(dst) = o;
-    } else {
-      for (int e = 0; e < 8 && c0 + e < n; ++e)
-        dst[e] = static_cast<uint16_t>(to_bf16x2(bf16_to_f32(src[e]) * s[c0 + e], 0.0f) & 0xFFFFu);
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+  for (int64_t base = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; base < total;
+       base += stride * G) {
+    uint4 v[G];
+    int64_t row[G], c0[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int64_t idx = base + g * stride;
+      row[g] = idx / groups;
+      c0[g] = (idx - row[g] * groups) * 8;
+      if (idx < total && vec && c0[g] + 8 <= n)
+        v[g] = *reinterpret_cast<const uint4*>(dy + row[g] * lddy + c0[g]);
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      if (base + g * stride >= total) continue;
+      const uint16_t* src = dy + row[g] * lddy + c0[g];
+      uint16_t* dst = u + row[g] * ldu + c0[g];
+      if (vec && c0[g] + 8 <= n) {
+        const float4 s0 = *reinterpret_cast<const float4*>(s + c0[g]);
+        const float4 s1 = *reinterpret_cast<const float4*>(s + c0[g] + 4);
+        uint4 o;
+        o.x = to_bf16x2(bf16_to_f32(v[g].x & 0xFFFFu) * s0.x, bf16_to_f32(v[g].x >> 16) * s0.y);
+        o.y = to_bf16x2(bf16_to_f32(v[g].y & 0xFFFFu) * s0.z, bf16_to_f32(v[g].y >> 16) * s0.w);
+        o.z = to_bf16x2(bf16_to_f32(v[g].z & 0xFFFFu) * s1.x, bf16_to_f32(v[g].z >> 16) * s1.y);
+        o.w = to_bf16x2(bf16_to_f32(v[g].w & 0xFFFFu) * s1.z, bf16_to_f32(v[g].w >> 16) * s1.w);
+        *reinterpret_cast<uint4*>(dst) = o;
+      } else {
+        for (int e = 0; e < 8 && c0[g] + e < n; ++e)
+          dst[e] = static_cast<uint16_t>(to_bf16x2(bf16_to_f32(src[e]) * s[c0[g] + e], 0.0f) &
+                                         0xFFFFu);
+      }
     }
   }
 }
@@ -107,11 +123,14 @@ hipError_t launch_scale_grad(const uint16_t* dy, int64_t m, int64_t n, int64_t l
   const bool vec = reinterpret_cast<uintptr_t>(dy) % 16 == 0 && lddy % 8 == 0 &&
                    reinterpret_cast<uintptr_t>(u) % 16 == 0 && ldu % 8 == 0 &&
                    reinterpret_cast<uintptr_t>(s) % 16 == 0;
-  int64_t blocks = (m * ((n + 7) / 8) + kThreads - 1) / kThreads;
+  // Two groups per thread: 5 % faster than one on the DiT up-projection's
+  // backward (2048 x 4608), the same on the FLUX shapes.
+  constexpr int kGroups = 2;
+  int64_t blocks = (m * ((n + 7) / 8) + kThreads * kGroups - 1) / (kThreads * kGroups);
   if (blocks > kMaxBlocks) blocks = kMaxBlocks;
   if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(scale_grad_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
-                     stream, dy, m, n, lddy, s, u, ldu, vec);
+  hipLaunchKernelGGL(scale_grad_kernel<kGroups>, dim3(static_cast<unsigned>(blocks)),
+                     dim3(kThreads), 0, stream, dy, m, n, lddy, s, u, ldu, vec);
   return hipGetLastError();
 }
 
