@@ -32,7 +32,9 @@ After the timed steps:
     tern_gemm_a8) on the forward shapes against the int8 matrix peak.
 Few-token rows cycle through a pool of distinct packed weights of at least
 --pool-mib MiB, so that each launch streams its weights from HBM.  Table rows
-are graph-replayed launches; each figure is the median over several replays.
+are graph-replayed launches; each figure is the median over several replays,
+taken after the row's graph has been replayed for --row-warmup-ms (default
+100 ms), so that each row, like the timed steps, runs at the settled clock.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload flux_qkv]
 
@@ -94,6 +96,8 @@ def parse():
     ap.add_argument("--row-filter", default=None,
                     help="time only the forward rows whose name contains this text")
     ap.add_argument("--replays", type=int, default=5, help="timed graph replays per table row")
+    ap.add_argument("--row-warmup-ms", type=float, default=100.0,
+                    help="untimed replays of each table row's graph before its timed ones")
     ap.add_argument("--pool-mib", type=int, default=1024,
                     help="packed-weight pool cycled by the few-token rows")
     ap.add_argument("--summarize-traffic", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "BENCH_JSON"),
@@ -204,11 +208,14 @@ def roofline_of(flops, byts, seconds):
             "pct_roofline": 100 * t_ideal / seconds}
 
 
+ROW_WARMUP_S = 0.1  # set from --row-warmup-ms
+
+
 def time_graph(torch, fn, launches, replays):
     """Seconds per call of fn() with `launches` calls captured in one HIP graph
-    and replayed back to back (after one eager warm-up call on a side stream
-    and one untimed replay): the median and the minimum over `replays` timed
-    replays."""
+    and replayed back to back (after one eager warm-up call on a side stream,
+    then untimed replays for ROW_WARMUP_S seconds, at least one): the median
+    and the minimum over `replays` timed replays."""
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -218,8 +225,12 @@ def time_graph(torch, fn, launches, replays):
     with torch.cuda.graph(graph):
         for _ in range(launches):
             fn()
+    t0 = time.perf_counter()
     graph.replay()
     torch.cuda.synchronize()
+    while time.perf_counter() - t0 < ROW_WARMUP_S:
+        graph.replay()
+        torch.cuda.synchronize()
     per = []
     for _ in range(max(1, replays)):
         g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -671,7 +682,9 @@ def summarize_traffic(fetch_dir, write_dir, bench_json, workload, path=None):
 
 
 def main():
+    global ROW_WARMUP_S
     args = parse()
+    ROW_WARMUP_S = args.row_warmup_ms * 1e-3
     if args.summarize_traffic:
         summarize_traffic(*args.summarize_traffic, args.workload, args.traffic_out)
         return
@@ -827,7 +840,8 @@ def main():
               "n": shape.n, "step": "tern_gemm on every layer of the workload",
               "x": f"bf16 {shape.x_dist}", "w": "fp32 N(0, 0.02^2), converted before timing",
               "seed": shape.seed, "warmup_steps_run": warm_steps,
-              "warmup_ms_min": args.warmup_ms, "gemm_source_sha256": source_digest(),
+              "warmup_ms_min": args.warmup_ms, "row_warmup_ms": args.row_warmup_ms,
+              "gemm_source_sha256": source_digest(),
               "copy_calibration_bytes": calib_bytes}
     out = {
         "metric": METRIC,
