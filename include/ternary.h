@@ -27,7 +27,9 @@
  *    pointers, leading dimensions, alignment.  A call whose output is empty (a zero size) is a
  *    no-op that returns TERN_OK without touching any pointer.
  *  - A kernel launch that the HIP runtime rejects returns TERN_ERR_HIP.
- *  - Outputs must not overlap inputs.  Calls are re-entrant and thread-safe.
+ *  - Outputs must not overlap inputs.  Calls are re-entrant and thread-safe,
+ *    and calls on different streams may run at the same time on one GPU: no
+ *    state is shared between calls (tern_gemm_dx_static's array aside).
  *  - Inputs are assumed finite; results for NaN or infinite inputs are
  *    unspecified.
  */
