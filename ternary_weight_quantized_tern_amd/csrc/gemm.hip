@@ -822,9 +822,10 @@ hipError_t launch_big(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, cons
   if (m % 64 == 0 && n % 576 == 0 && tiles(64, 576) == kPersistentGrid)
     return launch_tiles<64, 576, 1, 4, 1, EPI>(x, m, k, ldx, nullptr, p, n, ldp, s, bias,
                                                act_from, y, ldy, stream);
-  // Layers with about one 64 x 144 tile per CU and a long K (the DiT MLP
-  // down-projection at 2048 tokens): the workgroup's four waves split K
-  // (gemm_ksplit.hip).
+  // Layers that 64-token tiles of 96, 144 or 192 channels cut into at most
+  // one tile per CU, with K of at least 2048 (the DiT MLP down-projection at
+  // 2048 tokens, 64 to 256 tokens on a wide weight): the workgroup's four
+  // waves split K (gemm_ksplit.hip).
   if (gemm_ksplit_fits(m, k, n))
     return launch_gemm_ksplit(x, m, k, ldx, p, n, ldp, s, bias, act_from, y, ldy, stream);
   if (tiles(64, 256) >= 2 * kPersistentGrid)

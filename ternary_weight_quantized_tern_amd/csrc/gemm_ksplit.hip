@@ -6,21 +6,24 @@
 // 3.2, section 4 limitations), and "TerDiT: Ternary Diffusion Models with
 // Transformers" (abstract) applies the same weights to DiT-style models.  A
 // DiT MLP down-projection at 2048 tokens (X [2048, 4608], output 1152
-// channels) has only 256 output tiles of 64 x 144 but 4608 terms per sum: one
-// workgroup per tile with the whole K in sequence leaves the matrix cores
-// waiting on a long dependent stream, and smaller tiles re-read X many times.
+// channels) has only 256 output tiles of 64 x 144 but 4608 terms per sum, and
+// a layer of 64 to 256 tokens on a wide weight (the single-stream
+// in-projection's 21504 x 3072) few tiles of any size: one workgroup per tile
+// with the whole K in sequence leaves the matrix cores waiting on a long
+// dependent stream, and smaller tiles re-read X many times.
 //
 // Design:
-//  * One workgroup per 64 (tokens) x 144 (channels) tile, four waves that
+//  * One workgroup per 64 (tokens) x 16 TN (channels) tile, TN = 6, 9 or 12
+//    (the narrowest whose tiles fill the chip at most once), four waves that
 //    split K: wave w takes the K steps w, w + 4, w + 8, ... (64 values of K
-//    per step).  Each wave owns the whole tile as 9 x 4 tiles of
-//    v_mfma_f32_16x16x32_bf16 (144 accumulator registers): a decoded weight
-//    operand feeds 4 MFMAs, an X operand 9.
+//    per step).  Each wave owns the whole tile as TN x 4 tiles of
+//    v_mfma_f32_16x16x32_bf16 (16 TN accumulator registers): a decoded weight
+//    operand feeds 4 MFMAs, an X operand TN.
 //  * Every wave streams its own steps through its own three-stage ring in
 //    LDS by LDS-DMA buffer loads (16 bytes per lane; per step X 64 rows x 128
-//    bytes and the packed weights 144 rows x 16 bytes, padded to 192 rows
-//    that read as zero): there is no workgroup barrier in the loop, and a
-//    wave waits only for its own loads.  Each ring stage index is its own
+//    bytes and the packed weights 16 TN rows x 16 bytes, padded to a multiple
+//    of 64 rows that read as zero): there is no workgroup barrier in the
+//    loop, and a wave waits only for its own loads.  Each ring stage index is its own
 //    LDS object (holding that stage for all four waves), so the compiler
 //    tracks the DMA writes of the stages apart.
 //  * The data layout in a stage, the operand reads and the decode are those
@@ -36,8 +39,11 @@
 //    applies the scale (and the bias and GELU), rounds once to bf16 and
 //    stores its 16 token rows.
 //  * Workgroups are renumbered so that each XCD (one L2 each) takes a
-//    contiguous range of tiles in row-major order: the channel tiles of a
-//    64-token block run on one XCD and share its X rows in that L2.
+//    contiguous range of tiles, in token-major order (the channel tiles of a
+//    64-token block run on one XCD and share its X rows in that L2) or, where
+//    that fetches fewer bytes (the weights outweigh X: a few token blocks on a
+//    wide weight), channel-major (the token blocks of a channel tile share
+//    its weight rows).
 #include <type_traits>
 
 #include "gemm_common.h"
@@ -69,11 +75,19 @@ struct KsCfg {
   static constexpr int kXBytes = kBM * 128;         // X of one step: 64 bf16 per row
   static constexpr int kXInstr = kXBytes / 1024;    // DMA instructions of 8 rows
   static constexpr int kPInstr = (kBN + 63) / 64;   // DMA instructions of 64 weight rows
-  static constexpr int kPBytes = kPInstr * 1024;
+  // Weight bytes of a stage: the DMA rows, and at least TN - 8 KiB, so that a
+  // wave's three stages hold its 3 TN partial tiles of 1 KiB in the hand-over.
+  static constexpr int kPBytes = (kPInstr > TN - 8 ? kPInstr : TN - 8) * 1024;
   static constexpr int kStage = kXBytes + kPBytes;  // one wave's stage
   static constexpr int kLoads = kXInstr + kPInstr;  // DMA instructions per step
   static constexpr int kSlots = TN * kKsTM;         // MFMAs per half step
   static constexpr int kPerArr = kStage / 1024;     // 1 KiB partial tiles per stage object
+  // Where the next step's decode runs: the tq vectors of words 0 .. kTqA - 1
+  // in half A from slot kTqA0 on, those of the other words at the start of
+  // half B, then the wa operands of every word from slot kWaB0 of half B.
+  static constexpr int kTqA = TN == 6 ? 4 : (TN == 9 ? 5 : 8);
+  static constexpr int kTqA0 = TN == 6 ? 8 : 16;
+  static constexpr int kWaB0 = 4 * (TN - kTqA);
   static_assert(3 * TN <= kKsRing * kPerArr, "a wave's partial tiles fit in its ring");
   static_assert(kLoads + TN + kKsTM <= kSlots, "half B has a slot for every memory operation");
   static_assert(4 * kKsRing * kStage <= 160 * 1024, "LDS");
@@ -95,7 +109,9 @@ __device__ inline uint32_t ks_pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
-// y_flags bit 0: Y rows allow 8-byte stores (y 8-byte aligned, ldy % 4 == 0).
+// y_flags bit 0: Y rows allow 8-byte stores (y 8-byte aligned, ldy % 4 == 0);
+// bit 1: the logical tiles run in channel-major order (tile t covers channel
+// tile t / tiles_m and token block t % tiles_m) instead of token-major.
 template <int TN, bool EPI>
 __global__ __launch_bounds__(kKsThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_ternary_ksplit(const uint8_t* __restrict__ x, int m, int k, int ldx,
@@ -119,9 +135,17 @@ void gemm_ternary_ksplit(const uint8_t* __restrict__ x, int m, int k, int ldx,
   const uint32_t wbase = static_cast<uint32_t>(wave) * C::kStage;
 
   const int logical = ks_logical_tile(blockIdx.x, gridDim.x);
-  const int tm = logical / tiles_n;
+  const int tiles_m = (m + C::kBM - 1) / C::kBM;
+  int tm, tn;
+  if (y_flags & 2) {
+    tn = logical / tiles_m;
+    tm = logical - tn * tiles_m;
+  } else {
+    tm = logical / tiles_n;
+    tn = logical - tm * tiles_n;
+  }
   const int m0 = tm * C::kBM;
-  const int n0 = (logical - tm * tiles_n) * C::kBN;
+  const int n0 = tn * C::kBN;
   const int rows_m = (m - m0) < C::kBM ? (m - m0) : C::kBM;
   const int rows_n = (n - n0) < C::kBN ? (n - n0) : C::kBN;
   const int ldxb = ldx * 2;  // X pitch in bytes (< 2^24, checked by the host)
@@ -219,18 +243,18 @@ void gemm_ternary_ksplit(const uint8_t* __restrict__ x, int m, int k, int ldx,
   // of k-block 1 (xb) are read out of CUR; after the wait for the next step's
   // loads, its weight words are read out of NXT; the k-block 1 operands wb of
   // this step are decoded (the two hi units of each word), and the first part
-  // of the next step's decode (the tq vectors of words 0..4) follows each word's
-  // hi units.  Half B: k-block 1 (wb x xb).  Between its MFMAs: the step three
+  // of the next step's decode (the tq vectors of words 0 .. kTqA - 1) follows
+  // each word's hi units.  Half B: k-block 1 (wb x xb).  Between its MFMAs: the step three
   // ahead is requested into CUR (every read of CUR is complete: its last ones,
   // the xb chunks, feed the first MFMAs of this half), the next step's
   // k-block 0 X chunks are read out of NXT, and the rest of the next step's
-  // decode runs (tq of words 5..8, then every wa).  Each slot ends in a
+  // decode runs (tq of the other words, then every wa).  Each slot ends in a
   // scheduling barrier, so this interleave is the issue order, with at most
   // two decode units (four VALU instructions) per MFMA; every VALU-written
   // operand is written several slots before the MFMA that reads it.
-  static_assert(TM + 2 * TN <= C::kSlots && 16 + 20 <= C::kSlots, "half A slots");
-  static_assert(C::kLoads + TM <= C::kSlots && 16 + 2 * TN <= C::kSlots, "half B slots");
-  static_assert(TN == 9, "the split of the next step's decode assumes nine words");
+  static_assert(TM + 2 * TN <= C::kSlots && C::kTqA0 + 4 * C::kTqA <= C::kSlots, "half A slots");
+  static_assert(C::kTqA0 >= TM + 2, "a word's tq vectors follow its hi units");
+  static_assert(C::kLoads + TM <= C::kSlots && C::kWaB0 + 2 * TN <= C::kSlots, "half B slots");
 #define KS_STEP(CUR, NXT, ST)                                                              \
   {                                                                                       \
     _Pragma("unroll") for (int t = 0; t < C::kSlots; ++t) {                               \
@@ -243,7 +267,8 @@ void gemm_ternary_ksplit(const uint8_t* __restrict__ x, int m, int k, int ldx,
         KS_READ_PW(NXT, t - TM)                                                           \
       }                                                                                   \
       if (t >= TM && t < TM + 2 * TN) hi_unit((t - TM) / 2, (t - TM) % 2);                \
-      if (t >= 16 && t < 16 + 20) lo_unit((t - 16) / 4, (t - 16) % 4);                   \
+      if (t >= C::kTqA0 && t < C::kTqA0 + 4 * C::kTqA)                                    \
+        lo_unit((t - C::kTqA0) / 4, (t - C::kTqA0) % 4);                                  \
       __builtin_amdgcn_sched_barrier(0);                                                  \
     }                                                                                     \
     _Pragma("unroll") for (int t = 0; t < C::kSlots; ++t) {                               \
@@ -253,8 +278,9 @@ void gemm_ternary_ksplit(const uint8_t* __restrict__ x, int m, int k, int ldx,
       } else if (t < C::kLoads + TM) {                                                    \
         KS_READ_XA(NXT, t - C::kLoads)                                                    \
       }                                                                                   \
-      if (t < 16) lo_unit(5 + t / 4, t % 4);                                              \
-      if (t >= 16 && t < 16 + 2 * TN) lo_unit((t - 16) / 2, 4 + (t - 16) % 2);            \
+      if (t < C::kWaB0) lo_unit(C::kTqA + t / 4, t % 4);                                  \
+      if (t >= C::kWaB0 && t < C::kWaB0 + 2 * TN)                                         \
+        lo_unit((t - C::kWaB0) / 2, 4 + (t - C::kWaB0) % 2);                              \
       __builtin_amdgcn_sched_barrier(0);                                                  \
     }                                                                                     \
   }
@@ -400,6 +426,31 @@ void gemm_ternary_ksplit(const uint8_t* __restrict__ x, int m, int k, int ldx,
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
+// Bytes that the 8 XCDs fetch when the logical tiles are dealt to them in
+// contiguous ranges (ks_logical_tile), in token-major or channel-major
+// (col) order, each XCD reading the X rows of every token block and the
+// weight rows of every channel tile in its range once into its own L2.
+int64_t ks_fetch_estimate(int tiles_m, int tiles_n, int64_t x_block, int64_t w_block, bool col) {
+  const int grid = tiles_m * tiles_n;
+  const int minor = col ? tiles_m : tiles_n;
+  int64_t total = 0;
+  for (int xcd = 0; xcd < 8; ++xcd) {
+    const int lo = xcd * (grid / 8) + (xcd < grid % 8 ? xcd : grid % 8);
+    const int hi = lo + grid / 8 + (xcd < grid % 8 ? 1 : 0);
+    if (hi <= lo) continue;
+    const int majors = (hi - 1) / minor - lo / minor + 1;
+    int minors = minor;
+    if (majors == 1) {
+      minors = hi - lo;
+    } else if (majors == 2) {
+      const int span = (minor - lo % minor) + ((hi - 1) % minor + 1);
+      minors = span < minor ? span : minor;
+    }
+    total += (col ? minors : majors) * x_block + (col ? majors : minors) * w_block;
+  }
+  return total;
+}
+
 template <int TN, bool EPI>
 hipError_t launch_ks(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const uint8_t* p,
                      int64_t n, int64_t ldp, const float* s, const float* bias, int act_from,
@@ -407,7 +458,15 @@ hipError_t launch_ks(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const
   using C = KsCfg<TN>;
   const int tiles_m = static_cast<int>((m + C::kBM - 1) / C::kBM);
   const int tiles_n = static_cast<int>((n + C::kBN - 1) / C::kBN);
-  const int y_flags = ((reinterpret_cast<uintptr_t>(y) & 7) == 0 && ldy % 4 == 0) ? 1 : 0;
+  // Channel-major order where it fetches fewer bytes: layers whose weights
+  // outweigh their X (a few token blocks on a wide weight), so that the token
+  // blocks of a channel tile share its weight rows in one L2.
+  const int64_t x_block = int64_t{C::kBM} * k * 2;
+  const int64_t w_block = int64_t{C::kBN} * k / 4;
+  const bool col = ks_fetch_estimate(tiles_m, tiles_n, x_block, w_block, true) <
+                   ks_fetch_estimate(tiles_m, tiles_n, x_block, w_block, false);
+  const int y_flags = (((reinterpret_cast<uintptr_t>(y) & 7) == 0 && ldy % 4 == 0) ? 1 : 0) |
+                      (col ? 2 : 0);
   hipLaunchKernelGGL((gemm_ternary_ksplit<TN, EPI>), dim3(static_cast<unsigned>(tiles_m) * tiles_n),
                      dim3(kKsThreads), 0, stream, reinterpret_cast<const uint8_t*>(x),
                      static_cast<int>(m), static_cast<int>(k), static_cast<int>(ldx), p,
@@ -416,15 +475,27 @@ hipError_t launch_ks(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const
   return hipGetLastError();
 }
 
+// Channels per tile (16 TN) for a layer, or 0 when the K-split kernel does
+// not take it: the narrowest of 96, 144 and 192 channels whose 64-token tiles
+// fill the chip at most once (a workgroup holds 120-144 KiB of LDS, so one
+// runs per CU and a 257th tile would start a second round; a CU's work grows
+// with the tile width), for K of at least 32 steps (with 4 steps a wave the
+// three-stage prologue and the hand-over outweigh the split: 14.4 against
+// 12.3 us with 64 x 128 tiles at M = 1024, K = 1024, N = 3072).  These are
+// the layers whose larger tiles would leave CUs idle or whose 64 x 128
+// tiles, K in sequence, leave each CU a long dependent stream.
+int ksplit_channels_per_tile(int64_t m, int64_t k, int64_t n) {
+  if (k < 2048) return 0;
+  const int64_t tiles_m = (m + 63) / 64;
+  for (const int tn : {6, 9, 12})
+    if (tiles_m * ((n + 16 * tn - 1) / (16 * tn)) <= 256) return 16 * tn;
+  return 0;
+}
+
 }  // namespace
 
 bool gemm_ksplit_fits(int64_t m, int64_t k, int64_t n) {
-  // Worth it when the 64 x 144 tiles fill the chip at most once (a workgroup
-  // holds 132 KiB of LDS, one per CU, so a 257th tile would start a second
-  // round) and every wave has a few steps: the layers whose larger tiles would
-  // leave CUs idle or whose smaller tiles would re-read X many times.
-  const int64_t tiles = ((m + 63) / 64) * ((n + 143) / 144);
-  return k >= 1024 && tiles >= 128 && tiles <= 256;
+  return ksplit_channels_per_tile(m, k, n) != 0;
 }
 
 hipError_t launch_gemm_ksplit(const uint16_t* x, int64_t m, int64_t k, int64_t ldx,
@@ -432,9 +503,20 @@ hipError_t launch_gemm_ksplit(const uint16_t* x, int64_t m, int64_t k, int64_t l
                               const float* bias, int64_t act_from, uint16_t* y, int64_t ldy,
                               hipStream_t stream) {
   const int af = static_cast<int>(act_from);
-  if (bias != nullptr || act_from < n)
-    return launch_ks<9, true>(x, m, k, ldx, p, n, ldp, s, bias, af, y, ldy, stream);
-  return launch_ks<9, false>(x, m, k, ldx, p, n, ldp, s, nullptr, af, y, ldy, stream);
+  const bool epi = bias != nullptr || act_from < n;
+  switch (ksplit_channels_per_tile(m, k, n)) {
+    case 96:
+      if (epi) return launch_ks<6, true>(x, m, k, ldx, p, n, ldp, s, bias, af, y, ldy, stream);
+      return launch_ks<6, false>(x, m, k, ldx, p, n, ldp, s, nullptr, af, y, ldy, stream);
+    case 144:
+      if (epi) return launch_ks<9, true>(x, m, k, ldx, p, n, ldp, s, bias, af, y, ldy, stream);
+      return launch_ks<9, false>(x, m, k, ldx, p, n, ldp, s, nullptr, af, y, ldy, stream);
+    case 192:
+      if (epi) return launch_ks<12, true>(x, m, k, ldx, p, n, ldp, s, bias, af, y, ldy, stream);
+      return launch_ks<12, false>(x, m, k, ldx, p, n, ldp, s, nullptr, af, y, ldy, stream);
+    default:
+      return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace tern

@@ -200,12 +200,16 @@ GEMM_SHAPES = [
     # live slot)
     (5, 8448, 100), (31, 4352, 70), (10, 4352, 21504), (17, 4160, 21512),
     (3, 6400, 16400), (7, 6400, 6150),
-    # K-split kernel (128-256 tiles of 64 x 144, k >= 1024): ragged m and n (n
-    # ending inside a 4-channel group), 17 and 25 K steps over four waves (a
-    # wave with one step more than the others, and steps on zeros after the
-    # last), a DiT down-projection-like layer with 256 whole tiles, and the
-    # fewest tiles that take it
-    (1000, 1088, 1700), (1300, 1600, 1702), (2048, 1024, 1152), (640, 1216, 1880),
+    # K-split kernel (at most 256 tiles of 64 tokens x 96, 144 or 192
+    # channels, k >= 2048): ragged m and n (n ending inside a 4-channel group),
+    # 33 and 41 K steps over four waves (a wave with one step more than the
+    # others, and steps on zeros after the last), a DiT down-projection-like
+    # layer with 256 whole tiles of 144 channels, and tiles of 96 and 192
+    # channels
+    (1000, 2112, 1700), (1300, 2624, 1702), (2048, 2048, 1152), (640, 2112, 1880),
+    (100, 2112, 1002), (200, 2624, 10002),
+    # k just below the K-split bound: 64 x 128 tiles
+    (640, 1984, 1880),
 ]
 
 
@@ -244,7 +248,7 @@ def test_gemm_ksplit_strided_unaligned():
     # The K-split kernel with padded rows of X (NaN past k) and of the packed
     # weights (codes that would decode as -2 past k), a scale vector that is
     # not 16-byte aligned and an output whose rows do not allow 8-byte stores.
-    m, k, n = 1000, 1152, 1700
+    m, k, n = 1000, 2112, 1700
     log(f"gemm ksplit strided m={m} k={k} n={n}")
     x, w = tern_inputs.draw(m, k, n, seed=4242)
     t_ref, s_ref, p_ref = oracle_weights(w)
@@ -265,6 +269,21 @@ def test_gemm_ksplit_strided_unaligned():
     xb = tern_inputs.bf16_bits(x)
     y_ref = oracle.oracle_gemm(xb, p_ref, s_ref, k=k)
     assert_within_tolerance(yh[:, 1:n + 1], y_ref, s_ref, row_norms(xb), "ksplit strided")
+
+
+@pytest.mark.parametrize("m", [64, 128])
+def test_gemm_ksplit_wide_weight(m):
+    # 64 and 128 tokens on the single-stream in-projection weight (21504 x
+    # 3072), the K-split kernel's 96- and 192-channel tiles at full size: every
+    # row at an MFMA-block edge and sampled rows across all columns, every
+    # column at a tile edge across all rows; repeated runs identical.
+    k, n = 3072, 21504
+    log(f"gemm ksplit wide weight m={m} k={k} n={n}")
+    x, w = tern_inputs.draw(m, k, n, seed=5100 + m)
+    rows = edge_indices(m, extra=8, seed=m)
+    cols = edge_indices(n, tile=96 if m == 64 else 192, extra=64, seed=m + 1)
+    worst = check_layer(x, w, f"ksplit wide m={m}", rows=rows, cols=cols, repeat_check=True)
+    log(f"  ok, worst error / bound = {worst:.3f}")
 
 
 def test_gemm_k_zero_writes_zeros():
@@ -318,7 +337,8 @@ EPI_SHAPES = [
     (300, 320, 520), (513, 192, 700),                  # 64 x 128 tiles
     (1100, 128, 7500),                                 # 64 x 256 tiles
     (1024, 192, 9216),                                 # 64 x 576 tiles
-    (1000, 1088, 1700),                                # K-split (act_from inside a 4-channel group)
+    (1000, 2112, 1700),                                # K-split (act_from inside a 4-channel group)
+    (100, 2112, 1002), (200, 2112, 10002),             # K-split, 96- and 192-channel tiles
 ]
 
 
