@@ -731,6 +731,20 @@ def test_gemm_ex_few_tokens_ragged_activation_boundary(m, k, n, act_from):
                    f"ex few tokens m={m} n={n} from {act_from}", full=True)
 
 
+@pytest.mark.parametrize("m,k", [(24, 3072), (10, 4352)])
+def test_gemm_ex_few_tokens_wide_weight_looping(m, k):
+    # The few-token kernel's looping form with six channel blocks per
+    # workgroup and the fused epilogue, on the single-stream in-projection
+    # width with bias and GELU on its MLP columns: two MFMA row blocks over 12
+    # chunks on 8 waves (24 tokens), one row block over 17 chunks on 16 waves
+    # (10 tokens); every element.
+    n = 21504
+    log(f"gemm_ex few looping m={m} k={k} n={n}")
+    x, w = tern_inputs.draw(m, k, n, seed=m * 7 + k, x_dist="student_t3")
+    check_layer_ex(x, w, _bias(n, m), tern.TERN_ACT_GELU_TANH, 9216,
+                   f"ex few looping m={m} k={k}", full=True)
+
+
 @pytest.mark.parametrize("layer", ["dit.up.m2048", "flux_qkv", "flux_mlp.up"])
 def test_workload_dx(layer):
     # the input gradients of the layers at full size: every weight and the
