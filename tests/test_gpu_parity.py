@@ -208,6 +208,9 @@ GEMM_SHAPES = [
     # channels
     (1000, 2112, 1700), (1300, 2624, 1702), (2048, 2048, 1152), (640, 2112, 1880),
     (100, 2112, 1002), (200, 2624, 10002),
+    # K-split with one tile of 5 and of 1 channels (a single 4-channel group,
+    # partly or mostly past n), 32 and 40 K steps
+    (40, 2048, 5), (70, 2560, 1),
     # k just below the K-split bound: 64 x 128 tiles
     (640, 1984, 1880),
 ]
