@@ -23,7 +23,8 @@ After the timed steps:
   * "sweep": tern_gemm at M = 1, 8, 16, 32, 64, 128, 256 tokens on the
     16.5 MB packed in-projection weight [21504, 3072], cycling a pool of
     distinct weights larger than every cache (the crossover from the HBM to
-    the matrix-core bound);
+    the matrix-core bound); "sweep_reference": in the same setting, an almost
+    empty launch and a device copy of each packed weight (per-launch floors);
   * "rows": tern_gemm on every layer shape of the five workloads, and
     tern_gemm_ex with the bias and GELU of the layers that have them;
   * "dx_rows": the input gradient (tern_gemm_dx, tern_pack_transposed) on the
@@ -370,9 +371,31 @@ def time_sweep(tern, torch, dev, replays, pool_mib, ms=(1, 8, 16, 32, 64, 128, 2
               f"({row['pct_hbm']:.1f}% of HBM peak), {row['tflops']:.0f} TFLOP/s, "
               f"{row['pct_roofline']:.1f}% of roofline ({row['bound']})", file=sys.stderr,
               flush=True)
+    ref = sweep_reference(torch, dev, operands, replays)
+    print(f"# sweep reference: an almost empty launch {ref['empty_launch_us']:.2f} us; a device "
+          f"copy of the 16.5 MB weight {ref['weight_copy_us']:.2f} us per launch "
+          f"({ref['weight_copy_gbs']:.0f} GB/s read + written)", file=sys.stderr, flush=True)
     del operands
     torch.cuda.empty_cache()
-    return rows
+    return rows, ref
+
+
+def sweep_reference(torch, dev, operands, replays):
+    """Per-launch floors in the sweep's setting (graph replays over the same
+    pool of packed weights): an almost empty launch (a one-element add) and a
+    device copy of each packed weight into one buffer (torch's copy kernel,
+    the weight's bytes read and written once)."""
+    tiny = torch.zeros(1, device=dev)
+    t_empty, _ = time_graph(torch, lambda: tiny.add_(1), len(operands), replays)
+    dst = torch.empty_like(operands[0][0])
+
+    def copy(p_i, s_i):
+        dst.copy_(p_i)
+
+    t_copy, _ = time_graph(torch, Cycler(copy, operands), len(operands), replays)
+    byts = operands[0][0].numel()
+    return {"empty_launch_us": t_empty * 1e6, "weight_copy_us": t_copy * 1e6,
+            "weight_bytes": byts, "weight_copy_gbs": 2 * byts / t_copy / 1e9}
 
 
 def time_config3(tern, tern_inputs, torch, dev, replays):
@@ -810,7 +833,8 @@ def main():
         out_tables["config3"] = time_config3(tern, tern_inputs, torch, dev, args.replays)
     if "sweep" in tables:
         print("# timing the few-token sweep on the 16.5 MB weight", file=sys.stderr, flush=True)
-        out_tables["sweep"] = time_sweep(tern, torch, dev, args.replays, args.pool_mib)
+        out_tables["sweep"], out_tables["sweep_reference"] = time_sweep(
+            tern, torch, dev, args.replays, args.pool_mib)
     if "fwd" in tables:
         print("# timing tern_gemm on every layer shape", file=sys.stderr, flush=True)
         out_tables["rows"] = time_rows(tern, tern_inputs, torch, dev, args.row_reps,
